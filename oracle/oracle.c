@@ -1,0 +1,324 @@
+/*
+ * oracle.c -- plain, slow, obviously correct CPU reference for the
+ * memory-bound transformer ops: RMSNorm, fused add+RMSNorm, RoPE, fused
+ * RMSNorm+RoPE (QK-norm), SiLU-mul, add, embedding gather, greedy argmax.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The product library never links, loads or calls
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg do.  It shares no source with the HIP kernels.
+ *
+ * Sources (web pages; sections named, never line numbers):
+ *   [OPS]  "Operations" (glia runtime op spec): 2 Normalization / RmsNorm;
+ *          3 Position encoding / Rope; 4 Activation / Silu, SwiGlu;
+ *          5 Attention / QK-norm; 8 Sampling / Greedy; 10 Fused ops.
+ *   [ELT]  "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding,
+ *          add, argmax": 2.1 RMSNorm; 2.2 RoPE; 2.3 SiLU-mul (SwiGLU);
+ *          2.4 Embedding, add, argmax; 4 The interface.
+ *
+ * Arithmetic: every input is widened exactly to f64; all math is IEEE f64
+ * with libm sqrt/exp/sin/cos; every stored output is rounded once (RNE),
+ * straight from f64 to the storage type.  Build with
+ * -O2 -fno-fast-math -ffp-contract=off so that no fused multiply-add or
+ * reassociation changes what is written here.  Rows (tokens) are
+ * independent, so the OpenMP loops change no result.
+ *
+ * Parity: every function is pinned by the CPU tests (worked examples of
+ * [ELT] section 3, closed forms, invariants, brute force, library routines,
+ * and the mutants of [ELT] section 5).  No function here is parity unpinned.
+ */
+#include "oracle.h"
+
+#include <float.h>
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int orc_get_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ---------------------------------------------------------------- storage */
+
+/* Widen element i of a dt-typed array to f64 (exact for f32 and bf16). */
+static double ld(int dt, const void* p, int64_t i) {
+    if (dt == ORC_BF16) {
+        uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float*)p)[i];
+}
+
+/* Round-to-nearest-even from f64 straight to bfloat16 (8 significant bits,
+ * the exponent range of f32).  A value in binade e (2^e <= |v| < 2^(e+1))
+ * is rounded to a multiple of 2^(e-7); below 2^-126 the spacing stays 2^-133
+ * (bf16 subnormals).  Results of magnitude 2^128 or more are infinite. */
+uint16_t orc_bf16_from_f64(double v) {
+    if (isnan(v)) return signbit(v) ? 0xFFC0u : 0x7FC0u;
+    if (isinf(v)) return signbit(v) ? 0xFF80u : 0x7F80u;
+    if (v == 0.0) return signbit(v) ? 0x8000u : 0x0000u;
+    int e;
+    frexp(v, &e);                 /* |v| = m * 2^e with 0.5 <= m < 1 */
+    int binade = e - 1;
+    if (binade < -126) binade = -126;
+    const double q = ldexp(1.0, binade - 7);
+    const double r = nearbyint(v / q) * q;   /* ties to even (default mode) */
+    const float f = (float)r;                /* exact, or +-inf past 2^128 */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* Store v into element i, rounded once to the storage type. */
+static void st(int dt, void* p, int64_t i, double v) {
+    if (dt == ORC_BF16)
+        ((uint16_t*)p)[i] = orc_bf16_from_f64(v);
+    else
+        ((float*)p)[i] = (float)v;           /* C conversion: RNE */
+}
+
+/* Quiet NaN in the storage type (the row an out-of-range id produces). */
+static void st_nan(int dt, void* p, int64_t i) {
+    if (dt == ORC_BF16) {
+        ((uint16_t*)p)[i] = 0x7FC0u;
+    } else {
+        const uint32_t u = 0x7FC00000u;
+        memcpy((float*)p + i, &u, sizeof u);
+    }
+}
+
+static double* row_buffer(int64_t n) {
+    double* b = (double*)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    if (!b) abort();
+    return b;
+}
+
+/* ---------------------------------------------------------------- RMSNorm */
+
+/* [OPS] RmsNorm; [ELT] 2.1: y_i = x_i / sqrt(mean(x^2) + eps) * w_i, with eps
+ * inside the root and the mean taken over the row's d entries.  The row is
+ * given in f64 and normalised in place. */
+static void normalize_row(double* v, int64_t d, int dt, const void* w,
+                          float eps) {
+    double ss = 0.0;
+    for (int64_t i = 0; i < d; ++i) ss += v[i] * v[i];
+    const double ms = ss / (double)d;
+    const double inv = 1.0 / sqrt(ms + (double)eps);
+    for (int64_t i = 0; i < d; ++i) v[i] = v[i] * inv * ld(dt, w, i);
+}
+
+void orc_rmsnorm(int dt, const void* x, const void* w, int64_t rows,
+                 int64_t d, float eps, double* y64, void* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double* v = row_buffer(d);
+        for (int64_t i = 0; i < d; ++i) v[i] = ld(dt, x, r * d + i);
+        normalize_row(v, d, dt, w, eps);
+        for (int64_t i = 0; i < d; ++i) {
+            if (y64) y64[r * d + i] = v[i];
+            if (y) st(dt, y, r * d + i, v[i]);
+        }
+        free(v);
+    }
+}
+
+/* [OPS] 10 Fused ops, FusedSkipNorm: h = x + skip (the stored sum, rounded to
+ * the storage type) and y = RmsNorm(h); both are returned.  y is the unfused
+ * composition, so it normalises h as stored. */
+void orc_add_rmsnorm(int dt, const void* x, const void* res, const void* w,
+                     int64_t rows, int64_t d, float eps, double* y64, void* y,
+                     void* h) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double* v = row_buffer(d);
+        for (int64_t i = 0; i < d; ++i) {
+            const double hv = ld(dt, x, r * d + i) + ld(dt, res, r * d + i);
+            st(dt, h, r * d + i, hv);
+        }
+        for (int64_t i = 0; i < d; ++i) v[i] = ld(dt, h, r * d + i);
+        normalize_row(v, d, dt, w, eps);
+        for (int64_t i = 0; i < d; ++i) {
+            if (y64) y64[r * d + i] = v[i];
+            if (y) st(dt, y, r * d + i, v[i]);
+        }
+        free(v);
+    }
+}
+
+/* ------------------------------------------------------------------- RoPE */
+
+/* [ELT] 2.2: the angle of pair i at token t is p_t * w_i formed once in f64
+ * and rounded to f32 (equal to f32(p) * f32(w) whenever |p| < 2^24). */
+float orc_rope_angle(int32_t p, float w) {
+    return (float)((double)p * (double)w);
+}
+
+/* [ELT] 2.2: which two entries of a head form pair i.  Layout 0 ("half")
+ * pairs (x_i, x_{i+r/2}); layout 1 ("interleaved") pairs (x_2i, x_2i+1). */
+static void rope_pair(int layout, int64_t r, int64_t i, int64_t* ia,
+                      int64_t* ib) {
+    if (layout == 0) {
+        *ia = i;
+        *ib = i + r / 2;
+    } else {
+        *ia = 2 * i;
+        *ib = 2 * i + 1;
+    }
+}
+
+/* [ELT] 2.2 and [OPS] Rope: rotate the first r entries of each of the H head
+ * rows of one token (f64, rows[h*D + j]) in place:
+ *   a' = mu (a cos t - b sin t),  b' = mu (a sin t + b cos t),
+ * reading both members before writing either; entries r..D-1 are untouched.
+ * Loop order token, pair, head: one angle serves every head. */
+static void rope_token(double* rows, int64_t H, int64_t D, int64_t r,
+                       int32_t p, const float* inv_freq, float mu_f,
+                       int layout) {
+    const int64_t rr = r;
+    const double mu = (double)mu_f;
+    for (int64_t i = 0; i < rr / 2; ++i) {
+        const double ang = (double)orc_rope_angle(p, inv_freq[i]);
+        const double c = cos(ang);
+        const double s = sin(ang);
+        int64_t ia, ib;
+        rope_pair(layout, rr, i, &ia, &ib);
+        for (int64_t h = 0; h < H; ++h) {
+            double* v = rows + h * D;
+            const double a = v[ia];
+            const double b = v[ib];
+            const double an = mu * (a * c - b * s);
+            const double bn = mu * (a * s + b * c);
+            v[ia] = an;
+            v[ib] = bn;
+        }
+    }
+}
+
+/* In place on x [T, H, D]; only the first r entries of each head are
+ * written.  y64 (optional) receives all D entries (the tail as given). */
+void orc_rope(int dt, void* x, const int32_t* pos, int64_t T, int64_t H,
+              int64_t D, int64_t r, const float* inv_freq, float mu,
+              int layout, double* y64) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t base = t * H * D;
+        double* v = row_buffer(H * D);
+        for (int64_t j = 0; j < H * D; ++j) v[j] = ld(dt, x, base + j);
+        rope_token(v, H, D, r, pos[t], inv_freq, mu, layout);
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t j = 0; j < D; ++j) {
+                if (j < r) st(dt, x, base + h * D + j, v[h * D + j]);
+                if (y64) y64[base + h * D + j] = v[h * D + j];
+            }
+        free(v);
+    }
+}
+
+/* [OPS] 5 QK-norm: per (token, head) row of length D, RmsNorm over all D
+ * entries with the per-head gain g [D], then Rope on the normalised row.  The
+ * intermediate stays in f64; every entry is rounded once at the end. */
+void orc_rmsnorm_rope(int dt, void* x, const void* g, float eps,
+                      const int32_t* pos, int64_t T, int64_t H, int64_t D,
+                      int64_t r, const float* inv_freq, float mu, int layout,
+                      double* y64) {
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t base = t * H * D;
+        double* v = row_buffer(H * D);
+        for (int64_t j = 0; j < H * D; ++j) v[j] = ld(dt, x, base + j);
+        for (int64_t h = 0; h < H; ++h) normalize_row(v + h * D, D, dt, g, eps);
+        rope_token(v, H, D, r, pos[t], inv_freq, mu, layout);
+        for (int64_t j = 0; j < H * D; ++j) {
+            st(dt, x, base + j, v[j]);
+            if (y64) y64[base + j] = v[j];
+        }
+        free(v);
+    }
+}
+
+/* --------------------------------------------------------------- SiLU-mul */
+
+/* [ELT] 2.3 and [OPS] Silu, SwiGlu: y = g / (1 + e^-g) * u.  The page's
+ * single-precision exponential overflows to +inf once e^-g passes the f32
+ * range, giving g / inf = -0 for very negative g; the f64 value is taken to
+ * +inf at the same point so that limit is kept. */
+void orc_silu_mul(int dt, const void* gate, const void* up, int64_t n,
+                  double* y64, void* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        const double gv = ld(dt, gate, i);
+        const double u = ld(dt, up, i);
+        double e = exp(-gv);
+        if (e > FLT_MAX) e = INFINITY;
+        const double s = gv / (1.0 + e);
+        const double v = s * u;
+        if (y64) y64[i] = v;
+        if (y) st(dt, y, i, v);
+    }
+}
+
+/* ------------------------------------------------------------ add, gather */
+
+/* [ELT] 2.4 and [OPS] Add: y = a + b, the exact sum rounded once. */
+void orc_add(int dt, const void* a, const void* b, int64_t n, void* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        st(dt, y, i, ld(dt, a, i) + ld(dt, b, i));
+}
+
+/* [ELT] 2.4 and [OPS] TokenEmbed: out[t, :] = table[ids[t], :], the source
+ * row starting at element ids[t] * d; a bit copy.  An id outside [0, V) gives
+ * a row of quiet NaN (the kernels' documented behaviour for bad ids). */
+void orc_embedding(int dt, const void* table, int64_t V, const int32_t* ids,
+                   int64_t n, int64_t d, void* out) {
+    const size_t es = (dt == ORC_BF16) ? 2 : 4;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n; ++t) {
+        char* dst = (char*)out + (size_t)t * (size_t)d * es;
+        if (ids[t] < 0 || (int64_t)ids[t] >= V) {
+            for (int64_t j = 0; j < d; ++j) st_nan(dt, out, t * d + j);
+            continue;
+        }
+        const size_t off = (size_t)ids[t] * (size_t)d;
+        memcpy(dst, (const char*)table + off * es, (size_t)d * es);
+    }
+}
+
+/* ----------------------------------------------------------------- argmax */
+
+/* [ELT] 2.4 and [OPS] 8 Sampling, Greedy: scan forward keeping the first
+ * strictly greater value; NaN entries are skipped; -1 when the row holds no
+ * number (empty or all NaN). */
+void orc_argmax(int dt, const void* x, int64_t rows, int64_t n,
+                int32_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int32_t best = -1;
+        double bv = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            const double v = ld(dt, x, r * n + i);
+            if (isnan(v)) continue;
+            if (best < 0 || v > bv) {
+                best = (int32_t)i;
+                bv = v;
+            }
+        }
+        out[r] = best;
+    }
+}

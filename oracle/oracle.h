@@ -1,0 +1,58 @@
+/*
+ * oracle.h -- plain, slow CPU reference for the memory-bound transformer ops.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this code; only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark do.  It shares no source with the HIP kernels.
+ *
+ * Conventions
+ *   dt      storage type of every tensor argument: ORC_F32 (float) or
+ *           ORC_BF16 (uint16_t holding bfloat16 bits).
+ *   y64     optional (may be NULL) f64 buffer receiving the unrounded result
+ *           of each output element; tolerance checks use it.
+ *   All arithmetic is IEEE f64 (libm sqrt/exp/sin/cos); inputs are widened
+ *   exactly; each stored output is rounded once, round-to-nearest-even.
+ */
+#ifndef ET_ORACLE_H
+#define ET_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+
+/* Threads used by the row/element loops (OpenMP); <= 0 leaves the default. */
+void     orc_set_threads(int n);
+int      orc_get_threads(void);
+
+/* f64 -> bfloat16 bits, one round-to-nearest-even (no pass through f32). */
+uint16_t orc_bf16_from_f64(double v);
+/* The RoPE angle of position p and frequency w: the f64 product rounded once
+ * to f32. */
+float    orc_rope_angle(int32_t p, float w);
+
+void orc_rmsnorm(int dt, const void* x, const void* w, int64_t rows, int64_t d,
+                 float eps, double* y64, void* y);
+void orc_add_rmsnorm(int dt, const void* x, const void* res, const void* w,
+                     int64_t rows, int64_t d, float eps, double* y64, void* y,
+                     void* h);
+void orc_rope(int dt, void* x, const int32_t* pos, int64_t T, int64_t H,
+              int64_t D, int64_t r, const float* inv_freq, float mu,
+              int layout, double* y64);
+void orc_rmsnorm_rope(int dt, void* x, const void* g, float eps,
+                      const int32_t* pos, int64_t T, int64_t H, int64_t D,
+                      int64_t r, const float* inv_freq, float mu, int layout,
+                      double* y64);
+void orc_silu_mul(int dt, const void* gate, const void* up, int64_t n,
+                  double* y64, void* y);
+void orc_add(int dt, const void* a, const void* b, int64_t n, void* y);
+void orc_embedding(int dt, const void* table, int64_t V, const int32_t* ids,
+                   int64_t n, int64_t d, void* out);
+void orc_argmax(int dt, const void* x, int64_t rows, int64_t n, int32_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,95 @@
+"""Tiny, independent evaluations used to pin the oracle (pure Python).
+
+Each one reaches the op's result by a different route from ``oracle.c``:
+exact rational sums (``fractions``), complex multiplication (``cmath``), the
+tanh form of the logistic function, rounding by enumeration of neighbours.
+Slow on purpose: only for a few hundred elements.
+"""
+from __future__ import annotations
+
+import cmath
+import math
+import struct
+from fractions import Fraction
+from typing import List, Sequence, Tuple
+
+
+def f32(v: float) -> float:
+    """Round a Python float to the nearest f32 value (IEEE cast)."""
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def bf16_bits_exact(v) -> int:
+    """bfloat16 bits nearest to the exact value v (Fraction or float), ties to
+    even, found by comparing the two neighbouring bf16 values exactly."""
+    if isinstance(v, float):
+        if math.isnan(v):
+            return 0x7FC0
+        if math.isinf(v):
+            return 0xFF80 if v < 0 else 0x7F80
+        if v == 0.0:
+            return 0x8000 if math.copysign(1.0, v) < 0 else 0
+    v = Fraction(v)
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    if a == 0:
+        return sign
+    # binade e: 2^e <= a < 2^(e+1)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)
+    q = Fraction(2) ** (e - 7)
+    k = a // q                      # lower neighbour = k*q
+    rem = a - k * q
+    if rem * 2 > q or (rem * 2 == q and k % 2 == 1):
+        k += 1
+    val = k * q
+    if val >= Fraction(2) ** 128:
+        return sign | 0x7F80
+    bits = struct.unpack("<I", struct.pack("<f", float(val)))[0] >> 16
+    return sign | bits
+
+
+def rmsnorm_row(x: Sequence[float], w: Sequence[float], eps: float) -> List[float]:
+    """y_i = x_i w_i / sqrt(ss/d + eps) with the sum of squares exact."""
+    d = len(x)
+    ss = sum(Fraction(v) * Fraction(v) for v in x)
+    ms = ss / d + Fraction(f32(eps))
+    root = math.sqrt(ms)
+    return [float(Fraction(xi) * Fraction(wi)) / root for xi, wi in zip(x, w)]
+
+
+def rope_head(v: Sequence[float], pos: int, r: int, inv_freq: Sequence[float],
+              mu: float, layout: int) -> List[float]:
+    """Rotate one head row as complex numbers: (a + ib) mu e^{i theta}, with
+    theta the f32 product f32(p) * f32(w) (exact for |p| < 2^24)."""
+    out = list(v)
+    half = r // 2
+    for i in range(half):
+        if layout == 0:
+            ia, ib = i, i + half
+        else:
+            ia, ib = 2 * i, 2 * i + 1
+        theta = f32(f32(float(pos)) * f32(inv_freq[i]))
+        z = complex(v[ia], v[ib]) * f32(mu) * cmath.exp(1j * theta)
+        out[ia], out[ib] = z.real, z.imag
+    return out
+
+
+def silu_tanh(g: float) -> float:
+    """silu(g) = g * sigmoid(g), evaluated as g (1 + tanh(g/2)) / 2 for g >= 0
+    and as g e^g / (1 + e^g) for g < 0 (where the tanh form cancels)."""
+    if g >= 0:
+        return g * (1.0 + math.tanh(g / 2.0)) / 2.0
+    e = math.exp(g)
+    return g * e / (1.0 + e)
+
+
+def argmax_sorted(x: Sequence[float]) -> int:
+    """Lowest index among the largest non-NaN values, by sorting keys."""
+    keys: List[Tuple[float, int]] = [(-v, i) for i, v in enumerate(x) if not math.isnan(v)]
+    if not keys:
+        return -1
+    keys.sort()
+    return keys[0][1]

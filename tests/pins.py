@@ -1,0 +1,514 @@
+"""Pins that tie the CPU oracle to what the pages and the mathematics fix.
+
+Every pin takes an ``oracle.Oracle`` (the real build, or a mutant build in
+``test_oracle_mutants.py``) and raises ``AssertionError`` when the oracle
+disagrees.  Sources are the two pages the ops come from:
+
+  [OPS]  "Operations" (op spec): RmsNorm, Rope, Silu/SwiGlu, QK-norm,
+         Sampling/Greedy, Fused ops.
+  [ELT]  "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding, add,
+         argmax": sections 2.1-2.4 (definitions), 3 (worked examples, stored in
+         ``golden/worked_examples.txt``), 4 (test catalog), 5 (pitfalls).
+
+A pin never compares the oracle with itself through the same formula: it
+uses printed values, closed forms, invariants, library routines (numpy,
+torch CPU casts and adds) or the brute-force evaluations in ``brute.py``.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from typing import Callable, Dict
+
+import numpy as np
+
+try:
+    from . import brute
+except ImportError:  # imported as a top-level module
+    import brute
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                      "worked_examples.txt")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield json.loads(line)
+
+
+def _f32(a):
+    return np.array([float(v) for v in a], dtype=np.float32)
+
+
+def _bf16(a: np.ndarray) -> np.ndarray:
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _wide(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _pair_index(layout, r, i):
+    return (i, i + r // 2) if layout == 0 else (2 * i, 2 * i + 1)
+
+
+# ----------------------------------------------------------- worked examples
+
+def pin_hand_example(orc):
+    """[ELT] 3 and 4 (hand_example, rmsnorm_eps_is_inside_the_root,
+    argmax_ties_nan_and_empty): printed values."""
+    for case in _golden():
+        op = case["op"]
+        if op == "rmsnorm":
+            x = _f32(case["x"])[None, :]
+            y, y64 = orc.rmsnorm(x, _f32(case["w"]), case["eps"])
+            exp = np.array(case["expect"])
+            assert np.all(np.isfinite(y64)), case["cite"]
+            assert np.max(np.abs(y64[0] - exp)) <= case["tol"], (case["cite"], y64)
+            assert np.max(np.abs(y[0] - exp)) <= case["tol"] + 1e-7, (case["cite"], y)
+        elif op == "rope":
+            x = _f32(case["x"]).reshape(1, 1, case["D"])
+            out, y64 = orc.rope(x, np.array([case["pos"]]), case["r"], _f32(case["inv_freq"]),
+                                case["mu"], case["layout"])
+            exp = np.array(case["expect"])
+            assert np.max(np.abs(y64.ravel() - exp)) <= case["tol"], (case["cite"], y64)
+        elif op == "silu_mul":
+            y, y64 = orc.silu_mul(_f32(case["gate"]), _f32(case["up"]))
+            assert np.max(np.abs(y64 - np.array(case["expect"]))) <= case["tol"], case["cite"]
+        elif op == "argmax":
+            x = _f32(case["x"]).reshape(1, -1)
+            got = int(orc.argmax(x)[0])
+            assert got == case["expect"], (case["cite"], got)
+        else:
+            raise AssertionError(f"unknown golden op {op}")
+
+
+# ---------------------------------------------------------------- bf16 RNE
+
+def pin_bf16_rounding(orc):
+    """Rounding to bf16: agrees with torch's f32->bf16 cast on f32 values and
+    with an exact neighbour search (brute.bf16_bits_exact) on f64 values that
+    f32 cannot hold (no double rounding)."""
+    g = np.random.default_rng(7)
+    vals = np.concatenate([
+        g.standard_normal(2000).astype(np.float32) * np.float32(10.0) ** g.integers(-30, 30, 2000).astype(np.float32),
+        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 2 ** -130, 2 ** -133 * 1.5,
+                  2 ** -149, 3.3895313e38, 3.3961775e38, -3.40282347e38, 0.0, -0.0], dtype=np.float32),
+    ])
+    vals = vals[np.isfinite(vals)]
+    ref = _bf16(vals)
+    for v, rb in zip(vals, ref):
+        got = orc.bf16_from_f64(float(v))
+        assert got == int(rb), (float(v), hex(got), hex(int(rb)))
+    for v in [1.0 + 2 ** -8 + 2 ** -40, 1.0 + 2 ** -8 - 2 ** -40, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8,
+              -(2.0 + 2 ** -7 + 2 ** -45), 2 ** -135 * 1.5, 2 ** -134, 2 ** 128 - 2 ** 119,
+              2 ** 128 - 2 ** 120, 12345.6789, -1e-39]:
+        assert orc.bf16_from_f64(v) == brute.bf16_bits_exact(v), (v, hex(orc.bf16_from_f64(v)))
+    assert orc.bf16_from_f64(float("nan")) & 0x7FFF == 0x7FC0
+    assert orc.bf16_from_f64(float("inf")) == 0x7F80
+    assert orc.bf16_from_f64(-0.0) == 0x8000
+
+
+# ----------------------------------------------------------------- RMSNorm
+
+def pin_rmsnorm_eps_is_inside_the_root(orc):
+    """[ELT] 2.1 and 4; [OPS] RmsNorm: eps inside the root; a zero row is 0,
+    never NaN, in f32 and bf16."""
+    y, y64 = orc.rmsnorm(_f32([1e-3, 1e-3])[None], _f32([1, 1]), 1e-6)
+    assert abs(y64[0, 0] - 0.70710678) < 5e-5, y64       # outside the root: 0.9990
+    for dt in ("f32", "bf16"):
+        x = np.zeros((3, 16), np.float32)
+        x[1] = 1.0
+        w = np.linspace(0.5, 1.5, 16, dtype=np.float32)
+        xs, ws = (x, w) if dt == "f32" else (_bf16(x), _bf16(w))
+        y, y64 = orc.rmsnorm(xs, ws, 1e-5)
+        assert np.all(y64[0] == 0.0) and np.all(y64[2] == 0.0)
+        assert not np.any(np.isnan(y64))
+
+
+def pin_rmsnorm_closed_forms(orc):
+    """[OPS] RmsNorm definition: a constant row c gives c / sqrt(c^2 + eps) w;
+    with eps = 0 the output is scale invariant and mean((y/w)^2) = 1."""
+    for c, eps, d in [(2.0, 1e-5, 7), (0.003, 1e-6, 64), (-5.5, 0.0, 5)]:
+        w = np.linspace(0.5, 1.5, d, dtype=np.float32)
+        _, y64 = orc.rmsnorm(np.full((1, d), c, np.float32), w, eps)
+        c = float(np.float32(c))
+        expect = c / math.sqrt(c * c + float(np.float32(eps))) * w.astype(np.float64)
+        assert np.allclose(y64[0], expect, rtol=1e-14, atol=0), (c, eps, d)
+    g = np.random.default_rng(3)
+    x = g.standard_normal((4, 33)).astype(np.float32)
+    w = g.uniform(0.5, 1.5, 33).astype(np.float32)
+    _, y1 = orc.rmsnorm(x, w, 0.0)
+    _, y2 = orc.rmsnorm(x * np.float32(8.0), w, 0.0)
+    assert np.allclose(y1, y2, rtol=1e-14, atol=0)
+    assert np.allclose(np.mean((y1 / w.astype(np.float64)) ** 2, axis=1), 1.0, rtol=1e-13)
+
+
+def pin_rmsnorm_brute(orc):
+    """Brute force with the exact (Fraction) sum of squares on tiny rows."""
+    g = np.random.default_rng(11)
+    for d in (1, 2, 5, 16, 37):
+        x = g.standard_normal((3, d)).astype(np.float32)
+        w = g.uniform(0.5, 1.5, d).astype(np.float32)
+        _, y64 = orc.rmsnorm(x, w, 1e-5)
+        for r in range(3):
+            ref = brute.rmsnorm_row([float(v) for v in x[r]], [float(v) for v in w], 1e-5)
+            assert np.allclose(y64[r], ref, rtol=1e-13, atol=0), (d, r)
+
+
+def pin_rmsnorm_rows_are_independent_and_in_place(orc):
+    """[ELT] 2.1 and 4: every row alone equals the same row inside a batch of
+    up to 12, bit for bit; y == x in place gives the same bits."""
+    import ctypes
+    g = np.random.default_rng(5)
+    for dt in ("f32", "bf16"):
+        x = g.standard_normal((12, 40)).astype(np.float32) * 3
+        w = g.uniform(0.5, 1.5, 40).astype(np.float32)
+        xs, ws = (x, w) if dt == "f32" else (_bf16(x), _bf16(w))
+        for b in (1, 3, 12):
+            yb, _ = orc.rmsnorm(xs[:b], ws, 1e-5)
+            for r in range(b):
+                y1, _ = orc.rmsnorm(xs[r:r + 1], ws, 1e-5)
+                assert np.array_equal(y1[0].view(np.uint8), yb[r].view(np.uint8)), (dt, b, r)
+        yb, _ = orc.rmsnorm(xs, ws, 1e-5)
+        inplace = xs.copy()
+        p = inplace.ctypes.data_as(ctypes.c_void_p)
+        orc.lib.orc_rmsnorm(0 if dt == "f32" else 1, p, ws.ctypes.data_as(ctypes.c_void_p),
+                            12, 40, ctypes.c_float(1e-5), None, p)
+        assert np.array_equal(inplace.view(np.uint8), yb.view(np.uint8)), dt
+
+
+def pin_add_rmsnorm_is_the_composition(orc):
+    """[OPS] 10 Fused ops (FusedSkipNorm): h = x + skip exactly as the storage
+    type adds (numpy f32 add, torch bf16 add), y = RmsNorm(h as stored) by
+    brute force; in place (y over x, h over skip) gives the same bits."""
+    import ctypes
+    import torch
+    g = np.random.default_rng(9)
+    for dt in ("f32", "bf16"):
+        x = g.standard_normal((5, 24)).astype(np.float32)
+        s = (g.standard_normal((5, 24)) * 1e-2).astype(np.float32)
+        w = g.uniform(0.5, 1.5, 24).astype(np.float32)
+        if dt == "f32":
+            xs, ss, ws = x, s, w
+            h_ref = (x + s)
+            hw = h_ref
+        else:
+            xs, ss, ws = _bf16(x), _bf16(s), _bf16(w)
+            tx = torch.from_numpy(_wide(xs)).to(torch.bfloat16)
+            ts = torch.from_numpy(_wide(ss)).to(torch.bfloat16)
+            h_ref = (tx + ts).view(torch.int16).numpy().view(np.uint16)
+            hw = _wide(h_ref)
+        y, h, y64 = orc.add_rmsnorm(xs, ss, ws, 1e-5)
+        assert np.array_equal(h.view(np.uint8), np.ascontiguousarray(h_ref).view(np.uint8)), dt
+        wv = ws if dt == "f32" else _wide(ws)
+        for r in range(5):
+            ref = brute.rmsnorm_row([float(v) for v in hw[r]], [float(v) for v in wv], 1e-5)
+            assert np.allclose(y64[r], ref, rtol=1e-13, atol=0), (dt, r)
+        xi, si = xs.copy(), ss.copy()
+        px, ps = xi.ctypes.data_as(ctypes.c_void_p), si.ctypes.data_as(ctypes.c_void_p)
+        orc.lib.orc_add_rmsnorm(0 if dt == "f32" else 1, px, ps, ws.ctypes.data_as(ctypes.c_void_p),
+                                5, 24, ctypes.c_float(1e-5), None, px, ps)
+        assert np.array_equal(xi.view(np.uint8), y.view(np.uint8)), dt
+        assert np.array_equal(si.view(np.uint8), h.view(np.uint8)), dt
+
+
+# -------------------------------------------------------------------- RoPE
+
+def pin_rope_angle_is_the_f32_product(orc):
+    """[ELT] 2.2: the angle formed in f64 and rounded to f32 equals
+    f32(p) * f32(w) (numpy's IEEE f32 multiply) for every |p| < 2^24."""
+    g = np.random.default_rng(13)
+    p = g.integers(0, 2 ** 24, 4000)
+    w = np.power(1e4, -g.uniform(0, 1, 4000)).astype(np.float32)
+    for pi, wi in zip(p, w):
+        assert orc.rope_angle(int(pi), float(wi)) == np.float32(pi) * wi, (pi, wi)
+
+
+def pin_rope_interleaved_layout_and_position_zero(orc):
+    """[ELT] 4 (rope_interleaved_layout_and_position_zero) and [OPS] Rope edge
+    cases: the interleaved worked example of [ELT] 3; position 0 is the
+    identity rotation, bit for bit, both layouts."""
+    for case in _golden():
+        if case["op"] == "rope" and case["layout"] == 1:
+            x = _f32(case["x"]).reshape(1, 1, case["D"])
+            _, y64 = orc.rope(x, np.array([case["pos"]]), case["r"], _f32(case["inv_freq"]),
+                              case["mu"], 1)
+            assert np.max(np.abs(y64.ravel() - np.array(case["expect"]))) <= case["tol"], case["cite"]
+    g = np.random.default_rng(17)
+    for dt in ("f32", "bf16"):
+        for layout in (0, 1):
+            x = g.standard_normal((3, 2, 12)).astype(np.float32)
+            xs = x if dt == "f32" else _bf16(x)
+            out, _ = orc.rope(xs, np.zeros(3, np.int32), 8, np.array([1.0, 0.3, 0.1, 0.01, 0.5, 0.5],
+                                                                      np.float32), 1.0, layout)
+            assert np.array_equal(out.view(np.uint8), xs.view(np.uint8)), (dt, layout)
+
+
+def pin_rope_partial_rotary_and_scaling(orc):
+    """[ELT] 4 (rope_partial_rotary_and_scaling): the tail past r is untouched,
+    mu = 2 doubles each pair, and [T, H, D] indexing (each head row equals the
+    same row rotated alone with its token's position)."""
+    g = np.random.default_rng(19)
+    T, H, D, r = 4, 3, 10, 6
+    inv = np.array([1.0, 0.1, 0.01, 7.0, 7.0], np.float32)     # r/2 used, rest unused
+    pos = np.array([3, 0, 11, 250], np.int32)
+    for dt in ("f32", "bf16"):
+        for layout in (0, 1):
+            x = g.standard_normal((T, H, D)).astype(np.float32)
+            xs = x if dt == "f32" else _bf16(x)
+            out1, y1 = orc.rope(xs, pos, r, inv, 1.0, layout)
+            out2, y2 = orc.rope(xs, pos, r, inv, 2.0, layout)
+            assert np.array_equal(out1[..., r:].view(np.uint8), xs[..., r:].view(np.uint8))
+            assert np.array_equal(out2[..., r:].view(np.uint8), xs[..., r:].view(np.uint8))
+            xw = (xs if dt == "f32" else _wide(xs)).astype(np.float64)
+            assert np.array_equal(y1[..., r:], xw[..., r:]) and np.array_equal(y2[..., r:], xw[..., r:])
+            assert np.allclose(y2[..., :r], 2.0 * y1[..., :r], rtol=1e-15, atol=0)
+            for t in range(T):
+                for h in range(H):
+                    _, ys = orc.rope(np.ascontiguousarray(xs[t:t + 1, h:h + 1]), pos[t:t + 1], r, inv,
+                                     1.0, layout)
+                    assert np.array_equal(ys[0, 0], y1[t, h]), (dt, layout, t, h)
+
+
+def pin_rope_is_a_rotation(orc):
+    """[ELT] 2.2 and 4 (rope_is_a_rotation): every pair keeps its length times
+    mu, for random shapes, positions and both layouts."""
+    g = np.random.default_rng(23)
+    for _ in range(12):
+        T, H = int(g.integers(1, 5)), int(g.integers(1, 4))
+        half = int(g.integers(1, 9))
+        r = 2 * half
+        D = r + int(g.integers(0, 5))
+        layout = int(g.integers(0, 2))
+        mu = float(np.float32(g.uniform(0.5, 2.0)))
+        x = g.standard_normal((T, H, D)).astype(np.float32)
+        pos = g.integers(0, 100000, T).astype(np.int32)
+        inv = np.power(1e4, -np.arange(max(half, D // 2)) / half).astype(np.float32)
+        _, y = orc.rope(x, pos, r, inv, mu, layout)
+        for i in range(half):
+            ia, ib = _pair_index(layout, r, i)
+            n0 = np.hypot(x[..., ia].astype(np.float64), x[..., ib].astype(np.float64))
+            n1 = np.hypot(y[..., ia], y[..., ib])
+            assert np.allclose(n1, mu * n0, rtol=1e-13, atol=0), (T, H, D, r, layout, i)
+
+
+def pin_rope_layouts_are_a_permutation(orc):
+    """[ELT] 2.2: both layouts are the same rotation on a permuted vector:
+    interleaved(P x) = P half(x), P sending i -> 2i and i + r/2 -> 2i + 1."""
+    g = np.random.default_rng(29)
+    T, H, D, r = 3, 2, 12, 8
+    x = g.standard_normal((T, H, D)).astype(np.float32)
+    pos = np.array([5, 77, 1234], np.int32)
+    inv = np.array([1.0, 0.2, 0.03, 0.004, 9.0, 9.0], np.float32)
+    perm = np.arange(D)
+    for i in range(r // 2):
+        perm[2 * i], perm[2 * i + 1] = i, i + r // 2        # (P x)[2i] = x[i]
+    half, _ = orc.rope(x, pos, r, inv, 1.0, 0)
+    inter, _ = orc.rope(np.ascontiguousarray(x[..., perm]), pos, r, inv, 1.0, 1)
+    assert np.array_equal(inter.view(np.uint8), np.ascontiguousarray(half[..., perm]).view(np.uint8))
+
+
+def pin_rope_brute_complex(orc):
+    """Brute force: each pair as a complex number times mu e^{i theta}, with
+    theta = f32(p) f32(w); both layouts, partial width, mu != 1."""
+    g = np.random.default_rng(31)
+    for layout in (0, 1):
+        T, H, D, r = 3, 2, 14, 10
+        mu = float(np.float32(1.1))
+        x = g.standard_normal((T, H, D)).astype(np.float32)
+        pos = np.array([0, 1, 1048575], np.int32)
+        inv = np.power(np.float64(1e4), -2.0 * np.arange(D // 2) / r).astype(np.float32)
+        _, y = orc.rope(x, pos, r, inv, mu, layout)
+        for t in range(T):
+            for h in range(H):
+                ref = brute.rope_head([float(v) for v in x[t, h]], int(pos[t]), r, inv, mu, layout)
+                nrm = float(np.linalg.norm(x[t, h].astype(np.float64)))
+                assert np.max(np.abs(y[t, h] - np.array(ref))) <= 1e-13 * nrm, (layout, t, h)
+
+
+def pin_rope_relative_position(orc):
+    """[ELT] 2.2: the score of a rotated query and key depends only on the
+    position difference (up to the f32 rounding of each angle)."""
+    g = np.random.default_rng(37)
+    D = r = 16
+    q = g.standard_normal((1, 1, D)).astype(np.float32)
+    k = g.standard_normal((1, 1, D)).astype(np.float32)
+    inv = np.power(np.float64(1e4), -2.0 * np.arange(r // 2) / r).astype(np.float32)
+    for layout in (0, 1):
+        scores = []
+        for pq, pk in [(5, 2), (13, 10), (103, 100), (3, 0)]:
+            _, qy = orc.rope(q, np.array([pq], np.int32), r, inv, 1.0, layout)
+            _, ky = orc.rope(k, np.array([pk], np.int32), r, inv, 1.0, layout)
+            scores.append(float(np.dot(qy.ravel(), ky.ravel())))
+        nq, nk = np.linalg.norm(q.astype(np.float64)), np.linalg.norm(k.astype(np.float64))
+        assert max(scores) - min(scores) <= 1e-5 * nq * nk, (layout, scores)
+
+
+# ------------------------------------------------------ fused RMSNorm+RoPE
+
+def pin_qknorm_per_head_then_rope(orc):
+    """[OPS] 5 QK-norm: RmsNorm per head over head_dim (not over heads x
+    head_dim) with a [head_dim] gain, then Rope; brute force per head."""
+    g = np.random.default_rng(41)
+    for layout in (0, 1):
+        T, H, D, r = 2, 3, 12, 8
+        x = g.standard_normal((T, H, D)).astype(np.float32)
+        x[:, 1] *= 50.0                       # one loud head must not leak into others
+        gain = g.uniform(0.5, 1.5, D).astype(np.float32)
+        pos = np.array([9, 40000], np.int32)
+        inv = np.power(np.float64(5e5), -2.0 * np.arange(D // 2) / r).astype(np.float32)
+        mu = float(np.float32(1.25))
+        _, y = orc.rmsnorm_rope(x, gain, 1e-6, pos, r, inv, mu, layout)
+        for t in range(T):
+            for h in range(H):
+                n = brute.rmsnorm_row([float(v) for v in x[t, h]], [float(v) for v in gain], 1e-6)
+                ref = brute.rope_head(n, int(pos[t]), r, inv, mu, layout)
+                assert np.allclose(y[t, h], ref, rtol=0, atol=1e-13 * max(1.0, max(map(abs, ref)))), \
+                    (layout, t, h)
+
+
+# ---------------------------------------------------------------- SiLU-mul
+
+def pin_silu_mul_saturates_without_nan(orc):
+    """[ELT] 2.3 and 4 (silu_mul_saturates_without_nan): g = +100 gives g u,
+    g = -100 and -1e4 give -0 u (no NaN), g = 0 gives 0."""
+    gate = np.array([100.0, -100.0, -1e4, 0.0, 1e4, -1e4], np.float32)
+    up = np.array([3.0, 2.0, 5.0, 7.0, -2.0, -3.0], np.float32)
+    for dt in ("f32", "bf16"):
+        gs, us = (gate, up) if dt == "f32" else (_bf16(gate), _bf16(up))
+        y, y64 = orc.silu_mul(gs, us)
+        assert not np.any(np.isnan(y64))
+        gw = (gs if dt == "f32" else _wide(gs)).astype(np.float64)
+        uw = (us if dt == "f32" else _wide(us)).astype(np.float64)
+        assert y64[0] == gw[0] * uw[0] and y64[4] == gw[4] * uw[4]
+        assert y64[1] == 0.0 and math.copysign(1.0, y64[1]) < 0     # -0 * 2
+        assert y64[2] == 0.0 and math.copysign(1.0, y64[2]) < 0     # -0 * 5
+        assert y64[5] == 0.0 and math.copysign(1.0, y64[5]) > 0     # -0 * -3
+        assert y64[3] == 0.0
+
+
+def pin_silu_tanh_identity(orc):
+    """silu(g) = g (1 + tanh(g/2)) / 2, an independent evaluation."""
+    g = np.random.default_rng(43)
+    gate = g.uniform(-30, 30, 500).astype(np.float32)
+    up = g.standard_normal(500).astype(np.float32)
+    _, y64 = orc.silu_mul(gate, up)
+    ref = np.array([brute.silu_tanh(float(a)) * float(b) for a, b in zip(gate, up)])
+    assert np.allclose(y64, ref, rtol=1e-13, atol=1e-300)
+
+
+# ------------------------------------------------------- add, embedding
+
+def pin_add_in_place(orc):
+    """[ELT] 2.4 and 4 (add_in_place): y = a + b is IEEE addition in the
+    storage type (numpy f32 add, torch bf16 add) and works with y == a."""
+    import ctypes
+    import torch
+    g = np.random.default_rng(47)
+    a = (g.standard_normal(999) * 10.0 ** g.integers(-3, 3, 999)).astype(np.float32)
+    b = (g.standard_normal(999) * 10.0 ** g.integers(-3, 3, 999)).astype(np.float32)
+    y = orc.add(a, b)
+    assert np.array_equal(y.view(np.uint32), (a + b).view(np.uint32))
+    ab, bb = _bf16(a), _bf16(b)
+    yb = orc.add(ab, bb)
+    ref = (torch.from_numpy(_wide(ab)).to(torch.bfloat16) + torch.from_numpy(_wide(bb)).to(torch.bfloat16))
+    assert np.array_equal(yb, ref.view(torch.int16).numpy().view(np.uint16))
+    inpl = a.copy()
+    p = inpl.ctypes.data_as(ctypes.c_void_p)
+    orc.lib.orc_add(0, p, b.ctypes.data_as(ctypes.c_void_p), 999, p)
+    assert np.array_equal(inpl.view(np.uint32), y.view(np.uint32))
+
+
+def pin_embedding_gathers_rows(orc):
+    """[ELT] 2.4 and 4 (embedding_gathers_rows): repeated and out-of-order
+    ids copy rows bit for bit (numpy fancy indexing); a bad id gives NaN."""
+    g = np.random.default_rng(53)
+    for dt in ("f32", "bf16"):
+        table = g.standard_normal((9, 5)).astype(np.float32)
+        ts = table if dt == "f32" else _bf16(table)
+        ids = np.array([3, 3, 0, 8, 1, 3, 7, 0], np.int32)
+        out = orc.embedding(ts, ids)
+        assert np.array_equal(out.view(np.uint8), ts[ids].view(np.uint8)), dt
+        bad = orc.embedding(ts, np.array([2, 9, -1], np.int32))
+        wide = bad if dt == "f32" else _wide(bad)
+        assert np.array_equal(bad[0].view(np.uint8), ts[2].view(np.uint8))
+        assert np.all(np.isnan(wide[1])) and np.all(np.isnan(wide[2]))
+
+
+# ------------------------------------------------------------------ argmax
+
+def pin_argmax_ties_nan_and_empty(orc):
+    """[ELT] 2.4 and 4 (argmax_ties_nan_and_empty) and [OPS] Greedy: ties to
+    the lowest index, NaN skipped (also in first place), -1 when no number,
+    all -inf gives 0, -0 ties +0, +inf wins."""
+    nan, inf = float("nan"), float("inf")
+    cases = [([1.0, 5.0, 5.0, 2.0], 1), ([nan, 1.0, 0.5], 1), ([nan] * 4, -1),
+             ([-inf] * 3, 0), ([-1.0, -0.0, 0.0, -2.0], 1), ([-1.0, 0.0, -0.0], 1),
+             ([1.0, inf, 3.0, inf], 1), ([nan, -inf], 1), ([3.0], 0), ([2.0, nan, 2.0], 0)]
+    for dt in ("f32", "bf16"):
+        for vals, expect in cases:
+            x = _f32(vals)[None]
+            xs = x if dt == "f32" else _bf16(x)
+            assert int(orc.argmax(xs)[0]) == expect, (dt, vals)
+        empty = np.zeros((3, 0), np.float32 if dt == "f32" else np.uint16)
+        assert list(orc.argmax(empty)) == [-1, -1, -1]
+
+
+def pin_argmax_matches_library(orc):
+    """Rows with at least one number: numpy.nanargmax (first occurrence of the
+    maximum) and the sorted-key brute force agree with the oracle."""
+    g = np.random.default_rng(59)
+    x = np.round(g.standard_normal((40, 300)) * 4).astype(np.float32)     # many ties
+    x[g.random((40, 300)) < 0.05] = np.nan
+    x[3, :] = np.nan
+    got = orc.argmax(x)
+    for r in range(40):
+        if np.all(np.isnan(x[r])):
+            assert got[r] == -1
+        else:
+            assert got[r] == np.nanargmax(x[r]), r
+            assert got[r] == brute.argmax_sorted([float(v) for v in x[r]]), r
+    xb = _bf16(x)
+    gotb = orc.argmax(xb)
+    wide = _wide(xb)
+    for r in range(40):
+        expect = -1 if np.all(np.isnan(wide[r])) else int(np.nanargmax(wide[r]))
+        assert gotb[r] == expect, r
+
+
+# ------------------------------------------------------- batch invariance
+
+def pin_batch_invariance(orc):
+    """[ELT] 2.1 (a row's bits never depend on its batch) extended to every
+    row op: rows/tokens computed alone equal the same rows in a batch."""
+    g = np.random.default_rng(61)
+    for dt in ("f32", "bf16"):
+        cvt = (lambda a: a) if dt == "f32" else _bf16
+        x = cvt(g.standard_normal((6, 3, 16)).astype(np.float32))
+        gain = cvt(g.uniform(0.5, 1.5, 16).astype(np.float32))
+        pos = g.integers(0, 5000, 6).astype(np.int32)
+        inv = np.power(np.float64(1e4), -2.0 * np.arange(8) / 16).astype(np.float32)
+        full, _ = orc.rmsnorm_rope(x, gain, 1e-6, pos, 16, inv, 1.0, 0)
+        full_r, _ = orc.rope(x, pos, 16, inv, 1.0, 1)
+        res = cvt(g.standard_normal((6, 48)).astype(np.float32))
+        w48 = cvt(g.uniform(0.5, 1.5, 48).astype(np.float32))
+        yf, hf, _ = orc.add_rmsnorm(x.reshape(6, 48), res, w48, 1e-5)
+        for t in range(6):
+            one, _ = orc.rmsnorm_rope(np.ascontiguousarray(x[t:t + 1]), gain, 1e-6, pos[t:t + 1], 16, inv,
+                                      1.0, 0)
+            assert np.array_equal(one[0].view(np.uint8), full[t].view(np.uint8)), (dt, t)
+            one_r, _ = orc.rope(np.ascontiguousarray(x[t:t + 1]), pos[t:t + 1], 16, inv, 1.0, 1)
+            assert np.array_equal(one_r[0].view(np.uint8), full_r[t].view(np.uint8)), (dt, t)
+            y1, h1, _ = orc.add_rmsnorm(np.ascontiguousarray(x[t].reshape(1, 48)), res[t:t + 1], w48, 1e-5)
+            assert np.array_equal(y1[0].view(np.uint8), yf[t].view(np.uint8)), (dt, t)
+
+
+PINS: Dict[str, Callable] = {name[4:]: fn for name, fn in sorted(globals().items())
+                             if name.startswith("pin_") and callable(fn)}

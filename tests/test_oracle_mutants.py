@@ -1,0 +1,110 @@
+"""Mutation tests of the oracle's pins (CPU only).
+
+Each mutant is a copy of ``oracle/oracle.c`` with one plausible mistake
+planted by text substitution, built into a temporary library.  The pins must
+fail on every mutant.  s01-s15 are the mistakes listed in the Pitfalls table
+(section 5) of "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding,
+add, argmax", each with the test the page says catches it; x01-x10 are further
+slips (a wrong sign, index, dropped term or rounding) in the same code.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+from pins import PINS
+
+SRC = open(oracle.SRC).read()
+
+# name -> (pin the page names as the catcher or None, [(old, new), ...])
+MUTANTS = {
+    "s01_eps_outside_root": ("rmsnorm_eps_is_inside_the_root",
+                             [("1.0 / sqrt(ms + (double)eps)", "1.0 / (sqrt(ms) + (double)eps)")]),
+    "s02_no_division_by_d": ("rmsnorm_eps_is_inside_the_root",
+                             [("const double ms = ss / (double)d;", "const double ms = ss;")]),
+    "s03_no_gain": ("hand_example",
+                    [("v[i] = v[i] * inv * ld(dt, w, i);", "v[i] = v[i] * inv;")]),
+    "s15_accumulator_per_call": ("rmsnorm_rows_are_independent_and_in_place",
+                                 [("    double ss = 0.0;\n", "    static double ss = 0.0;\n")]),
+    "s04_layouts_swapped": ("rope_interleaved_layout_and_position_zero",
+                            [("if (layout == 0) {", "if (layout == 1) {")]),
+    "s05_minus_theta": ("hand_example",
+                        [("const double s = sin(ang);", "const double s = -sin(ang);")]),
+    "s06_b_from_new_a": ("rope_is_a_rotation",
+                         [("mu * (a * s + b * c)", "mu * (an * s + b * c)")]),
+    "s07_rotate_all_D": ("rope_partial_rotary_and_scaling",
+                         [("const int64_t rr = r;", "const int64_t rr = D;")]),
+    "s08_ignore_mu": ("rope_partial_rotary_and_scaling",
+                      [("const double mu = (double)mu_f;", "const double mu = 1.0;")]),
+    "s09_silu_as_sigmoid": ("silu_mul_saturates_without_nan",
+                            [("const double s = gv / (1.0 + e);", "const double s = 1.0 / (1.0 + e);")]),
+    "s10_exp_plus_g": ("silu_mul_saturates_without_nan",
+                       [("double e = exp(-gv);", "double e = exp(gv);")]),
+    "s11_row_at_id_not_id_times_d": ("embedding_gathers_rows",
+                                     [("const size_t off = (size_t)ids[t] * (size_t)d;",
+                                       "const size_t off = (size_t)ids[t];")]),
+    "s12_argmax_ge": ("argmax_ties_nan_and_empty",
+                      [("if (best < 0 || v > bv) {", "if (best < 0 || v >= bv) {")]),
+    "s13_argmax_no_nan_check": ("argmax_ties_nan_and_empty",
+                                [("if (isnan(v)) continue;", "")]),
+    "s14_argmax_zero_for_none": ("argmax_ties_nan_and_empty",
+                                 [("out[r] = best;", "out[r] = best < 0 ? 0 : best;")]),
+    "x01_bf16_truncates": (None, [("nearbyint(v / q) * q", "trunc(v / q) * q")]),
+    "x02_bf16_wrong_precision": (None, [("ldexp(1.0, binade - 7)", "ldexp(1.0, binade - 8)")]),
+    "x03_angle_not_rounded_to_f32": (None, [("const double ang = (double)orc_rope_angle(p, inv_freq[i]);",
+                                            "const double ang = (double)p * (double)inv_freq[i];")]),
+    "x04_fused_norm_of_unrounded_sum": (None, [("for (int64_t i = 0; i < d; ++i) v[i] = ld(dt, h, r * d + i);",
+                                                "for (int64_t i = 0; i < d; ++i) v[i] = ld(dt, x, r * d + i)"
+                                                " + ld(dt, res, r * d + i);")]),
+    "x05_cos_sin_swapped": (None, [("const double c = cos(ang);", "const double c = sin(ang);")]),
+    "x06_silu_no_overflow_limit": (None, [("if (e > FLT_MAX) e = INFINITY;", "")]),
+    "x07_gain_reversed": (None, [("v[i] = v[i] * inv * ld(dt, w, i);", "v[i] = v[i] * inv * ld(dt, w, d - 1 - i);")]),
+    "x08_add_subtracts": (None, [("st(dt, y, i, ld(dt, a, i) + ld(dt, b, i));",
+                                  "st(dt, y, i, ld(dt, a, i) - ld(dt, b, i));")]),
+    "x09_half_pairs_reversed": (None, [("*ib = i + r / 2;", "*ib = r - 1 - i;")]),
+    "x10_rotation_sign": (None, [("mu * (a * c - b * s)", "mu * (a * c + b * s)")]),
+}
+
+
+def _build_mutant(name, subs, tmp):
+    src = SRC
+    for old, new in subs:
+        assert src.count(old) == 1, f"{name}: pattern must occur once: {old!r}"
+        src = src.replace(old, new)
+    path = os.path.join(tmp, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src)
+    lib = os.path.join(tmp, f"lib{name}.so")
+    oracle.build(src=path, out=lib)
+    return oracle.Oracle(lib)
+
+
+@pytest.fixture(scope="module")
+def tmpdir_mut():
+    with tempfile.TemporaryDirectory() as d:
+        yield d
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmpdir_mut):
+    named, subs = MUTANTS[name]
+    m = _build_mutant(name, subs, tmpdir_mut)
+    m.set_threads(1)              # s15's shared accumulator must not race
+    failed = []
+    for pin_name, pin in PINS.items():
+        try:
+            pin(m)
+        except AssertionError:
+            failed.append(pin_name)
+    assert failed, f"mutant {name} survived every pin"
+    if named is not None:
+        assert named in failed, f"{name}: the page's catcher {named} did not fail (failed: {failed})"
+
+
+def test_unmutated_source_passes_every_pin(tmpdir_mut):
+    """Control: the same build route with no substitution passes."""
+    m = _build_mutant("control", [], tmpdir_mut)
+    m.set_threads(1)
+    for pin in PINS.values():
+        pin(m)
