@@ -1,0 +1,290 @@
+"""Benchmark of the memory-bound transformer ops on one MI355X.
+
+One step = one pass of every op on the workload's synthetic inputs:
+embedding gather, residual add, RMSNorm, fused add+RMSNorm, RoPE on Q and K,
+fused RMSNorm+RoPE on Q and K, SiLU-mul and greedy argmax (the ops a workload
+names; workload 2, the default, names them all).  Each op has its own
+buffers, so no op reads what the previous op just wrote (the 256 MB
+Infinity Cache cannot serve an op from its predecessor's output), and one
+step moves far more than 256 MB, so every op starts cold.
+
+Prints ONE JSON line: whole-step throughput in GB/s of algorithmic HBM
+traffic (each input read once, each output written once; in-place RoPE counts
+only rotated entries), per-op GB/s and fraction of the 8 TB/s peak from HIP
+events on the launch stream, rows/s for the fused RMSNorm+RoPE, the roofline
+record of the dominant kernel and the CPU oracle timed on a sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2|3|4|5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0          # MI355X HBM3E peak, vendor figure (8 TB/s)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=2)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="least CPU time spent timing the oracle on whole steps")
+    return p.parse_args()
+
+
+class Op:
+    def __init__(self, name, nbytes, fn, kernel, rows=None):
+        self.name, self.nbytes, self.fn, self.kernel, self.rows = name, nbytes, fn, kernel, rows
+        self.ms = []
+
+
+def build_ops(w, et, torch):
+    """Device buffers and one closure per op, with algorithmic bytes."""
+    import workloads as wl
+    from_np = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+                         if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a))).cuda()
+    es = 2 if w.dtype == "bf16" else 4
+    ops = []
+    if w.embed:
+        V, d, n, _ = w.embed
+        table, ids = wl.gen_embedding(w)
+        tt, it = from_np(table), from_np(ids)
+        out = torch.empty((n, d), dtype=tt.dtype, device="cuda")
+        ops.append(Op("embedding", 2 * n * d * es + 4 * n, lambda: et.embedding(tt, it, out=out),
+                      "embedding_kernel"))
+    if w.add:
+        rows, d = w.add
+        a, b = wl.gen_add(w)
+        at, bt = from_np(a), from_np(b)
+        yt = torch.empty_like(at)
+        ops.append(Op("add", 3 * rows * d * es, lambda: et.add(at, bt, out=yt), "eltwise_vec"))
+    if w.rmsnorm:
+        rows, d, eps = w.rmsnorm
+        x, g, eps = wl.gen_rmsnorm(w)
+        xt, gt = from_np(x), from_np(g)
+        yn = torch.empty_like(xt)
+        ops.append(Op("rmsnorm", 2 * rows * d * es + d * es,
+                      lambda: et.rmsnorm(xt, gt, eps, out=yn), "rmsnorm_rows"))
+    if w.add_rmsnorm:
+        rows, d, eps, in_place = w.add_rmsnorm
+        x, r, g, eps = wl.gen_add_rmsnorm(w)
+        xa, ra, ga = from_np(x), from_np(r), from_np(g)
+        if in_place:
+            fn = lambda: et.add_rmsnorm(xa, ra, ga, eps, out=xa, h=ra)
+        else:
+            ya, ha = torch.empty_like(xa), torch.empty_like(xa)
+            fn = lambda: et.add_rmsnorm(xa, ra, ga, eps, out=ya, h=ha)
+        ops.append(Op("add_rmsnorm", 4 * rows * d * es + d * es, fn, "rmsnorm_rows"))
+    if w.rope:
+        s = w.rope
+        q, k, pos, inv = wl.gen_rope(w)
+        qt, kt, pt, ft = from_np(q), (from_np(k) if k is not None else None), from_np(pos), from_np(inv)
+        heads = s.Hq + s.Hk
+        ops.append(Op("rope", 2 * s.T * heads * s.r * es + 4 * s.T + 4 * (s.r // 2),
+                      lambda: et.rope_qk(qt, kt, pt, ft, d_rot=s.r, attn_scaling=s.mu,
+                                         layout=s.layout), "rope_qk_kernel"))
+        q2, k2, gq, gk, pos2, inv2 = wl.gen_qknorm(w)
+        q2t, k2t = from_np(q2), (from_np(k2) if k2 is not None else None)
+        gqt, gkt = from_np(gq), (from_np(gk) if k2 is not None else None)
+        p2t, f2t = from_np(pos2), from_np(inv2)
+        ops.append(Op("rmsnorm_rope", 2 * s.T * heads * s.D * es + 2 * s.D * es + 4 * s.T
+                      + 4 * (s.r // 2),
+                      lambda: et.rmsnorm_rope_qk(q2t, gqt, k2t, gkt, s.eps, p2t, f2t, d_rot=s.r,
+                                                 attn_scaling=s.mu, layout=s.layout),
+                      "rmsnorm_rope_kernel", rows=s.T * heads))
+    if w.silu:
+        rows, cols, _ = w.silu
+        gate, up = wl.gen_silu(w)
+        gt_, ut = from_np(gate), from_np(up)
+        ys = torch.empty_like(gt_)
+        ops.append(Op("silu_mul", 3 * rows * cols * es, lambda: et.silu_mul(gt_, ut, out=ys),
+                      "eltwise_vec"))
+    if w.argmax:
+        rows, n = w.argmax
+        lg, _ = wl.gen_argmax(w)
+        lt = from_np(lg)
+        ao = torch.empty(rows, dtype=torch.int32, device="cuda")
+        ws = torch.empty(max(1, et.argmax_workspace_bytes(rows, n)), dtype=torch.uint8, device="cuda")
+        ops.append(Op("argmax", rows * n * lt.element_size() + 4 * rows,
+                      lambda: et.argmax(lt, out=ao, workspace=ws), "argmax_chunks"))
+    return ops
+
+
+def traffic_record(op):
+    """Counter-measured HBM bytes per launch for the dominant kernel, from the
+    committed rocprofv3 counter summary, if it was taken on the current
+    kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{op}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"source sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic bytes per launch:\s*([0-9.eE+]+)", text)
+    if not (m_src and m_b):
+        return None
+    src = os.path.join(ROOT, "elementwise_transformer_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(src)):
+        with open(os.path.join(src, f), "rb") as fh:
+            h.update(fh.read())
+    return float(m_b.group(1)) if h.hexdigest() == m_src.group(1) else None
+
+
+def cpu_baseline(w, min_seconds):
+    """The CPU oracle as it stands, timed on whole steps of the same workload
+    (every op at full size), repeated until at least min_seconds of work."""
+    import oracle
+    import workloads as wl
+    orc = oracle.load()
+    calls = []            # (bytes, closure)
+    es = 2 if w.dtype == "bf16" else 4
+    if w.embed:
+        V, d, n, _ = w.embed
+        table, ids = wl.gen_embedding(w)
+        calls.append((2 * n * d * es + 4 * n, lambda: orc.embedding(table, ids)))
+    if w.add:
+        rows, d = w.add
+        a, b = wl.gen_add(w)
+        calls.append((3 * rows * d * es, lambda: orc.add(a, b)))
+    if w.rmsnorm:
+        rows, d, eps = w.rmsnorm
+        x, g, eps1 = wl.gen_rmsnorm(w)
+        calls.append((2 * rows * d * es, lambda: orc.rmsnorm(x, g, eps1)))
+    if w.add_rmsnorm:
+        rows, d, eps, _ = w.add_rmsnorm
+        xa, ra, ga, eps2 = wl.gen_add_rmsnorm(w)
+        calls.append((4 * rows * d * es, lambda: orc.add_rmsnorm(xa, ra, ga, eps2)))
+    if w.rope:
+        s = w.rope
+        q, k, pos, inv = wl.gen_rope(w)
+        def rope_both():
+            orc.rope(q, pos, s.r, inv, s.mu, s.layout)
+            if k is not None:
+                orc.rope(k, pos, s.r, inv, s.mu, s.layout)
+        calls.append((2 * s.T * (s.Hq + s.Hk) * s.r * es, rope_both))
+        q2, k2, gq, gk, pos2, inv2 = wl.gen_qknorm(w)
+        def qk_both():
+            orc.rmsnorm_rope(q2, gq, s.eps, pos2, s.r, inv2, s.mu, s.layout)
+            if k2 is not None:
+                orc.rmsnorm_rope(k2, gk, s.eps, pos2, s.r, inv2, s.mu, s.layout)
+        calls.append((2 * s.T * (s.Hq + s.Hk) * s.D * es, qk_both))
+    if w.silu:
+        rows, cols, _ = w.silu
+        gate, up = wl.gen_silu(w)
+        calls.append((3 * rows * cols * es, lambda: orc.silu_mul(gate, up)))
+    if w.argmax:
+        rows, n = w.argmax
+        lg, _ = wl.gen_argmax(w)
+        calls.append((rows * n * lg.itemsize, lambda: orc.argmax(lg)))
+    step_bytes = sum(b for b, _ in calls)
+    reps, t_total = 0, 0.0
+    while t_total < min_seconds or reps == 0:
+        t0 = time.perf_counter()
+        for _, fn in calls:
+            fn()
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {"value": round(reps * step_bytes / t_total / 1e9, 3), "unit": "GB/s",
+            "cores": orc.threads(), "kind": "oracle", "seconds": round(t_total, 2),
+            "sample": f"{reps} whole steps of the same workload ({step_bytes} algorithmic bytes "
+                      f"each), all ops at full size"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the ops shard by rows with "
+                          "no communication, so per-GPU throughput is the one-GPU figure",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import elementwise_transformer_amd as et
+    import workloads as wl
+
+    w = wl.WORKLOADS[args.workload]
+    ops = build_ops(w, et, torch)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for op in ops:
+            op.fn()
+    torch.cuda.synchronize()
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in ops] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, op in enumerate(ops):
+            evs[s][i][0].record(stream)
+            op.fn()
+            evs[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for s in range(args.steps):
+        for i, op in enumerate(ops):
+            op.ms.append(evs[s][i][0].elapsed_time(evs[s][i][1]))
+
+    step_bytes = sum(op.nbytes for op in ops)
+    ms_step = wall * 1e3 / args.steps
+    per_op = {}
+    for op in ops:
+        avg = float(np.mean(op.ms))
+        med = float(np.median(op.ms))
+        gbps = op.nbytes / (avg * 1e-3) / 1e9
+        rec = {"bytes": op.nbytes, "avg_us": round(avg * 1e3, 2), "median_us": round(med * 1e3, 2),
+               "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_GBPS, 4)}
+        if op.rows:
+            rec["rows_per_s"] = float(f"{op.rows / (avg * 1e-3):.4g}")
+        per_op[op.name] = rec
+    dom = max(ops, key=lambda o: o.nbytes)
+    dom_avg_s = float(np.mean(dom.ms)) * 1e-3
+    achieved = dom.nbytes / dom_avg_s / 1e9
+    roofline = {"bound": "hbm", "kernel": dom.kernel, "op": dom.name, "achieved": round(achieved, 1),
+                "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
+                "traffic": traffic_record(dom.name), "bytes_per_launch": dom.nbytes,
+                "avg_launch_us": round(dom_avg_s * 1e6, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    s = w.rope
+    line = {
+        "metric": "achieved HBM GB/s (% of MI355X peak) per op; rows/s for fused RMSNorm+RoPE",
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "frac_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_GBPS, 4),
+        "config": {"workload": w.name, "storage": w.dtype, "step_bytes": step_bytes,
+                   "ops": [op.name for op in ops],
+                   "T": s.T if s else None, "heads_q": s.Hq if s else None,
+                   "heads_kv": s.Hk if s else None, "head_dim": s.D if s else None,
+                   "hidden": (w.add_rmsnorm or w.rmsnorm or (None, None))[1],
+                   "intermediate": w.silu[1] if w.silu else None,
+                   "vocab": w.embed[0] if w.embed else None},
+        "ops": per_op,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

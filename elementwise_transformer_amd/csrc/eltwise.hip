@@ -1,0 +1,154 @@
+// eltwise.hip -- residual add and SiLU-gated multiply for gfx950.
+//
+// Definitions: "Operations" 1 Add, 4 Activation / Silu, SwiGlu;
+// "Elementwise kernels in C ..." 2.3 SiLU-mul, 2.4 add.
+//   add:      y = a + b
+//   silu_mul: y = g / (1 + exp(-g)) * u   (exp overflows to +inf for very
+//             negative g, making the factor -0 rather than NaN)
+//
+// Design: three streams, each element read once and written once.  Each
+// thread moves kU 16-byte vectors per input, all loads issued before any
+// store (loads are clamped in range rather than guarded, so the compiler
+// keeps them in flight together).  Elements past the last whole vector are
+// done by the last block with scalar accesses.  Misaligned buffers use the
+// scalar kernel.  y may equal a or b: every element is read by the thread
+// that writes it, before it writes it.
+#include "et_common.hpp"
+
+namespace et {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kU = 4;  // vectors per thread per input
+
+enum Op { kAdd = 0, kSiluMul = 1 };
+
+template <int OP>
+__device__ inline float apply(float a, float b) {
+  if constexpr (OP == kAdd) {
+    return a + b;
+  } else {
+    const float e = expf(-a);
+    return a / (1.0f + e) * b;
+  }
+}
+
+template <typename S, int OP>
+__global__ __launch_bounds__(kBlock) void eltwise_vec(const S* a, const S* b, S* y, int64_t nvec,
+                                                      int64_t n) {
+  using E = Elem<S>;
+  constexpr int V = E::V;
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * (kBlock * kU) + threadIdx.x;
+  if (nvec > 0) {
+    u32x4 av[kU], bv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t j = first + u * kBlock;
+      const int64_t jc = j < nvec ? j : nvec - 1;
+      av[u] = ld16(a, jc * V);
+      bv[u] = ld16(b, jc * V);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t j = first + u * kBlock;
+      float o[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) o[e] = apply<OP>(E::get(av[u], e), E::get(bv[u], e));
+      if (j < nvec) st16(y, j * V, E::pack(o));
+    }
+  }
+  // Tail: fewer than V elements after the last whole vector.
+  if (blockIdx.x == gridDim.x - 1) {
+    const int64_t i = nvec * V + threadIdx.x;
+    if (i < n) E::st(y, i, apply<OP>(E::ld(a, i), E::ld(b, i)));
+  }
+}
+
+template <typename S, int OP>
+__global__ __launch_bounds__(kBlock) void eltwise_scalar(const S* a, const S* b, S* y, int64_t n) {
+  using E = Elem<S>;
+  constexpr int kPer = kU * 4;
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * (kBlock * kPer) + threadIdx.x;
+  float av[kPer], bv[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t i = first + u * kBlock;
+    const int64_t ic = i < n ? i : n - 1;
+    av[u] = E::ld(a, ic);
+    bv[u] = E::ld(b, ic);
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t i = first + u * kBlock;
+    if (i < n) E::st(y, i, apply<OP>(av[u], bv[u]));
+  }
+}
+
+template <typename S, int OP>
+et_status eltwise_entry(const S* a, const S* b, S* y, int64_t n, void* stream) {
+  if (n < 0) return ET_ERR_BAD_SIZE;
+  if (n == 0) return ET_OK;
+  int64_t bytes = 0;
+  if (!mul_ok(n, static_cast<int64_t>(sizeof(S)), &bytes)) return ET_ERR_BAD_SIZE;
+  if (!a || !b || !y) return ET_ERR_NULL_POINTER;
+  if (!ranges_ok(y, bytes, a, bytes, true) || !ranges_ok(y, bytes, b, bytes, true))
+    return ET_ERR_OVERLAP;
+  constexpr int V = Elem<S>::V;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (aligned16(a) && aligned16(b) && aligned16(y)) {
+    // Split into launches of at most kMaxGrid blocks; each launch starts on
+    // a vector boundary, only the last one has a tail.
+    const int64_t per_launch = kMaxGrid * kBlock * kU;  // vectors
+    const int64_t nvec_all = n / V;
+    for (int64_t v0 = 0;; v0 += per_launch) {
+      const int64_t nvec = nvec_all - v0 < per_launch ? nvec_all - v0 : per_launch;
+      const bool last = v0 + nvec >= nvec_all;
+      const int64_t elems = last ? n - v0 * V : nvec * V;
+      const int64_t blocks = nvec > 0 ? (nvec + kBlock * kU - 1) / (kBlock * kU) : 1;
+      const int64_t off = v0 * V;
+      eltwise_vec<S, OP><<<static_cast<unsigned>(blocks), kBlock, 0, s>>>(a + off, b + off,
+                                                                          y + off, nvec, elems);
+      if (last) break;
+    }
+  } else {
+    const int64_t per_launch = kMaxGrid * kBlock * kU * 4;
+    for (int64_t i0 = 0; i0 < n; i0 += per_launch) {
+      const int64_t m = n - i0 < per_launch ? n - i0 : per_launch;
+      const int64_t blocks = (m + kBlock * kU * 4 - 1) / (kBlock * kU * 4);
+      eltwise_scalar<S, OP><<<static_cast<unsigned>(blocks), kBlock, 0, s>>>(a + i0, b + i0,
+                                                                             y + i0, m);
+    }
+  }
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace et
+
+using et::Bf16;
+
+extern "C" {
+
+et_status et_add_f32(const float* a, const float* b, float* y, int64_t n, void* stream) {
+  return et::eltwise_entry<float, et::kAdd>(a, b, y, n, stream);
+}
+
+et_status et_add_bf16(const et_bf16* a, const et_bf16* b, et_bf16* y, int64_t n, void* stream) {
+  return et::eltwise_entry<Bf16, et::kAdd>(reinterpret_cast<const Bf16*>(a),
+                                           reinterpret_cast<const Bf16*>(b),
+                                           reinterpret_cast<Bf16*>(y), n, stream);
+}
+
+et_status et_silu_mul_f32(const float* gate, const float* up, float* y, int64_t n, void* stream) {
+  return et::eltwise_entry<float, et::kSiluMul>(gate, up, y, n, stream);
+}
+
+et_status et_silu_mul_bf16(const et_bf16* gate, const et_bf16* up, et_bf16* y, int64_t n,
+                           void* stream) {
+  return et::eltwise_entry<Bf16, et::kSiluMul>(reinterpret_cast<const Bf16*>(gate),
+                                               reinterpret_cast<const Bf16*>(up),
+                                               reinterpret_cast<Bf16*>(y), n, stream);
+}
+
+}  // extern "C"

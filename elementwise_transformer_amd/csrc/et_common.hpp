@@ -1,0 +1,177 @@
+// et_common.hpp -- shared pieces of the gfx950 kernels and their host-side
+// launchers: storage types, 16-byte vector I/O, fixed-order wavefront
+// reductions, exact integer division by run-time constants, and the argument
+// checks every entry point runs before it enqueues anything.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "et.h"
+
+namespace et {
+
+// ---------------------------------------------------------------- storage
+// Kernels are templated on the storage type: float (f32) or Bf16 (raw
+// bfloat16 bits).  Arithmetic is always f32.
+struct Bf16 {
+  uint16_t bits;
+};
+
+// One 16-byte vector as a native clang vector (usable with the nontemporal
+// builtins, unlike HIP's u32x4 struct).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename S>
+struct Elem;
+
+template <>
+struct Elem<float> {
+  static constexpr int V = 4;  // elements per 16-byte vector
+  __device__ static inline float ld(const float* p, int64_t i) { return p[i]; }
+  __device__ static inline void st(float* p, int64_t i, float v) { p[i] = v; }
+  __device__ static inline void unpack(const u32x4& u, float (&f)[4]) {
+    f[0] = __uint_as_float(u.x);
+    f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z);
+    f[3] = __uint_as_float(u.w);
+  }
+  __device__ static inline u32x4 pack(const float (&f)[4]) {
+    return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                 __float_as_uint(f[3])};
+  }
+  __device__ static inline float round(float v) { return v; }  // to storage precision
+  // Element e (compile-time after unrolling) of a packed vector.
+  __device__ static inline float get(const u32x4& u, int e) { return __uint_as_float(u[e]); }
+  static constexpr uint32_t kQuietNaN = 0x7FC00000u;
+};
+
+// bf16 -> f32 is exact (the bf16 bits are the high half of the f32 bits).
+// f32 -> bf16 rounds to nearest even; on gfx950 the conversion below is the
+// hardware v_cvt_pk_bf16_f32.
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ inline uint32_t bf16_pack2(float lo, float hi) {
+  const uint16_t a = __builtin_bit_cast(uint16_t, static_cast<__bf16>(lo));
+  const uint16_t b = __builtin_bit_cast(uint16_t, static_cast<__bf16>(hi));
+  return static_cast<uint32_t>(a) | (static_cast<uint32_t>(b) << 16);
+}
+
+template <>
+struct Elem<Bf16> {
+  static constexpr int V = 8;
+  __device__ static inline float ld(const Bf16* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(p[i].bits) << 16);
+  }
+  __device__ static inline void st(Bf16* p, int64_t i, float v) {
+    p[i].bits = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+  }
+  __device__ static inline void unpack(const u32x4& u, float (&f)[8]) {
+    f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x);
+    f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);
+    f[4] = bf16_lo(u.z); f[5] = bf16_hi(u.z);
+    f[6] = bf16_lo(u.w); f[7] = bf16_hi(u.w);
+  }
+  __device__ static inline u32x4 pack(const float (&f)[8]) {
+    return u32x4{bf16_pack2(f[0], f[1]), bf16_pack2(f[2], f[3]), bf16_pack2(f[4], f[5]),
+                 bf16_pack2(f[6], f[7])};
+  }
+  __device__ static inline float round(float v) {  // to storage precision (RNE)
+    return __uint_as_float(static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v)))
+                           << 16);
+  }
+  __device__ static inline float get(const u32x4& u, int e) {
+    return (e & 1) ? bf16_hi(u[e >> 1]) : bf16_lo(u[e >> 1]);
+  }
+  static constexpr uint32_t kQuietNaN = 0x7FC07FC0u;  // two bf16 quiet NaNs
+};
+
+// 16-byte vector access.  The caller guarantees 16-byte alignment.
+template <typename S>
+__device__ inline u32x4 ld16(const S* p, int64_t elem) {
+  return *reinterpret_cast<const u32x4*>(p + elem);
+}
+template <typename S>
+__device__ inline void st16(S* p, int64_t elem, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p + elem) = v;
+}
+// Streaming variants for data touched exactly once.
+template <typename S>
+__device__ inline u32x4 ld16_stream(const S* p, int64_t elem) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + elem));
+}
+template <typename S>
+__device__ inline void st16_stream(S* p, int64_t elem, const u32x4& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p + elem));
+}
+
+// -------------------------------------------------------- wave reductions
+// Sum over aligned groups of W lanes (W a power of two, W <= 64) by an xor
+// butterfly: step 1, 2, 4, ... W/2.  The tree is fixed, every lane of the
+// group ends with the same bits, and nothing depends on the launch size.
+template <int W>
+__device__ inline float group_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < W; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// ------------------------------------------------- division by constants
+// Exact n / d for 32-bit unsigned n and a run-time divisor d >= 1 fixed for
+// the launch (multiply-high plus shift; Granlund & Montgomery, "Division by
+// invariant integers using multiplication", PLDI 1994).
+struct FastDiv {
+  uint32_t d;
+  uint32_t magic;
+  uint32_t shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t s = 0;
+  while ((uint64_t{1} << s) < d) ++s;  // s = ceil(log2 d)
+  f.shift = s;
+  f.magic = static_cast<uint32_t>(((uint64_t{1} << 32) * ((uint64_t{1} << s) - d)) / d + 1);
+  return f;
+}
+
+__host__ __device__ inline uint32_t fdiv(uint32_t n, const FastDiv& f) {
+#ifdef __HIP_DEVICE_COMPILE__
+  const uint64_t hi = __umulhi(n, f.magic);
+#else
+  const uint64_t hi = (static_cast<uint64_t>(n) * f.magic) >> 32;
+#endif
+  return static_cast<uint32_t>((hi + n) >> f.shift);
+}
+
+// ------------------------------------------------------------ host checks
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a * b with overflow detection; false if negative or overflowing.
+inline bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  return !__builtin_mul_overflow(a, b, out);
+}
+
+// Two byte ranges either coincide exactly (when `may_alias`) or are
+// disjoint.  Empty ranges never overlap.
+inline bool ranges_ok(const void* a, int64_t abytes, const void* b, int64_t bbytes,
+                      bool may_alias) {
+  if (abytes <= 0 || bbytes <= 0 || a == nullptr || b == nullptr) return true;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  const uintptr_t a1 = a0 + static_cast<uintptr_t>(abytes);
+  const uintptr_t b1 = b0 + static_cast<uintptr_t>(bbytes);
+  if (a1 <= b0 || b1 <= a0) return true;
+  return may_alias && a0 == b0 && abytes == bbytes;
+}
+
+inline et_status launch_status() {
+  return hipGetLastError() == hipSuccess ? ET_OK : ET_ERR_HIP;
+}
+
+// Largest grid.x the launchers use per launch; longer work is split.
+constexpr int64_t kMaxGrid = int64_t{1} << 30;
+
+}  // namespace et

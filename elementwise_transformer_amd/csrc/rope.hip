@@ -1,0 +1,569 @@
+// rope.hip -- rotary position embedding (Q and K in one launch) and the
+// fused per-head RMSNorm + RoPE (QK-norm) for gfx950.
+//
+// Definitions: "Operations" 3 Position encoding / Rope and 5 Attention /
+// QK-norm; "Elementwise kernels in C ..." 2.2 RoPE and 4 The interface.
+//   angle of pair i at token t: p_t * w_i formed in f64, rounded to f32
+//   (a, b) -> mu (a cos - b sin, a sin + b cos)
+//   layout 0 (half) pairs (i, i + r/2); layout 1 (interleaved) (2i, 2i+1)
+//   entries r..D-1 pass through (RoPE) or are only normalised (QK-norm).
+//
+// Design (HBM-bound: each rotated element read and written once):
+//   * Work is cut into "slots" of PS pairs of one head row: with 16-byte
+//     vectors PS = V (two vectors: V pairs), else PS = 1 (two scalars).
+//     Both layouts make a slot's pairs i0..i0+PS-1 contiguous in i.
+//   * A workgroup owns kBlock*U consecutive slots (possibly spanning token
+//     boundaries).  It first issues all its loads, then builds a table of
+//     (mu cos, mu sin) for its tokens' pairs in LDS -- one sincosf per
+//     (token, pair), shared by all Hq + Hk heads -- then rotates and stores.
+//   * sincosf is the accurate library routine (full range reduction), since
+//     angles reach ~1e6 rad for positions near 2^20.
+//   * In place: each slot is read and written by one thread, reads first.
+//   * QK-norm: a group of G = D/(2V) lanes owns one head row (two vectors per
+//     lane); the sum of squares is per-lane then an xor butterfly over the G
+//     lanes -- fixed by D, so rows are batch-invariant.  Shapes without that
+//     vector layout use a one-wave-per-row kernel.
+#include "et_common.hpp"
+
+namespace et {
+namespace {
+
+constexpr int kBlock = 256;
+constexpr int kMaxTableBytes = 48 * 1024;
+
+struct RopeArgs {
+  int64_t T;
+  int hq, hk, D, r, half, layout;
+  float mu;
+  uint32_t sph;       // slots per head row
+  uint32_t spt;       // slots per token
+  uint32_t total;     // slots in the call (T * spt)
+  FastDiv fd_spt;     // divide by slots per token
+  FastDiv fd_sph;     // divide by slots per head row
+  FastDiv fd_half;    // divide by r/2
+  int ntok_max;       // tokens one workgroup can touch (table rows)
+};
+
+// Angle of pair i of position p: the f64 product rounded once to f32.
+__device__ inline float rope_angle(int32_t p, float w) {
+  return static_cast<float>(static_cast<double>(p) * static_cast<double>(w));
+}
+
+// Fill cs[tl * half + i] = (mu cos, mu sin) for tokens t0 .. t0 + ntok - 1.
+__device__ inline void fill_table(float2* cs, int64_t t0, int ntok, const RopeArgs& a,
+                                  const int32_t* __restrict__ pos,
+                                  const float* __restrict__ inv_freq) {
+  const uint32_t n = static_cast<uint32_t>(ntok) * a.half;
+  for (uint32_t idx = threadIdx.x; idx < n; idx += kBlock) {
+    const uint32_t tl = fdiv(idx, a.fd_half);
+    const uint32_t i = idx - tl * a.half;
+    float sn, cn;
+    sincosf(rope_angle(pos[t0 + tl], inv_freq[i]), &sn, &cn);
+    cs[idx] = make_float2(a.mu * cn, a.mu * sn);
+  }
+}
+
+// Element offsets (within a head row) of the two halves of slot kk.
+template <int PS>
+__device__ inline void slot_offsets(int kk, const RopeArgs& a, int* ea, int* eb) {
+  if constexpr (PS == 1) {
+    if (a.layout == ET_ROPE_HALF) {
+      *ea = kk;
+      *eb = kk + a.half;
+    } else {
+      *ea = 2 * kk;
+      *eb = 2 * kk + 1;
+    }
+  } else {
+    if (a.layout == ET_ROPE_HALF) {
+      *ea = kk * PS;
+      *eb = kk * PS + a.half;
+    } else {
+      *ea = 2 * kk * PS;
+      *eb = 2 * kk * PS + PS;
+    }
+  }
+}
+
+// Rotate one pair with the pre-scaled (mu cos, mu sin).
+__device__ inline void rotate(float& x0, float& x1, float2 c) {
+  const float a = x0, b = x1;
+  x0 = __builtin_fmaf(a, c.x, -(b * c.y));
+  x1 = __builtin_fmaf(a, c.y, b * c.x);
+}
+
+// ------------------------------------------------------------------ RoPE
+
+template <typename S, int PS, int U>
+__global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32_t* __restrict__ pos,
+                                                        const float* __restrict__ inv_freq,
+                                                        RopeArgs a) {
+  using E = Elem<S>;
+  extern __shared__ float2 cs[];
+  const uint32_t base = blockIdx.x * static_cast<uint32_t>(kBlock * U);
+  const uint32_t t0 = fdiv(base, a.fd_spt);
+  uint32_t last = base + kBlock * U - 1;
+  if (last >= a.total) last = a.total - 1;
+  const int ntok = static_cast<int>(fdiv(last, a.fd_spt) - t0 + 1);
+
+  // Phase 1: issue every load of this thread.
+  S* rowp[U];
+  int ea[U], eb[U], tl[U], kk[U];
+  u32x4 va[U], vb[U];
+  float sa[U], sb[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    uint32_t s = base + u * kBlock + threadIdx.x;
+    if (s >= a.total) s = a.total - 1;  // clamped: loaded, never stored
+    const uint32_t t = fdiv(s, a.fd_spt);
+    const uint32_t rem = s - t * a.spt;
+    const uint32_t hh = fdiv(rem, a.fd_sph);
+    kk[u] = static_cast<int>(rem - hh * a.sph);
+    tl[u] = static_cast<int>(t - t0);
+    rowp[u] = static_cast<int>(hh) < a.hq
+                  ? q + (static_cast<int64_t>(t) * a.hq + hh) * a.D
+                  : k + (static_cast<int64_t>(t) * a.hk + (hh - a.hq)) * a.D;
+    slot_offsets<PS>(kk[u], a, &ea[u], &eb[u]);
+    if constexpr (PS == 1) {
+      sa[u] = E::ld(rowp[u], ea[u]);
+      sb[u] = E::ld(rowp[u], eb[u]);
+    } else {
+      va[u] = ld16(rowp[u], ea[u]);
+      vb[u] = ld16(rowp[u], eb[u]);
+    }
+  }
+
+  // Phase 2: the angle table of this block's tokens.
+  fill_table(cs, t0, ntok, a, pos, inv_freq);
+  __syncthreads();
+
+  // Phase 3: rotate and store.
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t s = base + u * kBlock + threadIdx.x;
+    if (s >= a.total) continue;
+    const float2* c = cs + tl[u] * a.half + kk[u] * PS;
+    if constexpr (PS == 1) {
+      float x0 = sa[u], x1 = sb[u];
+      rotate(x0, x1, c[0]);
+      E::st(rowp[u], ea[u], x0);
+      E::st(rowp[u], eb[u], x1);
+    } else {
+      constexpr int V = E::V;
+      float xa[V], xb[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        xa[e] = E::get(va[u], e);
+        xb[e] = E::get(vb[u], e);
+      }
+      if (a.layout == ET_ROPE_HALF) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) rotate(xa[e], xb[e], c[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; e += 2) {
+          rotate(xa[e], xa[e + 1], c[e / 2]);
+          rotate(xb[e], xb[e + 1], c[V / 2 + e / 2]);
+        }
+      }
+      st16(rowp[u], ea[u], E::pack(xa));
+      st16(rowp[u], eb[u], E::pack(xb));
+    }
+  }
+}
+
+// --------------------------------------------------------- RMSNorm + RoPE
+
+struct QkNormArgs {
+  RopeArgs rope;      // fd_spt unused here
+  float eps;
+  uint32_t rows;      // head rows in the call (T * (Hq + Hk))
+  FastDiv fd_heads;   // divide by Hq + Hk
+  int rsl;            // rotated slots per head row (r / (2V))
+};
+
+// Vector path: G lanes per head row, each owns two 16-byte vectors.
+// Slot kk < rsl holds V rotated pairs; slot kk >= rsl holds 2V tail entries.
+template <typename S, int G, int U>
+__global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __restrict__ gq, S* k,
+                                                             const S* __restrict__ gk,
+                                                             const int32_t* __restrict__ pos,
+                                                             const float* __restrict__ inv_freq,
+                                                             QkNormArgs a) {
+  using E = Elem<S>;
+  constexpr int V = E::V;
+  constexpr int kRowsPerPass = kBlock / G;
+  extern __shared__ float2 cs[];
+  const RopeArgs& ra = a.rope;
+  const int heads = ra.hq + ra.hk;
+  const int kk = threadIdx.x % G;
+  const int grp = threadIdx.x / G;
+  const uint32_t base = blockIdx.x * static_cast<uint32_t>(kRowsPerPass * U);
+  const uint32_t t0 = fdiv(base, a.fd_heads);
+  uint32_t last = base + kRowsPerPass * U - 1;
+  if (last >= a.rows) last = a.rows - 1;
+  const int ntok = static_cast<int>(fdiv(last, a.fd_heads) - t0 + 1);
+
+  int ea, eb;
+  if (kk < a.rsl) {
+    slot_offsets<V>(kk, ra, &ea, &eb);
+  } else {
+    ea = ra.r + (kk - a.rsl) * 2 * V;
+    eb = ea + V;
+  }
+
+  S* rowp[U];
+  int tl[U];
+  bool isq[U];
+  u32x4 va[U], vb[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    uint32_t hr = base + u * kRowsPerPass + grp;
+    if (hr >= a.rows) hr = a.rows - 1;  // clamped: loaded, never stored
+    const uint32_t t = fdiv(hr, a.fd_heads);
+    const int hh = static_cast<int>(hr - t * heads);
+    tl[u] = static_cast<int>(t - t0);
+    isq[u] = hh < ra.hq;
+    rowp[u] = isq[u] ? q + (static_cast<int64_t>(t) * ra.hq + hh) * ra.D
+                     : k + (static_cast<int64_t>(t) * ra.hk + (hh - ra.hq)) * ra.D;
+    va[u] = ld16(rowp[u], ea);
+    vb[u] = ld16(rowp[u], eb);
+  }
+  const u32x4 gqa = ld16(gq, ea), gqb = ld16(gq, eb);
+  u32x4 gka = gqa, gkb = gqb;
+  if (ra.hk > 0) {
+    gka = ld16(gk, ea);
+    gkb = ld16(gk, eb);
+  }
+
+  fill_table(cs, t0, ntok, ra, pos, inv_freq);
+  __syncthreads();
+
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float xa[V], xb[V];
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      xa[e] = E::get(va[u], e);
+      ss = __builtin_fmaf(xa[e], xa[e], ss);
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      xb[e] = E::get(vb[u], e);
+      ss = __builtin_fmaf(xb[e], xb[e], ss);
+    }
+    ss = group_sum<G>(ss);
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(ra.D) + a.eps);
+    const u32x4& ga = isq[u] ? gqa : gka;
+    const u32x4& gb = isq[u] ? gqb : gkb;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      xa[e] = xa[e] * inv * E::get(ga, e);
+      xb[e] = xb[e] * inv * E::get(gb, e);
+    }
+    if (kk < a.rsl) {
+      const float2* c = cs + tl[u] * ra.half + kk * V;
+      if (ra.layout == ET_ROPE_HALF) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) rotate(xa[e], xb[e], c[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; e += 2) {
+          rotate(xa[e], xa[e + 1], c[e / 2]);
+          rotate(xb[e], xb[e + 1], c[V / 2 + e / 2]);
+        }
+      }
+    }
+    if (base + u * kRowsPerPass + grp < a.rows) {
+      st16(rowp[u], ea, E::pack(xa));
+      st16(rowp[u], eb, E::pack(xb));
+    }
+  }
+}
+
+// General path: one wave per head row.  Lane l owns pairs i = l, l+64, ...
+// (i < r/2) and tail entries r + l, r + l + 64, ...; pass 1 sums their
+// squares (pairs first, then tail, each in increasing order), pass 2 re-reads,
+// normalises, rotates and writes.  A lane only touches what it owns.
+template <typename S>
+__global__ __launch_bounds__(kBlock) void rmsnorm_rope_wave_kernel(
+    S* q, const S* __restrict__ gq, S* k, const S* __restrict__ gk,
+    const int32_t* __restrict__ pos, const float* __restrict__ inv_freq, QkNormArgs a) {
+  using E = Elem<S>;
+  const RopeArgs& ra = a.rope;
+  const int heads = ra.hq + ra.hk;
+  const int lane = threadIdx.x % 64;
+  const uint32_t hr = blockIdx.x * (kBlock / 64) + threadIdx.x / 64;
+  if (hr >= a.rows) return;  // whole wave exits together; no block barrier below
+  const uint32_t t = fdiv(hr, a.fd_heads);
+  const int hh = static_cast<int>(hr - t * heads);
+  const bool isq = hh < ra.hq;
+  S* row = isq ? q + (static_cast<int64_t>(t) * ra.hq + hh) * ra.D
+               : k + (static_cast<int64_t>(t) * ra.hk + (hh - ra.hq)) * ra.D;
+  const S* g = isq ? gq : gk;
+
+  float ss = 0.0f;
+  for (int i = lane; i < ra.half; i += 64) {
+    int ia, ib;
+    slot_offsets<1>(i, ra, &ia, &ib);
+    const float x0 = E::ld(row, ia), x1 = E::ld(row, ib);
+    ss = __builtin_fmaf(x0, x0, ss);
+    ss = __builtin_fmaf(x1, x1, ss);
+  }
+  for (int j = ra.r + lane; j < ra.D; j += 64) {
+    const float x = E::ld(row, j);
+    ss = __builtin_fmaf(x, x, ss);
+  }
+  ss = group_sum<64>(ss);
+  const float inv = 1.0f / sqrtf(ss / static_cast<float>(ra.D) + a.eps);
+  const int32_t p = ra.half > 0 ? pos[t] : 0;  // pos may be NULL when nothing rotates
+  for (int i = lane; i < ra.half; i += 64) {
+    int ia, ib;
+    slot_offsets<1>(i, ra, &ia, &ib);
+    float x0 = E::ld(row, ia) * inv * E::ld(g, ia);
+    float x1 = E::ld(row, ib) * inv * E::ld(g, ib);
+    float sn, cn;
+    sincosf(rope_angle(p, inv_freq[i]), &sn, &cn);
+    rotate(x0, x1, make_float2(ra.mu * cn, ra.mu * sn));
+    E::st(row, ia, x0);
+    E::st(row, ib, x1);
+  }
+  for (int j = ra.r + lane; j < ra.D; j += 64) E::st(row, j, E::ld(row, j) * inv * E::ld(g, j));
+}
+
+// ---------------------------------------------------------------- host
+
+template <typename S>
+et_status check_rope(const S* q, int64_t hq, const S* k, int64_t hk, const int32_t* pos,
+                     int64_t T, int64_t D, int64_t r, const float* inv_freq, float mu, int layout,
+                     int64_t* qbytes, int64_t* kbytes) {
+  if (T < 0 || hq < 0 || hk < 0 || D < 0) return ET_ERR_BAD_SIZE;
+  if (r < 0 || r > D || (r & 1)) return ET_ERR_BAD_ARG;
+  if (layout != ET_ROPE_HALF && layout != ET_ROPE_INTERLEAVED) return ET_ERR_BAD_ARG;
+  if (!__builtin_isfinite(mu)) return ET_ERR_BAD_ARG;
+  int64_t qn = 0, kn = 0;
+  if (!mul_ok(T, hq, &qn) || !mul_ok(qn, D, &qn) || !mul_ok(qn, int64_t(sizeof(S)), qbytes) ||
+      !mul_ok(T, hk, &kn) || !mul_ok(kn, D, &kn) || !mul_ok(kn, int64_t(sizeof(S)), kbytes))
+    return ET_ERR_BAD_SIZE;
+  if (D > INT32_MAX / 2 || hq + hk > INT32_MAX / 2) return ET_ERR_BAD_SIZE;
+  if ((*qbytes > 0 && !q) || (*kbytes > 0 && !k)) return ET_ERR_NULL_POINTER;
+  if (T > 0 && (hq + hk) > 0 && r > 0 && (!pos || !inv_freq)) return ET_ERR_NULL_POINTER;
+  if (!ranges_ok(q, *qbytes, k, *kbytes, false)) return ET_ERR_OVERLAP;
+  const int64_t pbytes = T * int64_t(sizeof(int32_t)), fbytes = (r / 2) * int64_t(sizeof(float));
+  if (!ranges_ok(q, *qbytes, pos, pbytes, false) || !ranges_ok(k, *kbytes, pos, pbytes, false) ||
+      !ranges_ok(q, *qbytes, inv_freq, fbytes, false) ||
+      !ranges_ok(k, *kbytes, inv_freq, fbytes, false))
+    return ET_ERR_OVERLAP;
+  return ET_OK;
+}
+
+RopeArgs make_args(int64_t T, int64_t hq, int64_t hk, int64_t D, int64_t r, float mu, int layout,
+                   int ps) {
+  RopeArgs a{};
+  a.T = T;
+  a.hq = static_cast<int>(hq);
+  a.hk = static_cast<int>(hk);
+  a.D = static_cast<int>(D);
+  a.r = static_cast<int>(r);
+  a.half = static_cast<int>(r / 2);
+  a.layout = layout;
+  a.mu = mu;
+  a.sph = static_cast<uint32_t>(a.half / ps);
+  a.spt = a.sph * static_cast<uint32_t>(hq + hk);
+  a.fd_spt = make_fastdiv(a.spt > 0 ? a.spt : 1);
+  a.fd_sph = make_fastdiv(a.sph > 0 ? a.sph : 1);
+  a.fd_half = make_fastdiv(a.half > 0 ? a.half : 1);
+  return a;
+}
+
+template <typename S, int PS, int U>
+void launch_rope(S* q, S* k, const int32_t* pos, const float* inv_freq, RopeArgs a, int64_t T,
+                 hipStream_t s) {
+  // Tokens per launch keep slot indices below 2^31.
+  const int64_t tok_per_launch = (int64_t{1} << 31) / a.spt;
+  a.ntok_max = static_cast<int>((kBlock * U + a.spt - 1) / a.spt + 1);
+  const size_t shmem = static_cast<size_t>(a.ntok_max) * a.half * sizeof(float2);
+  for (int64_t t0 = 0; t0 < T; t0 += tok_per_launch) {
+    const int64_t m = T - t0 < tok_per_launch ? T - t0 : tok_per_launch;
+    a.T = m;
+    a.total = static_cast<uint32_t>(m * a.spt);
+    const unsigned grid = (a.total + kBlock * U - 1) / (kBlock * U);
+    rope_qk_kernel<S, PS, U><<<grid, kBlock, shmem, s>>>(
+        q + t0 * a.hq * a.D, a.hk ? k + t0 * a.hk * a.D : k, pos + t0, inv_freq, a);
+  }
+}
+
+// Largest unroll (4, 2, 1) whose angle table fits the LDS budget.
+inline int pick_u(int64_t spt, int64_t half, int64_t per_u) {
+  for (int u = 4; u >= 1; u >>= 1) {
+    const int64_t ntok = (per_u * u + spt - 1) / spt + 1;
+    if (ntok * half * int64_t(sizeof(float2)) <= kMaxTableBytes) return u;
+  }
+  return 0;
+}
+
+template <typename S>
+et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int64_t T, int64_t D,
+                     int64_t r, const float* inv_freq, float mu, int layout, void* stream) {
+  int64_t qb = 0, kb = 0;
+  const et_status st = check_rope(q, hq, k, hk, pos, T, D, r, inv_freq, mu, layout, &qb, &kb);
+  if (st != ET_OK) return st;
+  if (T == 0 || hq + hk == 0 || r == 0) return ET_OK;
+  constexpr int V = Elem<S>::V;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool vec = (r % (2 * V)) == 0 && (D % V) == 0 && aligned16(q) && (hk == 0 || aligned16(k));
+  const int ps = vec ? V : 1;
+  RopeArgs a = make_args(T, hq, hk, D, r, mu, layout, ps);
+  if (a.spt > (1u << 30)) return ET_ERR_BAD_SIZE;
+  const int u = pick_u(a.spt, a.half, kBlock);
+  if (u == 0) return ET_ERR_BAD_SIZE;
+  (void)hipGetLastError();
+  if (vec) {
+    if (u == 4) launch_rope<S, V, 4>(q, k, pos, inv_freq, a, T, s);
+    else if (u == 2) launch_rope<S, V, 2>(q, k, pos, inv_freq, a, T, s);
+    else launch_rope<S, V, 1>(q, k, pos, inv_freq, a, T, s);
+  } else {
+    if (u == 4) launch_rope<S, 1, 4>(q, k, pos, inv_freq, a, T, s);
+    else if (u == 2) launch_rope<S, 1, 2>(q, k, pos, inv_freq, a, T, s);
+    else launch_rope<S, 1, 1>(q, k, pos, inv_freq, a, T, s);
+  }
+  return launch_status();
+}
+
+template <typename S, int G, int U>
+void launch_qknorm_vec(S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
+                       const float* inv_freq, QkNormArgs a, int64_t T, hipStream_t s) {
+  constexpr int kRowsPerPass = kBlock / G;
+  const int64_t heads = a.rope.hq + a.rope.hk;
+  const int64_t tok_per_launch = (int64_t{1} << 31) / heads;
+  const int64_t rows_per_block = int64_t{kRowsPerPass} * U;
+  const int ntok_max = static_cast<int>((rows_per_block + heads - 1) / heads + 1);
+  const size_t shmem = static_cast<size_t>(ntok_max) * a.rope.half * sizeof(float2);
+  for (int64_t t0 = 0; t0 < T; t0 += tok_per_launch) {
+    const int64_t m = T - t0 < tok_per_launch ? T - t0 : tok_per_launch;
+    a.rows = static_cast<uint32_t>(m * heads);
+    const unsigned grid = static_cast<unsigned>((a.rows + rows_per_block - 1) / rows_per_block);
+    rmsnorm_rope_kernel<S, G, U><<<grid, kBlock, shmem, s>>>(
+        q + t0 * a.rope.hq * a.rope.D, gq, a.rope.hk ? k + t0 * a.rope.hk * a.rope.D : k, gk,
+        pos + t0, inv_freq, a);
+  }
+}
+
+template <typename S, int G>
+void launch_qknorm_vec_u(int u, S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
+                         const float* inv_freq, QkNormArgs a, int64_t T, hipStream_t s) {
+  if (u == 4) launch_qknorm_vec<S, G, 4>(q, gq, k, gk, pos, inv_freq, a, T, s);
+  else if (u == 2) launch_qknorm_vec<S, G, 2>(q, gq, k, gk, pos, inv_freq, a, T, s);
+  else launch_qknorm_vec<S, G, 1>(q, gq, k, gk, pos, inv_freq, a, T, s);
+}
+
+template <typename S>
+et_status qknorm_entry(S* q, const S* gq, int64_t hq, S* k, const S* gk, int64_t hk, float eps,
+                       const int32_t* pos, int64_t T, int64_t D, int64_t r, const float* inv_freq,
+                       float mu, int layout, void* stream) {
+  int64_t qb = 0, kb = 0;
+  et_status st = check_rope(q, hq, k, hk, pos, T, D, r, inv_freq, mu, layout, &qb, &kb);
+  if (st != ET_OK) return st;
+  if (!(eps >= 0.0f) || !__builtin_isfinite(eps)) return ET_ERR_BAD_ARG;
+  if (T == 0 || hq + hk == 0) return ET_OK;
+  if (D == 0) return ET_ERR_BAD_SIZE;
+  if ((hq > 0 && !gq) || (hk > 0 && !gk)) return ET_ERR_NULL_POINTER;
+  const int64_t gbytes = D * int64_t(sizeof(S));
+  if (!ranges_ok(q, qb, gq, gbytes, false) || !ranges_ok(q, qb, gk, gbytes, false) ||
+      !ranges_ok(k, kb, gq, gbytes, false) || !ranges_ok(k, kb, gk, gbytes, false))
+    return ET_ERR_OVERLAP;
+  int64_t rows = 0;
+  if (!mul_ok(T, hq + hk, &rows)) return ET_ERR_BAD_SIZE;
+  constexpr int V = Elem<S>::V;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QkNormArgs a{};
+  a.eps = eps;
+  const int64_t heads = hq + hk;
+  a.fd_heads = make_fastdiv(static_cast<uint32_t>(heads));
+  const int64_t g = D / (2 * V);
+  const bool pow2 = g >= 1 && g <= 64 && (g & (g - 1)) == 0;
+  const bool vec = pow2 && (D % (2 * V)) == 0 && (r % (2 * V)) == 0 && aligned16(q) &&
+                   aligned16(gq) && (hk == 0 || (aligned16(k) && aligned16(gk)));
+  (void)hipGetLastError();
+  if (vec) {
+    a.rope = make_args(T, hq, hk, D, r, mu, layout, V);
+    a.rsl = static_cast<int>(r / (2 * V));
+    const int u = pick_u(heads, a.rope.half, kBlock / g);
+    if (u == 0) return ET_ERR_BAD_SIZE;
+    const S* gkk = hk > 0 ? gk : gq;
+    switch (g) {
+      case 1: launch_qknorm_vec_u<S, 1>(u, q, gq, k, gkk, pos, inv_freq, a, T, s); break;
+      case 2: launch_qknorm_vec_u<S, 2>(u, q, gq, k, gkk, pos, inv_freq, a, T, s); break;
+      case 4: launch_qknorm_vec_u<S, 4>(u, q, gq, k, gkk, pos, inv_freq, a, T, s); break;
+      case 8: launch_qknorm_vec_u<S, 8>(u, q, gq, k, gkk, pos, inv_freq, a, T, s); break;
+      case 16: launch_qknorm_vec_u<S, 16>(u, q, gq, k, gkk, pos, inv_freq, a, T, s); break;
+      case 32: launch_qknorm_vec_u<S, 32>(u, q, gq, k, gkk, pos, inv_freq, a, T, s); break;
+      default: launch_qknorm_vec_u<S, 64>(u, q, gq, k, gkk, pos, inv_freq, a, T, s); break;
+    }
+  } else {
+    a.rope = make_args(T, hq, hk, D, r, mu, layout, 1);
+    const int64_t tok_per_launch = (int64_t{1} << 31) / heads;
+    for (int64_t t0 = 0; t0 < T; t0 += tok_per_launch) {
+      const int64_t m = T - t0 < tok_per_launch ? T - t0 : tok_per_launch;
+      a.rows = static_cast<uint32_t>(m * heads);
+      const unsigned grid = (a.rows + kBlock / 64 - 1) / (kBlock / 64);
+      rmsnorm_rope_wave_kernel<S><<<grid, kBlock, 0, s>>>(
+          q + t0 * hq * D, gq, hk ? k + t0 * hk * D : k, gk, pos + t0, inv_freq, a);
+    }
+  }
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace et
+
+using et::Bf16;
+
+extern "C" {
+
+et_status et_rope_f32(float* x, const int32_t* pos, int64_t T, int64_t H, int64_t D, int64_t d_rot,
+                      const float* inv_freq, float attn_scaling, int layout, void* stream) {
+  return et::rope_entry<float>(x, H, nullptr, 0, pos, T, D, d_rot, inv_freq, attn_scaling, layout,
+                               stream);
+}
+
+et_status et_rope_bf16(et_bf16* x, const int32_t* pos, int64_t T, int64_t H, int64_t D,
+                       int64_t d_rot, const float* inv_freq, float attn_scaling, int layout,
+                       void* stream) {
+  return et::rope_entry<Bf16>(reinterpret_cast<Bf16*>(x), H, nullptr, 0, pos, T, D, d_rot,
+                              inv_freq, attn_scaling, layout, stream);
+}
+
+et_status et_rope_qk_f32(float* q, int64_t Hq, float* k, int64_t Hk, const int32_t* pos, int64_t T,
+                         int64_t D, int64_t d_rot, const float* inv_freq, float attn_scaling,
+                         int layout, void* stream) {
+  return et::rope_entry<float>(q, Hq, k, Hk, pos, T, D, d_rot, inv_freq, attn_scaling, layout,
+                               stream);
+}
+
+et_status et_rope_qk_bf16(et_bf16* q, int64_t Hq, et_bf16* k, int64_t Hk, const int32_t* pos,
+                          int64_t T, int64_t D, int64_t d_rot, const float* inv_freq,
+                          float attn_scaling, int layout, void* stream) {
+  return et::rope_entry<Bf16>(reinterpret_cast<Bf16*>(q), Hq, reinterpret_cast<Bf16*>(k), Hk, pos,
+                              T, D, d_rot, inv_freq, attn_scaling, layout, stream);
+}
+
+et_status et_rmsnorm_rope_qk_f32(float* q, const float* gq, int64_t Hq, float* k, const float* gk,
+                                 int64_t Hk, float eps, const int32_t* pos, int64_t T, int64_t D,
+                                 int64_t d_rot, const float* inv_freq, float attn_scaling,
+                                 int layout, void* stream) {
+  return et::qknorm_entry<float>(q, gq, Hq, k, gk, Hk, eps, pos, T, D, d_rot, inv_freq,
+                                 attn_scaling, layout, stream);
+}
+
+et_status et_rmsnorm_rope_qk_bf16(et_bf16* q, const et_bf16* gq, int64_t Hq, et_bf16* k,
+                                  const et_bf16* gk, int64_t Hk, float eps, const int32_t* pos,
+                                  int64_t T, int64_t D, int64_t d_rot, const float* inv_freq,
+                                  float attn_scaling, int layout, void* stream) {
+  return et::qknorm_entry<Bf16>(reinterpret_cast<Bf16*>(q), reinterpret_cast<const Bf16*>(gq), Hq,
+                                reinterpret_cast<Bf16*>(k), reinterpret_cast<const Bf16*>(gk), Hk,
+                                eps, pos, T, D, d_rot, inv_freq, attn_scaling, layout, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,208 @@
+/*
+ * et.h -- C ABI of libet.so: memory-bound transformer ops for AMD Instinct
+ * MI355X (gfx950), as hand-written HIP kernels.
+ *
+ * Ops and the passages that define them (web pages, by section):
+ *   [OPS] "Operations" (op spec of the glia runtime): 2 Normalization /
+ *         RmsNorm; 3 Position encoding / Rope; 4 Activation / Silu, SwiGlu;
+ *         5 Attention / QK-norm; 8 Sampling / Greedy; 10 Fused ops
+ *         (FusedSkipNorm, and fused = unfused within tolerance).
+ *   [ELT] "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding,
+ *         add, argmax": 2.1 RMSNorm; 2.2 RoPE; 2.3 SiLU-mul (SwiGLU);
+ *         2.4 Embedding, add, argmax; 4 The interface (names and argument
+ *         order of the six routines kept here).
+ *
+ * Common rules for every entry point
+ *   - Types: the _f32 variant stores float; the _bf16 variant stores
+ *     bfloat16 bits (et_bf16) and computes in f32, rounding each stored
+ *     result once to nearest-even.  inv_freq and scalars are f32 in both.
+ *   - Pointers are DEVICE pointers of the current HIP device, except scalars
+ *     passed by value.  The caller owns every buffer; the library allocates
+ *     nothing, keeps no state and is reentrant.
+ *   - stream is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; it never synchronises.  Device faults
+ *     surface at the caller's next synchronisation.
+ *   - Layout: every tensor is dense row-major with no padding.
+ *   - Sizes are int64_t element counts.  A size of 0 makes the call a no-op
+ *     returning ET_OK (argmax with n == 0 writes -1 per row, see below).
+ *   - Aliasing: only the exact aliases stated per op are allowed (same start,
+ *     same extent); any other overlap of an output with another buffer
+ *     returns ET_ERR_OVERLAP before anything is enqueued.
+ *   - Results are deterministic.  For the row ops (RMSNorm, fused
+ *     add+RMSNorm, RoPE, fused RMSNorm+RoPE) the bits of a row depend only on
+ *     that row's inputs, the row length and the 16-byte alignment of the
+ *     buffers -- never on the number of rows in the call.
+ *   - Errors: argument problems are reported before any launch and nothing is
+ *     written; ET_ERR_HIP reports a failed launch.
+ */
+#ifndef ET_H
+#define ET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ET_ABI_VERSION 1
+
+/* Raw bfloat16 bits (sign, 8-bit exponent, 7-bit fraction). */
+typedef uint16_t et_bf16;
+
+typedef enum {
+    ET_OK = 0,
+    ET_ERR_NULL_POINTER = 1, /* a required pointer is NULL while its size is nonzero */
+    ET_ERR_BAD_SIZE = 2,     /* negative size, size product overflow, or a size past a limit */
+    ET_ERR_BAD_ARG = 3,      /* d_rot odd / > D, bad layout, eps < 0 or not finite, ... */
+    ET_ERR_OVERLAP = 4,      /* buffers overlap other than by an allowed exact alias */
+    ET_ERR_WORKSPACE = 5,    /* argmax workspace smaller than et_argmax_workspace_bytes() */
+    ET_ERR_HIP = 6           /* the HIP runtime rejected a launch */
+} et_status;
+
+enum { ET_ROPE_HALF = 0, ET_ROPE_INTERLEAVED = 1 };
+
+/* ------------------------------------------------------------------------
+ * RMSNorm  ([OPS] RmsNorm; [ELT] 2.1)
+ *   y[r, i] = x[r, i] / sqrt(mean_i(x[r, :]^2) + eps) * w[i]
+ *   eps is added inside the root; a zero row maps to 0 (eps > 0).
+ *   x, y: [rows, d]; w: [d].  eps: finite, >= 0.  d >= 1 when rows > 0.
+ *   Alias allowed: y == x (in place).
+ *   The sum of squares is f32 in a fixed order that depends on d only.
+ */
+et_status et_rmsnorm_f32(const float* x, const float* w, float* y,
+                         int64_t rows, int64_t d, float eps, void* stream);
+et_status et_rmsnorm_bf16(const et_bf16* x, const et_bf16* w, et_bf16* y,
+                          int64_t rows, int64_t d, float eps, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Fused residual add + RMSNorm  ([OPS] 10 Fused ops, FusedSkipNorm)
+ *   h = x + residual, rounded to the storage type (the value returned);
+ *   y = RMSNorm(h as stored, w, eps).  One pass; both outputs written.
+ *   x, residual, y, h: [rows, d]; w: [d].
+ *   Aliases allowed: y == x and/or h == residual (in place), h == x when
+ *   y != x.
+ */
+et_status et_add_rmsnorm_f32(const float* x, const float* residual,
+                             const float* w, float* y, float* h,
+                             int64_t rows, int64_t d, float eps, void* stream);
+et_status et_add_rmsnorm_bf16(const et_bf16* x, const et_bf16* residual,
+                              const et_bf16* w, et_bf16* y, et_bf16* h,
+                              int64_t rows, int64_t d, float eps, void* stream);
+
+/* ------------------------------------------------------------------------
+ * RoPE, in place  ([OPS] Rope; [ELT] 2.2 and 4, tl_rope_f32)
+ *   x: [T, H, D]; pos: int32 [T]; inv_freq: f32 [d_rot / 2].
+ *   For token t and pair i < d_rot/2 the angle is p_t * w_i formed in f64
+ *   and rounded to f32 (= f32(p) * f32(w) for |p| < 2^24); then
+ *     a' = mu (a cos - b sin),  b' = mu (a sin + b cos),  mu = attn_scaling.
+ *   layout ET_ROPE_HALF pairs (i, i + d_rot/2); ET_ROPE_INTERLEAVED pairs
+ *   (2i, 2i + 1).  Entries d_rot..D-1 of each head are not touched.
+ *   d_rot: even, 0 <= d_rot <= D.  attn_scaling: finite.
+ */
+et_status et_rope_f32(float* x, const int32_t* pos, int64_t T, int64_t H,
+                      int64_t D, int64_t d_rot, const float* inv_freq,
+                      float attn_scaling, int layout, void* stream);
+et_status et_rope_bf16(et_bf16* x, const int32_t* pos, int64_t T, int64_t H,
+                       int64_t D, int64_t d_rot, const float* inv_freq,
+                       float attn_scaling, int layout, void* stream);
+
+/* RoPE on a query and a key tensor in one launch (one angle per (token,
+ * pair) serves all Hq + Hk heads).  q: [T, Hq, D]; k: [T, Hk, D] (k may be
+ * NULL when Hk == 0).  Same rules as et_rope_*; q and k must not overlap. */
+et_status et_rope_qk_f32(float* q, int64_t Hq, float* k, int64_t Hk,
+                         const int32_t* pos, int64_t T, int64_t D,
+                         int64_t d_rot, const float* inv_freq,
+                         float attn_scaling, int layout, void* stream);
+et_status et_rope_qk_bf16(et_bf16* q, int64_t Hq, et_bf16* k, int64_t Hk,
+                          const int32_t* pos, int64_t T, int64_t D,
+                          int64_t d_rot, const float* inv_freq,
+                          float attn_scaling, int layout, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Fused RMSNorm + RoPE on Q and K, in place  ([OPS] 5 QK-norm)
+ *   Each (token, head) row of length D is normalised over all D entries
+ *   with the gain gq [D] (query heads) or gk [D] (key heads) and eps, then
+ *   rotated as et_rope_qk_* on its first d_rot entries; the f32
+ *   intermediate is not rounded; entries d_rot..D-1 are normalised only.
+ *   q: [T, Hq, D]; k: [T, Hk, D] (NULL with Hk == 0; gk may then be NULL).
+ */
+et_status et_rmsnorm_rope_qk_f32(float* q, const float* gq, int64_t Hq,
+                                 float* k, const float* gk, int64_t Hk,
+                                 float eps, const int32_t* pos, int64_t T,
+                                 int64_t D, int64_t d_rot,
+                                 const float* inv_freq, float attn_scaling,
+                                 int layout, void* stream);
+et_status et_rmsnorm_rope_qk_bf16(et_bf16* q, const et_bf16* gq, int64_t Hq,
+                                  et_bf16* k, const et_bf16* gk, int64_t Hk,
+                                  float eps, const int32_t* pos, int64_t T,
+                                  int64_t D, int64_t d_rot,
+                                  const float* inv_freq, float attn_scaling,
+                                  int layout, void* stream);
+
+/* ------------------------------------------------------------------------
+ * SiLU-gated multiply  ([OPS] Silu, SwiGlu; [ELT] 2.3, tl_silu_mul_f32)
+ *   y[i] = gate[i] / (1 + exp(-gate[i])) * up[i]; for very negative gates
+ *   exp overflows to +inf and the factor is -0 (never NaN).
+ *   gate, up, y: [n].  Aliases allowed: y == gate, y == up.
+ */
+et_status et_silu_mul_f32(const float* gate, const float* up, float* y,
+                          int64_t n, void* stream);
+et_status et_silu_mul_bf16(const et_bf16* gate, const et_bf16* up, et_bf16* y,
+                           int64_t n, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Residual add  ([OPS] Add; [ELT] 2.4, tl_add_f32)
+ *   y[i] = a[i] + b[i], IEEE addition in the storage type (bf16: the f32
+ *   sum rounded once, which is the correctly rounded bf16 sum).
+ *   a, b, y: [n].  Aliases allowed: y == a, y == b.
+ */
+et_status et_add_f32(const float* a, const float* b, float* y, int64_t n,
+                     void* stream);
+et_status et_add_bf16(const et_bf16* a, const et_bf16* b, et_bf16* y,
+                      int64_t n, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Embedding gather  ([OPS] TokenEmbed; [ELT] 2.4, tl_embedding_f32)
+ *   out[t, :] = table[ids[t], :], a bit copy of the row that starts at
+ *   element ids[t] * d.  table: [V, d]; ids: int32 [n]; out: [n, d].
+ *   The pages make valid ids the caller's duty; here an id outside [0, V)
+ *   is never dereferenced and yields a row of quiet NaN instead.
+ *   out must not overlap table or ids.
+ */
+et_status et_embedding_f32(const float* table, int64_t V, const int32_t* ids,
+                           float* out, int64_t n, int64_t d, void* stream);
+et_status et_embedding_bf16(const et_bf16* table, int64_t V,
+                            const int32_t* ids, et_bf16* out, int64_t n,
+                            int64_t d, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Greedy argmax per row  ([OPS] Argmax, 8 Sampling / Greedy; [ELT] 2.4)
+ *   out[r] = the lowest index of the largest non-NaN value of x[r, :]
+ *   (-0 and +0 are equal; +inf is a number), or -1 when the row holds no
+ *   number (all NaN, or n == 0).  x: [rows, n]; out: int32 [rows].
+ *   n <= INT32_MAX.
+ *   workspace: device scratch that lets long rows be split over several
+ *   workgroups (two launches).  Either workspace == NULL with
+ *   workspace_bytes == 0 (one workgroup per row, one launch, no scratch), or
+ *   workspace != NULL with workspace_bytes >= et_argmax_workspace_bytes(rows,
+ *   n), else ET_ERR_WORKSPACE (ET_ERR_NULL_POINTER for NULL with a nonzero
+ *   size).  The caller owns the workspace; its contents on entry do not
+ *   matter.  The result is the same either way.
+ */
+size_t et_argmax_workspace_bytes(int64_t rows, int64_t n);
+et_status et_argmax_f32(const float* x, int64_t rows, int64_t n, int32_t* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+et_status et_argmax_bf16(const et_bf16* x, int64_t rows, int64_t n,
+                         int32_t* out, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* ------------------------------------------------------------------------
+ * Library information. */
+const char* et_status_string(et_status s); /* static string, never NULL */
+int et_abi_version(void);                  /* ET_ABI_VERSION of the build */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ET_H */

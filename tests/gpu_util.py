@@ -1,0 +1,139 @@
+"""Helpers for the GPU parity tests: moving storage-form numpy arrays to and
+from the device, and the tolerance checks of the parity bar.
+
+Tolerances (written out here, used by every parity test):
+  EXACT     equal bits; NaN compared by class (embedding, add, argmax,
+            fused h, RoPE pass-through entries).
+  F32_REL   |got - y| <= 1e-6 |y| + 2^-140, y the oracle's unrounded f64
+            value (RMSNorm, SiLU-mul in f32).
+  BF16_ULP  at most 1 bf16 ulp from the oracle's correctly rounded value,
+            with +0 == -0 (RMSNorm, SiLU-mul, normalised tails in bf16).
+  PAIR      RoPE outputs: error relative to the rotated pair's length,
+            |got - y| <= 1e-6 * |(y_a, y_b)| in f32 (|(y_a, y_b)| = mu |(a, b)|,
+            since rotation keeps the length); in bf16 either 1 ulp or
+            |got - y| <= 2^-16 |(y_a, y_b)|.  Per-element relative error is
+            unbounded under cancellation in a cos - b sin, the pair-relative
+            one is not.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+F32_REL = 1e-6
+F32_FLOOR = 2.0 ** -140
+BF16_PAIR = 2.0 ** -16
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    """Storage-form numpy (float32, or uint16 bf16 bits, or int32) -> cuda."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    """cuda tensor -> storage-form numpy."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def widen(a: np.ndarray) -> np.ndarray:
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _isnan(a: np.ndarray) -> np.ndarray:
+    return np.isnan(widen(a))
+
+
+def assert_bits(got: np.ndarray, ref: np.ndarray, what: str = "") -> None:
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    gn, rn = _isnan(got), _isnan(ref)
+    assert np.array_equal(gn, rn), f"{what}: NaN positions differ ({gn.sum()} vs {rn.sum()})"
+    g = got[~gn].view(np.uint16 if got.dtype == np.uint16 else np.uint32)
+    r = ref[~rn].view(np.uint16 if ref.dtype == np.uint16 else np.uint32)
+    bad = np.flatnonzero(g != r)
+    assert bad.size == 0, f"{what}: {bad.size} elements differ in bits, first at {bad[:5]}"
+
+
+def assert_f32_rel(got: np.ndarray, y64: np.ndarray, what: str = "", rel: float = F32_REL) -> None:
+    assert got.dtype == np.float32 and got.shape == y64.shape, what
+    g = got.astype(np.float64)
+    gn, rn = np.isnan(g), np.isnan(y64)
+    assert np.array_equal(gn, rn), f"{what}: NaN positions differ"
+    fin = ~rn
+    err = np.abs(g[fin] - y64[fin])
+    lim = rel * np.abs(y64[fin]) + F32_FLOOR
+    bad = np.flatnonzero(~(err <= lim))
+    if bad.size:
+        i = bad[np.argmax(err[bad] / lim[bad])]
+        raise AssertionError(f"{what}: {bad.size} elements over 1e-6 rel; worst got={g[fin][i]!r} "
+                             f"ref={y64[fin][i]!r} rel={err[i] / max(abs(y64[fin][i]), 1e-300):.3g}")
+
+
+def bf16_key(bits: np.ndarray) -> np.ndarray:
+    """Integer line of bf16 values: adjacent values differ by 1, +0 == -0."""
+    b = bits.astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def assert_bf16_ulp(got: np.ndarray, ref: np.ndarray, what: str = "", ulps: int = 1) -> None:
+    """got, ref: bf16 bits; ref is the oracle's correctly rounded output."""
+    assert got.dtype == np.uint16 and ref.dtype == np.uint16 and got.shape == ref.shape, what
+    gn, rn = _isnan(got), _isnan(ref)
+    assert np.array_equal(gn, rn), f"{what}: NaN positions differ"
+    d = np.abs(bf16_key(got[~gn]) - bf16_key(ref[~rn]))
+    bad = np.flatnonzero(d > ulps)
+    assert bad.size == 0, f"{what}: {bad.size} elements over {ulps} bf16 ulp (max {d.max()})"
+
+
+def assert_close(got: np.ndarray, y64: np.ndarray, ref: np.ndarray, what: str = "") -> None:
+    """F32_REL for f32 storage, BF16_ULP for bf16 storage."""
+    if got.dtype == np.float32:
+        assert_f32_rel(got, y64, what)
+    else:
+        assert_bf16_ulp(got, ref, what)
+
+
+def pair_norms(y64: np.ndarray, r: int, layout: int) -> np.ndarray:
+    """|(y_a, y_b)| for every rotated entry of [..., D] (NaN elsewhere)."""
+    out = np.full(y64.shape, np.nan)
+    half = r // 2
+    if half == 0:
+        return out
+    if layout == 0:
+        a, b = y64[..., :half], y64[..., half:r]
+        n = np.hypot(a, b)
+        out[..., :half] = n
+        out[..., half:r] = n
+    else:
+        a, b = y64[..., 0:r:2], y64[..., 1:r:2]
+        n = np.hypot(a, b)
+        out[..., 0:r:2] = n
+        out[..., 1:r:2] = n
+    return out
+
+
+def assert_pair(got: np.ndarray, y64: np.ndarray, ref: np.ndarray, r: int, layout: int,
+                what: str = "") -> None:
+    """PAIR tolerance on the first r entries of each head row."""
+    pn = pair_norms(y64, r, layout)[..., :r]
+    g = widen(got[..., :r])
+    y = y64[..., :r]
+    err = np.abs(g - y)
+    if got.dtype == np.float32:
+        bad = np.flatnonzero(~(err <= F32_REL * pn + F32_FLOOR))
+        if bad.size:
+            i = bad[np.argmax((err / np.maximum(pn, 1e-300)).ravel()[bad])]
+            raise AssertionError(f"{what}: {bad.size} rotated entries over 1e-6 of the pair length; "
+                                 f"worst err/len={(err.ravel()[i] / pn.ravel()[i]):.3g}")
+    else:
+        ud = np.abs(bf16_key(got[..., :r]) - bf16_key(ref[..., :r]))
+        bad = np.flatnonzero(~((ud <= 1) | (err <= BF16_PAIR * pn)))
+        assert bad.size == 0, f"{what}: {bad.size} rotated bf16 entries over 1 ulp and 2^-16 |pair|"

@@ -1,0 +1,216 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/et.h declares, and rejects bad arguments before touching the GPU.
+
+No test here launches a kernel: every call below fails host-side validation
+(which runs before any HIP call) and passes only fake pointers that are never
+dereferenced.  They are skipped where a GPU is visible, so that a validation
+bug can never send a fake pointer to a real device; the GPU tests cover the
+same paths with real tensors.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "et.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(et_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_ops():
+    names = _declared()
+    for op in ("rmsnorm", "add_rmsnorm", "rope", "rope_qk", "rmsnorm_rope_qk", "silu_mul", "add",
+               "embedding", "argmax"):
+        for sfx in ("f32", "bf16"):
+            assert f"et_{op}_{sfx}" in names
+    assert "et_argmax_workspace_bytes" in names and "et_status_string" in names
+
+
+def test_library_exports_every_declared_symbol():
+    import elementwise_transformer_amd as et
+    out = subprocess.run(["nm", "-D", "--defined-only", et.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (et_[a-z0-9_]+)$", out, re.M))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    for n in _declared():
+        getattr(et.lib, n)          # resolvable through ctypes as well
+
+
+def test_abi_version_and_status_strings():
+    import elementwise_transformer_amd as et
+    assert et.abi_version() == 1
+    for code in range(7):
+        assert et.lib.et_status_string(code).decode()
+    assert et.lib.et_status_string(99).decode() == "unknown status"
+
+
+gpu_visible = pytest.mark.skipif(
+    __import__("torch").cuda.device_count() > 0,
+    reason="fake-pointer validation tests run only where no GPU is visible")
+
+P = ctypes.c_void_p
+G = 1 << 32          # fake buffers 4 GiB apart, 16-byte aligned, never dereferenced
+A = P(1 * G)
+B = P(2 * G)
+C = P(3 * G)
+D = P(4 * G)
+E5 = P(5 * G)
+NULL = None
+S = P(0)             # default stream
+
+
+@gpu_visible
+@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+def test_rmsnorm_validation(sfx):
+    import elementwise_transformer_amd as et
+    f = getattr(et.lib, f"et_rmsnorm_{sfx}")
+    assert f(A, B, C, -1, 8, 1e-5, S) == 2                   # negative rows
+    assert f(A, B, C, 4, -8, 1e-5, S) == 2                   # negative d
+    assert f(A, B, C, 4, 0, 1e-5, S) == 2                    # empty final axis
+    assert f(A, B, C, 1 << 40, 1 << 40, 1e-5, S) == 2        # size product overflows
+    assert f(A, B, C, 4, 8, -1.0, S) == 3                    # eps < 0
+    assert f(A, B, C, 4, 8, float("nan"), S) == 3
+    assert f(A, B, C, 4, 8, float("inf"), S) == 3
+    assert f(NULL, B, C, 4, 8, 1e-5, S) == 1
+    assert f(A, NULL, C, 4, 8, 1e-5, S) == 1
+    assert f(A, B, NULL, 4, 8, 1e-5, S) == 1
+    assert f(A, B, P(G + 16), 4, 8, 1e-5, S) == 4           # y overlaps x partially
+    assert f(A, B, B, 4, 8, 1e-5, S) == 4                    # y over the gain
+    assert f(NULL, NULL, NULL, 0, 8, 1e-5, S) == 0           # rows == 0: no-op
+
+
+@gpu_visible
+@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+def test_add_rmsnorm_validation(sfx):
+    import elementwise_transformer_amd as et
+    f = getattr(et.lib, f"et_add_rmsnorm_{sfx}")
+    assert f(A, NULL, C, D, E5, 4, 8, 1e-5, S) == 1
+    assert f(A, B, C, D, NULL, 4, 8, 1e-5, S) == 1
+    assert f(A, B, C, D, D, 4, 8, 1e-5, S) == 4              # h == y
+    assert f(A, B, C, B, E5, 4, 8, 1e-5, S) == 4    # y == residual
+    assert f(A, B, C, A, A, 4, 8, 1e-5, S) == 4              # h == x while y == x
+    assert f(A, B, C, D, E5, 4, 8, -2.0, S) == 3
+
+
+@gpu_visible
+@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+def test_rope_validation(sfx):
+    import elementwise_transformer_amd as et
+    f = getattr(et.lib, f"et_rope_{sfx}")
+    assert f(A, B, 4, 2, 8, 3, C, 1.0, 0, S) == 3            # odd d_rot
+    assert f(A, B, 4, 2, 8, 10, C, 1.0, 0, S) == 3           # d_rot > D
+    assert f(A, B, 4, 2, 8, -2, C, 1.0, 0, S) == 3
+    assert f(A, B, 4, 2, 8, 8, C, 1.0, 2, S) == 3            # bad layout
+    assert f(A, B, 4, 2, 8, 8, C, float("inf"), 0, S) == 3   # attn_scaling
+    assert f(A, B, -4, 2, 8, 8, C, 1.0, 0, S) == 2
+    assert f(A, NULL, 4, 2, 8, 8, C, 1.0, 0, S) == 1         # pos
+    assert f(A, B, 4, 2, 8, 8, NULL, 1.0, 0, S) == 1         # inv_freq
+    assert f(NULL, B, 4, 2, 8, 8, C, 1.0, 0, S) == 1
+    assert f(A, P(G + 8), 4, 2, 8, 8, C, 1.0, 0, S) == 4  # pos inside x
+    assert f(NULL, NULL, 0, 2, 8, 8, NULL, 1.0, 0, S) == 0   # T == 0
+    q = getattr(et.lib, f"et_rope_qk_{sfx}")
+    assert q(A, 2, P(G + 16), 2, B, 4, 8, 8, C, 1.0, 0, S) == 4   # q and k overlap
+    assert q(A, 2, NULL, 3, B, 4, 8, 8, C, 1.0, 0, S) == 1          # k NULL with Hk > 0
+
+
+@gpu_visible
+@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+def test_rmsnorm_rope_validation(sfx):
+    import elementwise_transformer_amd as et
+    f = getattr(et.lib, f"et_rmsnorm_rope_qk_{sfx}")
+    assert f(A, NULL, 2, B, C, 2, 1e-6, D, 4, 8, 8, E5, 1.0, 0, S) == 1  # gq
+    assert f(A, C, 2, B, NULL, 2, 1e-6, D, 4, 8, 8, E5, 1.0, 0, S) == 1  # gk
+    assert f(A, C, 2, B, C, 2, -1.0, D, 4, 8, 8, E5, 1.0, 0, S) == 3     # eps
+    assert f(A, C, 2, B, C, 2, 1e-6, D, 4, 8, 7, E5, 1.0, 0, S) == 3     # odd d_rot
+    assert f(A, A, 2, B, C, 2, 1e-6, D, 4, 8, 8, E5, 1.0, 0, S) == 4     # gq inside q
+
+
+@gpu_visible
+@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+def test_flat_validation(sfx):
+    import elementwise_transformer_amd as et
+    for op in ("add", "silu_mul"):
+        f = getattr(et.lib, f"et_{op}_{sfx}")
+        assert f(A, B, C, -1, S) == 2
+        assert f(NULL, B, C, 4, S) == 1
+        assert f(A, B, P(G + 4), 64, S) == 4              # y overlaps a partially
+        assert f(NULL, NULL, NULL, 0, S) == 0
+        assert f(A, B, C, 1 << 62, S) == 2
+
+
+@gpu_visible
+@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+def test_embedding_and_argmax_validation(sfx):
+    import elementwise_transformer_amd as et
+    e = getattr(et.lib, f"et_embedding_{sfx}")
+    assert e(A, 10, B, C, -1, 8, S) == 2
+    assert e(A, 10, NULL, C, 4, 8, S) == 1
+    assert e(A, 10, B, A, 4, 8, S) == 4                      # out over the table
+    assert e(A, 10, B, C, 0, 8, S) == 0
+    a = getattr(et.lib, f"et_argmax_{sfx}")
+    assert a(A, -1, 8, B, NULL, 0, S) == 2
+    assert a(A, 4, 1 << 31, B, NULL, 0, S) == 2               # n > INT32_MAX
+    assert a(A, 4, 8, NULL, NULL, 0, S) == 1
+    assert a(A, 4, 8, B, NULL, 64, S) == 1                    # NULL workspace, nonzero size
+    need = et.argmax_workspace_bytes(256, 128256)
+    assert need > 0
+    assert a(A, 256, 128256, B, C, need - 1, S) == 5          # workspace too small
+    assert a(A, 4, 8, A, NULL, 0, S) == 4                     # out inside x
+    assert a(NULL, 0, 8, NULL, NULL, 0, S) == 0
+
+
+def test_argmax_workspace_sizes():
+    import elementwise_transformer_amd as et
+    assert et.argmax_workspace_bytes(0, 100) == 0
+    assert et.argmax_workspace_bytes(4, 0) == 0
+    assert et.argmax_workspace_bytes(100000, 1000) == 0       # one chunk per row: none needed
+    n256 = et.argmax_workspace_bytes(256, 128256)
+    assert n256 == 256 * 16 * 8
+    assert et.argmax_workspace_bytes(1, 128256) >= 8 * 2
+
+
+def test_fastdiv_host_logic():
+    """Exact division by run-time constants (host side of et_common.hpp),
+    compiled as plain host C++ and checked against integer division."""
+    src = r'''
+#include "et_common.hpp"
+#include <cstdio>
+#include <cstdint>
+int main() {
+  const uint32_t divs[] = {1u, 2u, 3u, 5u, 6u, 7u, 8u, 40u, 64u, 72u, 320u, 576u, 1000u, 4096u,
+                           65535u, 65536u, 65537u, 1000003u, 2147483647u, 2147483648u, 4294967295u};
+  const uint32_t ns[] = {0u, 1u, 2u, 3u, 7u, 8u, 63u, 64u, 65u, 1000u, 65535u, 65536u,
+                         2147483647u, 2147483648u, 4294967294u, 4294967295u};
+  for (uint32_t d : divs) {
+    et::FastDiv f = et::make_fastdiv(d);
+    for (uint32_t n : ns) if (et::fdiv(n, f) != n / d) { std::printf("%u/%u\n", n, d); return 1; }
+    uint64_t x = 12345;
+    for (int k = 0; k < 200000; ++k) {
+      x = x * 6364136223846793005ull + 1442695040888963407ull;
+      const uint32_t n = static_cast<uint32_t>(x >> 32);
+      if (et::fdiv(n, f) != n / d) { std::printf("%u/%u\n", n, d); return 1; }
+    }
+  }
+  return 0;
+}
+'''
+    with tempfile.TemporaryDirectory() as tmp:
+        c = os.path.join(tmp, "fd.cpp")
+        exe = os.path.join(tmp, "fd")
+        with open(c, "w") as f:
+            f.write(src)
+        inc = [f"-I{os.path.join(ROOT, 'include')}",
+               f"-I{os.path.join(ROOT, 'elementwise_transformer_amd', 'csrc')}"]
+        r = subprocess.run(["/opt/rocm/bin/hipcc", "-x", "hip", "--offload-arch=gfx950", "-O2", *inc,
+                            c, "-o", exe], capture_output=True, text=True)
+        if r.returncode != 0:
+            pytest.fail(r.stderr[-3000:])
+        assert subprocess.run([exe]).returncode == 0

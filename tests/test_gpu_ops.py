@@ -1,0 +1,311 @@
+"""GPU parity of every op against the CPU oracle, through the C ABI.
+
+Sizes span several tiles and ragged tails, both storage types, both RoPE
+layouts, partial rotary widths, in-place aliases, misaligned (scalar-path)
+buffers and the degenerate cases (empty inputs, zero rows, all-NaN rows,
+out-of-range ids).  Tolerances are the ones documented in gpu_util.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_util import (assert_bits, assert_close, assert_f32_rel, assert_pair, dev, host, widen)
+
+pytestmark = pytest.mark.gpu
+
+DTS = ["f32", "bf16"]
+
+
+@pytest.fixture(scope="module")
+def et():
+    import elementwise_transformer_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return m
+
+
+def _rng(*key):
+    return np.random.default_rng([4242, *key])
+
+
+def _store(a, dt):
+    return wl.store(a, dt)
+
+
+def _misaligned(t: torch.Tensor) -> torch.Tensor:
+    """A contiguous copy of t whose data pointer is 4 bytes (f32) or 2 bytes
+    (bf16) past a 16-byte boundary: the kernels must take their scalar path."""
+    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    v = flat[1:1 + t.numel()].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 != 0
+    return v
+
+
+# ------------------------------------------------------------- RMSNorm
+
+NORM_SHAPES = [(1, 1), (3, 3), (5, 7), (4, 64), (33, 100), (7, 1000), (9, 4096), (6, 4100),
+               (3, 8192), (2, 14336), (2, 40000), (2, 70001)]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("rows,d", NORM_SHAPES)
+def test_rmsnorm(et, orc, dt, rows, d):
+    g = _rng(1, rows, d, DTS.index(dt))
+    x = _store(g.standard_normal((rows, d)).astype(np.float32) * 2, dt)
+    w = _store(g.uniform(0.5, 1.5, d).astype(np.float32), dt)
+    x[0, :] = 0                                           # zero row -> 0, not NaN
+    yr, y64 = orc.rmsnorm(x, w, 1e-5)
+    got = host(et.rmsnorm(dev(x), dev(w), 1e-5))
+    assert_close(got, y64, yr, f"rmsnorm {dt} {rows}x{d}")
+    assert not np.any(np.isnan(widen(got[0]))) and np.all(widen(got[0]) == 0)
+    xt = dev(x)
+    et.rmsnorm(xt, dev(w), 1e-5, out=xt)                  # in place
+    assert_bits(host(xt), got, "in place")
+    xm = _misaligned(dev(x))
+    assert_close(host(et.rmsnorm(xm, dev(w), 1e-5)), y64, yr, "misaligned")
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("rows,d", NORM_SHAPES)
+def test_add_rmsnorm(et, orc, dt, rows, d):
+    g = _rng(2, rows, d, DTS.index(dt))
+    x = _store(g.standard_normal((rows, d)).astype(np.float32), dt)
+    r = _store(g.standard_normal((rows, d)).astype(np.float32), dt)
+    w = _store(g.uniform(0.5, 1.5, d).astype(np.float32), dt)
+    yr, hr, y64 = orc.add_rmsnorm(x, r, w, 1e-5)
+    y, h = et.add_rmsnorm(dev(x), dev(r), dev(w), 1e-5)
+    assert_bits(host(h), hr, f"h {dt} {rows}x{d}")
+    assert_close(host(y), y64, yr, f"y {dt} {rows}x{d}")
+    # in place: y over x, h over the residual (the large-hidden layout)
+    xt, rt = dev(x), dev(r)
+    et.add_rmsnorm(xt, rt, dev(w), 1e-5, out=xt, h=rt)
+    assert_bits(host(rt), hr, "h in place")
+    assert_bits(host(xt), host(y), "y in place")
+    # h over x (allowed when y is elsewhere)
+    xt = dev(x)
+    y2, _ = et.add_rmsnorm(xt, dev(r), dev(w), 1e-5, h=xt)
+    assert_bits(host(xt), hr, "h over x")
+    assert_bits(host(y2), host(y), "y with h over x")
+    ym, hm = et.add_rmsnorm(_misaligned(dev(x)), dev(r), dev(w), 1e-5)
+    assert_bits(host(hm), hr, "h misaligned")
+    assert_close(host(ym), y64, yr, "y misaligned")
+
+
+# ---------------------------------------------------------------- RoPE
+
+ROPE_CASES = [
+    # T, Hq, Hk, D, r, layout, mu, pos_hi
+    (5, 3, 2, 128, 128, 0, 1.0, 4096),
+    (5, 3, 2, 128, 128, 1, 1.0, 4096),
+    (7, 4, 0, 128, 64, 1, 1.1, 1 << 20),
+    (7, 4, 0, 128, 64, 0, 1.1, 1 << 20),
+    (3, 2, 1, 10, 6, 0, 2.0, 100),        # scalar path (r not a multiple of 2V)
+    (3, 2, 1, 10, 6, 1, 0.5, 100),
+    (33, 32, 8, 128, 128, 0, 1.0, 8192),
+    (4, 1, 1, 96, 96, 1, 1.0, 1 << 24),
+    (9, 2, 2, 64, 0, 0, 1.0, 10),         # nothing rotates
+    (1, 64, 8, 128, 128, 0, 1.0, 8191),
+    (70, 5, 3, 32, 16, 0, 1.0, 70000),
+]
+
+
+def _rope_inputs(case, dt, key):
+    T, Hq, Hk, D, r, layout, mu, pos_hi = case
+    g = _rng(3, key, DTS.index(dt))
+    q = _store(g.standard_normal((T, Hq, D)).astype(np.float32), dt)
+    k = _store(g.standard_normal((T, Hk, D)).astype(np.float32), dt) if Hk else None
+    pos = g.integers(0, pos_hi, T).astype(np.int32)
+    inv = wl.inv_freq(1e4, r) if r else np.zeros(1, np.float32)
+    return q, k, pos, inv
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("ci", range(len(ROPE_CASES)))
+def test_rope_qk(et, orc, dt, ci):
+    case = ROPE_CASES[ci]
+    T, Hq, Hk, D, r, layout, mu, _ = case
+    q, k, pos, inv = _rope_inputs(case, dt, ci)
+    mu = float(np.float32(mu))
+    qt, kt = dev(q), (dev(k) if k is not None else None)
+    et.rope_qk(qt, kt, dev(pos), dev(inv), d_rot=r, attn_scaling=mu, layout=layout)
+    for name, src, t in (("q", q, qt), ("k", k, kt)):
+        if src is None:
+            continue
+        ref, y64 = orc.rope(src, pos, r, inv, mu, layout)
+        got = host(t)
+        assert_pair(got, y64, ref, r, layout, f"rope {name} {dt} case {ci}")
+        assert_bits(got[..., r:], src[..., r:], f"pass-through {name}")
+    # the single-tensor entry point agrees bit for bit with the q part
+    q1 = dev(q)
+    et.rope(q1, dev(pos), dev(inv), d_rot=r, attn_scaling=mu, layout=layout)
+    assert_bits(host(q1), host(qt), "rope == rope_qk on q")
+    # scalar path (misaligned buffer) gives the same bits: no reduction involved
+    qm = _misaligned(dev(q))
+    et.rope(qm, dev(pos), dev(inv), d_rot=r, attn_scaling=mu, layout=layout)
+    assert_bits(host(qm), host(qt), "misaligned rope")
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("ci", range(len(ROPE_CASES)))
+def test_rmsnorm_rope_qk(et, orc, dt, ci):
+    case = ROPE_CASES[ci]
+    T, Hq, Hk, D, r, layout, mu, _ = case
+    q, k, pos, inv = _rope_inputs(case, dt, 100 + ci)
+    g = _rng(4, ci, DTS.index(dt))
+    gq = _store(g.uniform(0.5, 1.5, D).astype(np.float32), dt)
+    gk = _store(g.uniform(0.5, 1.5, D).astype(np.float32), dt)
+    if T > 1:
+        q[1, 0, :] = 0 if dt == "f32" else np.uint16(0)   # a zero head row -> 0
+    mu = float(np.float32(mu))
+    qt, kt = dev(q), (dev(k) if k is not None else None)
+    et.rmsnorm_rope_qk(qt, dev(gq), kt, dev(gk) if k is not None else None, 1e-6, dev(pos),
+                       dev(inv), d_rot=r, attn_scaling=mu, layout=layout)
+    for name, src, gain, t in (("q", q, gq, qt), ("k", k, gk, kt)):
+        if src is None:
+            continue
+        ref, y64 = orc.rmsnorm_rope(src, gain, 1e-6, pos, r, inv, mu, layout)
+        got = host(t)
+        assert_pair(got, y64, ref, r, layout, f"qknorm {name} {dt} case {ci}")
+        assert_close(got[..., r:], y64[..., r:], ref[..., r:], f"qknorm tail {name}")
+    if T > 1:
+        assert np.all(widen(host(qt)[1, 0]) == 0)
+
+
+# ------------------------------------------------------------- flat ops
+
+FLAT_N = [1, 7, 8, 9, 1000, 4097, 65539, (1 << 20) + 5]
+
+
+def _gates(g, n):
+    gate = (g.standard_normal(n) * 3).astype(np.float32)
+    special = np.array([1e4, -1e4, 100.0, -100.0, 0.0, -0.0, 30.0, -30.0, 80.0, -80.0], np.float32)
+    gate[: min(n, special.size)] = special[: min(n, special.size)]
+    return gate
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("n", FLAT_N)
+def test_silu_mul(et, orc, dt, n):
+    g = _rng(5, n, DTS.index(dt))
+    gate = _store(_gates(g, n), dt)
+    up = _store(g.standard_normal(n).astype(np.float32), dt)
+    yr, y64 = orc.silu_mul(gate, up)
+    got = host(et.silu_mul(dev(gate), dev(up)))
+    assert not np.any(np.isnan(widen(got)))
+    assert_close(got, y64, yr, f"silu_mul {dt} n={n}")
+    gt = dev(gate)
+    et.silu_mul(gt, dev(up), out=gt)                      # y over gate
+    assert_bits(host(gt), got, "y over gate")
+    ut = dev(up)
+    et.silu_mul(dev(gate), ut, out=ut)                    # y over up
+    assert_bits(host(ut), got, "y over up")
+    assert_bits(host(et.silu_mul(_misaligned(dev(gate)), dev(up))), got, "misaligned")
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("n", FLAT_N)
+def test_add(et, orc, dt, n):
+    g = _rng(6, n, DTS.index(dt))
+    a = _store((g.standard_normal(n) * 10.0 ** g.integers(-4, 4, n)).astype(np.float32), dt)
+    b = _store((g.standard_normal(n) * 10.0 ** g.integers(-4, 4, n)).astype(np.float32), dt)
+    ref = orc.add(a, b)
+    got = host(et.add(dev(a), dev(b)))
+    assert_bits(got, ref, f"add {dt} n={n}")
+    at = dev(a)
+    et.add(at, dev(b), out=at)
+    assert_bits(host(at), ref, "y over a")
+    bt = dev(b)
+    et.add(dev(a), bt, out=bt)
+    assert_bits(host(bt), ref, "y over b")
+    assert_bits(host(et.add(dev(a), _misaligned(dev(b)))), ref, "misaligned")
+
+
+# ------------------------------------------------------------ embedding
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("V,d,n", [(9, 5, 8), (256, 64, 8), (1000, 4096, 37), (50, 6000, 5),
+                                   (128256, 4096, 3), (7, 1, 20)])
+def test_embedding(et, orc, dt, V, d, n):
+    g = _rng(7, V, d, n, DTS.index(dt))
+    table = _store(g.standard_normal((V, d)).astype(np.float32), dt)
+    ids = g.integers(0, V, n).astype(np.int32)
+    ids[: min(n, 3)] = ids[0]                              # repeated
+    if n > 4:
+        ids[3], ids[4] = V, -1                             # out of range -> NaN row
+    ref = orc.embedding(table, ids)
+    got = host(et.embedding(dev(table), dev(ids)))
+    assert_bits(got, ref, f"embedding {dt} V={V} d={d} n={n}")
+    assert_bits(host(et.embedding(_misaligned(dev(table)), dev(ids))), ref, "misaligned table")
+
+
+# ---------------------------------------------------------------- argmax
+
+def _argmax_rows(g, rows, n):
+    x = np.round(g.standard_normal((rows, n)) * 8).astype(np.float32)   # many ties
+    if rows >= 6 and n >= 4:
+        x[1, :] = np.nan
+        x[2, :] = -np.inf
+        x[3, :] = -1.0
+        x[3, n // 2] = -0.0
+        x[3, n - 1] = 0.0
+        x[4, n - 1] = np.inf
+        x[4, 0] = np.inf if n > 1 else x[4, 0]
+        x[5, 0] = np.nan
+    return x
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("rows,n", [(1, 1), (6, 4), (7, 9), (8, 256), (6, 2047), (6, 2048),
+                                    (9, 2049), (6, 70000), (1, 128256), (257, 3000), (6, 128256)])
+@pytest.mark.parametrize("split", [True, False])
+def test_argmax(et, orc, dt, rows, n, split):
+    g = _rng(8, rows, n, DTS.index(dt))
+    x = _store(_argmax_rows(g, rows, n), dt)
+    ref = orc.argmax(x)
+    got = host(et.argmax(dev(x), split=split))
+    assert_bits(got, ref, f"argmax {dt} {rows}x{n} split={split}")
+    got_m = host(et.argmax(_misaligned(dev(x)), split=split))
+    assert_bits(got_m, ref, "misaligned")
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_argmax_empty_rows(et, dt):
+    x = torch.empty((3, 0), dtype=torch.float32 if dt == "f32" else torch.bfloat16, device="cuda")
+    assert host(et.argmax(x)).tolist() == [-1, -1, -1]
+
+
+# ------------------------------------------------------------ tiny chain
+
+def test_tiny_f32_chain(et, orc):
+    """The tiny decoder-layer chain (vocab 256, hidden 64, 8 tokens) op by op."""
+    w = wl.WORKLOADS[1]
+    table, ids = wl.gen_embedding(w)
+    assert_bits(host(et.embedding(dev(table), dev(ids))), orc.embedding(table, ids), "embedding")
+    a, b = wl.gen_add(w)
+    assert_bits(host(et.add(dev(a), dev(b))), orc.add(a, b), "add")
+    x, gain, eps = wl.gen_rmsnorm(w)
+    yr, y64 = orc.rmsnorm(x, gain, eps)
+    got = host(et.rmsnorm(dev(x), dev(gain), eps))
+    assert_f32_rel(got, y64, "rmsnorm")
+    assert np.all(got[3] == 0)
+    q, _, pos, inv = wl.gen_rope(w)
+    s = w.rope
+    ref, y64 = orc.rope(q, pos, s.r, inv, s.mu, s.layout)
+    qt = dev(q)
+    et.rope(qt, dev(pos), dev(inv), d_rot=s.r, attn_scaling=s.mu, layout=s.layout)
+    got = host(qt)
+    assert_pair(got, y64, ref, s.r, s.layout, "rope")
+    assert_bits(got[0], q[0], "position 0 is the identity")
+    gate, up = wl.gen_silu(w)
+    yr, y64 = orc.silu_mul(gate, up)
+    got = host(et.silu_mul(dev(gate), dev(up)))
+    assert_f32_rel(got, y64, "silu_mul")
+    assert got[0, 1] == 0 and np.signbit(got[0, 1]) == np.signbit(-up[0, 1])
+    lg, _ = wl.gen_argmax(w)
+    got = host(et.argmax(dev(lg)))
+    assert_bits(got, orc.argmax(lg), "argmax")
+    # planted rows: a max at indices 10/100/200; all NaN; all -inf; -0 and +0
+    # as the max; two +inf
+    assert [got[1], got[3], got[4], got[5], got[6]] == [10, -1, 0, 5, 17]
+    assert host(et.argmax(torch.empty((1, 0), device="cuda"))).tolist() == [-1]
