@@ -23,13 +23,32 @@ constexpr int kU = 4;  // vectors per thread per input
 
 enum Op { kAdd = 0, kSiluMul = 1 };
 
-template <int OP>
+// silu(g) = g / (1 + e^-g).  f32 storage: library expf and IEEE division.
+// bf16 storage: the f32 value only has to be within ~1e-5 relative before the
+// final rounding to 8 significant bits, so the hardware exp2 and reciprocal
+// (quarter-rate transcendental instructions) replace the library calls -- at
+// bf16 the op moves 6 bytes per element and the accurate sequence would make
+// it ALU-bound.  The reciprocal flushes denormal results, so a 1 + e^-g above
+// 2^64 is scaled by 2^-64 together with g (both exact); e^-g overflowing to
+// +inf still gives g * 0 = -0 for very negative g.
+template <typename S>
+__device__ inline float silu(float g) {
+  if constexpr (sizeof(S) == 4) {
+    return g / (1.0f + expf(-g));
+  } else {
+    const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896340736f);
+    const float t = 1.0f + e;
+    const float sc = t > 0x1p+64f ? 0x1p-64f : 1.0f;
+    return (g * sc) * __builtin_amdgcn_rcpf(t * sc);
+  }
+}
+
+template <typename S, int OP>
 __device__ inline float apply(float a, float b) {
   if constexpr (OP == kAdd) {
     return a + b;
   } else {
-    const float e = expf(-a);
-    return a / (1.0f + e) * b;
+    return silu<S>(a) * b;
   }
 }
 
@@ -53,14 +72,14 @@ __global__ __launch_bounds__(kBlock) void eltwise_vec(const S* a, const S* b, S*
       const int64_t j = first + u * kBlock;
       float o[V];
 #pragma unroll
-      for (int e = 0; e < V; ++e) o[e] = apply<OP>(E::get(av[u], e), E::get(bv[u], e));
+      for (int e = 0; e < V; ++e) o[e] = apply<S, OP>(E::get(av[u], e), E::get(bv[u], e));
       if (j < nvec) st16(y, j * V, E::pack(o));
     }
   }
   // Tail: fewer than V elements after the last whole vector.
   if (blockIdx.x == gridDim.x - 1) {
     const int64_t i = nvec * V + threadIdx.x;
-    if (i < n) E::st(y, i, apply<OP>(E::ld(a, i), E::ld(b, i)));
+    if (i < n) E::st(y, i, apply<S, OP>(E::ld(a, i), E::ld(b, i)));
   }
 }
 
@@ -80,7 +99,7 @@ __global__ __launch_bounds__(kBlock) void eltwise_scalar(const S* a, const S* b,
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int64_t i = first + u * kBlock;
-    if (i < n) E::st(y, i, apply<OP>(av[u], bv[u]));
+    if (i < n) E::st(y, i, apply<S, OP>(av[u], bv[u]));
   }
 }
 

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
 #pragma unroll
     for (int k = 0; k < kVPT; ++k) {
       const int j = k * TPR + t;
-      wr[k] = ld16(w, static_cast<int64_t>(j < nvec ? j : nvec - 1) * V);
+      wr[k] = ld16_keep(w, static_cast<int64_t>(j < nvec ? j : nvec - 1) * V);
     }
 #pragma unroll
     for (int k = 0; k < kVPT; ++k) {
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kLargeTPR) void rmsnorm_rows_large(
     if constexpr (VEC) {
       float g[V], o[V];
       if constexpr (FUSED) st16(h, base + static_cast<int64_t>(j) * V, E::pack(a));
-      E::unpack(ld16(w, static_cast<int64_t>(j) * V), g);
+      E::unpack(ld16_keep(w, static_cast<int64_t>(j) * V), g);
 #pragma unroll
       for (int e = 0; e < V; ++e) o[e] = a[e] * inv * g[e];
       st16(y, base + static_cast<int64_t>(j) * V, E::pack(o));

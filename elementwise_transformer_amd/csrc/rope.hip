@@ -229,11 +229,11 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
     va[u] = ld16(rowp[u], ea);
     vb[u] = ld16(rowp[u], eb);
   }
-  const u32x4 gqa = ld16(gq, ea), gqb = ld16(gq, eb);
+  const u32x4 gqa = ld16_keep(gq, ea), gqb = ld16_keep(gq, eb);
   u32x4 gka = gqa, gkb = gqb;
   if (ra.hk > 0) {
-    gka = ld16(gk, ea);
-    gkb = ld16(gk, eb);
+    gka = ld16_keep(gk, ea);
+    gkb = ld16_keep(gk, eb);
   }
 
   fill_table(cs, t0, ntok, ra, pos, inv_freq);
