@@ -19,7 +19,10 @@ namespace et {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kU = 4;  // vectors per thread per input
+#ifndef ET_ELT_U
+#define ET_ELT_U 4
+#endif
+constexpr int kU = ET_ELT_U;  // vectors per thread per input
 
 enum Op { kAdd = 0, kSiluMul = 1 };
 

@@ -107,13 +107,36 @@ __device__ inline u32x4 ld16_keep(const S* p, int64_t elem) {
 }
 
 // -------------------------------------------------------- wave reductions
-// Sum over aligned groups of W lanes (W a power of two, W <= 64) by an xor
-// butterfly: step 1, 2, 4, ... W/2.  The tree is fixed, every lane of the
-// group ends with the same bits, and nothing depends on the launch size.
+// Sum over aligned groups of W lanes (W a power of two, W <= 64).  Within a
+// 16-lane DPP row the partners come from DPP lane permutations (no LDS
+// crossbar): quad_perm [1,0,3,2] and [2,3,0,1] pair lanes xor 1 and xor 2,
+// row_half_mirror pairs each lane of a quad with a lane of the other quad of
+// its 8-lane half, row_mirror pairs the two halves of the 16-lane row; groups
+// of 32 and 64 add the partner 16 and 32 lanes away.  At every step a lane
+// and its partner add the same two values (in swapped order, which IEEE
+// addition does not see), so every lane of a group ends with the same bits,
+// and the tree depends only on W.
+namespace dpp {
+constexpr int kXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;  // row_half_mirror
+constexpr int kMirror = 0x140;      // row_mirror
+template <int CTRL>
+__device__ inline float mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
+                                                            0xF, false));
+}
+}  // namespace dpp
+
 template <int W>
 __device__ inline float group_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < W; m <<= 1) v += __shfl_xor(v, m, 64);
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "W: power of two <= 64");
+  if constexpr (W >= 2) v += dpp::mov<dpp::kXor1>(v);
+  if constexpr (W >= 4) v += dpp::mov<dpp::kXor2>(v);
+  if constexpr (W >= 8) v += dpp::mov<dpp::kHalfMirror>(v);
+  if constexpr (W >= 16) v += dpp::mov<dpp::kMirror>(v);
+  if constexpr (W >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
   return v;
 }
 

@@ -14,7 +14,10 @@ namespace et {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr int kU = 4;
+#ifndef ET_GATHER_U
+#define ET_GATHER_U 4
+#endif
+constexpr int kU = ET_GATHER_U;
 
 template <typename S, bool VEC>
 __global__ __launch_bounds__(kBlock) void embedding_kernel(const S* __restrict__ table,

@@ -24,8 +24,14 @@
 namespace et {
 namespace {
 
-constexpr int kVPT = 8;          // 16-byte vectors per thread in the register path
+#ifndef ET_NORM_VPT
+#define ET_NORM_VPT 8
+#endif
+constexpr int kVPT = ET_NORM_VPT;  // 16-byte vectors per thread in the register path
 constexpr int kLargeTPR = 1024;  // threads per row in the two-pass path
+#ifndef ET_NORM_W_EARLY
+#define ET_NORM_W_EARLY 0
+#endif
 
 template <int TPR>
 struct NormShape {
@@ -81,6 +87,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
 
   // The row slice of this thread, packed in storage format (h when fused).
   u32x4 xr[kVPT];
+  u32x4 wr[kVPT];
   if constexpr (VEC) {
     u32x4 rr[kVPT];
 #pragma unroll
@@ -89,6 +96,15 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
       const int64_t off = base + static_cast<int64_t>(j < nvec ? j : nvec - 1) * V;
       xr[k] = ld16(x, off);
       if constexpr (FUSED) rr[k] = ld16(res, off);
+    }
+    if constexpr (ET_NORM_W_EARLY) {
+      // The gain is cached (every row reads it); issuing its loads now hides
+      // their latency behind the row loads and the reduction.
+#pragma unroll
+      for (int k = 0; k < kVPT; ++k) {
+        const int j = k * TPR + t;
+        wr[k] = ld16_keep(w, static_cast<int64_t>(j < nvec ? j : nvec - 1) * V);
+      }
     }
     if constexpr (FUSED) {
 #pragma unroll
@@ -141,11 +157,12 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
   if (!live) return;
 
   if constexpr (VEC) {
-    u32x4 wr[kVPT];
+    if constexpr (!ET_NORM_W_EARLY) {
 #pragma unroll
-    for (int k = 0; k < kVPT; ++k) {
-      const int j = k * TPR + t;
-      wr[k] = ld16_keep(w, static_cast<int64_t>(j < nvec ? j : nvec - 1) * V);
+      for (int k = 0; k < kVPT; ++k) {
+        const int j = k * TPR + t;
+        wr[k] = ld16_keep(w, static_cast<int64_t>(j < nvec ? j : nvec - 1) * V);
+      }
     }
 #pragma unroll
     for (int k = 0; k < kVPT; ++k) {

@@ -30,6 +30,12 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kMaxTableBytes = 48 * 1024;
+#ifndef ET_ROPE_UMAX
+#define ET_ROPE_UMAX 4
+#endif
+#ifndef ET_QK_UMAX
+#define ET_QK_UMAX 1
+#endif
 
 struct RopeArgs {
   int64_t T;
@@ -239,28 +245,37 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
   fill_table(cs, t0, ntok, ra, pos, inv_freq);
   __syncthreads();
 
+  // Sums of squares of all U rows first, so their butterflies interleave.
+  float inv[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    float xa[V], xb[V];
     float ss = 0.0f;
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      xa[e] = E::get(va[u], e);
-      ss = __builtin_fmaf(xa[e], xa[e], ss);
+      const float x = E::get(va[u], e);
+      ss = __builtin_fmaf(x, x, ss);
     }
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      xb[e] = E::get(vb[u], e);
-      ss = __builtin_fmaf(xb[e], xb[e], ss);
+      const float x = E::get(vb[u], e);
+      ss = __builtin_fmaf(x, x, ss);
     }
-    ss = group_sum<G>(ss);
-    const float inv = 1.0f / sqrtf(ss / static_cast<float>(ra.D) + a.eps);
+    inv[u] = ss;
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) inv[u] = group_sum<G>(inv[u]);
+#pragma unroll
+  for (int u = 0; u < U; ++u) inv[u] = 1.0f / sqrtf(inv[u] / static_cast<float>(ra.D) + a.eps);
+
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float xa[V], xb[V];
     const u32x4& ga = isq[u] ? gqa : gka;
     const u32x4& gb = isq[u] ? gqb : gkb;
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      xa[e] = xa[e] * inv * E::get(ga, e);
-      xb[e] = xb[e] * inv * E::get(gb, e);
+      xa[e] = E::get(va[u], e) * inv[u] * E::get(ga, e);
+      xb[e] = E::get(vb[u], e) * inv[u] * E::get(gb, e);
     }
     if (kk < a.rsl) {
       const float2* c = cs + tl[u] * ra.half + kk * V;
@@ -395,8 +410,8 @@ void launch_rope(S* q, S* k, const int32_t* pos, const float* inv_freq, RopeArgs
 }
 
 // Largest unroll (4, 2, 1) whose angle table fits the LDS budget.
-inline int pick_u(int64_t spt, int64_t half, int64_t per_u) {
-  for (int u = 4; u >= 1; u >>= 1) {
+inline int pick_u(int64_t spt, int64_t half, int64_t per_u, int umax) {
+  for (int u = umax; u >= 1; u >>= 1) {
     const int64_t ntok = (per_u * u + spt - 1) / spt + 1;
     if (ntok * half * int64_t(sizeof(float2)) <= kMaxTableBytes) return u;
   }
@@ -416,7 +431,7 @@ et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int
   const int ps = vec ? V : 1;
   RopeArgs a = make_args(T, hq, hk, D, r, mu, layout, ps);
   if (a.spt > (1u << 30)) return ET_ERR_BAD_SIZE;
-  const int u = pick_u(a.spt, a.half, kBlock);
+  const int u = pick_u(a.spt, a.half, kBlock, ET_ROPE_UMAX);
   if (u == 0) return ET_ERR_BAD_SIZE;
   (void)hipGetLastError();
   if (vec) {
@@ -489,7 +504,7 @@ et_status qknorm_entry(S* q, const S* gq, int64_t hq, S* k, const S* gk, int64_t
   if (vec) {
     a.rope = make_args(T, hq, hk, D, r, mu, layout, V);
     a.rsl = static_cast<int>(r / (2 * V));
-    const int u = pick_u(heads, a.rope.half, kBlock / g);
+    const int u = pick_u(heads, a.rope.half, kBlock / g, ET_QK_UMAX);
     if (u == 0) return ET_ERR_BAD_SIZE;
     const S* gkk = hk > 0 ? gk : gq;
     switch (g) {
