@@ -118,7 +118,7 @@ def build_ops(w, et, torch):
         lg, _ = wl.gen_argmax(w)
         lt = from_np(lg)
         ao = torch.empty(rows, dtype=torch.int32, device="cuda")
-        ws = torch.empty(max(1, et.argmax_workspace_bytes(rows, n)), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(1, et.argmax_workspace_bytes(rows, n)), dtype=torch.uint8, device="cuda")
         ops.append(Op("argmax", rows * n * lt.element_size() + 4 * rows,
                       lambda: et.argmax(lt, out=ao, workspace=ws), "argmax_chunks"))
     return ops

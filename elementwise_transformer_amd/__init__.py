@@ -258,7 +258,8 @@ def argmax(x: torch.Tensor, out: Optional[torch.Tensor] = None,
            workspace: Optional[torch.Tensor] = None, split: bool = True) -> torch.Tensor:
     """Greedy argmax over the last axis (et_argmax_*): int32 per row, -1 for a
     row with no number.  ``split`` lets long rows spread over several
-    workgroups through a workspace (allocated here unless given)."""
+    workgroups through a workspace: zero-filled here unless given; a given
+    one must be zero-filled before its first use (each call leaves it so)."""
     n = x.shape[-1]
     rows = math.prod(x.shape[:-1])
     out = torch.empty(rows, dtype=torch.int32, device=x.device) if out is None else out
@@ -270,7 +271,7 @@ def argmax(x: torch.Tensor, out: Optional[torch.Tensor] = None,
         need = argmax_workspace_bytes(rows, n)
         if need > 0:
             if workspace is None:
-                workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+                workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
             _dev(workspace)
             ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     _call(f"et_argmax_{_sfx(x)}", _ptr(x), rows, n, _ptr(out), ws_ptr, ws_bytes, _stream(x))

@@ -13,8 +13,9 @@
 //     value and lower index; no-number loses".  That merge is associative and
 //     commutative and -0 == +0, so the answer is the same for any split of
 //     the row: the row is cut into chunks of whole 2048-element tiles, spread
-//     over many workgroups (enough to fill the chip even for one row), and a
-//     second small kernel merges the chunks of each row.
+//     over many workgroups (enough to fill the chip even for one row); the
+//     last workgroup of a row to finish merges the row's partials (one
+//     launch in all).
 //   * Without a workspace one workgroup scans a whole row in one launch.
 #include "et_common.hpp"
 
@@ -108,39 +109,50 @@ __device__ inline Best scan_range(const S* __restrict__ x, int64_t row, int64_t 
 }
 
 // One block per (row, chunk): block b handles chunk b % chunks of row
-// b / chunks.  With chunks == 1 the result goes straight to out.
+// b / chunks.  With chunks == 1 the result goes straight to out.  Otherwise
+// each block stores its (value, index) in the workspace and counts itself in
+// the row's counter; the block that finds it was the last one merges the
+// row's partials, writes out[row] and zeroes the row's cells and counter, so
+// one launch does the whole row and the workspace is left zero-filled.
+// Device-scope release/acquire fences make the partials written by blocks on
+// other XCDs (other L2s) visible to the merging block.
 template <typename S, bool VEC>
 __global__ __launch_bounds__(kBlock) void argmax_chunks(const S* __restrict__ x, int64_t n,
-                                                        int64_t chunk, int chunks,
-                                                        float* __restrict__ wv,
-                                                        int32_t* __restrict__ wi,
+                                                        int64_t chunk, int chunks, float* wv,
+                                                        int32_t* wi, uint32_t* cnt,
                                                         int32_t* __restrict__ out) {
+  __shared__ int last;
   const int64_t row = blockIdx.x / chunks;
   const int c = blockIdx.x % chunks;
   const int64_t lo = c * chunk;
   const int64_t hi = lo + chunk < n ? lo + chunk : n;
   const Best b = scan_range<S, VEC>(x, row, n, lo, hi);
-  if (threadIdx.x == 0) {
-    if (chunks == 1) {
-      out[row] = b.i;
-    } else {
-      wv[blockIdx.x] = b.v;
-      wi[blockIdx.x] = b.i;
-    }
+  if (chunks == 1) {
+    if (threadIdx.x == 0) out[row] = b.i;
+    return;
   }
-}
-
-// One wave per row merges that row's chunk results.
-__global__ __launch_bounds__(kBlock) void argmax_merge(const float* __restrict__ wv,
-                                                       const int32_t* __restrict__ wi, int chunks,
-                                                       int64_t rows, int32_t* __restrict__ out) {
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * (kBlock / 64) + threadIdx.x / 64;
-  if (row >= rows) return;  // per wave; no block barrier below
-  const int lane = threadIdx.x & 63;
-  Best b{0.0f, -1};
-  for (int c = lane; c < chunks; c += 64) b = better(b, Best{wv[row * chunks + c], wi[row * chunks + c]});
-  b = wave_best(b);
-  if (lane == 0) out[row] = b.i;
+  if (threadIdx.x == 0) {
+    wv[blockIdx.x] = b.v;
+    wi[blockIdx.x] = b.i;
+    __threadfence();                                  // release the partial
+    last = atomicAdd(&cnt[row], 1u) == static_cast<uint32_t>(chunks - 1);
+  }
+  __syncthreads();
+  if (!last) return;                                  // uniform per block
+  __threadfence();                                    // acquire the others
+  Best m{0.0f, -1};
+  const int64_t first = row * chunks;
+  for (int k = threadIdx.x; k < chunks; k += kBlock) {
+    m = better(m, Best{__builtin_nontemporal_load(wv + first + k),
+                       __builtin_nontemporal_load(wi + first + k)});
+    wv[first + k] = 0.0f;                             // the row's cells back to zero
+    wi[first + k] = 0;
+  }
+  m = block_best(m);
+  if (threadIdx.x == 0) {
+    out[row] = m.i;
+    cnt[row] = 0u;                                    // ready for the next call
+  }
 }
 
 __global__ void fill_minus_one(int32_t* out, int64_t rows) {
@@ -196,21 +208,21 @@ et_status argmax_entry(const S* x, int64_t rows, int64_t n, int32_t* out, void* 
   const bool vec = (n % V) == 0 && aligned16(x);
   float* wv = static_cast<float*>(ws);
   int32_t* wi = chunks > 1 ? reinterpret_cast<int32_t*>(wv + rows * chunks) : nullptr;
+  uint32_t* cnt = chunks > 1 ? reinterpret_cast<uint32_t*>(wi + rows * chunks) : nullptr;
   const int64_t rows_per_launch = kMaxGrid / chunks;
   for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
     const int64_t m = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
     const unsigned grid = static_cast<unsigned>(m * chunks);
     float* wvp = chunks > 1 ? wv + r0 * chunks : nullptr;
     int32_t* wip = chunks > 1 ? wi + r0 * chunks : nullptr;
+    uint32_t* cp = chunks > 1 ? cnt + r0 : nullptr;
     if (vec)
       argmax_chunks<S, true><<<grid, kBlock, 0, s>>>(x + r0 * n, n, chunk, static_cast<int>(chunks),
-                                                     wvp, wip, out + r0);
+                                                     wvp, wip, cp, out + r0);
     else
       argmax_chunks<S, false><<<grid, kBlock, 0, s>>>(x + r0 * n, n, chunk,
-                                                      static_cast<int>(chunks), wvp, wip, out + r0);
-    if (chunks > 1)
-      argmax_merge<<<static_cast<unsigned>((m + kBlock / 64 - 1) / (kBlock / 64)), kBlock, 0, s>>>(
-          wvp, wip, static_cast<int>(chunks), m, out + r0);
+                                                      static_cast<int>(chunks), wvp, wip, cp,
+                                                      out + r0);
   }
   return launch_status();
 }
@@ -229,7 +241,8 @@ size_t et_argmax_workspace_bytes(int64_t rows, int64_t n) {
   if (chunks <= 1) return 0;
   int64_t cells = 0;
   if (!et::mul_ok(rows, chunks, &cells)) return 0;
-  return static_cast<size_t>(cells) * (sizeof(float) + sizeof(int32_t));
+  return static_cast<size_t>(cells) * (sizeof(float) + sizeof(int32_t)) +
+         static_cast<size_t>(rows) * sizeof(uint32_t);
 }
 
 et_status et_argmax_f32(const float* x, int64_t rows, int64_t n, int32_t* out, void* workspace,

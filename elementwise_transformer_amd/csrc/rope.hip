@@ -16,8 +16,9 @@
 //     boundaries).  It first issues all its loads, then builds a table of
 //     (mu cos, mu sin) for its tokens' pairs in LDS -- one sincosf per
 //     (token, pair), shared by all Hq + Hk heads -- then rotates and stores.
-//   * sincosf is the accurate library routine (full range reduction), since
-//     angles reach ~1e6 rad for positions near 2^20.
+//   * sin/cos come from sincos_angle below: f64 Cody-Waite reduction plus
+//     f32 Taylor polynomials, accurate for the ~1e6 rad angles of positions
+//     near 2^20 at a fraction of the library's large-argument cost.
 //   * In place: each slot is read and written by one thread, reads first.
 //   * QK-norm: a group of G = D/(2V) lanes owns one head row (two vectors per
 //     lane); the sum of squares is per-lane then an xor butterfly over the G
@@ -55,21 +56,99 @@ __device__ inline float rope_angle(int32_t p, float w) {
   return static_cast<float>(static_cast<double>(p) * static_cast<double>(w));
 }
 
-// Fill cs[tl * half + i] = (mu cos, mu sin) for tokens t0 .. t0 + ntok - 1.
-__device__ inline void fill_table(float2* cs, int64_t t0, int ntok, const RopeArgs& a,
-                                  const int32_t* __restrict__ pos,
+// sin and cos of an f32 angle x.  For |x| < 2^31 (every int32 position
+// times a frequency <= 1): Cody-Waite reduction by pi/2 in f64 -- k =
+// rint(x * 2/pi), r = x - k*(pi/2) with pi/2 held as two doubles and fused
+// multiply-adds, so r is exact to ~1e-16 -- then the Taylor series of sin
+// (to r^9) and cos (to r^10) on |r| <= pi/4 in f32, and the quadrant k mod 4.
+// Absolute error < 1e-7 (about 1.5 ulp of the result away from its zeros).
+// The library's sincosf takes a far slower reduction path for the ~1e6 rad
+// angles of positions near 2^20; larger |x| still goes to it.
+__device__ inline void sincos_angle(float x, float* s, float* c) {
+  if (!(fabsf(x) < 0x1p31f)) {
+    sincosf(x, s, c);
+    return;
+  }
+  constexpr double kTwoOverPi = 0x1.45f306dc9c883p-1;
+  constexpr double kPio2Hi = 0x1.921fb54442d18p+0;   // pi/2 = hi + lo + O(2^-108)
+  constexpr double kPio2Lo = 0x1.1a62633145c07p-54;
+  const double xd = static_cast<double>(x);
+  const double k = rint(xd * kTwoOverPi);
+  const double r = fma(-k, kPio2Lo, fma(-k, kPio2Hi, xd));
+  const float rf = static_cast<float>(r);
+  const float r2 = rf * rf;
+  // (-1)^n / (2n+1)! and (-1)^n / (2n)!, rounded to f32
+  float ps = __builtin_fmaf(r2, 0x1.71de3ap-19f, -0x1.a01a02p-13f);
+  ps = __builtin_fmaf(r2, ps, 0x1.111112p-7f);
+  ps = __builtin_fmaf(r2, ps, -0x1.555556p-3f);
+  const float sn = __builtin_fmaf(rf * r2, ps, rf);
+  float pc = __builtin_fmaf(r2, -0x1.27e4fcp-22f, 0x1.a01a02p-16f);
+  pc = __builtin_fmaf(r2, pc, -0x1.6c16c2p-10f);
+  pc = __builtin_fmaf(r2, pc, 0x1.555556p-5f);
+  pc = __builtin_fmaf(r2, pc, -0.5f);
+  const float cn = __builtin_fmaf(r2, pc, 1.0f);
+  const int q = static_cast<int>(k - 4.0 * floor(k * 0.25));  // k mod 4, in 0..3
+  const float s_ = (q & 1) ? cn : sn;
+  const float c_ = (q & 1) ? sn : cn;
+  *s = (q & 2) ? -s_ : s_;
+  *c = ((q + 1) & 2) ? -c_ : c_;
+}
+
+// The block's angle table cs[tl * half + i] = (mu cos, mu sin) for tokens
+// t0 .. t0 + ntok - 1, built in two steps.  table_inputs fetches the position
+// and frequency of this thread's first kTabPre entries; it runs before the
+// row loads, because the row loads are waited for in issue order and a table
+// input fetched after them would wait for every one of them.  table_fill
+// then computes those entries (and, rarely, further ones).
+constexpr int kTabPre = 2;
+struct TabIn {
+  int32_t p[kTabPre];
+  float w[kTabPre];
+};
+
+// Needs half >= 1 (the caller launches no table otherwise).
+__device__ inline TabIn table_inputs(int64_t t0, int ntok, const RopeArgs& a,
+                                     const int32_t* __restrict__ pos,
+                                     const float* __restrict__ inv_freq) {
+  TabIn in;
+  const uint32_t n = static_cast<uint32_t>(ntok) * a.half;
+#pragma unroll
+  for (int k = 0; k < kTabPre; ++k) {
+    uint32_t idx = threadIdx.x + k * kBlock;
+    if (idx >= n) idx = n - 1;  // clamped, never guarded (see above)
+    const uint32_t tl = fdiv(idx, a.fd_half);
+    in.p[k] = pos[t0 + tl];
+    in.w[k] = inv_freq[idx - tl * a.half];
+  }
+  return in;
+}
+
+__device__ inline void table_fill(float2* cs, const TabIn& in, int64_t t0, int ntok,
+                                  const RopeArgs& a, const int32_t* __restrict__ pos,
                                   const float* __restrict__ inv_freq) {
   const uint32_t n = static_cast<uint32_t>(ntok) * a.half;
-  for (uint32_t idx = threadIdx.x; idx < n; idx += kBlock) {
+#pragma unroll
+  for (int k = 0; k < kTabPre; ++k) {
+    const uint32_t idx = threadIdx.x + k * kBlock;
+    if (idx < n) {
+      float sn, cn;
+      sincos_angle(rope_angle(in.p[k], in.w[k]), &sn, &cn);
+      cs[idx] = make_float2(a.mu * cn, a.mu * sn);
+    }
+  }
+  for (uint32_t idx = threadIdx.x + kTabPre * kBlock; idx < n; idx += kBlock) {
     const uint32_t tl = fdiv(idx, a.fd_half);
-    const uint32_t i = idx - tl * a.half;
     float sn, cn;
-    sincosf(rope_angle(pos[t0 + tl], inv_freq[i]), &sn, &cn);
+    sincos_angle(rope_angle(pos[t0 + tl], inv_freq[idx - tl * a.half]), &sn, &cn);
     cs[idx] = make_float2(a.mu * cn, a.mu * sn);
   }
 }
 
 // Element offsets (within a head row) of the two halves of slot kk.
+// Scalar slots (PS == 1) are one pair.  Vector slots are the 16-byte vectors
+// at kk*V and kk*V + r/2 in both layouts, so each load instruction of a wave
+// covers whole contiguous lines: half-layout pairs are (A[e], B[e]);
+// interleaved pairs sit inside each vector.
 template <int PS>
 __device__ inline void slot_offsets(int kk, const RopeArgs& a, int* ea, int* eb) {
   if constexpr (PS == 1) {
@@ -81,13 +160,8 @@ __device__ inline void slot_offsets(int kk, const RopeArgs& a, int* ea, int* eb)
       *eb = 2 * kk + 1;
     }
   } else {
-    if (a.layout == ET_ROPE_HALF) {
-      *ea = kk * PS;
-      *eb = kk * PS + a.half;
-    } else {
-      *ea = 2 * kk * PS;
-      *eb = 2 * kk * PS + PS;
-    }
+    *ea = kk * PS;
+    *eb = kk * PS + a.half;
   }
 }
 
@@ -111,6 +185,7 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32
   uint32_t last = base + kBlock * U - 1;
   if (last >= a.total) last = a.total - 1;
   const int ntok = static_cast<int>(fdiv(last, a.fd_spt) - t0 + 1);
+  const TabIn tin = table_inputs(t0, ntok, a, pos, inv_freq);
 
   // Phase 1: issue every load of this thread.
   S* rowp[U];
@@ -139,8 +214,12 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32
     }
   }
 
+  // Nothing below may be scheduled above this point: the table inputs must
+  // not be consumed before every row load has been issued.
+  __builtin_amdgcn_sched_barrier(0);
+
   // Phase 2: the angle table of this block's tokens.
-  fill_table(cs, t0, ntok, a, pos, inv_freq);
+  table_fill(cs, tin, t0, ntok, a, pos, inv_freq);
   __syncthreads();
 
   // Phase 3: rotate and store.
@@ -148,10 +227,10 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32
   for (int u = 0; u < U; ++u) {
     const uint32_t s = base + u * kBlock + threadIdx.x;
     if (s >= a.total) continue;
-    const float2* c = cs + tl[u] * a.half + kk[u] * PS;
+    const float2* tab = cs + tl[u] * a.half;  // this token's (mu cos, mu sin)
     if constexpr (PS == 1) {
       float x0 = sa[u], x1 = sb[u];
-      rotate(x0, x1, c[0]);
+      rotate(x0, x1, tab[kk[u]]);
       E::st(rowp[u], ea[u], x0);
       E::st(rowp[u], eb[u], x1);
     } else {
@@ -164,12 +243,13 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32
       }
       if (a.layout == ET_ROPE_HALF) {
 #pragma unroll
-        for (int e = 0; e < V; ++e) rotate(xa[e], xb[e], c[e]);
+        for (int e = 0; e < V; ++e) rotate(xa[e], xb[e], tab[ea[u] + e]);
       } else {
+        // element j of the head pairs as pair j / 2
 #pragma unroll
         for (int e = 0; e < V; e += 2) {
-          rotate(xa[e], xa[e + 1], c[e / 2]);
-          rotate(xb[e], xb[e + 1], c[V / 2 + e / 2]);
+          rotate(xa[e], xa[e + 1], tab[ea[u] / 2 + e / 2]);
+          rotate(xb[e], xb[e + 1], tab[eb[u] / 2 + e / 2]);
         }
       }
       st16(rowp[u], ea[u], E::pack(xa));
@@ -188,9 +268,13 @@ struct QkNormArgs {
   int rsl;            // rotated slots per head row (r / (2V))
 };
 
-// Vector path: G lanes per head row, each owns two 16-byte vectors.
-// Slot kk < rsl holds V rotated pairs; slot kk >= rsl holds 2V tail entries.
-template <typename S, int G, int U>
+// Vector path: G lanes per head row, each owns two 16-byte vectors A and B.
+// Interleaved layout: A = vector kk, B = vector kk + G (element D/2 + kk*V),
+// so each load instruction covers a contiguous half of the head rows; a
+// vector rotates (pairs inside it) if it lies below r.  Half layout: lanes
+// kk < rsl own the partners A = kk*V, B = kk*V + r/2; the other lanes own
+// tail vectors r + m*V and r + (nt + m)*V (m = kk - rsl, nt = G - rsl).
+template <typename S, int G, int U, bool ROT>
 __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __restrict__ gq, S* k,
                                                              const S* __restrict__ gk,
                                                              const int32_t* __restrict__ pos,
@@ -209,13 +293,25 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
   uint32_t last = base + kRowsPerPass * U - 1;
   if (last >= a.rows) last = a.rows - 1;
   const int ntok = static_cast<int>(fdiv(last, a.fd_heads) - t0 + 1);
+  TabIn tin{};
+  if constexpr (ROT) tin = table_inputs(t0, ntok, ra, pos, inv_freq);
 
   int ea, eb;
-  if (kk < a.rsl) {
-    slot_offsets<V>(kk, ra, &ea, &eb);
+  bool a_rot, b_rot;
+  if (ra.layout == ET_ROPE_INTERLEAVED) {
+    ea = kk * V;
+    eb = ra.D / 2 + kk * V;
+    a_rot = ea < ra.r;
+    b_rot = eb < ra.r;
+  } else if (kk < a.rsl) {
+    ea = kk * V;
+    eb = kk * V + ra.half;
+    a_rot = b_rot = true;
   } else {
-    ea = ra.r + (kk - a.rsl) * 2 * V;
-    eb = ea + V;
+    const int m = kk - a.rsl;
+    ea = ra.r + m * V;
+    eb = ra.r + (G - a.rsl + m) * V;
+    a_rot = b_rot = false;
   }
 
   S* rowp[U];
@@ -235,15 +331,16 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
     va[u] = ld16(rowp[u], ea);
     vb[u] = ld16(rowp[u], eb);
   }
+  // gk is gq when there are no key heads (the host passes it so), so both
+  // gains load unconditionally.
   const u32x4 gqa = ld16_keep(gq, ea), gqb = ld16_keep(gq, eb);
-  u32x4 gka = gqa, gkb = gqb;
-  if (ra.hk > 0) {
-    gka = ld16_keep(gk, ea);
-    gkb = ld16_keep(gk, eb);
-  }
+  const u32x4 gka = ld16_keep(gk, ea), gkb = ld16_keep(gk, eb);
+  __builtin_amdgcn_sched_barrier(0);  // table inputs are used only below
 
-  fill_table(cs, t0, ntok, ra, pos, inv_freq);
-  __syncthreads();
+  if constexpr (ROT) {
+    table_fill(cs, tin, t0, ntok, ra, pos, inv_freq);
+    __syncthreads();
+  }
 
   // Sums of squares of all U rows first, so their butterflies interleave.
   float inv[U];
@@ -277,17 +374,21 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
       xa[e] = E::get(va[u], e) * inv[u] * E::get(ga, e);
       xb[e] = E::get(vb[u], e) * inv[u] * E::get(gb, e);
     }
-    if (kk < a.rsl) {
-      const float2* c = cs + tl[u] * ra.half + kk * V;
-      if (ra.layout == ET_ROPE_HALF) {
+    const float2* tab = cs + tl[u] * ra.half;  // this token's (mu cos, mu sin)
+    if (!ROT) {
+    } else if (ra.layout == ET_ROPE_HALF) {
+      if (a_rot) {
 #pragma unroll
-        for (int e = 0; e < V; ++e) rotate(xa[e], xb[e], c[e]);
-      } else {
+        for (int e = 0; e < V; ++e) rotate(xa[e], xb[e], tab[ea + e]);
+      }
+    } else {
+      if (a_rot) {
 #pragma unroll
-        for (int e = 0; e < V; e += 2) {
-          rotate(xa[e], xa[e + 1], c[e / 2]);
-          rotate(xb[e], xb[e + 1], c[V / 2 + e / 2]);
-        }
+        for (int e = 0; e < V; e += 2) rotate(xa[e], xa[e + 1], tab[ea / 2 + e / 2]);
+      }
+      if (b_rot) {
+#pragma unroll
+        for (int e = 0; e < V; e += 2) rotate(xb[e], xb[e + 1], tab[eb / 2 + e / 2]);
       }
     }
     if (base + u * kRowsPerPass + grp < a.rows) {
@@ -339,7 +440,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_wave_kernel(
     float x0 = E::ld(row, ia) * inv * E::ld(g, ia);
     float x1 = E::ld(row, ib) * inv * E::ld(g, ib);
     float sn, cn;
-    sincosf(rope_angle(p, inv_freq[i]), &sn, &cn);
+    sincos_angle(rope_angle(p, inv_freq[i]), &sn, &cn);
     rotate(x0, x1, make_float2(ra.mu * cn, ra.mu * sn));
     E::st(row, ia, x0);
     E::st(row, ib, x1);
@@ -446,7 +547,7 @@ et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int
   return launch_status();
 }
 
-template <typename S, int G, int U>
+template <typename S, int G, int U, bool ROT>
 void launch_qknorm_vec(S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
                        const float* inv_freq, QkNormArgs a, int64_t T, hipStream_t s) {
   constexpr int kRowsPerPass = kBlock / G;
@@ -459,7 +560,7 @@ void launch_qknorm_vec(S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
     const int64_t m = T - t0 < tok_per_launch ? T - t0 : tok_per_launch;
     a.rows = static_cast<uint32_t>(m * heads);
     const unsigned grid = static_cast<unsigned>((a.rows + rows_per_block - 1) / rows_per_block);
-    rmsnorm_rope_kernel<S, G, U><<<grid, kBlock, shmem, s>>>(
+    rmsnorm_rope_kernel<S, G, U, ROT><<<grid, kBlock, shmem, s>>>(
         q + t0 * a.rope.hq * a.rope.D, gq, a.rope.hk ? k + t0 * a.rope.hk * a.rope.D : k, gk,
         pos + t0, inv_freq, a);
   }
@@ -468,9 +569,17 @@ void launch_qknorm_vec(S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
 template <typename S, int G>
 void launch_qknorm_vec_u(int u, S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
                          const float* inv_freq, QkNormArgs a, int64_t T, hipStream_t s) {
-  if (u == 4) launch_qknorm_vec<S, G, 4>(q, gq, k, gk, pos, inv_freq, a, T, s);
-  else if (u == 2) launch_qknorm_vec<S, G, 2>(q, gq, k, gk, pos, inv_freq, a, T, s);
-  else launch_qknorm_vec<S, G, 1>(q, gq, k, gk, pos, inv_freq, a, T, s);
+  const bool rot = a.rope.half > 0;
+  if (u == 4) {
+    if (rot) launch_qknorm_vec<S, G, 4, true>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    else launch_qknorm_vec<S, G, 4, false>(q, gq, k, gk, pos, inv_freq, a, T, s);
+  } else if (u == 2) {
+    if (rot) launch_qknorm_vec<S, G, 2, true>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    else launch_qknorm_vec<S, G, 2, false>(q, gq, k, gk, pos, inv_freq, a, T, s);
+  } else {
+    if (rot) launch_qknorm_vec<S, G, 1, true>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    else launch_qknorm_vec<S, G, 1, false>(q, gq, k, gk, pos, inv_freq, a, T, s);
+  }
 }
 
 template <typename S>

@@ -183,12 +183,14 @@ et_status et_embedding_bf16(const et_bf16* table, int64_t V,
  *   number (all NaN, or n == 0).  x: [rows, n]; out: int32 [rows].
  *   n <= INT32_MAX.
  *   workspace: device scratch that lets long rows be split over several
- *   workgroups (two launches).  Either workspace == NULL with
- *   workspace_bytes == 0 (one workgroup per row, one launch, no scratch), or
+ *   workgroups (still one launch).  Either workspace == NULL with
+ *   workspace_bytes == 0 (one workgroup per row, no scratch), or
  *   workspace != NULL with workspace_bytes >= et_argmax_workspace_bytes(rows,
  *   n), else ET_ERR_WORKSPACE (ET_ERR_NULL_POINTER for NULL with a nonzero
- *   size).  The caller owns the workspace; its contents on entry do not
- *   matter.  The result is the same either way.
+ *   size).  The caller owns the workspace.  It must be zero-filled before its
+ *   first use; every call leaves it zero-filled again, so it can be reused as
+ *   is.  Calls that share a workspace must not run concurrently.  The result
+ *   is the same with or without a workspace.
  */
 size_t et_argmax_workspace_bytes(int64_t rows, int64_t n);
 et_status et_argmax_f32(const float* x, int64_t rows, int64_t n, int32_t* out,

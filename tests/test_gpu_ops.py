@@ -309,3 +309,36 @@ def test_tiny_f32_chain(et, orc):
     # as the max; two +inf
     assert [got[1], got[3], got[4], got[5], got[6]] == [10, -1, 0, 5, 17]
     assert host(et.argmax(torch.empty((1, 0), device="cuda"))).tolist() == [-1]
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_argmax_workspace_reuse(et, orc, dt):
+    """One zero-filled workspace serves calls of different shapes in turn and
+    is left all zero by each of them."""
+    shapes = [(1, 128256), (5, 70000), (300, 9000), (1, 128256), (5, 70000), (2, 4096)]
+    need = max(et.argmax_workspace_bytes(r, n) for r, n in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for k, (rows, n) in enumerate(shapes):
+        g = _rng(9, k, DTS.index(dt))
+        x = _store(_argmax_rows(g, rows, n), dt)
+        got = host(et.argmax(dev(x), workspace=ws))
+        assert_bits(got, orc.argmax(x), f"argmax call {k} {rows}x{n}")
+        assert int(ws.count_nonzero()) == 0, f"workspace not left zero after call {k}"
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("layout", [0, 1])
+def test_rope_extreme_positions(et, orc, dt, layout):
+    """Angles across the whole int32 position range (negative, near 2^31,
+    exactly -2^31) with frequencies up to 1: the rotation stays within the
+    pair tolerance everywhere."""
+    g = _rng(10, layout, DTS.index(dt))
+    T, H, D, r = 64, 3, 16, 16
+    x = _store(g.standard_normal((T, H, D)).astype(np.float32), dt)
+    pos = np.concatenate([g.integers(-2**31, 2**31 - 1, T - 6, dtype=np.int64),
+                          [-2**31, 2**31 - 1, -1, 0, 1, 2**24 + 1]]).astype(np.int32)
+    inv = np.array([1.0, 0.999, 0.5, 0.25, 1e-3, 1e-5, 3.3e-8, 1.0], np.float32)
+    xt = dev(x)
+    et.rope(xt, dev(pos), dev(inv), d_rot=r, layout=layout)
+    ref, y64 = orc.rope(x, pos, r, inv, 1.0, layout)
+    assert_pair(host(xt), y64, ref, r, layout, f"extreme positions {dt}")
