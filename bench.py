@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after the timed region, run three 256 MiB device-to-device copies (a "
+                        "plain copy kernel of known size, to scale HBM traffic counters)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="least CPU time spent timing the oracle on whole steps")
     return p.parse_args()
@@ -124,16 +127,21 @@ def build_ops(w, et, torch):
     return ops
 
 
-def traffic_record(op):
-    """Counter-measured HBM bytes per launch for the dominant kernel, from the
-    committed rocprofv3 counter summary, if it was taken on the current
-    kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"{op}_counters.md")
-    if not os.path.exists(path):
+COUNTER_SUMMARY = {2: "prefill_bf16_T4096_hbm_counters.md"}
+
+
+def traffic_record(workload, op):
+    """HBM bytes per launch of `op` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size),
+    if that summary covers this workload and was taken on the current kernel
+    sources; else None."""
+    name = COUNTER_SUMMARY.get(workload)
+    path = os.path.join(ROOT, "profiles", name) if name else ""
+    if not name or not os.path.exists(path):
         return None
     text = open(path).read()
     m_src = re.search(r"source sha256:\s*([0-9a-f]{64})", text)
-    m_b = re.search(r"traffic bytes per launch:\s*([0-9.eE+]+)", text)
+    m_b = re.search(r"traffic bytes per launch:\s*" + re.escape(op) + r"\s+([0-9.eE+]+)", text)
     if not (m_src and m_b):
         return None
     src = os.path.join(ROOT, "elementwise_transformer_amd", "csrc")
@@ -255,6 +263,14 @@ def main():
         for i, (a, b) in plan[s].items():
             ops[i].ms.append(a.elapsed_time(b))
 
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     step_bytes = sum(op.nbytes for op in ops)
     ms_step = wall * 1e3 / args.steps
     per_op = {}
@@ -274,7 +290,7 @@ def main():
     achieved = dom.nbytes / dom_avg_s / 1e9
     roofline = {"bound": "hbm", "kernel": dom.kernel, "op": dom.name, "achieved": round(achieved, 1),
                 "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
-                "traffic": traffic_record(dom.name), "bytes_per_launch": dom.nbytes,
+                "traffic": traffic_record(args.workload, dom.name), "bytes_per_launch": dom.nbytes,
                 "avg_launch_us": round(dom_avg_s * 1e6, 2)}
 
     cpu = None

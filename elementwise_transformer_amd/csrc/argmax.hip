@@ -25,6 +25,9 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kTile = 2048;         // elements per chunk granule
 constexpr int kTargetBlocks = 4096; // aim for this many workgroups in pass 1
+#ifndef ET_ARGMAX_KEY
+#define ET_ARGMAX_KEY 1             // merge through a 64-bit key per row
+#endif
 
 struct Best {
   float v;
@@ -155,6 +158,49 @@ __global__ __launch_bounds__(kBlock) void argmax_chunks(const S* __restrict__ x,
   }
 }
 
+// Same split, merged through one 64-bit key per row instead of a partial per
+// chunk: key = (order-preserving bits of the value) << 32 | ~index, so the
+// largest key is the largest value and, among equal values, the lowest index
+// (-0 is folded into +0 first, so the two tie; 0 means "no number").  Each
+// block atomically maxes its key into the row's slot, waits for that atomic
+// to complete, then counts itself; the last block reads the slot, writes
+// out[row] and zeroes the slot and the counter.  Workspace per row: the key
+// (8 bytes) and the counter (4 bytes, padded to 8).
+__device__ inline uint64_t best_key(Best b) {
+  if (b.i < 0) return 0;
+  uint32_t u = __float_as_uint(b.v);
+  if ((u & 0x7FFFFFFFu) == 0) u = 0;  // -0 -> +0
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(ord) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(b.i));
+}
+
+template <typename S, bool VEC>
+__global__ __launch_bounds__(kBlock) void argmax_chunks_key(const S* __restrict__ x, int64_t n,
+                                                            int64_t chunk, int chunks,
+                                                            unsigned long long* slot, uint32_t* cnt,
+                                                            int32_t* __restrict__ out) {
+  __shared__ int last;
+  const int64_t row = blockIdx.x / chunks;
+  const int c = blockIdx.x % chunks;
+  const int64_t lo = c * chunk;
+  const int64_t hi = lo + chunk < n ? lo + chunk : n;
+  const Best b = scan_range<S, VEC>(x, row, n, lo, hi);
+  if (threadIdx.x == 0) {
+    atomicMax(slot + row, static_cast<unsigned long long>(best_key(b)));
+    // The max must be performed (acknowledged by the memory system) before
+    // this block is counted; wait for every outstanding memory operation.
+    __builtin_amdgcn_s_waitcnt(0);
+    last = atomicAdd(&cnt[2 * row], 1u) == static_cast<uint32_t>(chunks - 1);
+  }
+  __syncthreads();
+  if (last && threadIdx.x == 0) {
+    const unsigned long long key = atomicMax(slot + row, 0ull);  // coherent read
+    out[row] = key == 0 ? -1 : static_cast<int32_t>(~static_cast<uint32_t>(key));
+    slot[row] = 0ull;                                              // ready for the next call
+    cnt[2 * row] = 0u;
+  }
+}
+
 __global__ void fill_minus_one(int32_t* out, int64_t rows) {
   const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (r < rows) out[r] = -1;
@@ -195,6 +241,7 @@ et_status argmax_entry(const S* x, int64_t rows, int64_t n, int32_t* out, void* 
   if (ws) {
     const size_t need = et_argmax_workspace_bytes(rows, n);
     if (ws_bytes < need) return ET_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(ws)) return ET_ERR_WORKSPACE;
     if (need > 0) plan(rows, n, &chunk, &chunks);
     if (!ranges_ok(ws, static_cast<int64_t>(ws_bytes), x, xbytes, false) ||
         !ranges_ok(ws, static_cast<int64_t>(ws_bytes), out, obytes, false))
@@ -206,22 +253,42 @@ et_status argmax_entry(const S* x, int64_t rows, int64_t n, int32_t* out, void* 
   }
   constexpr int V = Elem<S>::V;
   const bool vec = (n % V) == 0 && aligned16(x);
+#if ET_ARGMAX_KEY
+  unsigned long long* slot = static_cast<unsigned long long*>(ws);
+  uint32_t* cnt = chunks > 1 ? reinterpret_cast<uint32_t*>(slot + rows) : nullptr;
+#else
   float* wv = static_cast<float*>(ws);
   int32_t* wi = chunks > 1 ? reinterpret_cast<int32_t*>(wv + rows * chunks) : nullptr;
   uint32_t* cnt = chunks > 1 ? reinterpret_cast<uint32_t*>(wi + rows * chunks) : nullptr;
+#endif
   const int64_t rows_per_launch = kMaxGrid / chunks;
   for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
     const int64_t m = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
     const unsigned grid = static_cast<unsigned>(m * chunks);
+    const int ch = static_cast<int>(chunks);
+#if ET_ARGMAX_KEY
+    if (chunks > 1) {
+      if (vec)
+        argmax_chunks_key<S, true><<<grid, kBlock, 0, s>>>(x + r0 * n, n, chunk, ch, slot + r0,
+                                                           cnt + 2 * r0, out + r0);
+      else
+        argmax_chunks_key<S, false><<<grid, kBlock, 0, s>>>(x + r0 * n, n, chunk, ch, slot + r0,
+                                                            cnt + 2 * r0, out + r0);
+      continue;
+    }
+    float* wvp = nullptr;
+    int32_t* wip = nullptr;
+    uint32_t* cp = nullptr;
+#else
     float* wvp = chunks > 1 ? wv + r0 * chunks : nullptr;
     int32_t* wip = chunks > 1 ? wi + r0 * chunks : nullptr;
     uint32_t* cp = chunks > 1 ? cnt + r0 : nullptr;
+#endif
     if (vec)
-      argmax_chunks<S, true><<<grid, kBlock, 0, s>>>(x + r0 * n, n, chunk, static_cast<int>(chunks),
-                                                     wvp, wip, cp, out + r0);
+      argmax_chunks<S, true><<<grid, kBlock, 0, s>>>(x + r0 * n, n, chunk, ch, wvp, wip, cp,
+                                                     out + r0);
     else
-      argmax_chunks<S, false><<<grid, kBlock, 0, s>>>(x + r0 * n, n, chunk,
-                                                      static_cast<int>(chunks), wvp, wip, cp,
+      argmax_chunks<S, false><<<grid, kBlock, 0, s>>>(x + r0 * n, n, chunk, ch, wvp, wip, cp,
                                                       out + r0);
   }
   return launch_status();
@@ -241,8 +308,13 @@ size_t et_argmax_workspace_bytes(int64_t rows, int64_t n) {
   if (chunks <= 1) return 0;
   int64_t cells = 0;
   if (!et::mul_ok(rows, chunks, &cells)) return 0;
+#if ET_ARGMAX_KEY
+  (void)cells;
+  return static_cast<size_t>(rows) * 16;  // key (8 bytes) + counter (4) + padding (4)
+#else
   return static_cast<size_t>(cells) * (sizeof(float) + sizeof(int32_t)) +
          static_cast<size_t>(rows) * sizeof(uint32_t);
+#endif
 }
 
 et_status et_argmax_f32(const float* x, int64_t rows, int64_t n, int32_t* out, void* workspace,

@@ -29,8 +29,11 @@ namespace {
 #endif
 constexpr int kVPT = ET_NORM_VPT;  // 16-byte vectors per thread in the register path
 constexpr int kLargeTPR = 1024;  // threads per row in the two-pass path
-#ifndef ET_NORM_W_EARLY
-#define ET_NORM_W_EARLY 0
+// Issue the gain loads right after the row loads when a row spans several
+// waves (its cross-wave reduction is long enough to hide them); for one-wave
+// rows the extra registers cost more occupancy than they save.
+#ifndef ET_NORM_W_EARLY_MIN_TPR
+#define ET_NORM_W_EARLY_MIN_TPR 128
 #endif
 
 template <int TPR>
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
       xr[k] = ld16(x, off);
       if constexpr (FUSED) rr[k] = ld16(res, off);
     }
-    if constexpr (ET_NORM_W_EARLY) {
+    if constexpr (TPR >= ET_NORM_W_EARLY_MIN_TPR) {
       // The gain is cached (every row reads it); issuing its loads now hides
       // their latency behind the row loads and the reduction.
 #pragma unroll
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
   if (!live) return;
 
   if constexpr (VEC) {
-    if constexpr (!ET_NORM_W_EARLY) {
+    if constexpr (TPR < ET_NORM_W_EARLY_MIN_TPR) {
 #pragma unroll
       for (int k = 0; k < kVPT; ++k) {
         const int j = k * TPR + t;

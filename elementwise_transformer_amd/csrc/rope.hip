@@ -32,10 +32,13 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kMaxTableBytes = 48 * 1024;
 #ifndef ET_ROPE_UMAX
-#define ET_ROPE_UMAX 4
+#define ET_ROPE_UMAX 2
 #endif
 #ifndef ET_QK_UMAX
-#define ET_QK_UMAX 1
+#define ET_QK_UMAX 2
+#endif
+#ifndef ET_ROPE_SCHED_BARRIER
+#define ET_ROPE_SCHED_BARRIER 1
 #endif
 
 struct RopeArgs {
@@ -214,9 +217,11 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32
     }
   }
 
+#if ET_ROPE_SCHED_BARRIER
   // Nothing below may be scheduled above this point: the table inputs must
   // not be consumed before every row load has been issued.
   __builtin_amdgcn_sched_barrier(0);
+#endif
 
   // Phase 2: the angle table of this block's tokens.
   table_fill(cs, tin, t0, ntok, a, pos, inv_freq);

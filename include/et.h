@@ -186,8 +186,8 @@ et_status et_embedding_bf16(const et_bf16* table, int64_t V,
  *   workgroups (still one launch).  Either workspace == NULL with
  *   workspace_bytes == 0 (one workgroup per row, no scratch), or
  *   workspace != NULL with workspace_bytes >= et_argmax_workspace_bytes(rows,
- *   n), else ET_ERR_WORKSPACE (ET_ERR_NULL_POINTER for NULL with a nonzero
- *   size).  The caller owns the workspace.  It must be zero-filled before its
+ *   n) and 16-byte aligned, else ET_ERR_WORKSPACE (ET_ERR_NULL_POINTER for
+ *   NULL with a nonzero size).  The caller owns the workspace.  It must be zero-filled before its
  *   first use; every call leaves it zero-filled again, so it can be reused as
  *   is.  Calls that share a workspace must not run concurrently.  The result
  *   is the same with or without a workspace.

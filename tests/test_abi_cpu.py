@@ -163,6 +163,7 @@ def test_embedding_and_argmax_validation(sfx):
     need = et.argmax_workspace_bytes(256, 128256)
     assert need > 0
     assert a(A, 256, 128256, B, C, need - 1, S) == 5          # workspace too small
+    assert a(A, 256, 128256, B, P(3 * G + 8), need, S) == 5   # workspace not 16-byte aligned
     assert a(A, 4, 8, A, NULL, 0, S) == 4                     # out inside x
     assert a(NULL, 0, 8, NULL, NULL, 0, S) == 0
 
@@ -173,7 +174,7 @@ def test_argmax_workspace_sizes():
     assert et.argmax_workspace_bytes(4, 0) == 0
     assert et.argmax_workspace_bytes(100000, 1000) == 0       # one chunk per row: none needed
     n256 = et.argmax_workspace_bytes(256, 128256)
-    assert n256 == 256 * 16 * 8 + 256 * 4        # partials + one counter per row
+    assert n256 == 256 * 16                     # per row: a 64-bit key and a counter
     assert et.argmax_workspace_bytes(1, 128256) >= 8 * 2
 
 
