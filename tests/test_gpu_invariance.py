@@ -134,3 +134,22 @@ def test_fused_rmsnorm_rope_equals_unfused(et, dt, D, r, layout):
         scale = np.abs(bn)
         scale[..., :r] = pair_norms(bn, r, layout)[..., :r]
         assert np.all(np.abs(an - bn) <= rel * scale + 1e-30), f"fused qknorm {name} {dt}"
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("d", [64, 4096, 8192, 40000])
+def test_rmsnorm_scalar_path_same_bits(et, dt, d):
+    """A misaligned buffer takes the scalar path, which keeps the vector
+    path's element ownership and summation tree: identical bits."""
+    x = dev(_x((8, d), dt, 11))
+    r = dev(_x((8, d), dt, 12))
+    w = dev(wl.store(np.linspace(0.5, 1.5, d, dtype=np.float32), dt))
+    flat = torch.empty(x.numel() + 8, dtype=x.dtype, device="cuda")
+    xm = flat[1:1 + x.numel()].view(x.shape)
+    xm.copy_(x)
+    assert xm.data_ptr() % 16 != 0
+    assert_bits(host(et.rmsnorm(xm, w, 1e-5)), host(et.rmsnorm(x, w, 1e-5)), f"rmsnorm d={d}")
+    ya, ha = et.add_rmsnorm(x, r, w, 1e-5)
+    yb, hb = et.add_rmsnorm(xm, r, w, 1e-5)
+    assert_bits(host(hb), host(ha), f"h d={d}")
+    assert_bits(host(yb), host(ya), f"add_rmsnorm d={d}")
