@@ -37,7 +37,7 @@ PEAK_GBPS = 8000.0          # MI355X HBM3E peak, vendor figure (8 TB/s)
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", type=int, default=2)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -234,16 +234,19 @@ def main():
     # Timed region: K eager steps, launched back to back on one stream (the
     # host issues a step in far less time than the GPU runs it, so the queue
     # stays ahead).  Inside it, HIP events on the launch stream bracket the
-    # dominant op in every step and one other op per step in turn, so every
-    # op gets live per-launch durations without an event pair around each
-    # launch of every step.
+    # dominant op in every fourth step and, two steps later, one other op in
+    # turn: every op gets live per-launch durations, while each event record
+    # (a marker packet that costs the queue a few microseconds) touches only
+    # a quarter of the steps.
     dom = max(range(len(ops)), key=lambda i: ops[i].nbytes)
     others = [i for i in range(len(ops)) if i != dom]
     plan = []
     for s in range(args.steps):
-        pair = {dom: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))}
-        if others:
-            j = others[s % len(others)]
+        pair = {}
+        if s % 4 == 0:
+            pair[dom] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        elif s % 4 == 2 and others:
+            j = others[(s // 4) % len(others)]
             pair[j] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
         plan.append(pair)
     torch.cuda.synchronize()

@@ -8,7 +8,8 @@
 // Design (HBM-bound; one read and one write per element):
 //   * A row is owned by a group of TPR threads (TPR a power of two, 1..1024)
 //     picked from d alone.  Thread t of the group owns 16-byte vectors
-//     j = k*TPR + t, k = 0..7, so consecutive lanes touch consecutive 16 B.
+//     j = k*TPR + t, k = 0..VPT-1 (VPT 4 or 8, also from d alone), so
+//     consecutive lanes touch consecutive 16 B.
 //   * The whole row stays in registers: read once, reduced, scaled, written.
 //   * Sum of squares: f32 FMA over the thread's elements in (k, element)
 //     order, then an xor butterfly over min(TPR, 64) lanes, then (TPR > 64)
@@ -17,6 +18,7 @@
 //     call holds.
 //   * Rows longer than 8192 vectors fall back to a two-pass kernel (1024
 //     threads per row, the row re-read for the write pass).
+//   * Blocks of 128 threads (or one row of more): rows are independent.
 //   * Unaligned buffers or d not a multiple of the vector width take the same
 //     kernels with scalar loads (same ownership, same sums).
 #include "et_common.hpp"
@@ -24,10 +26,9 @@
 namespace et {
 namespace {
 
-#ifndef ET_NORM_VPT
-#define ET_NORM_VPT 8
-#endif
-constexpr int kVPT = ET_NORM_VPT;  // 16-byte vectors per thread in the register path
+// 16-byte vectors per thread in the register path: 4 for rows of 1024..4096
+// vectors (256..1024 threads per row), 8 otherwise.
+constexpr int kVPTMax = 8;
 constexpr int kLargeTPR = 1024;  // threads per row in the two-pass path
 // Issue the gain loads right after the row loads when a row spans several
 // waves (its cross-wave reduction is long enough to hide them); for one-wave
@@ -36,9 +37,13 @@ constexpr int kLargeTPR = 1024;  // threads per row in the two-pass path
 #define ET_NORM_W_EARLY_MIN_TPR 128
 #endif
 
+#ifndef ET_NORM_BLOCK
+#define ET_NORM_BLOCK 128
+#endif
+
 template <int TPR>
 struct NormShape {
-  static constexpr int kBlock = TPR < 256 ? 256 : TPR;
+  static constexpr int kBlock = TPR < ET_NORM_BLOCK ? ET_NORM_BLOCK : TPR;
   static constexpr int kRowsPerBlock = kBlock / TPR;
   static constexpr int kGroup = TPR < 64 ? TPR : 64;  // lanes of one row inside a wave
   static constexpr int kWavesPerRow = TPR > 64 ? TPR / 64 : 1;
@@ -68,7 +73,7 @@ __device__ inline float inv_rms(float ss, int d, float eps) {
 // __restrict__: y may be x and h may be res (in place).  Every load of a
 // thread is issued before its first store, and a thread touches only the
 // elements it owns.
-template <typename S, int TPR, bool FUSED, bool VEC>
+template <typename S, int TPR, int VPT, bool FUSED, bool VEC>
 __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
     const S* x, const S* res, const S* __restrict__ w, S* y, S* h, int64_t rows, int d,
     float eps) {
@@ -89,12 +94,12 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
   const int nvec = (d + V - 1) / V;
 
   // The row slice of this thread, packed in storage format (h when fused).
-  u32x4 xr[kVPT];
-  u32x4 wr[kVPT];
+  u32x4 xr[VPT];
+  u32x4 wr[VPT];
   if constexpr (VEC) {
-    u32x4 rr[kVPT];
+    u32x4 rr[VPT];
 #pragma unroll
-    for (int k = 0; k < kVPT; ++k) {
+    for (int k = 0; k < VPT; ++k) {
       const int j = k * TPR + t;
       const int64_t off = base + static_cast<int64_t>(j < nvec ? j : nvec - 1) * V;
       xr[k] = ld16(x, off);
@@ -104,14 +109,14 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
       // The gain is cached (every row reads it); issuing its loads now hides
       // their latency behind the row loads and the reduction.
 #pragma unroll
-      for (int k = 0; k < kVPT; ++k) {
+      for (int k = 0; k < VPT; ++k) {
         const int j = k * TPR + t;
         wr[k] = ld16_keep(w, static_cast<int64_t>(j < nvec ? j : nvec - 1) * V);
       }
     }
     if constexpr (FUSED) {
 #pragma unroll
-      for (int k = 0; k < kVPT; ++k) {
+      for (int k = 0; k < VPT; ++k) {
         const int j = k * TPR + t;
         float a[V];
 #pragma unroll
@@ -121,9 +126,9 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
       }
     }
   } else {
-    float a[kVPT][V];
+    float a[VPT][V];
 #pragma unroll
-    for (int k = 0; k < kVPT; ++k) {
+    for (int k = 0; k < VPT; ++k) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const int i = (k * TPR + t) * V + e;
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
       }
     }
 #pragma unroll
-    for (int k = 0; k < kVPT; ++k) {
+    for (int k = 0; k < VPT; ++k) {
       xr[k] = E::pack(a[k]);
       if constexpr (FUSED) {
 #pragma unroll
@@ -147,7 +152,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
 
   float ss = 0.0f;
 #pragma unroll
-  for (int k = 0; k < kVPT; ++k) {
+  for (int k = 0; k < VPT; ++k) {
 #pragma unroll
     for (int e = 0; e < V; ++e) {
       const int i = (k * TPR + t) * V + e;
@@ -162,13 +167,13 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
   if constexpr (VEC) {
     if constexpr (TPR < ET_NORM_W_EARLY_MIN_TPR) {
 #pragma unroll
-      for (int k = 0; k < kVPT; ++k) {
+      for (int k = 0; k < VPT; ++k) {
         const int j = k * TPR + t;
         wr[k] = ld16_keep(w, static_cast<int64_t>(j < nvec ? j : nvec - 1) * V);
       }
     }
 #pragma unroll
-    for (int k = 0; k < kVPT; ++k) {
+    for (int k = 0; k < VPT; ++k) {
       const int j = k * TPR + t;
       float o[V];
 #pragma unroll
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < kVPT; ++k) {
+    for (int k = 0; k < VPT; ++k) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
         const int i = (k * TPR + t) * V + e;
@@ -259,18 +264,24 @@ __global__ __launch_bounds__(kLargeTPR) void rmsnorm_rows_large(
   }
 }
 
-// Threads per row for the register path: the smallest power of two with
-// TPR * 8 >= number of vectors; 0 selects the two-pass path.
-inline int pick_tpr(int64_t nvec) {
+// Launch shape from the row length alone: vectors per thread (4 for rows of
+// 1024..4096 vectors, else 8) and threads per row (the smallest power of two
+// with TPR * VPT >= number of vectors); TPR 0 selects the two-pass path.
+inline void pick_shape(int64_t nvec, int* tpr_out, int* vpt_out) {
+  const int vpt = (nvec >= 1024 && nvec <= 4096) ? 4 : kVPTMax;
   int tpr = 1;
-  while (static_cast<int64_t>(tpr) * kVPT < nvec) {
+  while (static_cast<int64_t>(tpr) * vpt < nvec) {
     tpr <<= 1;
-    if (tpr > 1024) return 0;
+    if (tpr > 1024) {
+      tpr = 0;
+      break;
+    }
   }
-  return tpr;
+  *tpr_out = tpr;
+  *vpt_out = vpt;
 }
 
-template <typename S, int TPR, bool FUSED, bool VEC>
+template <typename S, int TPR, int VPT, bool FUSED, bool VEC>
 void launch_rows(const S* x, const S* res, const S* w, S* y, S* h, int64_t rows, int d, float eps,
                  hipStream_t s) {
   using Sh = NormShape<TPR>;
@@ -279,26 +290,35 @@ void launch_rows(const S* x, const S* res, const S* w, S* y, S* h, int64_t rows,
                                                                 : kMaxGrid * Sh::kRowsPerBlock;
     const int64_t off = r0 * d;
     const unsigned grid = static_cast<unsigned>((n + Sh::kRowsPerBlock - 1) / Sh::kRowsPerBlock);
-    rmsnorm_rows<S, TPR, FUSED, VEC><<<grid, Sh::kBlock, 0, s>>>(
+    rmsnorm_rows<S, TPR, VPT, FUSED, VEC><<<grid, Sh::kBlock, 0, s>>>(
         x + off, FUSED ? res + off : nullptr, w, y + off, FUSED ? h + off : nullptr, n, d, eps);
   }
 }
 
 template <typename S, bool FUSED, bool VEC>
-void dispatch_tpr(int tpr, const S* x, const S* res, const S* w, S* y, S* h, int64_t rows, int d,
+void dispatch_tpr(int tpr, int vpt, const S* x, const S* res, const S* w, S* y, S* h, int64_t rows, int d,
                   float eps, hipStream_t s) {
   switch (tpr) {
-    case 1: launch_rows<S, 1, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
-    case 2: launch_rows<S, 2, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
-    case 4: launch_rows<S, 4, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
-    case 8: launch_rows<S, 8, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
-    case 16: launch_rows<S, 16, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
-    case 32: launch_rows<S, 32, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
-    case 64: launch_rows<S, 64, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
-    case 128: launch_rows<S, 128, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
-    case 256: launch_rows<S, 256, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
-    case 512: launch_rows<S, 512, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
-    case 1024: launch_rows<S, 1024, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
+    case 1: launch_rows<S, 1, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
+    case 2: launch_rows<S, 2, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
+    case 4: launch_rows<S, 4, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
+    case 8: launch_rows<S, 8, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
+    case 16: launch_rows<S, 16, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
+    case 32: launch_rows<S, 32, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
+    case 64: launch_rows<S, 64, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
+    case 128: launch_rows<S, 128, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
+    case 256:
+      if (vpt == 4) launch_rows<S, 256, 4, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s);
+      else launch_rows<S, 256, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s);
+      break;
+    case 512:
+      if (vpt == 4) launch_rows<S, 512, 4, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s);
+      else launch_rows<S, 512, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s);
+      break;
+    case 1024:
+      if (vpt == 4) launch_rows<S, 1024, 4, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s);
+      else launch_rows<S, 1024, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s);
+      break;
     default: {
       for (int64_t r0 = 0; r0 < rows; r0 += kMaxGrid) {
         const int64_t n = rows - r0 < kMaxGrid ? rows - r0 : kMaxGrid;
@@ -335,13 +355,14 @@ et_status norm_entry(const S* x, const S* res, const S* w, S* y, S* h, int64_t r
   constexpr int V = Elem<S>::V;
   const bool vec = (d % V) == 0 && aligned16(x) && aligned16(w) && aligned16(y) &&
                    (!FUSED || (aligned16(res) && aligned16(h)));
-  const int tpr = pick_tpr((d + V - 1) / V);
+  int tpr = 0, vpt = 0;
+  pick_shape((d + V - 1) / V, &tpr, &vpt);
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (vec)
-    dispatch_tpr<S, FUSED, true>(tpr, x, res, w, y, h, rows, static_cast<int>(d), eps, s);
+    dispatch_tpr<S, FUSED, true>(tpr, vpt, x, res, w, y, h, rows, static_cast<int>(d), eps, s);
   else
-    dispatch_tpr<S, FUSED, false>(tpr, x, res, w, y, h, rows, static_cast<int>(d), eps, s);
+    dispatch_tpr<S, FUSED, false>(tpr, vpt, x, res, w, y, h, rows, static_cast<int>(d), eps, s);
   return launch_status();
 }
 
