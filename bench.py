@@ -354,7 +354,11 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom.kernel, "op": dom.name, "achieved": round(achieved, 1),
                 "peak": PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
                 "traffic": traffic_record(args.workload, dom.name), "bytes_per_launch": dom.nbytes,
-                "avg_launch_us": round(dom_avg_s * 1e6, 2)}
+                "avg_launch_us": round(dom_avg_s * 1e6, 2),
+                "note": "SiLU-mul and RoPE kernels whose output fits the 256 MB Infinity Cache use "
+                        "device-scope stores; the cache writes part of their output back to HBM "
+                        "after the kernel ends, so their per-kernel figures exclude that part, "
+                        "while the whole-step value includes it"}
 
     cpu = None
     if not args.no_cpu_baseline:

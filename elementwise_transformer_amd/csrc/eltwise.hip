@@ -18,11 +18,33 @@
 namespace et {
 namespace {
 
+#ifndef ET_POL_ELT
+#define ET_POL_ELT 0  // 0: by size, 1: non-temporal, 2: device scope
+#endif
+#ifndef ET_POL_ADD
+#define ET_POL_ADD 0  // 0: by size, 1: non-temporal, 2: device scope
+#endif
+
 constexpr int kBlock = 256;
 #ifndef ET_ELT_U
 #define ET_ELT_U 4
 #endif
 constexpr int kU = ET_ELT_U;  // vectors per thread per input
+#ifndef ET_ELT_WAVE
+#define ET_ELT_WAVE 1
+#endif
+
+// Vector index of slot u of thread tid in block b.  A block covers
+// kBlock * kU consecutive vectors; with ET_ELT_WAVE each wave owns a
+// contiguous quarter of them (slot u of lane l at u * 64 + l), else slot u
+// of the block is one contiguous kBlock-vector stripe.
+__device__ inline int64_t slot_index(int64_t b, int tid, int u) {
+  if constexpr (ET_ELT_WAVE) {
+    return b * (kBlock * kU) + (tid / 64) * (64 * kU) + u * 64 + (tid % 64);
+  } else {
+    return b * (kBlock * kU) + u * kBlock + tid;
+  }
+}
 
 enum Op { kAdd = 0, kSiluMul = 1 };
 
@@ -55,28 +77,31 @@ __device__ inline float apply(float a, float b) {
   }
 }
 
-template <typename S, int OP>
+template <typename S, int OP, int POL>
 __global__ __launch_bounds__(kBlock) void eltwise_vec(const S* a, const S* b, S* y, int64_t nvec,
                                                       int64_t n) {
   using E = Elem<S>;
   constexpr int V = E::V;
-  const int64_t first = static_cast<int64_t>(blockIdx.x) * (kBlock * kU) + threadIdx.x;
+  const int64_t blk = blockIdx.x;
   if (nvec > 0) {
     u32x4 av[kU], bv[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int64_t j = first + u * kBlock;
+      const int64_t j = slot_index(blk, threadIdx.x, u);
       const int64_t jc = j < nvec ? j : nvec - 1;
       av[u] = ld16(a, jc * V);
       bv[u] = ld16(b, jc * V);
     }
+    // Stores go through a resource based at the block's first vector.
+    const int64_t vbase = blk * (kBlock * kU);
+    const __amdgpu_buffer_rsrc_t ry = out_rsrc(y + vbase * V, (nvec - vbase) * 16);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int64_t j = first + u * kBlock;
+      const int64_t j = slot_index(blk, threadIdx.x, u);
       float o[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) o[e] = apply<S, OP>(E::get(av[u], e), E::get(bv[u], e));
-      if (j < nvec) st16(y, j * V, E::pack(o));
+      if (j < nvec) st16_buf<POL>(ry, static_cast<int>((j - vbase) * 16), E::pack(o));
     }
   }
   // Tail: fewer than V elements after the last whole vector.
@@ -123,14 +148,19 @@ et_status eltwise_entry(const S* a, const S* b, S* y, int64_t n, void* stream) {
     // a vector boundary, only the last one has a tail.
     const int64_t per_launch = kMaxGrid * kBlock * kU;  // vectors
     const int64_t nvec_all = n / V;
+    const int pol = store_policy(bytes, OP == kAdd ? ET_POL_ADD : ET_POL_ELT);
     for (int64_t v0 = 0;; v0 += per_launch) {
       const int64_t nvec = nvec_all - v0 < per_launch ? nvec_all - v0 : per_launch;
       const bool last = v0 + nvec >= nvec_all;
       const int64_t elems = last ? n - v0 * V : nvec * V;
       const int64_t blocks = nvec > 0 ? (nvec + kBlock * kU - 1) / (kBlock * kU) : 1;
       const int64_t off = v0 * V;
-      eltwise_vec<S, OP><<<static_cast<unsigned>(blocks), kBlock, 0, s>>>(a + off, b + off,
-                                                                          y + off, nvec, elems);
+      if (pol == kStoreDevice)
+        eltwise_vec<S, OP, kStoreDevice><<<static_cast<unsigned>(blocks), kBlock, 0, s>>>(
+            a + off, b + off, y + off, nvec, elems);
+      else
+        eltwise_vec<S, OP, kStoreStream><<<static_cast<unsigned>(blocks), kBlock, 0, s>>>(
+            a + off, b + off, y + off, nvec, elems);
       if (last) break;
     }
   } else {

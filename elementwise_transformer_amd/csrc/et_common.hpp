@@ -106,6 +106,32 @@ __device__ inline u32x4 ld16_keep(const S* p, int64_t elem) {
   return *reinterpret_cast<const u32x4*>(p + elem);
 }
 
+// Output stores through a buffer resource, which carries the cache-policy
+// bits a plain pointer store cannot:
+//   kStoreStream (nt): non-temporal, the store streams to HBM.
+//   kStoreDevice (sc1): device-scope write-through; the line leaves this
+//     XCD's L2 at once.  Measured on MI355X: a SiLU-mul writing 117 MB ran
+//     51.4 us with these stores against 56.1 us with non-temporal ones (and
+//     the whole eight-op step 2.5 % faster), while one writing 470 MB ran
+//     2 % slower -- the gain holds while the output fits the 256 MB
+//     Infinity Cache, which then writes it back to HBM behind later work.
+// The host picks the policy from the output size (store_policy below).
+enum StorePolicy : int { kStoreStream = 2, kStoreDevice = 16 };
+
+// A resource for `bytes` bytes from `base` (a uniform pointer); stores at
+// byte offsets beyond min(bytes, 2^31 - 1) are dropped by the hardware.
+__device__ inline __amdgpu_buffer_rsrc_t out_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (bytes < 0 ? 0 : static_cast<int>(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+template <int POL>
+__device__ inline void st16_buf(__amdgpu_buffer_rsrc_t r, int byte_off, const u32x4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, byte_off, 0, POL);
+}
+
 // -------------------------------------------------------- wave reductions
 // Sum over aligned groups of W lanes (W a power of two, W <= 64).  Within a
 // 16-lane DPP row the partners come from DPP lane permutations (no LDS
@@ -196,5 +222,14 @@ inline et_status launch_status() {
 
 // Largest grid.x the launchers use per launch; longer work is split.
 constexpr int64_t kMaxGrid = int64_t{1} << 30;
+
+// Device-scope stores while a launch writes at most this much, else
+// non-temporal ones (see StorePolicy).
+constexpr int64_t kDeviceStoreMaxBytes = int64_t{128} << 20;
+inline int store_policy(int64_t out_bytes, int force = 0) {
+  if (force == 1) return kStoreStream;
+  if (force == 2) return kStoreDevice;
+  return out_bytes <= kDeviceStoreMaxBytes ? kStoreDevice : kStoreStream;
+}
 
 }  // namespace et

@@ -13,13 +13,20 @@
 namespace et {
 namespace {
 
-constexpr int kBlock = 256;
+#ifndef ET_POL_GATHER
+#define ET_POL_GATHER 1  // 0: by size, 1: non-temporal, 2: device scope
+#endif
+
+#ifndef ET_GATHER_BLOCK
+#define ET_GATHER_BLOCK 64
+#endif
+constexpr int kBlock = ET_GATHER_BLOCK;
 #ifndef ET_GATHER_U
-#define ET_GATHER_U 4
+#define ET_GATHER_U 8
 #endif
 constexpr int kU = ET_GATHER_U;
 
-template <typename S, bool VEC>
+template <typename S, bool VEC, int POL>
 __global__ __launch_bounds__(kBlock) void embedding_kernel(const S* __restrict__ table,
                                                            int64_t vocab,
                                                            const int32_t* __restrict__ ids,
@@ -34,6 +41,10 @@ __global__ __launch_bounds__(kBlock) void embedding_kernel(const S* __restrict__
   if constexpr (VEC) {
     const int nvec = d / V;
     const int first = c * (kBlock * kU) + threadIdx.x;
+    // Stores through a resource based at this block's chunk of the row.
+    const int64_t cbase = dst + static_cast<int64_t>(c) * (kBlock * kU) * V;
+    const __amdgpu_buffer_rsrc_t ro =
+        out_rsrc(out + cbase, (static_cast<int64_t>(nvec) - c * (kBlock * kU)) * 16);
     if (ok) {
       const int64_t src = static_cast<int64_t>(id) * d;
       u32x4 r[kU];
@@ -45,14 +56,14 @@ __global__ __launch_bounds__(kBlock) void embedding_kernel(const S* __restrict__
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int j = first + u * kBlock;
-        if (j < nvec) st16(out, dst + static_cast<int64_t>(j) * V, r[u]);
+        if (j < nvec) st16_buf<POL>(ro, (threadIdx.x + u * kBlock) * 16, r[u]);
       }
     } else {
       const u32x4 nan = u32x4{E::kQuietNaN, E::kQuietNaN, E::kQuietNaN, E::kQuietNaN};
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int j = first + u * kBlock;
-        if (j < nvec) st16(out, dst + static_cast<int64_t>(j) * V, nan);
+        if (j < nvec) st16_buf<POL>(ro, (threadIdx.x + u * kBlock) * 16, nan);
       }
     }
   } else {
@@ -102,13 +113,17 @@ et_status embedding_entry(const S* table, int64_t vocab, const int32_t* ids, S* 
   for (int64_t t0 = 0; t0 < n; t0 += rows_per_launch) {
     const int64_t m = n - t0 < rows_per_launch ? n - t0 : rows_per_launch;
     const unsigned grid = static_cast<unsigned>(m * cpr);
-    if (vec)
-      embedding_kernel<S, true><<<grid, kBlock, 0, s>>>(table, vocab, ids + t0, out + t0 * d,
-                                                        static_cast<int>(d), static_cast<int>(cpr));
+    // Non-temporal stores by default: device-scope ones (see StorePolicy)
+    // made the measured eight-op step slower here.
+    if (vec && store_policy(obytes, ET_POL_GATHER) == kStoreDevice)
+      embedding_kernel<S, true, kStoreDevice><<<grid, kBlock, 0, s>>>(
+          table, vocab, ids + t0, out + t0 * d, static_cast<int>(d), static_cast<int>(cpr));
+    else if (vec)
+      embedding_kernel<S, true, kStoreStream><<<grid, kBlock, 0, s>>>(
+          table, vocab, ids + t0, out + t0 * d, static_cast<int>(d), static_cast<int>(cpr));
     else
-      embedding_kernel<S, false><<<grid, kBlock, 0, s>>>(table, vocab, ids + t0, out + t0 * d,
-                                                         static_cast<int>(d),
-                                                         static_cast<int>(cpr));
+      embedding_kernel<S, false, kStoreStream><<<grid, kBlock, 0, s>>>(
+          table, vocab, ids + t0, out + t0 * d, static_cast<int>(d), static_cast<int>(cpr));
   }
   return launch_status();
 }

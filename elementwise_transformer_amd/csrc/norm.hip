@@ -26,6 +26,10 @@
 namespace et {
 namespace {
 
+#ifndef ET_POL_NORM
+#define ET_POL_NORM 1  // 0: by size, 1: non-temporal, 2: device scope
+#endif
+
 // 16-byte vectors per thread in the register path: 4 for rows of 1024..4096
 // vectors (256..1024 threads per row), 8 otherwise.
 constexpr int kVPTMax = 8;
@@ -35,6 +39,10 @@ constexpr int kLargeTPR = 1024;  // threads per row in the two-pass path
 // rows the extra registers cost more occupancy than they save.
 #ifndef ET_NORM_W_EARLY_MIN_TPR
 #define ET_NORM_W_EARLY_MIN_TPR 128
+#endif
+
+#ifndef ET_NORM_VPT4_MIN
+#define ET_NORM_VPT4_MIN 1024
 #endif
 
 #ifndef ET_NORM_BLOCK
@@ -65,6 +73,22 @@ __device__ inline float row_sum(float part, float* lds, int row_in_block, int la
   return s;
 }
 
+#ifndef ET_NORM_WAVE
+#define ET_NORM_WAVE 1
+#endif
+
+// Vector slot k of thread t in its row.  Rows of one wave or less: slot k is
+// the k-th TPR-vector stripe.  Longer rows: each wave owns a contiguous run of
+// 64 * VPT vectors, slot k of lane l at k * 64 + l inside it.
+template <int TPR, int VPT>
+__device__ inline int own(int k, int t) {
+  if constexpr (TPR > 64 && ET_NORM_WAVE) {
+    return (t / 64) * (64 * VPT) + k * 64 + (t % 64);
+  } else {
+    return k * TPR + t;
+  }
+}
+
 __device__ inline float inv_rms(float ss, int d, float eps) {
   return 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
 }
@@ -73,7 +97,7 @@ __device__ inline float inv_rms(float ss, int d, float eps) {
 // __restrict__: y may be x and h may be res (in place).  Every load of a
 // thread is issued before its first store, and a thread touches only the
 // elements it owns.
-template <typename S, int TPR, int VPT, bool FUSED, bool VEC>
+template <typename S, int TPR, int VPT, bool FUSED, bool VEC, int POL>
 __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
     const S* x, const S* res, const S* __restrict__ w, S* y, S* h, int64_t rows, int d,
     float eps) {
@@ -92,6 +116,12 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
   // masked to 0.
   const int64_t base = (live ? row : rows - 1) * d;
   const int nvec = (d + V - 1) / V;
+  // Vector stores go through resources based at the block's first row; the
+  // byte offset of element e of this thread's row is (row_in_block * d + e)
+  // times the element size, well below 2^31 for the register path.
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * Sh::kRowsPerBlock;
+  const int64_t span = (rows - row0) * d * static_cast<int64_t>(sizeof(S));
+  const int rel = row_in_block * d;
 
   // The row slice of this thread, packed in storage format (h when fused).
   u32x4 xr[VPT];
@@ -100,7 +130,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
     u32x4 rr[VPT];
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      const int j = k * TPR + t;
+      const int j = own<TPR, VPT>(k, t);
       const int64_t off = base + static_cast<int64_t>(j < nvec ? j : nvec - 1) * V;
       xr[k] = ld16(x, off);
       if constexpr (FUSED) rr[k] = ld16(res, off);
@@ -110,19 +140,20 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
       // their latency behind the row loads and the reduction.
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
-        const int j = k * TPR + t;
+        const int j = own<TPR, VPT>(k, t);
         wr[k] = ld16_keep(w, static_cast<int64_t>(j < nvec ? j : nvec - 1) * V);
       }
     }
     if constexpr (FUSED) {
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
-        const int j = k * TPR + t;
+        const int j = own<TPR, VPT>(k, t);
         float a[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) a[e] = E::get(xr[k], e) + E::get(rr[k], e);
         xr[k] = E::pack(a);  // h rounded to storage, normalised as stored
-        if (live && j < nvec) st16(h, base + static_cast<int64_t>(j) * V, xr[k]);
+        if (live && j < nvec)
+          st16_buf<POL>(out_rsrc(h + row0 * d, span), (rel + j * V) * int(sizeof(S)), xr[k]);
       }
     }
   } else {
@@ -131,7 +162,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
     for (int k = 0; k < VPT; ++k) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        const int i = (k * TPR + t) * V + e;
+        const int i = (own<TPR, VPT>(k, t)) * V + e;
         const int64_t off = base + (i < d ? i : d - 1);
         a[k][e] = E::ld(x, off);
         if constexpr (FUSED) a[k][e] = a[k][e] + E::ld(res, off);
@@ -143,7 +174,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
       if constexpr (FUSED) {
 #pragma unroll
         for (int e = 0; e < V; ++e) {
-          const int i = (k * TPR + t) * V + e;
+          const int i = (own<TPR, VPT>(k, t)) * V + e;
           if (live && i < d) E::st(h, base + i, E::get(xr[k], e));
         }
       }
@@ -155,7 +186,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
   for (int k = 0; k < VPT; ++k) {
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      const int i = (k * TPR + t) * V + e;
+      const int i = (own<TPR, VPT>(k, t)) * V + e;
       const float a = i < d ? E::get(xr[k], e) : 0.0f;
       ss = __builtin_fmaf(a, a, ss);
     }
@@ -168,24 +199,25 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
     if constexpr (TPR < ET_NORM_W_EARLY_MIN_TPR) {
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
-        const int j = k * TPR + t;
+        const int j = own<TPR, VPT>(k, t);
         wr[k] = ld16_keep(w, static_cast<int64_t>(j < nvec ? j : nvec - 1) * V);
       }
     }
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
-      const int j = k * TPR + t;
+      const int j = own<TPR, VPT>(k, t);
       float o[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) o[e] = E::get(xr[k], e) * inv * E::get(wr[k], e);
-      if (j < nvec) st16(y, base + static_cast<int64_t>(j) * V, E::pack(o));
+      if (j < nvec)
+        st16_buf<POL>(out_rsrc(y + row0 * d, span), (rel + j * V) * int(sizeof(S)), E::pack(o));
     }
   } else {
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
 #pragma unroll
       for (int e = 0; e < V; ++e) {
-        const int i = (k * TPR + t) * V + e;
+        const int i = (own<TPR, VPT>(k, t)) * V + e;
         const float g = E::ld(w, i < d ? i : d - 1);
         if (i < d) E::st(y, base + i, E::get(xr[k], e) * inv * g);
       }
@@ -268,7 +300,7 @@ __global__ __launch_bounds__(kLargeTPR) void rmsnorm_rows_large(
 // 1024..4096 vectors, else 8) and threads per row (the smallest power of two
 // with TPR * VPT >= number of vectors); TPR 0 selects the two-pass path.
 inline void pick_shape(int64_t nvec, int* tpr_out, int* vpt_out) {
-  const int vpt = (nvec >= 1024 && nvec <= 4096) ? 4 : kVPTMax;
+  const int vpt = (nvec >= ET_NORM_VPT4_MIN && nvec <= 4096) ? 4 : kVPTMax;
   int tpr = 1;
   while (static_cast<int64_t>(tpr) * vpt < nvec) {
     tpr <<= 1;
@@ -284,14 +316,23 @@ inline void pick_shape(int64_t nvec, int* tpr_out, int* vpt_out) {
 template <typename S, int TPR, int VPT, bool FUSED, bool VEC>
 void launch_rows(const S* x, const S* res, const S* w, S* y, S* h, int64_t rows, int d, float eps,
                  hipStream_t s) {
+  // Non-temporal stores at every size: device-scope ones here (see
+  // StorePolicy) made the measured eight-op step 10 % slower, the cache's
+  // write-backs of the norm outputs competing with the next kernels' reads.
+  const int64_t out_bytes = rows * d * static_cast<int64_t>(sizeof(S)) * (FUSED ? 2 : 1);
+  const bool dev = store_policy(out_bytes, ET_POL_NORM) == kStoreDevice;
   using Sh = NormShape<TPR>;
   for (int64_t r0 = 0; r0 < rows; r0 += kMaxGrid * Sh::kRowsPerBlock) {
     const int64_t n = rows - r0 < kMaxGrid * Sh::kRowsPerBlock ? rows - r0
                                                                 : kMaxGrid * Sh::kRowsPerBlock;
     const int64_t off = r0 * d;
     const unsigned grid = static_cast<unsigned>((n + Sh::kRowsPerBlock - 1) / Sh::kRowsPerBlock);
-    rmsnorm_rows<S, TPR, VPT, FUSED, VEC><<<grid, Sh::kBlock, 0, s>>>(
-        x + off, FUSED ? res + off : nullptr, w, y + off, FUSED ? h + off : nullptr, n, d, eps);
+    if (dev)
+      rmsnorm_rows<S, TPR, VPT, FUSED, VEC, kStoreDevice><<<grid, Sh::kBlock, 0, s>>>(
+          x + off, FUSED ? res + off : nullptr, w, y + off, FUSED ? h + off : nullptr, n, d, eps);
+    else
+      rmsnorm_rows<S, TPR, VPT, FUSED, VEC, kStoreStream><<<grid, Sh::kBlock, 0, s>>>(
+          x + off, FUSED ? res + off : nullptr, w, y + off, FUSED ? h + off : nullptr, n, d, eps);
   }
 }
 
@@ -306,7 +347,13 @@ void dispatch_tpr(int tpr, int vpt, const S* x, const S* res, const S* w, S* y, 
     case 16: launch_rows<S, 16, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
     case 32: launch_rows<S, 32, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
     case 64: launch_rows<S, 64, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
-    case 128: launch_rows<S, 128, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
+    case 128:
+#if ET_NORM_VPT4_MIN <= 512
+      if (vpt == 4) launch_rows<S, 128, 4, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s);
+      else
+#endif
+      launch_rows<S, 128, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s);
+      break;
     case 256:
       if (vpt == 4) launch_rows<S, 256, 4, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s);
       else launch_rows<S, 256, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s);

@@ -29,6 +29,10 @@
 namespace et {
 namespace {
 
+#ifndef ET_POL_ROPE
+#define ET_POL_ROPE 0  // 0: by size, 1: non-temporal, 2: device scope
+#endif
+
 constexpr int kBlock = 256;
 constexpr int kMaxTableBytes = 48 * 1024;
 #ifndef ET_ROPE_UMAX
@@ -177,7 +181,59 @@ __device__ inline void rotate(float& x0, float& x1, float2 c) {
 
 // ------------------------------------------------------------------ RoPE
 
-template <typename S, int PS, int U>
+#ifndef ET_ROPE_WAVE
+#define ET_ROPE_WAVE 1
+#endif
+#ifndef ET_QK_WAVE
+#define ET_QK_WAVE 1
+#endif
+
+// Slot u of thread tid in a block whose slots start at base.  With
+// ET_ROPE_WAVE each wave owns a contiguous run of 64 * U slots (slot u of
+// lane l at u * 64 + l in it); else slot u of the block is a contiguous
+// kBlock-slot stripe.
+template <int U>
+__device__ inline uint32_t rope_slot(uint32_t base, int tid, int u) {
+  if constexpr (ET_ROPE_WAVE) {
+    return base + static_cast<uint32_t>((tid / 64) * (64 * U) + u * 64 + (tid % 64));
+  } else {
+    return base + static_cast<uint32_t>(u * kBlock + tid);
+  }
+}
+
+// Vector stores of one workgroup go through two buffer resources, one based
+// at the first q row and one at the first k row the workgroup touches.  Its
+// head rows (token-major: t * (Hq + Hk) + h) are consecutive, and so are the
+// q rows (t * Hq + h) and the k rows (t * Hk + h - Hq) among them, so every
+// offset is below (head rows per workgroup) * D elements; the host keeps that
+// below 2^31 bytes.
+template <typename S, int POL>
+struct QkOut {
+  __amdgpu_buffer_rsrc_t rq, rk;
+  int64_t qrow0, krow0;
+  // t0, hh0: token and head of the workgroup's first head row; T: tokens in
+  // the launch.
+  __device__ QkOut(S* q, S* k, int64_t t0, int hh0, const RopeArgs& a) {
+    const bool in_q = hh0 < a.hq;
+    qrow0 = t0 * a.hq + (in_q ? hh0 : a.hq);
+    krow0 = t0 * a.hk + (in_q ? 0 : hh0 - a.hq);
+    constexpr int64_t es = sizeof(S);
+    rq = out_rsrc(q + qrow0 * a.D, (a.T * a.hq - qrow0) * a.D * es);
+    rk = out_rsrc(a.hk > 0 ? k + krow0 * a.D : q, a.hk > 0 ? (a.T * a.hk - krow0) * a.D * es : 0);
+  }
+  // Element offset of head h of token t from its resource's base.
+  __device__ int rel(int64_t t, int hh, const RopeArgs& a) const {
+    return hh < a.hq ? static_cast<int>((t * a.hq + hh - qrow0) * a.D)
+                     : static_cast<int>((t * a.hk + (hh - a.hq) - krow0) * a.D);
+  }
+  __device__ void store(bool isq, int elem, const u32x4& v) const {
+    const int off = elem * static_cast<int>(sizeof(S));
+    if (isq) st16_buf<POL>(rq, off, v);
+    else st16_buf<POL>(rk, off, v);
+  }
+};
+
+template <typename S, int PS, int U, int POL>
 __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32_t* __restrict__ pos,
                                                         const float* __restrict__ inv_freq,
                                                         RopeArgs a) {
@@ -189,24 +245,27 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32
   if (last >= a.total) last = a.total - 1;
   const int ntok = static_cast<int>(fdiv(last, a.fd_spt) - t0 + 1);
   const TabIn tin = table_inputs(t0, ntok, a, pos, inv_freq);
+  const QkOut<S, POL> out(q, k, t0, static_cast<int>(fdiv(base - t0 * a.spt, a.fd_sph)), a);
 
   // Phase 1: issue every load of this thread.
   S* rowp[U];
-  int ea[U], eb[U], tl[U], kk[U];
+  int ea[U], eb[U], tl[U], kk[U], rel[U];
+  bool isq[U];
   u32x4 va[U], vb[U];
   float sa[U], sb[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    uint32_t s = base + u * kBlock + threadIdx.x;
+    uint32_t s = rope_slot<U>(base, threadIdx.x, u);
     if (s >= a.total) s = a.total - 1;  // clamped: loaded, never stored
     const uint32_t t = fdiv(s, a.fd_spt);
     const uint32_t rem = s - t * a.spt;
     const uint32_t hh = fdiv(rem, a.fd_sph);
     kk[u] = static_cast<int>(rem - hh * a.sph);
     tl[u] = static_cast<int>(t - t0);
-    rowp[u] = static_cast<int>(hh) < a.hq
-                  ? q + (static_cast<int64_t>(t) * a.hq + hh) * a.D
-                  : k + (static_cast<int64_t>(t) * a.hk + (hh - a.hq)) * a.D;
+    isq[u] = static_cast<int>(hh) < a.hq;
+    rowp[u] = isq[u] ? q + (static_cast<int64_t>(t) * a.hq + hh) * a.D
+                     : k + (static_cast<int64_t>(t) * a.hk + (hh - a.hq)) * a.D;
+    rel[u] = out.rel(t, static_cast<int>(hh), a);
     slot_offsets<PS>(kk[u], a, &ea[u], &eb[u]);
     if constexpr (PS == 1) {
       sa[u] = E::ld(rowp[u], ea[u]);
@@ -230,7 +289,7 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32
   // Phase 3: rotate and store.
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const uint32_t s = base + u * kBlock + threadIdx.x;
+    const uint32_t s = rope_slot<U>(base, threadIdx.x, u);
     if (s >= a.total) continue;
     const float2* tab = cs + tl[u] * a.half;  // this token's (mu cos, mu sin)
     if constexpr (PS == 1) {
@@ -257,8 +316,8 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32
           rotate(xb[e], xb[e + 1], tab[eb[u] / 2 + e / 2]);
         }
       }
-      st16(rowp[u], ea[u], E::pack(xa));
-      st16(rowp[u], eb[u], E::pack(xb));
+      out.store(isq[u], rel[u] + ea[u], E::pack(xa));
+      out.store(isq[u], rel[u] + eb[u], E::pack(xb));
     }
   }
 }
@@ -279,7 +338,7 @@ struct QkNormArgs {
 // vector rotates (pairs inside it) if it lies below r.  Half layout: lanes
 // kk < rsl own the partners A = kk*V, B = kk*V + r/2; the other lanes own
 // tail vectors r + m*V and r + (nt + m)*V (m = kk - rsl, nt = G - rsl).
-template <typename S, int G, int U, bool ROT>
+template <typename S, int G, int U, bool ROT, int POL>
 __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __restrict__ gq, S* k,
                                                              const S* __restrict__ gk,
                                                              const int32_t* __restrict__ pos,
@@ -292,8 +351,20 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
   const RopeArgs& ra = a.rope;
   const int heads = ra.hq + ra.hk;
   const int kk = threadIdx.x % G;
-  const int grp = threadIdx.x / G;
   const uint32_t base = blockIdx.x * static_cast<uint32_t>(kRowsPerPass * U);
+  // Head row of slot u of this lane group: with ET_QK_WAVE each wave owns a
+  // contiguous run of (64 / G) * U head rows, else slot u of the block is a
+  // contiguous kRowsPerPass-row stripe.
+  auto head_row = [&](int u) -> uint32_t {
+    if constexpr (ET_QK_WAVE && G < 64) {
+      constexpr int kRowsPerWave = 64 / G;
+      const int wave = threadIdx.x / 64;
+      return base + static_cast<uint32_t>(wave * kRowsPerWave * U + u * kRowsPerWave +
+                                          (threadIdx.x % 64) / G);
+    } else {
+      return base + static_cast<uint32_t>(u * kRowsPerPass + threadIdx.x / G);
+    }
+  };
   const uint32_t t0 = fdiv(base, a.fd_heads);
   uint32_t last = base + kRowsPerPass * U - 1;
   if (last >= a.rows) last = a.rows - 1;
@@ -319,13 +390,14 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
     a_rot = b_rot = false;
   }
 
+  const QkOut<S, POL> out(q, k, t0, static_cast<int>(base - t0 * heads), ra);
   S* rowp[U];
-  int tl[U];
+  int tl[U], rel[U];
   bool isq[U];
   u32x4 va[U], vb[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    uint32_t hr = base + u * kRowsPerPass + grp;
+    uint32_t hr = head_row(u);
     if (hr >= a.rows) hr = a.rows - 1;  // clamped: loaded, never stored
     const uint32_t t = fdiv(hr, a.fd_heads);
     const int hh = static_cast<int>(hr - t * heads);
@@ -333,6 +405,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
     isq[u] = hh < ra.hq;
     rowp[u] = isq[u] ? q + (static_cast<int64_t>(t) * ra.hq + hh) * ra.D
                      : k + (static_cast<int64_t>(t) * ra.hk + (hh - ra.hq)) * ra.D;
+    rel[u] = out.rel(t, hh, ra);
     va[u] = ld16(rowp[u], ea);
     vb[u] = ld16(rowp[u], eb);
   }
@@ -396,9 +469,9 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
         for (int e = 0; e < V; e += 2) rotate(xb[e], xb[e + 1], tab[eb / 2 + e / 2]);
       }
     }
-    if (base + u * kRowsPerPass + grp < a.rows) {
-      st16(rowp[u], ea, E::pack(xa));
-      st16(rowp[u], eb, E::pack(xb));
+    if (head_row(u) < a.rows) {
+      out.store(isq[u], rel[u] + ea, E::pack(xa));
+      out.store(isq[u], rel[u] + eb, E::pack(xb));
     }
   }
 }
@@ -498,7 +571,7 @@ RopeArgs make_args(int64_t T, int64_t hq, int64_t hk, int64_t D, int64_t r, floa
   return a;
 }
 
-template <typename S, int PS, int U>
+template <typename S, int PS, int U, int POL>
 void launch_rope(S* q, S* k, const int32_t* pos, const float* inv_freq, RopeArgs a, int64_t T,
                  hipStream_t s) {
   // Tokens per launch keep slot indices below 2^31.
@@ -510,7 +583,7 @@ void launch_rope(S* q, S* k, const int32_t* pos, const float* inv_freq, RopeArgs
     a.T = m;
     a.total = static_cast<uint32_t>(m * a.spt);
     const unsigned grid = (a.total + kBlock * U - 1) / (kBlock * U);
-    rope_qk_kernel<S, PS, U><<<grid, kBlock, shmem, s>>>(
+    rope_qk_kernel<S, PS, U, POL><<<grid, kBlock, shmem, s>>>(
         q + t0 * a.hq * a.D, a.hk ? k + t0 * a.hk * a.D : k, pos + t0, inv_freq, a);
   }
 }
@@ -533,26 +606,41 @@ et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int
   if (T == 0 || hq + hk == 0 || r == 0) return ET_OK;
   constexpr int V = Elem<S>::V;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool vec = (r % (2 * V)) == 0 && (D % V) == 0 && aligned16(q) && (hk == 0 || aligned16(k));
-  const int ps = vec ? V : 1;
-  RopeArgs a = make_args(T, hq, hk, D, r, mu, layout, ps);
+  bool vec = (r % (2 * V)) == 0 && (D % V) == 0 && aligned16(q) && (hk == 0 || aligned16(k));
+  RopeArgs a = make_args(T, hq, hk, D, r, mu, layout, vec ? V : 1);
   if (a.spt > (1u << 30)) return ET_ERR_BAD_SIZE;
-  const int u = pick_u(a.spt, a.half, kBlock, ET_ROPE_UMAX);
+  int u = pick_u(a.spt, a.half, kBlock, ET_ROPE_UMAX);
   if (u == 0) return ET_ERR_BAD_SIZE;
-  (void)hipGetLastError();
   if (vec) {
-    if (u == 4) launch_rope<S, V, 4>(q, k, pos, inv_freq, a, T, s);
-    else if (u == 2) launch_rope<S, V, 2>(q, k, pos, inv_freq, a, T, s);
-    else launch_rope<S, V, 1>(q, k, pos, inv_freq, a, T, s);
+    // The vector path stores at byte offsets below (head rows a workgroup
+    // touches) * D * sizeof(S); past 2^31 take the scalar path.
+    const int64_t rows_blk = (int64_t{kBlock} * u + a.sph - 1) / a.sph + 2;
+    if (rows_blk * D * int64_t(sizeof(S)) >= (int64_t{1} << 31)) {
+      vec = false;
+      a = make_args(T, hq, hk, D, r, mu, layout, 1);
+      if (a.spt > (1u << 30)) return ET_ERR_BAD_SIZE;
+      u = pick_u(a.spt, a.half, kBlock, ET_ROPE_UMAX);
+      if (u == 0) return ET_ERR_BAD_SIZE;
+    }
+  }
+  (void)hipGetLastError();
+  if (vec && store_policy(T * (hq + hk) * r * int64_t(sizeof(S)), ET_POL_ROPE) == kStoreDevice) {
+    if (u == 4) launch_rope<S, V, 4, kStoreDevice>(q, k, pos, inv_freq, a, T, s);
+    else if (u == 2) launch_rope<S, V, 2, kStoreDevice>(q, k, pos, inv_freq, a, T, s);
+    else launch_rope<S, V, 1, kStoreDevice>(q, k, pos, inv_freq, a, T, s);
+  } else if (vec) {
+    if (u == 4) launch_rope<S, V, 4, kStoreStream>(q, k, pos, inv_freq, a, T, s);
+    else if (u == 2) launch_rope<S, V, 2, kStoreStream>(q, k, pos, inv_freq, a, T, s);
+    else launch_rope<S, V, 1, kStoreStream>(q, k, pos, inv_freq, a, T, s);
   } else {
-    if (u == 4) launch_rope<S, 1, 4>(q, k, pos, inv_freq, a, T, s);
-    else if (u == 2) launch_rope<S, 1, 2>(q, k, pos, inv_freq, a, T, s);
-    else launch_rope<S, 1, 1>(q, k, pos, inv_freq, a, T, s);
+    if (u == 4) launch_rope<S, 1, 4, kStoreStream>(q, k, pos, inv_freq, a, T, s);
+    else if (u == 2) launch_rope<S, 1, 2, kStoreStream>(q, k, pos, inv_freq, a, T, s);
+    else launch_rope<S, 1, 1, kStoreStream>(q, k, pos, inv_freq, a, T, s);
   }
   return launch_status();
 }
 
-template <typename S, int G, int U, bool ROT>
+template <typename S, int G, int U, bool ROT, int POL>
 void launch_qknorm_vec(S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
                        const float* inv_freq, QkNormArgs a, int64_t T, hipStream_t s) {
   constexpr int kRowsPerPass = kBlock / G;
@@ -564,8 +652,9 @@ void launch_qknorm_vec(S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
   for (int64_t t0 = 0; t0 < T; t0 += tok_per_launch) {
     const int64_t m = T - t0 < tok_per_launch ? T - t0 : tok_per_launch;
     a.rows = static_cast<uint32_t>(m * heads);
+    a.rope.T = m;
     const unsigned grid = static_cast<unsigned>((a.rows + rows_per_block - 1) / rows_per_block);
-    rmsnorm_rope_kernel<S, G, U, ROT><<<grid, kBlock, shmem, s>>>(
+    rmsnorm_rope_kernel<S, G, U, ROT, POL><<<grid, kBlock, shmem, s>>>(
         q + t0 * a.rope.hq * a.rope.D, gq, a.rope.hk ? k + t0 * a.rope.hk * a.rope.D : k, gk,
         pos + t0, inv_freq, a);
   }
@@ -575,15 +664,30 @@ template <typename S, int G>
 void launch_qknorm_vec_u(int u, S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
                          const float* inv_freq, QkNormArgs a, int64_t T, hipStream_t s) {
   const bool rot = a.rope.half > 0;
-  if (u == 4) {
-    if (rot) launch_qknorm_vec<S, G, 4, true>(q, gq, k, gk, pos, inv_freq, a, T, s);
-    else launch_qknorm_vec<S, G, 4, false>(q, gq, k, gk, pos, inv_freq, a, T, s);
-  } else if (u == 2) {
-    if (rot) launch_qknorm_vec<S, G, 2, true>(q, gq, k, gk, pos, inv_freq, a, T, s);
-    else launch_qknorm_vec<S, G, 2, false>(q, gq, k, gk, pos, inv_freq, a, T, s);
+  const bool dev = store_policy(T * (a.rope.hq + a.rope.hk) * a.rope.D * int64_t(sizeof(S)), ET_POL_ROPE) ==
+                   kStoreDevice;
+  if (dev) {
+    if (u == 4) {
+      if (rot) launch_qknorm_vec<S, G, 4, true, kStoreDevice>(q, gq, k, gk, pos, inv_freq, a, T, s);
+      else launch_qknorm_vec<S, G, 4, false, kStoreDevice>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    } else if (u == 2) {
+      if (rot) launch_qknorm_vec<S, G, 2, true, kStoreDevice>(q, gq, k, gk, pos, inv_freq, a, T, s);
+      else launch_qknorm_vec<S, G, 2, false, kStoreDevice>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    } else {
+      if (rot) launch_qknorm_vec<S, G, 1, true, kStoreDevice>(q, gq, k, gk, pos, inv_freq, a, T, s);
+      else launch_qknorm_vec<S, G, 1, false, kStoreDevice>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    }
   } else {
-    if (rot) launch_qknorm_vec<S, G, 1, true>(q, gq, k, gk, pos, inv_freq, a, T, s);
-    else launch_qknorm_vec<S, G, 1, false>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    if (u == 4) {
+      if (rot) launch_qknorm_vec<S, G, 4, true, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
+      else launch_qknorm_vec<S, G, 4, false, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    } else if (u == 2) {
+      if (rot) launch_qknorm_vec<S, G, 2, true, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
+      else launch_qknorm_vec<S, G, 2, false, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    } else {
+      if (rot) launch_qknorm_vec<S, G, 1, true, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
+      else launch_qknorm_vec<S, G, 1, false, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    }
   }
 }
 
