@@ -264,8 +264,17 @@ def cpu_baseline(w, min_seconds):
             fn()
         t_total += time.perf_counter() - t0
         reps += 1
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(reps * step_bytes / t_total / 1e9, 3), "unit": "GB/s",
-            "cores": orc.threads(), "kind": "oracle", "seconds": round(t_total, 2),
+            "cores": orc.threads(), "cpu": cpu, "kind": "oracle", "seconds": round(t_total, 2),
             "sample": f"{reps} whole steps of the same workload ({step_bytes} algorithmic bytes "
                       f"each), all ops at full size"}
 
@@ -326,6 +335,32 @@ def main():
             ops[i].ms.append(ev.elapsed_ms())
             ev.close()
 
+    # Attainable-bandwidth context: a plain device-to-device copy as large as
+    # the dominant op's largest operand (read once, written once), timed the
+    # same way after the timed region.
+    copy_ctx = None
+    if not args.copy_calibration:
+        nb = max(op.nbytes for op in ops) // 3
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(10):
+            ev = TimingEvents(stream)
+            ev.start()
+            dst.copy_(src)
+            ev.stop()
+            torch.cuda.synchronize()
+            ms.append(ev.elapsed_ms())
+            ev.close()
+        med = float(np.median(ms))
+        copy_ctx = {"bytes": 2 * nb, "median_us": round(med * 1e3, 2),
+                    "GBps": round(2 * nb / (med * 1e-3) / 1e9, 1),
+                    "what": "device-to-device copy of one operand-sized buffer (torch copy_)"}
+        del src, dst
+
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -383,6 +418,7 @@ def main():
                    "vocab": w.embed[0] if w.embed else None},
         "ops": per_op,
         "roofline": roofline,
+        "copy_context": copy_ctx,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
