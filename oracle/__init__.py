@@ -67,6 +67,7 @@ class Oracle:
         lib.orc_rope_angle.argtypes = [ctypes.c_int32, _f32]
         lib.orc_rope_angle.restype = _f32
         lib.orc_rmsnorm.argtypes = [_int, _vp, _vp, _i64, _i64, _f32, _vp, _vp]
+        lib.orc_softmax.argtypes = [_int, _vp, _i64, _i64, _f32, _vp, _vp]
         lib.orc_add_rmsnorm.argtypes = [_int, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp, _vp]
         lib.orc_rope.argtypes = [_int, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _f32, _int, _vp]
         lib.orc_rmsnorm_rope.argtypes = [_int, _vp, _vp, _f32, _vp, _i64, _i64, _i64, _i64,
@@ -182,6 +183,16 @@ class Oracle:
         out = np.empty(rows, np.int32)
         self.lib.orc_argmax(dt, _p(x), rows, n, _p(out))
         return out
+
+    def softmax(self, x: np.ndarray, t: float = 1.0):
+        """[rows, n] -> (y in storage type, y64): softmax of x / t per row."""
+        x = np.ascontiguousarray(x)
+        dt = _dt(x)
+        rows, n = x.shape
+        y = np.empty_like(x)
+        y64 = np.empty(x.shape, np.float64)
+        self.lib.orc_softmax(dt, _p(x), rows, n, t, _p(y64), _p(y))
+        return y, y64
 
 
 _default: Optional[Oracle] = None

@@ -7,6 +7,9 @@
  * this file; only the tests, the smoke check and the benchmark's CPU-baseline
  * leg do.  It shares no source with the HIP kernels.
  *
+ * Also the first of the next rows: softmax over the last axis with a
+ * temperature.
+ *
  * Sources (web pages; sections named, never line numbers):
  *   [OPS]  "Operations" (glia runtime op spec): 2 Normalization / RmsNorm;
  *          3 Position encoding / Rope; 4 Activation / Silu, SwiGlu;
@@ -14,6 +17,7 @@
  *   [ELT]  "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding,
  *          add, argmax": 2.1 RMSNorm; 2.2 RoPE; 2.3 SiLU-mul (SwiGLU);
  *          2.4 Embedding, add, argmax; 4 The interface.
+ *   [DNN]  "ruDNN User Guide": 7 LayerNorm, RMSNorm, and Softmax.
  *
  * Arithmetic: every input is widened exactly to f64; all math is IEEE f64
  * with libm sqrt/exp/sin/cos; every stored output is rounded once (RNE),
@@ -320,5 +324,42 @@ void orc_argmax(int dt, const void* x, int64_t rows, int64_t n,
             }
         }
         out[r] = best;
+    }
+}
+
+/* ---------------------------------------------------------------- softmax */
+
+/* [OPS] 4 Activation / Softmax and 8 Sampling / Temperature; [DNN] 7: over
+ * each row, z_i = x_i / t, m = max_i z_i, e_i = exp(z_i - m),
+ * y_i = e_i / sum_j e_j.  The max is subtracted so that large logits do not
+ * overflow.  z is the f64 quotient, except that a quotient beyond the f32
+ * range is taken to +-inf, as the single-precision division the pages'
+ * statistics use would give.  Special values follow the formula: a NaN
+ * anywhere in a row, or a row whose max is +-inf, makes the whole row NaN. */
+void orc_softmax(int dt, const void* x, int64_t rows, int64_t n, float t,
+                 double* y64, void* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double* z = row_buffer(n);
+        double m = -INFINITY;
+        for (int64_t i = 0; i < n; ++i) {
+            double v = ld(dt, x, r * n + i) / (double)t;
+            if (v > FLT_MAX) v = INFINITY;
+            if (v < -FLT_MAX) v = -INFINITY;
+            z[i] = v;
+            if (isnan(v) || isnan(m)) m = NAN;
+            else if (v > m) m = v;
+        }
+        double sum = 0.0;
+        for (int64_t i = 0; i < n; ++i) {
+            z[i] = exp(z[i] - m);
+            sum += z[i];
+        }
+        for (int64_t i = 0; i < n; ++i) {
+            const double v = z[i] / sum;
+            if (y64) y64[r * n + i] = v;
+            if (y) st(dt, y, r * n + i, v);
+        }
+        free(z);
     }
 }

@@ -51,6 +51,8 @@ void orc_add(int dt, const void* a, const void* b, int64_t n, void* y);
 void orc_embedding(int dt, const void* table, int64_t V, const int32_t* ids,
                    int64_t n, int64_t d, void* out);
 void orc_argmax(int dt, const void* x, int64_t rows, int64_t n, int32_t* out);
+void orc_softmax(int dt, const void* x, int64_t rows, int64_t n, float t,
+                 double* y64, void* y);
 
 #ifdef __cplusplus
 }

@@ -93,3 +93,18 @@ def argmax_sorted(x: Sequence[float]) -> int:
         return -1
     keys.sort()
     return keys[0][1]
+
+
+def softmax_decimal(x: Sequence[float], t: float, digits: int = 50) -> List[float]:
+    """Softmax of x / t for finite inputs in 50-digit decimal arithmetic
+    (``decimal``'s own exp, no libm), written as 1 / sum_j exp(z_j - z_i) --
+    a different arrangement from the oracle's max-subtracted quotient."""
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = digits
+        z = [Decimal(v) / Decimal(t) for v in x]
+        out = []
+        for zi in z:
+            s = sum(((zj - zi).exp() for zj in z), Decimal(0))
+            out.append(float(Decimal(1) / s))
+        return out

@@ -19,6 +19,7 @@ from __future__ import annotations
 import json
 import math
 import os
+from fractions import Fraction
 from typing import Callable, Dict
 
 import numpy as np
@@ -481,6 +482,111 @@ def pin_argmax_matches_library(orc):
     for r in range(40):
         expect = -1 if np.all(np.isnan(wide[r])) else int(np.nanargmax(wide[r]))
         assert gotb[r] == expect, r
+
+
+# ---------------------------------------------------------------- softmax
+
+def pin_softmax_closed_forms(orc):
+    """[OPS] Softmax: a constant row is uniform (1/n exactly, rounded once);
+    two entries give the logistic function of their scaled difference;
+    every row sums to 1."""
+    for n in (1, 3, 7, 64):
+        for dt in ("f32", "bf16"):
+            x = np.full((2, n), 0.75, np.float32)
+            xs = x if dt == "f32" else _bf16(x)
+            y, y64 = orc.softmax(xs, 1.0)
+            assert np.all(y64 == 1.0 / n), (n, dt)
+            expect = np.float32(1.0 / n) if dt == "f32" else brute.bf16_bits_exact(Fraction(1, n))
+            assert np.all(y == expect), (n, dt)
+    for a, b, t in ((0.0, 1.0, 1.0), (2.5, -1.0, 0.5), (-3.0, -3.25, 4.0)):
+        _, y64 = orc.softmax(_f32([a, b])[None], t)
+        logistic = 0.5 * (1.0 + math.tanh((float(np.float32(a)) - float(np.float32(b))) / (2 * float(np.float32(t)))))
+        assert abs(y64[0, 0] - logistic) <= 1e-15, (a, b, t)
+        assert abs(y64[0, 0] + y64[0, 1] - 1.0) <= 1e-15
+    g = np.random.default_rng(71)
+    _, y64 = orc.softmax(g.standard_normal((5, 333)).astype(np.float32) * 3, 0.7)
+    assert np.all(np.abs(y64.sum(axis=1) - 1.0) <= 1e-13)
+
+
+def pin_softmax_max_is_subtracted(orc):
+    """[OPS] Softmax: the max is subtracted so large logits stay finite --
+    a shifted row gives the same result, and rows spanning a range wider than
+    the exponential's gives 0 for the far entries, not NaN."""
+    base = _f32([0.0, 1.0, 2.0])[None]
+    y0, _ = orc.softmax(base, 1.0)
+    for shift in (1000.0, -1000.0, 3.0e38 / 1.5):
+        ys, _ = orc.softmax(base + np.float32(shift) if abs(shift) < 1e30 else _f32([shift, shift, shift])[None], 1.0)
+        assert np.all(np.isfinite(ys)), shift
+        if abs(shift) < 1e30:
+            assert np.array_equal(ys.view(np.uint32), y0.view(np.uint32)), shift
+    y, y64 = orc.softmax(_f32([-800.0, 0.0, -1.0e4])[None], 1.0)
+    assert np.all(np.isfinite(y64)) and y64[0, 2] == 0.0
+    assert abs(y64[0, 0] - math.exp(-800.0) / (1.0 + math.exp(-800.0))) <= 1e-320
+    assert abs(y64[0, 1] - 1.0) <= 1e-15
+
+
+def pin_softmax_temperature(orc):
+    """[OPS] 8 Sampling / Temperature: probs = softmax(logits / t).  With t = 2
+    the result equals t = 1 on the halved logits (exact in f32); a large t
+    flattens the row towards uniform; brute force in 50-digit decimal."""
+    g = np.random.default_rng(73)
+    x = (g.standard_normal((4, 50)) * 4).astype(np.float32)
+    y2, y2_64 = orc.softmax(x, 2.0)
+    yh, yh_64 = orc.softmax(x * np.float32(0.5), 1.0)
+    assert np.array_equal(y2.view(np.uint32), yh.view(np.uint32))
+    assert np.array_equal(y2_64, yh_64)
+    _, flat = orc.softmax(x, 1.0e6)
+    assert np.all(np.abs(flat - 1.0 / 50) <= 1e-6)
+    for t in (1.0, 0.3, 2.5):
+        xs = (g.standard_normal(12) * 3).astype(np.float32)
+        _, y64 = orc.softmax(xs[None], t)
+        ref = brute.softmax_decimal([float(v) for v in xs], float(np.float32(t)))
+        assert np.allclose(y64[0], ref, rtol=1e-14, atol=0.0), t
+
+
+def pin_softmax_special_values(orc):
+    """Special values follow the formula: a NaN anywhere makes the row NaN; a
+    row of -inf (max -inf) or holding +inf is NaN (inf - inf); a single -inf
+    among numbers gets 0; a quotient x/t beyond the f32 range is +-inf, as
+    the single-precision division gives; rows are independent."""
+    nan, inf = float("nan"), float("inf")
+    x = _f32([1.0, 2.0, 3.0, 4.0] + [nan, 1.0, 2.0, 3.0] + [-inf] * 4 + [1.0, inf, 0.0, 2.0]
+             + [0.0, -inf, 1.0, 2.0]).reshape(5, 4)
+    for dt in ("f32", "bf16"):
+        xs = x if dt == "f32" else _bf16(x)
+        y, y64 = orc.softmax(xs, 1.0)
+        assert np.all(np.isfinite(y64[0])) and abs(y64[0].sum() - 1.0) <= 1e-15
+        assert np.all(np.isnan(y64[1:4])), dt
+        assert y64[4, 1] == 0.0 and np.all(np.isfinite(y64[4]))
+        wide = y if dt == "f32" else _wide(y)
+        assert np.all(np.isnan(wide[1:4])) and wide[4, 1] == 0.0
+        alone, _ = orc.softmax(np.ascontiguousarray(xs[4:5]), 1.0)
+        assert np.array_equal(alone[0].view(np.uint8), y[4].view(np.uint8))
+    _, y64 = orc.softmax(_f32([3.0, 4.0])[None], 1.0e-38)
+    assert np.all(np.isnan(y64))
+    _, y64 = orc.softmax(_f32([1.0, 2.0])[None], 1.0e-38)
+    assert y64[0, 0] == 0.0 and y64[0, 1] == 1.0
+
+
+def pin_softmax_matches_library(orc):
+    """torch's CPU softmax in f64 on the same quotients (a library routine),
+    for f32 and bf16 storage; the stored value is the f64 result rounded
+    once."""
+    import torch
+    g = np.random.default_rng(79)
+    x = (g.standard_normal((6, 1000)) * 3).astype(np.float32)
+    for dt in ("f32", "bf16"):
+        xs = x if dt == "f32" else _bf16(x)
+        wide = xs if dt == "f32" else _wide(xs)
+        t = np.float32(0.7)
+        y, y64 = orc.softmax(xs, float(t))
+        ref = torch.softmax(torch.from_numpy(wide.astype(np.float64)) / float(t), dim=1).numpy()
+        assert np.allclose(y64, ref, rtol=1e-13, atol=1e-300)
+        if dt == "f32":
+            assert np.array_equal(y, ref.astype(np.float32))
+        else:
+            assert np.array_equal(y, _bf16(ref.astype(np.float32))) or \
+                np.max(np.abs(y.astype(np.int32) - _bf16(ref.astype(np.float32)).astype(np.int32))) <= 1
 
 
 # ------------------------------------------------------- batch invariance

@@ -4,8 +4,9 @@ Each mutant is a copy of ``oracle/oracle.c`` with one plausible mistake
 planted by text substitution, built into a temporary library.  The pins must
 fail on every mutant.  s01-s15 are the mistakes listed in the Pitfalls table
 (section 5) of "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding,
-add, argmax", each with the test the page says catches it; x01-x10 are further
-slips (a wrong sign, index, dropped term or rounding) in the same code.
+add, argmax", each with the test the page says catches it; x01-x16 are further
+slips (a wrong sign, index, dropped term or rounding) in the same code, x11-x16
+in the softmax.
 """
 import os
 import tempfile
@@ -64,6 +65,18 @@ MUTANTS = {
                                   "st(dt, y, i, ld(dt, a, i) - ld(dt, b, i));")]),
     "x09_half_pairs_reversed": (None, [("*ib = i + r / 2;", "*ib = r - 1 - i;")]),
     "x10_rotation_sign": (None, [("mu * (a * c - b * s)", "mu * (a * c + b * s)")]),
+    "x11_softmax_no_max_subtraction": ("softmax_max_is_subtracted",
+                                       [("z[i] = exp(z[i] - m);", "z[i] = exp(z[i]);")]),
+    "x12_softmax_min_subtracted": ("softmax_max_is_subtracted",
+                                   [("else if (v > m) m = v;", "else if (v < m || m == -INFINITY) m = v;")]),
+    "x13_temperature_multiplies": ("softmax_temperature",
+                                   [("ld(dt, x, r * n + i) / (double)t;", "ld(dt, x, r * n + i) * (double)t;")]),
+    "x14_softmax_divides_by_n": ("softmax_closed_forms",
+                                 [("const double v = z[i] / sum;", "const double v = z[i] / (double)n;")]),
+    "x15_softmax_no_f32_quotient_limit": ("softmax_special_values",
+                                          [("if (v > FLT_MAX) v = INFINITY;\n            if (v < -FLT_MAX) v = -INFINITY;\n", "")]),
+    "x16_softmax_exp_sign": ("softmax_temperature",
+                             [("z[i] = exp(z[i] - m);", "z[i] = exp(m - z[i]);")]),
 }
 
 
