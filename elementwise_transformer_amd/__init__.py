@@ -57,6 +57,7 @@ _SIGS = {
     "add": [_vp, _vp, _vp, _i64, _vp],
     "embedding": [_vp, _i64, _vp, _vp, _i64, _i64, _vp],
     "argmax": [_vp, _i64, _i64, _vp, _vp, _sz, _vp],
+    "softmax": [_vp, _vp, _i64, _i64, _f32, _vp, _sz, _vp],
 }
 for _op, _args in _SIGS.items():
     for _sfx in ("f32", "bf16"):
@@ -65,6 +66,8 @@ for _op, _args in _SIGS.items():
         _f.restype = ctypes.c_int
 lib.et_argmax_workspace_bytes.argtypes = [_i64, _i64]
 lib.et_argmax_workspace_bytes.restype = _sz
+lib.et_softmax_workspace_bytes.argtypes = [_i64, _i64]
+lib.et_softmax_workspace_bytes.restype = _sz
 lib.et_status_string.argtypes = [ctypes.c_int]
 lib.et_status_string.restype = ctypes.c_char_p
 lib.et_abi_version.argtypes = []
@@ -275,4 +278,32 @@ def argmax(x: torch.Tensor, out: Optional[torch.Tensor] = None,
             _dev(workspace)
             ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     _call(f"et_argmax_{_sfx(x)}", _ptr(x), rows, n, _ptr(out), ws_ptr, ws_bytes, _stream(x))
+    return out
+
+
+def softmax_workspace_bytes(rows: int, n: int) -> int:
+    return int(lib.et_softmax_workspace_bytes(int(rows), int(n)))
+
+
+def softmax(x: torch.Tensor, temperature: float = 1.0, out: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None, split: bool = True) -> torch.Tensor:
+    """Softmax of x / temperature over the last axis (et_softmax_*); out may be
+    x.  ``split`` lets rows longer than 32768 elements spread over several
+    workgroups through a workspace (allocated here unless given; its contents
+    need no initialisation)."""
+    n = x.shape[-1]
+    rows = math.prod(x.shape[:-1])
+    out = torch.empty_like(x) if out is None else out
+    _dev(x, out)
+    _same(x, out)
+    ws_ptr, ws_bytes = None, 0
+    if split:
+        need = softmax_workspace_bytes(rows, n)
+        if need > 0:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            _dev(workspace)
+            ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    _call(f"et_softmax_{_sfx(x)}", _ptr(x), _ptr(out), rows, n, float(temperature), ws_ptr, ws_bytes,
+          _stream(x))
     return out

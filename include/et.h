@@ -11,6 +11,8 @@
  *         add, argmax": 2.1 RMSNorm; 2.2 RoPE; 2.3 SiLU-mul (SwiGLU);
  *         2.4 Embedding, add, argmax; 4 The interface (names and argument
  *         order of the six routines kept here).
+ *   [DNN] "ruDNN User Guide": 7 LayerNorm, RMSNorm, and Softmax (softmax over
+ *         the final axis, f32 statistics, output in the input type).
  *
  * Common rules for every entry point
  *   - Types: the _f32 variant stores float; the _bf16 variant stores
@@ -29,7 +31,7 @@
  *     same extent); any other overlap of an output with another buffer
  *     returns ET_ERR_OVERLAP before anything is enqueued.
  *   - Results are deterministic.  For the row ops (RMSNorm, fused
- *     add+RMSNorm, RoPE, fused RMSNorm+RoPE) the bits of a row depend only on
+ *     add+RMSNorm, RoPE, fused RMSNorm+RoPE, softmax) the bits of a row depend only on
  *     that row's inputs, the row length and the 16-byte alignment of the
  *     buffers -- never on the number of rows in the call.
  *   - Errors: argument problems are reported before any launch and nothing is
@@ -198,6 +200,33 @@ et_status et_argmax_f32(const float* x, int64_t rows, int64_t n, int32_t* out,
 et_status et_argmax_bf16(const et_bf16* x, int64_t rows, int64_t n,
                          int32_t* out, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* ------------------------------------------------------------------------
+ * Softmax over the last axis with a temperature  ([OPS] 4 Activation /
+ * Softmax, 8 Sampling / Temperature; [DNN] 7)
+ *   y[r, i] = exp(z_i - m) / sum_j exp(z_j - m) with z = x[r, :] / temperature
+ *   and m = max_j z_j, in f32.  x, y: [rows, n]; y may be x (in place).
+ *   temperature must be finite and > 0, else ET_ERR_BAD_ARG.  n <= INT32_MAX.
+ *   Special values follow the formula: a NaN anywhere in a row, or a row
+ *   whose largest z is +-inf, gives a row of NaN.
+ *   workspace: device scratch for rows longer than 32768 elements, which are
+ *   then split over several workgroups (two launches).  Either
+ *   workspace == NULL with workspace_bytes == 0 (one workgroup per long row;
+ *   rows of more than 8000 * 8192 elements then return ET_ERR_WORKSPACE), or
+ *   workspace != NULL, 8-byte aligned, with workspace_bytes >=
+ *   et_softmax_workspace_bytes(rows, n) (0 for rows of at most 32768
+ *   elements), else ET_ERR_WORKSPACE.  The caller owns the workspace; its
+ *   contents need no initialisation and are overwritten.  Calls that share a
+ *   workspace must not run concurrently.  The result is the same with or
+ *   without a workspace.
+ */
+size_t et_softmax_workspace_bytes(int64_t rows, int64_t n);
+et_status et_softmax_f32(const float* x, float* y, int64_t rows, int64_t n,
+                         float temperature, void* workspace,
+                         size_t workspace_bytes, void* stream);
+et_status et_softmax_bf16(const et_bf16* x, et_bf16* y, int64_t rows,
+                          int64_t n, float temperature, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Library information. */

@@ -27,10 +27,11 @@ def _declared():
 def test_header_declares_the_ops():
     names = _declared()
     for op in ("rmsnorm", "add_rmsnorm", "rope", "rope_qk", "rmsnorm_rope_qk", "silu_mul", "add",
-               "embedding", "argmax"):
+               "embedding", "argmax", "softmax"):
         for sfx in ("f32", "bf16"):
             assert f"et_{op}_{sfx}" in names
     assert "et_argmax_workspace_bytes" in names and "et_status_string" in names
+    assert "et_softmax_workspace_bytes" in names
 
 
 def test_library_exports_every_declared_symbol():
@@ -166,6 +167,38 @@ def test_embedding_and_argmax_validation(sfx):
     assert a(A, 256, 128256, B, P(3 * G + 8), need, S) == 5   # workspace not 16-byte aligned
     assert a(A, 4, 8, A, NULL, 0, S) == 4                     # out inside x
     assert a(NULL, 0, 8, NULL, NULL, 0, S) == 0
+
+
+@gpu_visible
+@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+def test_softmax_validation(sfx):
+    import elementwise_transformer_amd as et
+    f = getattr(et.lib, f"et_softmax_{sfx}")
+    assert f(A, B, -1, 8, 1.0, NULL, 0, S) == 2
+    assert f(A, B, 4, 1 << 31, 1.0, NULL, 0, S) == 2           # n > INT32_MAX
+    assert f(A, B, 4, 8, 0.0, NULL, 0, S) == 3                  # temperature must be > 0
+    assert f(A, B, 4, 8, -1.0, NULL, 0, S) == 3
+    assert f(A, B, 4, 8, float("inf"), NULL, 0, S) == 3
+    assert f(A, B, 4, 8, float("nan"), NULL, 0, S) == 3
+    assert f(NULL, B, 4, 8, 1.0, NULL, 0, S) == 1
+    assert f(A, NULL, 4, 8, 1.0, NULL, 0, S) == 1
+    assert f(A, B, 4, 8, 1.0, NULL, 64, S) == 1                 # NULL workspace, nonzero size
+    assert f(A, P(G + 4), 4, 8, 1.0, NULL, 0, S) == 4           # y overlaps x partially
+    need = et.softmax_workspace_bytes(256, 128256)
+    assert f(A, B, 256, 128256, 1.0, C, need - 1, S) == 5       # workspace too small
+    assert f(A, B, 256, 128256, 1.0, P(3 * G + 4), need, S) == 5  # not 8-byte aligned
+    assert f(A, B, 256, 128256, 1.0, P(G + 64), need, S) == 4   # workspace inside x
+    assert f(A, B, 1, 8192 * 8192 + 1, 1.0, NULL, 0, S) == 5    # too long without a workspace
+    assert f(NULL, NULL, 0, 8, 1.0, NULL, 0, S) == 0
+    assert f(A, B, 4, 0, 1.0, NULL, 0, S) == 0
+
+
+def test_softmax_workspace_sizes():
+    import elementwise_transformer_amd as et
+    assert et.softmax_workspace_bytes(0, 100000) == 0
+    assert et.softmax_workspace_bytes(256, 32768) == 0           # register path: none needed
+    assert et.softmax_workspace_bytes(256, 32769) == 256 * 5 * 8
+    assert et.softmax_workspace_bytes(256, 128256) == 256 * 16 * 8   # (m, s) per 8192-element chunk
 
 
 def test_argmax_workspace_sizes():

@@ -1,0 +1,175 @@
+"""GPU parity of the softmax-with-temperature entry point against the CPU
+oracle, through the C ABI.
+
+Tolerances, derived from the f32 arithmetic of the kernels (u = 2^-24):
+  f32   |got - y| <= u (|z| + 2|M| + 2|z - M| + 96) y + 2^-140, with z = x/t
+        and M the row max.  z carries one rounding of the quotient (u |z|),
+        z - M one more plus M's own (2 u |M|, u |z - M|); the exponential and
+        the final division a few ulp; the sum of a row's exponentials at most
+        32 sequential additions per thread, a 6-level butterfly, 16 wave
+        partials and the chunk combine -- well under 96 u in all.
+  bf16  at most 1 bf16 ulp from the oracle's correctly rounded value (the
+        f32 result above is far inside half a bf16 ulp); results below
+        2^-126 may also be flushed to zero by the hardware exponential.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_util import assert_bf16_ulp, assert_bits, dev, host, widen
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+@pytest.fixture(scope="module")
+def et():
+    import elementwise_transformer_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return m
+
+
+def _rng(*key):
+    return np.random.default_rng([4343, *key])
+
+
+def _check(got, x_store, t, y, y64, what):
+    if got.dtype == np.float32:
+        z = widen(x_store) / np.float64(np.float32(t))
+        with np.errstate(invalid="ignore"):
+            m = np.max(z, axis=-1, keepdims=True)
+            tol = U * (np.abs(z) + 2 * np.abs(m) + 2 * np.abs(z - m) + 96.0)
+        g = got.astype(np.float64)
+        gn, rn = np.isnan(g), np.isnan(y64)
+        assert np.array_equal(gn, rn), f"{what}: NaN positions differ"
+        fin = ~rn
+        err = np.abs(g[fin] - y64[fin])
+        # an exact 0 (the exponential of -inf) must come out as 0 (+ the floor)
+        with np.errstate(invalid="ignore"):
+            lim = np.where(y64[fin] == 0, 0.0, tol[fin] * np.abs(y64[fin])) + 2.0 ** -140
+        bad = np.flatnonzero(~(err <= lim))
+        if bad.size:
+            i = bad[np.argmax(err[bad] / lim[bad])]
+            raise AssertionError(f"{what}: {bad.size} over tolerance; worst got={g[fin][i]!r} "
+                                 f"ref={y64[fin][i]!r} rel={err[i] / max(abs(y64[fin][i]), 1e-300):.3g} "
+                                 f"tol={tol[fin][i]:.3g}")
+    else:
+        flushed = (np.abs(y64) < 2.0 ** -126) & (got == 0)
+        g = np.where(flushed, y, got)
+        assert_bf16_ulp(g, y, what)
+
+
+def _logits(shape, dt, key, scale=3.0):
+    x = (_rng(*key).standard_normal(shape) * scale).astype(np.float32)
+    return wl.store(x, dt)
+
+
+SHAPES = [(1, 1), (3, 5), (4, 64), (7, 100), (5, 1000), (3, 4096), (2, 8191), (2, 32768),
+          (2, 32769), (3, 40000), (2, 128256)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_softmax_matches_oracle(et, orc, dt, shape):
+    for t in (1.0, 0.7):
+        xs = _logits(shape, dt, (shape[1], 1 if dt == "f32" else 2))
+        y, y64 = orc.softmax(xs, t)
+        got = host(et.softmax(dev(xs), t))
+        _check(got, xs, t, y, y64, f"{dt} {shape} t={t}")
+        assert np.all(np.abs(y64.sum(axis=1) - 1.0) < 1e-12)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [40000, 128256])
+def test_softmax_workspace_and_single_block_agree(et, dt, n):
+    """Long rows: the two-launch split (workspace) and one workgroup per row
+    (no workspace) give identical bits."""
+    xs = dev(_logits((5, n), dt, (n, 3)))
+    a = host(et.softmax(xs, 0.9, split=True))
+    b = host(et.softmax(xs, 0.9, split=False))
+    assert_bits(a, b, f"{dt} n={n}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [100, 4096, 32768, 40000, 128256])
+def test_softmax_batch_invariance_and_in_place(et, dt, n):
+    """A row's bits do not depend on the rows beside it; y == x works."""
+    rows = 64 if n <= 4096 else 9
+    xs = _logits((rows, n), dt, (n, 4))
+    xd = dev(xs)
+    full = host(et.softmax(xd, 1.3))
+    for r in (0, rows // 2, rows - 1):
+        one = host(et.softmax(dev(np.ascontiguousarray(xs[r:r + 1])), 1.3))
+        assert_bits(one[0], full[r], f"{dt} n={n} row {r}")
+    inplace = xd.clone()
+    et.softmax(inplace, 1.3, out=inplace)
+    assert_bits(host(inplace), full, f"{dt} n={n} in place")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [7, 1001, 40003])
+def test_softmax_scalar_path(et, orc, dt, n):
+    """Misaligned buffers and lengths that are not whole vectors take the
+    scalar loads with the same ownership; results match the oracle."""
+    xs = _logits((3, n), dt, (n, 5))
+    y, y64 = orc.softmax(xs, 0.8)
+    t = dev(xs)
+    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    mis = flat[1:1 + t.numel()].view(t.shape)
+    mis.copy_(t)
+    assert mis.data_ptr() % 16 != 0
+    got = host(et.softmax(mis, 0.8))
+    _check(got, xs, 0.8, y, y64, f"{dt} n={n} misaligned")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("n", [16, 5000, 40000])
+def test_softmax_special_values(et, orc, dt, n):
+    """NaN anywhere, all -inf, a +inf entry: NaN rows; a single -inf entry
+    gets 0; logits of 1e4 stay finite (the max is subtracted)."""
+    x = (_rng(n, 6).standard_normal((6, n)) * 2).astype(np.float32)
+    x[0, n // 3] = np.nan
+    x[1, :] = -np.inf
+    x[2, n // 2] = np.inf
+    x[3, n - 1] = -np.inf
+    x[4, :] += 1.0e4
+    x[5, :] -= 1.0e4
+    xs = wl.store(x, dt)
+    y, y64 = orc.softmax(xs, 1.0)
+    got = host(et.softmax(dev(xs), 1.0))
+    assert np.all(np.isnan(widen(got[:3])))
+    assert widen(got[3:4])[0, n - 1] == 0.0
+    assert np.all(np.isfinite(widen(got[3:])))
+    _check(got[3:], xs[3:], 1.0, y[3:], y64[3:], f"{dt} n={n} special")
+
+
+def test_softmax_empty_and_degenerate(et):
+    x = torch.empty((0, 10), device="cuda")
+    assert et.softmax(x).shape == (0, 10)
+    x = torch.empty((4, 0), device="cuda")
+    assert et.softmax(x).shape == (4, 0)
+    one = et.softmax(torch.tensor([[3.0]], device="cuda"))
+    assert float(one[0, 0]) == 1.0
+    with pytest.raises(Exception):
+        et.softmax(torch.ones((2, 3), device="cuda"), 0.0)
+
+
+def test_softmax_decode_logits_full_size(et, orc):
+    """The decode logits at full size, [256, 128256] f32 N(0, 3) with planted
+    ties and NaN rows, temperature 0.7, in the launch configuration the
+    benchmark times (split over workgroups): sampled rows against the oracle,
+    every row summing to 1 where it holds no NaN."""
+    w = wl.WORKLOADS[3]
+    lg, _ = wl.gen_argmax(w)
+    xd = dev(lg)
+    got_d = et.softmax(xd, 0.7)
+    sums = got_d.double().sum(dim=1).cpu().numpy()
+    nan_rows = np.any(np.isnan(lg), axis=1)
+    assert np.all(np.abs(sums[~nan_rows] - 1.0) < 1e-4)
+    got = host(got_d)
+    rows = sorted(set([0, 1, 127, 255] + list(np.flatnonzero(nan_rows)[:2])))
+    sub = np.ascontiguousarray(lg[rows])
+    y, y64 = orc.softmax(sub, 0.7)
+    _check(got[rows], sub, 0.7, y, y64, "decode logits")
