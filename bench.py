@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed region, run three 256 MiB device-to-device copies (a "
                         "plain copy kernel of known size, to scale HBM traffic counters)")
+    p.add_argument("--no-next-ops", action="store_true",
+                   help="skip timing the ops beyond the step (softmax with temperature)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="least CPU time spent timing the oracle on whole steps")
     return p.parse_args()
@@ -210,6 +212,41 @@ def traffic_record(workload, op):
     return float(m_b.group(1)) if h.hexdigest() == m_src.group(1) else None
 
 
+def time_next_ops(et, torch, wl, stream, sets=3, launches=60):
+    """Per-launch HIP-event times of the ops beyond the step, on the inputs
+    their workloads name: softmax with temperature 0.7 over the decode
+    logits [256, 128256] f32 (read once, written once)."""
+    w = wl.WORKLOADS[3]
+    lg, _ = wl.gen_argmax(w)
+    rows, n = lg.shape
+    xs = [torch.from_numpy(lg).cuda() for _ in range(sets)]
+    ys = [torch.empty_like(x) for x in xs]
+    ws = torch.zeros(max(et.softmax_workspace_bytes(rows, n), 16), dtype=torch.uint8, device="cuda")
+    fn = lambda i: et.softmax(xs[i % sets], 0.7, out=ys[i % sets], workspace=ws)
+    for i in range(sets * 2):
+        fn(i)
+    torch.cuda.synchronize()
+    ms = []
+    for i in range(launches):
+        ev = TimingEvents(stream)
+        ev.start()
+        fn(i)
+        ev.stop()
+        ms.append(ev)
+    torch.cuda.synchronize()
+    t = [ev.elapsed_ms() for ev in ms]
+    for ev in ms:
+        ev.close()
+    nbytes = 2 * rows * n * 4
+    avg = float(np.mean(t))
+    gbps = nbytes / (avg * 1e-3) / 1e9
+    return {"softmax": {"workload": "decode logits [256,128256] f32, temperature 0.7",
+                        "bytes": nbytes, "avg_us": round(avg * 1e3, 2),
+                        "median_us": round(float(np.median(t)) * 1e3, 2), "samples": len(t),
+                        "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_GBPS, 4),
+                        "kernels": "softmax_chunks (one launch)"}}
+
+
 def cpu_baseline(w, min_seconds):
     """The CPU oracle as it stands, timed on whole steps of the same workload
     (every op at full size), repeated until at least min_seconds of work."""
@@ -335,6 +372,11 @@ def main():
             ops[i].ms.append(ev.elapsed_ms())
             ev.close()
 
+    # Ops beyond the step (the next rows built to the same bar), each timed on
+    # its own workload after the timed region, as back-to-back launches over
+    # rotating buffer sets with one pair of events per launch.
+    next_ops = None if args.no_next_ops else time_next_ops(et, torch, wl, stream)
+
     # Attainable-bandwidth context: a plain device-to-device copy as large as
     # the dominant op's largest operand (read once, written once), timed the
     # same way after the timed region.
@@ -419,6 +461,7 @@ def main():
         "ops": per_op,
         "roofline": roofline,
         "copy_context": copy_ctx,
+        "next_ops": next_ops,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -289,8 +289,8 @@ def softmax(x: torch.Tensor, temperature: float = 1.0, out: Optional[torch.Tenso
             workspace: Optional[torch.Tensor] = None, split: bool = True) -> torch.Tensor:
     """Softmax of x / temperature over the last axis (et_softmax_*); out may be
     x.  ``split`` lets rows longer than 32768 elements spread over several
-    workgroups through a workspace (allocated here unless given; its contents
-    need no initialisation)."""
+    workgroups through a workspace: zero-filled here unless given; a given
+    one must be zero-filled before its first use (each call leaves it so)."""
     n = x.shape[-1]
     rows = math.prod(x.shape[:-1])
     out = torch.empty_like(x) if out is None else out
@@ -301,7 +301,7 @@ def softmax(x: torch.Tensor, temperature: float = 1.0, out: Optional[torch.Tenso
         need = softmax_workspace_bytes(rows, n)
         if need > 0:
             if workspace is None:
-                workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+                workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
             _dev(workspace)
             ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     _call(f"et_softmax_{_sfx(x)}", _ptr(x), _ptr(out), rows, n, float(temperature), ws_ptr, ws_bytes,

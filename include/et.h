@@ -210,15 +210,15 @@ et_status et_argmax_bf16(const et_bf16* x, int64_t rows, int64_t n,
  *   Special values follow the formula: a NaN anywhere in a row, or a row
  *   whose largest z is +-inf, gives a row of NaN.
  *   workspace: device scratch for rows longer than 32768 elements, which are
- *   then split over several workgroups (two launches).  Either
- *   workspace == NULL with workspace_bytes == 0 (one workgroup per long row;
- *   rows of more than 8000 * 8192 elements then return ET_ERR_WORKSPACE), or
- *   workspace != NULL, 8-byte aligned, with workspace_bytes >=
- *   et_softmax_workspace_bytes(rows, n) (0 for rows of at most 32768
- *   elements), else ET_ERR_WORKSPACE.  The caller owns the workspace; its
- *   contents need no initialisation and are overwritten.  Calls that share a
- *   workspace must not run concurrently.  The result is the same with or
- *   without a workspace.
+ *   then split over several workgroups in one launch (each element read
+ *   once).  Either workspace == NULL with workspace_bytes == 0 (one workgroup
+ *   per long row, reading the row three times), or workspace != NULL,
+ *   16-byte aligned, with workspace_bytes >= et_softmax_workspace_bytes(rows,
+ *   n) (0 for rows of at most 32768 elements), else ET_ERR_WORKSPACE.  The
+ *   caller owns the workspace.  It must be zero-filled before its first use;
+ *   every call leaves its counters zero again, so it can be reused as is.
+ *   Calls that share a workspace must not run concurrently.  The result is
+ *   the same with or without a workspace.
  */
 size_t et_softmax_workspace_bytes(int64_t rows, int64_t n);
 et_status et_softmax_f32(const float* x, float* y, int64_t rows, int64_t n,

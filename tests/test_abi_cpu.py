@@ -186,9 +186,8 @@ def test_softmax_validation(sfx):
     assert f(A, P(G + 4), 4, 8, 1.0, NULL, 0, S) == 4           # y overlaps x partially
     need = et.softmax_workspace_bytes(256, 128256)
     assert f(A, B, 256, 128256, 1.0, C, need - 1, S) == 5       # workspace too small
-    assert f(A, B, 256, 128256, 1.0, P(3 * G + 4), need, S) == 5  # not 8-byte aligned
+    assert f(A, B, 256, 128256, 1.0, P(3 * G + 8), need, S) == 5  # not 16-byte aligned
     assert f(A, B, 256, 128256, 1.0, P(G + 64), need, S) == 4   # workspace inside x
-    assert f(A, B, 1, 8192 * 8192 + 1, 1.0, NULL, 0, S) == 5    # too long without a workspace
     assert f(NULL, NULL, 0, 8, 1.0, NULL, 0, S) == 0
     assert f(A, B, 4, 0, 1.0, NULL, 0, S) == 0
 
@@ -197,8 +196,10 @@ def test_softmax_workspace_sizes():
     import elementwise_transformer_amd as et
     assert et.softmax_workspace_bytes(0, 100000) == 0
     assert et.softmax_workspace_bytes(256, 32768) == 0           # register path: none needed
-    assert et.softmax_workspace_bytes(256, 32769) == 256 * 5 * 8
-    assert et.softmax_workspace_bytes(256, 128256) == 256 * 16 * 8   # (m, s) per 8192-element chunk
+    # two counters per row (rounded up to 16 bytes), then (m, s) per 8192-element chunk
+    assert et.softmax_workspace_bytes(256, 32769) == 256 * 8 + 256 * 5 * 8
+    assert et.softmax_workspace_bytes(256, 128256) == 256 * 8 + 256 * 16 * 8
+    assert et.softmax_workspace_bytes(3, 40000) == 32 + 3 * 5 * 8
 
 
 def test_argmax_workspace_sizes():
