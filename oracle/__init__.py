@@ -68,6 +68,8 @@ class Oracle:
         lib.orc_rope_angle.restype = _f32
         lib.orc_rmsnorm.argtypes = [_int, _vp, _vp, _i64, _i64, _f32, _vp, _vp]
         lib.orc_softmax.argtypes = [_int, _vp, _i64, _i64, _f32, _vp, _vp]
+        lib.orc_layernorm.argtypes = [_int, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp]
+        lib.orc_geglu.argtypes = [_int, _vp, _vp, _i64, _int, _vp, _vp]
         lib.orc_add_rmsnorm.argtypes = [_int, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp, _vp]
         lib.orc_rope.argtypes = [_int, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _f32, _int, _vp]
         lib.orc_rmsnorm_rope.argtypes = [_int, _vp, _vp, _f32, _vp, _i64, _i64, _i64, _i64,
@@ -192,6 +194,32 @@ class Oracle:
         y = np.empty_like(x)
         y64 = np.empty(x.shape, np.float64)
         self.lib.orc_softmax(dt, _p(x), rows, n, t, _p(y64), _p(y))
+        return y, y64
+
+    def layernorm(self, x: np.ndarray, g: np.ndarray, b: Optional[np.ndarray], eps: float):
+        """[rows, d] -> (y, y64); b may be None (no bias)."""
+        x = np.ascontiguousarray(x)
+        dt = _dt(x)
+        rows, d = x.shape
+        assert g.dtype == x.dtype and g.shape == (d,)
+        if b is not None:
+            assert b.dtype == x.dtype and b.shape == (d,)
+            b = np.ascontiguousarray(b)
+        y = np.empty_like(x)
+        y64 = np.empty(x.shape, np.float64)
+        self.lib.orc_layernorm(dt, _p(x), _p(np.ascontiguousarray(g)), _p(b) if b is not None else None,
+                               rows, d, eps, _p(y64), _p(y))
+        return y, y64
+
+    def geglu(self, gate: np.ndarray, up: np.ndarray, form: int = 0):
+        """GELU(gate) * up; form 0 = erf (exact), 1 = tanh approximation."""
+        gate = np.ascontiguousarray(gate)
+        up = np.ascontiguousarray(up)
+        dt = _dt(gate)
+        assert up.shape == gate.shape and up.dtype == gate.dtype
+        y = np.empty_like(gate)
+        y64 = np.empty(gate.shape, np.float64)
+        self.lib.orc_geglu(dt, _p(gate), _p(up), gate.size, form, _p(y64), _p(y))
         return y, y64
 
 

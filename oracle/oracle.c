@@ -7,12 +7,14 @@
  * this file; only the tests, the smoke check and the benchmark's CPU-baseline
  * leg do.  It shares no source with the HIP kernels.
  *
- * Also the first of the next rows: softmax over the last axis with a
- * temperature.
+ * Also the next rows built after those: softmax over the last axis with a
+ * temperature; LayerNorm; GELU-gated multiply (GeGLU, erf and tanh forms).
  *
  * Sources (web pages; sections named, never line numbers):
- *   [OPS]  "Operations" (glia runtime op spec): 2 Normalization / RmsNorm;
- *          3 Position encoding / Rope; 4 Activation / Silu, SwiGlu;
+ *   [OPS]  "Operations" (glia runtime op spec): 2 Normalization / RmsNorm,
+ *          LayerNorm;
+ *          3 Position encoding / Rope; 4 Activation / Silu, Gelu, SwiGlu,
+ *          GeGlu, Softmax;
  *          5 Attention / QK-norm; 8 Sampling / Greedy; 10 Fused ops.
  *   [ELT]  "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding,
  *          add, argmax": 2.1 RMSNorm; 2.2 RoPE; 2.3 SiLU-mul (SwiGLU);
@@ -361,5 +363,61 @@ void orc_softmax(int dt, const void* x, int64_t rows, int64_t n, float t,
             if (y) st(dt, y, r * n + i, v);
         }
         free(z);
+    }
+}
+
+/* -------------------------------------------------------------- LayerNorm */
+
+/* [OPS] 2 Normalization / LayerNorm; [DNN] 7: mu = mean(x),
+ * var = mean((x - mu)^2), y = (x - mu) / sqrt(var + eps) * g + b over the
+ * last axis (the two-pass variance, as written).  b may be NULL (no bias,
+ * [DNN] 7's optional beta). */
+void orc_layernorm(int dt, const void* x, const void* g, const void* b,
+                   int64_t rows, int64_t d, float eps, double* y64, void* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        double sum = 0.0;
+        for (int64_t i = 0; i < d; ++i) sum += ld(dt, x, r * d + i);
+        const double mu = sum / (double)d;
+        double ss = 0.0;
+        for (int64_t i = 0; i < d; ++i) {
+            const double c = ld(dt, x, r * d + i) - mu;
+            ss += c * c;
+        }
+        const double var = ss / (double)d;
+        const double inv = 1.0 / sqrt(var + (double)eps);
+        for (int64_t i = 0; i < d; ++i) {
+            double v = (ld(dt, x, r * d + i) - mu) * inv * ld(dt, g, i);
+            if (b) v += ld(dt, b, i);
+            if (y64) y64[r * d + i] = v;
+            if (y) st(dt, y, r * d + i, v);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ GeGLU */
+
+/* [OPS] 4 Activation / Gelu and GeGlu: y = Gelu(gate) * up with
+ *   form 0 (exact):  Gelu(x) = x * 0.5 * (1 + erf(x / sqrt(2)))
+ *   form 1 (tanh):   Gelu(x) = 0.5 * x * (1 + tanh(sqrt(2/pi) * (x + 0.044715 x^3)))
+ * (the page's constant inside the tanh form is garbled; it is 2/pi, the
+ * form's published definition).  Each is evaluated through an exact
+ * identity that avoids the cancellation of 1 + (-1 + tiny) for negative x:
+ * 1 + erf(z) = erfc(-z), and (1 + tanh(u)) / 2 = 1 / (1 + e^(-2u)).
+ * f64 throughout with libm erfc and exp. */
+void orc_geglu(int dt, const void* gate, const void* up, int64_t n, int form,
+               double* y64, void* y) {
+    const double k = sqrt(2.0 / acos(-1.0));   /* acos(-1) is pi rounded to f64 */
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        const double x = ld(dt, gate, i);
+        double gl;
+        if (form == 0)
+            gl = x * 0.5 * erfc(-x / sqrt(2.0));
+        else
+            gl = x / (1.0 + exp(-2.0 * k * (x + 0.044715 * x * x * x)));
+        const double v = gl * ld(dt, up, i);
+        if (y64) y64[i] = v;
+        if (y) st(dt, y, i, v);
     }
 }

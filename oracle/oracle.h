@@ -53,6 +53,10 @@ void orc_embedding(int dt, const void* table, int64_t V, const int32_t* ids,
 void orc_argmax(int dt, const void* x, int64_t rows, int64_t n, int32_t* out);
 void orc_softmax(int dt, const void* x, int64_t rows, int64_t n, float t,
                  double* y64, void* y);
+void orc_layernorm(int dt, const void* x, const void* g, const void* b,
+                   int64_t rows, int64_t d, float eps, double* y64, void* y);
+void orc_geglu(int dt, const void* gate, const void* up, int64_t n, int form,
+               double* y64, void* y);
 
 #ifdef __cplusplus
 }

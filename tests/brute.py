@@ -108,3 +108,90 @@ def softmax_decimal(x: Sequence[float], t: float, digits: int = 50) -> List[floa
             s = sum(((zj - zi).exp() for zj in z), Decimal(0))
             out.append(float(Decimal(1) / s))
         return out
+
+
+def _dec_pi(ctx_prec: int):
+    """pi in Decimal by Machin's formula, 16 * atan(1/5) - 4 * atan(1/239)."""
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = ctx_prec + 10
+
+        def atan_inv(n):
+            x = Decimal(1) / n
+            x2 = x * x
+            term, total, k = x, x, 1
+            while True:
+                term *= -x2
+                k += 2
+                add = term / k
+                if add == 0 or abs(add) < Decimal(10) ** (-(ctx_prec + 8)):
+                    break
+                total += add
+            return total
+        return +(16 * atan_inv(5) - 4 * atan_inv(239))
+
+
+def erfc_decimal(z: float, digits: int = 90):
+    """erfc(z) = 1 - (2/sqrt(pi)) sum_n (-1)^n z^(2n+1) / (n! (2n+1)), summed in
+    high-precision decimal (enough digits that 1 - erf keeps ~25 significant
+    ones for |z| < 7.5).  Returns a Decimal."""
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = digits
+        zz = Decimal(z)
+        total, term, n = Decimal(0), zz, 0
+        while True:
+            add = term / (2 * n + 1)
+            total += add
+            n += 1
+            term = -term * zz * zz / n
+            if abs(add) < Decimal(10) ** (-(digits - 5)) and n > 5:
+                break
+        pi = _dec_pi(digits)
+        return 1 - 2 * total / pi.sqrt()
+
+
+def gelu_erf_decimal(x: float) -> float:
+    """x * erfc(-x / sqrt 2) / 2 with erfc from the decimal series (the
+    argument x / sqrt 2 is formed in 90-digit decimal and passed on as the
+    nearest double, a relative change of 1e-16)."""
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = 90
+        z = float(-Decimal(x) / Decimal(2).sqrt())
+        return float(Decimal(x) * erfc_decimal(z) / 2)
+
+
+def gelu_tanh_decimal(x: float) -> float:
+    """0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3), with
+    tanh(u) = (e^(2u) - 1) / (e^(2u) + 1) in 60-digit decimal."""
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = 60
+        xx = Decimal(x)
+        pi = _dec_pi(60)
+        u = (2 / pi).sqrt() * (xx + Decimal("0.044715") * xx ** 3)
+        e2 = (2 * u).exp()
+        th = (e2 - 1) / (e2 + 1)
+        return float(xx * (1 + th) / 2)
+
+
+def layernorm_row_exact(x: Sequence[float], g: Sequence[float], b, eps: float) -> List[float]:
+    """LayerNorm of one row with the mean and variance as exact fractions and
+    the square root in 50-digit decimal."""
+    from decimal import Decimal, localcontext
+    d = len(x)
+    fx = [Fraction(v) for v in x]
+    mu = sum(fx) / d
+    var = sum((v - mu) ** 2 for v in fx) / d
+    with localcontext() as ctx:
+        ctx.prec = 50
+        den = (Decimal(var.numerator) / Decimal(var.denominator) + Decimal(eps)).sqrt()
+        out = []
+        for i, v in enumerate(fx):
+            c = v - mu
+            val = Decimal(c.numerator) / Decimal(c.denominator) / den * Decimal(g[i])
+            if b is not None:
+                val += Decimal(b[i])
+            out.append(float(val))
+        return out

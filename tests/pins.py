@@ -589,6 +589,135 @@ def pin_softmax_matches_library(orc):
                 np.max(np.abs(y.astype(np.int32) - _bf16(ref.astype(np.float32)).astype(np.int32))) <= 1
 
 
+# -------------------------------------------------------------- LayerNorm
+
+def pin_layernorm_closed_forms(orc):
+    """[OPS] LayerNorm: a constant row gives exactly the bias (x - mu = 0), or
+    0 without one; two entries give +-|a - c|/2 / sqrt(((a - c)/2)^2 + eps);
+    eps is inside the root (the [ELT] 3 example's numbers: +-1e-3, eps 1e-6
+    gives +-0.70711, not the 0.999 of eps outside)."""
+    for dt in ("f32", "bf16"):
+        cvt = (lambda a: a) if dt == "f32" else _bf16
+        wide = (lambda a: a.astype(np.float64)) if dt == "f32" else (lambda a: _wide(a).astype(np.float64))
+        x = cvt(np.full((3, 9), 1.75, np.float32))
+        g = cvt(np.linspace(0.5, 1.5, 9).astype(np.float32))
+        b = cvt(np.linspace(-1, 1, 9).astype(np.float32))
+        y, y64 = orc.layernorm(x, g, b, 1e-5)
+        assert np.array_equal(y64, np.broadcast_to(wide(b), (3, 9)))
+        assert np.array_equal(y.view(np.uint8), np.broadcast_to(b, (3, 9)).view(np.uint8))
+        _, y64 = orc.layernorm(x, g, None, 1e-5)
+        assert np.all(y64 == 0.0)
+    a, c, eps = 2.5, -1.0, 1e-3
+    _, y64 = orc.layernorm(_f32([a, c])[None], _f32([1.0, 1.0]), None, eps)
+    h = abs(a - c) / 2
+    expect = h / math.sqrt(h * h + float(np.float32(eps)))
+    assert abs(y64[0, 0] - expect) <= 1e-15 and abs(y64[0, 1] + expect) <= 1e-15
+    _, y64 = orc.layernorm(_f32([1e-3, -1e-3])[None], _f32([1.0, 1.0]), None, 1e-6)
+    assert abs(y64[0, 0] - 0.70711) < 1e-5 and abs(y64[0, 1] + 0.70711) < 1e-5
+
+
+def pin_layernorm_invariants(orc):
+    """Shifting a row by a constant changes nothing; with unit gain and zero
+    bias the output has mean 0 and mean square var / (var + eps); the bias is
+    added after the gain; a row's result does not depend on the others."""
+    g = np.random.default_rng(83)
+    x = np.round(g.standard_normal((5, 64)) * 8).astype(np.float32)    # integers: exact shifts
+    one, zero = np.ones(64, np.float32), np.zeros(64, np.float32)
+    y0, y64 = orc.layernorm(x, one, zero, 1e-5)
+    ys, _ = orc.layernorm(x + np.float32(1024.0), one, zero, 1e-5)
+    assert np.array_equal(y0.view(np.uint32), ys.view(np.uint32))
+    xd = x.astype(np.float64)
+    var = xd.var(axis=1)
+    assert np.all(np.abs(y64.mean(axis=1)) < 1e-14)
+    assert np.allclose((y64 ** 2).mean(axis=1), var / (var + float(np.float32(1e-5))), rtol=1e-13)
+    gain = g.uniform(0.5, 1.5, 64).astype(np.float32)
+    bias = g.standard_normal(64).astype(np.float32)
+    _, yg = orc.layernorm(x, gain, bias, 1e-5)
+    assert np.allclose(yg, y64 * gain.astype(np.float64) + bias.astype(np.float64), rtol=1e-14, atol=1e-14)
+    alone, _ = orc.layernorm(np.ascontiguousarray(x[3:4]), gain, bias, 1e-5)
+    full, _ = orc.layernorm(x, gain, bias, 1e-5)
+    assert np.array_equal(alone[0].view(np.uint32), full[3].view(np.uint32))
+
+
+def pin_layernorm_brute_and_library(orc):
+    """Exact-fraction mean and variance with a 50-digit square root, and
+    torch's f64 layer_norm, on random rows (with and without bias)."""
+    import torch
+    g = np.random.default_rng(89)
+    x = (g.standard_normal((4, 37)) * 3 + 1).astype(np.float32)
+    gain = g.uniform(0.5, 1.5, 37).astype(np.float32)
+    bias = g.standard_normal(37).astype(np.float32)
+    for b in (bias, None):
+        _, y64 = orc.layernorm(x, gain, b, 1e-5)
+        for r in range(4):
+            ref = brute.layernorm_row_exact([float(v) for v in x[r]], [float(v) for v in gain],
+                                            None if b is None else [float(v) for v in b], float(np.float32(1e-5)))
+            assert np.allclose(y64[r], ref, rtol=1e-13, atol=1e-14), r
+        lib = torch.nn.functional.layer_norm(torch.from_numpy(x.astype(np.float64)), (37,),
+                                             torch.from_numpy(gain.astype(np.float64)),
+                                             None if b is None else torch.from_numpy(b.astype(np.float64)),
+                                             eps=float(np.float32(1e-5))).numpy()
+        assert np.allclose(y64, lib, rtol=1e-12, atol=1e-13)
+    xb, gb, bb = _bf16(x), _bf16(gain), _bf16(bias)
+    y, y64 = orc.layernorm(xb, gb, bb, 1e-5)
+    assert np.array_equal(y, np.array([brute.bf16_bits_exact(v) for v in y64.ravel()], np.uint16).reshape(y.shape))
+
+
+# ------------------------------------------------------------------ GeGLU
+
+def pin_gelu_symmetry_and_limits(orc):
+    """[OPS] Gelu, both forms: Gelu(x) - Gelu(-x) = x (erf and tanh are
+    odd), Gelu(0) = 0, Gelu(x) -> x for large x and -> -0 far below zero; the
+    up factor multiplies."""
+    xs = _f32([0.25, 0.5, 1.0, 1.7, 2.5, 4.0, 6.0])
+    for form in (0, 1):
+        yp, yp64 = orc.geglu(xs, np.ones_like(xs), form)
+        yn, yn64 = orc.geglu(-xs, np.ones_like(xs), form)
+        assert np.allclose(yp64 - yn64, xs.astype(np.float64), rtol=1e-15, atol=0.0), form
+        _, z64 = orc.geglu(_f32([0.0, 12.0, -60.0]), _f32([1.0, 1.0, 1.0]), form)
+        assert z64[0] == 0.0 and z64[1] == 12.0 and z64[2] == 0.0 and math.copysign(1.0, z64[2]) < 0
+        _, u64 = orc.geglu(xs, _f32([3.0] * 7), form)
+        assert np.allclose(u64, 3.0 * yp64, rtol=1e-15, atol=0.0)
+
+
+def pin_gelu_brute(orc):
+    """Both forms against high-precision decimal evaluations that take a
+    different route: the erfc power series (with pi from Machin's formula) and
+    tanh from decimal exponentials -- including x = -10, where 1 + erf(x/sqrt 2)
+    cancels in f64 and only the exact identity keeps the 7.6e-23."""
+    xs = [-10.0, -5.5, -2.0, -0.75, -0.1, 0.3, 1.0, 2.25, 4.5]
+    x = _f32(xs)
+    _, e64 = orc.geglu(x, np.ones_like(x), 0)
+    _, t64 = orc.geglu(x, np.ones_like(x), 1)
+    for i, v in enumerate(x):
+        ref_e = brute.gelu_erf_decimal(float(v))
+        ref_t = brute.gelu_tanh_decimal(float(v))
+        assert abs(e64[i] - ref_e) <= 1e-13 * abs(ref_e) + 1e-300, (v, e64[i], ref_e)
+        assert abs(t64[i] - ref_t) <= 1e-13 * abs(ref_t) + 1e-300, (v, t64[i], ref_t)
+
+
+def pin_gelu_matches_library(orc):
+    """torch's f64 gelu (approximate 'none' and 'tanh') on the same inputs,
+    f32 and bf16 storage; the two forms stay within 1e-3 of each other but
+    are not equal."""
+    import torch
+    g = np.random.default_rng(97)
+    gate = (g.standard_normal(2000) * 2).astype(np.float32)
+    up = g.standard_normal(2000).astype(np.float32)
+    for dt in ("f32", "bf16"):
+        gs, us = (gate, up) if dt == "f32" else (_bf16(gate), _bf16(up))
+        gw = gs.astype(np.float64) if dt == "f32" else _wide(gs).astype(np.float64)
+        uw = us.astype(np.float64) if dt == "f32" else _wide(us).astype(np.float64)
+        for form, approx in ((0, "none"), (1, "tanh")):
+            _, y64 = orc.geglu(gs, us, form)
+            ref = torch.nn.functional.gelu(torch.from_numpy(gw), approximate=approx).numpy() * uw
+            assert np.allclose(y64, ref, rtol=1e-12, atol=1e-15), (dt, form)
+    _, e64 = orc.geglu(gate, np.ones_like(gate), 0)
+    _, t64 = orc.geglu(gate, np.ones_like(gate), 1)
+    d = np.abs(e64 - t64)
+    assert d.max() < 1e-3 and d.max() > 1e-5
+
+
 # ------------------------------------------------------- batch invariance
 
 def pin_batch_invariance(orc):

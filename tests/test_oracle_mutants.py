@@ -4,9 +4,9 @@ Each mutant is a copy of ``oracle/oracle.c`` with one plausible mistake
 planted by text substitution, built into a temporary library.  The pins must
 fail on every mutant.  s01-s15 are the mistakes listed in the Pitfalls table
 (section 5) of "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding,
-add, argmax", each with the test the page says catches it; x01-x16 are further
+add, argmax", each with the test the page says catches it; x01-x24 are further
 slips (a wrong sign, index, dropped term or rounding) in the same code, x11-x16
-in the softmax.
+in the softmax, x17-x20 in LayerNorm, x21-x24 in the GELU-gated multiply.
 """
 import os
 import tempfile
@@ -27,7 +27,8 @@ MUTANTS = {
     "s03_no_gain": ("hand_example",
                     [("v[i] = v[i] * inv * ld(dt, w, i);", "v[i] = v[i] * inv;")]),
     "s15_accumulator_per_call": ("rmsnorm_rows_are_independent_and_in_place",
-                                 [("    double ss = 0.0;\n", "    static double ss = 0.0;\n")]),
+                                 [("    double ss = 0.0;\n    for (int64_t i = 0; i < d; ++i) ss += v[i] * v[i];",
+                                   "    static double ss = 0.0;\n    for (int64_t i = 0; i < d; ++i) ss += v[i] * v[i];")]),
     "s04_layouts_swapped": ("rope_interleaved_layout_and_position_zero",
                             [("if (layout == 0) {", "if (layout == 1) {")]),
     "s05_minus_theta": ("hand_example",
@@ -77,6 +78,19 @@ MUTANTS = {
                                           [("if (v > FLT_MAX) v = INFINITY;\n            if (v < -FLT_MAX) v = -INFINITY;\n", "")]),
     "x16_softmax_exp_sign": ("softmax_temperature",
                              [("z[i] = exp(z[i] - m);", "z[i] = exp(m - z[i]);")]),
+    "x17_layernorm_not_centred": ("layernorm_closed_forms",
+                                  [("double v = (ld(dt, x, r * d + i) - mu) * inv * ld(dt, g, i);",
+                                    "double v = ld(dt, x, r * d + i) * inv * ld(dt, g, i);")]),
+    "x18_layernorm_eps_outside_root": ("layernorm_closed_forms",
+                                       [("1.0 / sqrt(var + (double)eps);", "1.0 / (sqrt(var) + (double)eps);")]),
+    "x19_layernorm_bias_dropped": ("layernorm_closed_forms", [("if (b) v += ld(dt, b, i);", "")]),
+    "x20_variance_over_d_minus_1": ("layernorm_invariants",
+                                    [("const double var = ss / (double)d;", "const double var = ss / (double)(d - 1);")]),
+    "x21_gelu_no_sqrt2": ("gelu_brute", [("erfc(-x / sqrt(2.0))", "erfc(-x)")]),
+    "x22_gelu_tanh_cubic_coefficient": ("gelu_brute", [("0.044715 * x * x * x", "0.44715 * x * x * x")]),
+    "x23_geglu_up_ignored": ("gelu_symmetry_and_limits",
+                             [("const double v = gl * ld(dt, up, i);", "const double v = gl;")]),
+    "x24_gelu_forms_swapped": ("gelu_brute", [("if (form == 0)\n", "if (form == 1)\n")]),
 }
 
 
