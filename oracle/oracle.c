@@ -404,7 +404,8 @@ void orc_layernorm(int dt, const void* x, const void* g, const void* b,
  * form's published definition).  Each is evaluated through an exact
  * identity that avoids the cancellation of 1 + (-1 + tiny) for negative x:
  * 1 + erf(z) = erfc(-z), and (1 + tanh(u)) / 2 = 1 / (1 + e^(-2u)).
- * f64 throughout with libm erfc and exp. */
+ * f64 throughout with libm erfc and exp; as for SiLU, e^(-2u) is taken to
+ * +inf once it passes the f32 range (x / inf = -0 far below zero). */
 void orc_geglu(int dt, const void* gate, const void* up, int64_t n, int form,
                double* y64, void* y) {
     const double k = sqrt(2.0 / acos(-1.0));   /* acos(-1) is pi rounded to f64 */
@@ -412,10 +413,13 @@ void orc_geglu(int dt, const void* gate, const void* up, int64_t n, int form,
     for (int64_t i = 0; i < n; ++i) {
         const double x = ld(dt, gate, i);
         double gl;
-        if (form == 0)
+        if (form == 0) {
             gl = x * 0.5 * erfc(-x / sqrt(2.0));
-        else
-            gl = x / (1.0 + exp(-2.0 * k * (x + 0.044715 * x * x * x)));
+        } else {
+            double e = exp(-2.0 * k * (x + 0.044715 * x * x * x));
+            if (e > FLT_MAX) e = INFINITY;  /* the f32 exponential's limit, as for SiLU */
+            gl = x / (1.0 + e);
+        }
         const double v = gl * ld(dt, up, i);
         if (y64) y64[i] = v;
         if (y) st(dt, y, i, v);

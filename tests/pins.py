@@ -678,6 +678,11 @@ def pin_gelu_symmetry_and_limits(orc):
         assert z64[0] == 0.0 and z64[1] == 12.0 and z64[2] == 0.0 and math.copysign(1.0, z64[2]) < 0
         _, u64 = orc.geglu(xs, _f32([3.0] * 7), form)
         assert np.allclose(u64, 3.0 * yp64, rtol=1e-15, atol=0.0)
+    # tanh form: e^(-2u) passes the f32 range between x = -10 and x = -10.5,
+    # after which the value is -0, as for SiLU (x / inf)
+    _, z64 = orc.geglu(_f32([-10.0, -10.5]), _f32([1.0, 1.0]), 1)
+    assert z64[0] < 0 and abs(z64[0] - brute.gelu_tanh_decimal(-10.0)) <= 1e-13 * abs(z64[0])
+    assert z64[1] == 0.0 and math.copysign(1.0, z64[1]) < 0
 
 
 def pin_gelu_brute(orc):

@@ -4,9 +4,9 @@ Each mutant is a copy of ``oracle/oracle.c`` with one plausible mistake
 planted by text substitution, built into a temporary library.  The pins must
 fail on every mutant.  s01-s15 are the mistakes listed in the Pitfalls table
 (section 5) of "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding,
-add, argmax", each with the test the page says catches it; x01-x24 are further
+add, argmax", each with the test the page says catches it; x01-x25 are further
 slips (a wrong sign, index, dropped term or rounding) in the same code, x11-x16
-in the softmax, x17-x20 in LayerNorm, x21-x24 in the GELU-gated multiply.
+in the softmax, x17-x20 in LayerNorm, x21-x25 in the GELU-gated multiply.
 """
 import os
 import tempfile
@@ -60,7 +60,8 @@ MUTANTS = {
                                                 "for (int64_t i = 0; i < d; ++i) v[i] = ld(dt, x, r * d + i)"
                                                 " + ld(dt, res, r * d + i);")]),
     "x05_cos_sin_swapped": (None, [("const double c = cos(ang);", "const double c = sin(ang);")]),
-    "x06_silu_no_overflow_limit": (None, [("if (e > FLT_MAX) e = INFINITY;", "")]),
+    "x06_silu_no_overflow_limit": (None, [("double e = exp(-gv);\n        if (e > FLT_MAX) e = INFINITY;",
+                                           "double e = exp(-gv);\n")]),
     "x07_gain_reversed": (None, [("v[i] = v[i] * inv * ld(dt, w, i);", "v[i] = v[i] * inv * ld(dt, w, d - 1 - i);")]),
     "x08_add_subtracts": (None, [("st(dt, y, i, ld(dt, a, i) + ld(dt, b, i));",
                                   "st(dt, y, i, ld(dt, a, i) - ld(dt, b, i));")]),
@@ -90,7 +91,9 @@ MUTANTS = {
     "x22_gelu_tanh_cubic_coefficient": ("gelu_brute", [("0.044715 * x * x * x", "0.44715 * x * x * x")]),
     "x23_geglu_up_ignored": ("gelu_symmetry_and_limits",
                              [("const double v = gl * ld(dt, up, i);", "const double v = gl;")]),
-    "x24_gelu_forms_swapped": ("gelu_brute", [("if (form == 0)\n", "if (form == 1)\n")]),
+    "x24_gelu_forms_swapped": ("gelu_brute", [("if (form == 0) {", "if (form == 1) {")]),
+    "x25_gelu_tanh_no_f32_limit": ("gelu_symmetry_and_limits",
+                                   [("if (e > FLT_MAX) e = INFINITY;  /* the f32", "/* the f32")]),
 }
 
 
