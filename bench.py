@@ -45,7 +45,7 @@ def parse():
                    help="after the timed region, run three 256 MiB device-to-device copies (a "
                         "plain copy kernel of known size, to scale HBM traffic counters)")
     p.add_argument("--no-next-ops", action="store_true",
-                   help="skip timing the ops beyond the step (softmax with temperature)")
+                   help="skip timing the ops beyond the step (softmax, LayerNorm, GeGLU)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="least CPU time spent timing the oracle on whole steps")
     return p.parse_args()
@@ -212,39 +212,80 @@ def traffic_record(workload, op):
     return float(m_b.group(1)) if h.hexdigest() == m_src.group(1) else None
 
 
-def time_next_ops(et, torch, wl, stream, sets=3, launches=60):
-    """Per-launch HIP-event times of the ops beyond the step, on the inputs
-    their workloads name: softmax with temperature 0.7 over the decode
-    logits [256, 128256] f32 (read once, written once)."""
-    w = wl.WORKLOADS[3]
-    lg, _ = wl.gen_argmax(w)
-    rows, n = lg.shape
-    xs = [torch.from_numpy(lg).cuda() for _ in range(sets)]
-    ys = [torch.empty_like(x) for x in xs]
-    ws = torch.zeros(max(et.softmax_workspace_bytes(rows, n), 16), dtype=torch.uint8, device="cuda")
-    fn = lambda i: et.softmax(xs[i % sets], 0.7, out=ys[i % sets], workspace=ws)
+def _time_launches(stream, fn, sets, launches):
+    """Per-launch HIP-event times (ms) of fn(i), i over rotating buffer sets."""
+    import torch
     for i in range(sets * 2):
         fn(i)
     torch.cuda.synchronize()
-    ms = []
+    evs = []
     for i in range(launches):
         ev = TimingEvents(stream)
         ev.start()
         fn(i)
         ev.stop()
-        ms.append(ev)
+        evs.append(ev)
     torch.cuda.synchronize()
-    t = [ev.elapsed_ms() for ev in ms]
-    for ev in ms:
+    t = [ev.elapsed_ms() for ev in evs]
+    for ev in evs:
         ev.close()
-    nbytes = 2 * rows * n * 4
-    avg = float(np.mean(t))
-    gbps = nbytes / (avg * 1e-3) / 1e9
-    return {"softmax": {"workload": "decode logits [256,128256] f32, temperature 0.7",
-                        "bytes": nbytes, "avg_us": round(avg * 1e3, 2),
-                        "median_us": round(float(np.median(t)) * 1e3, 2), "samples": len(t),
-                        "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_GBPS, 4),
-                        "kernels": "softmax_chunks (one launch)"}}
+    return t
+
+
+def time_next_ops(et, torch, wl, stream, sets=3, launches=60):
+    """Per-launch HIP-event times of the ops beyond the step, each on the
+    inputs its workload names:
+      softmax   temperature 0.7 over the decode logits [256, 128256] f32
+      layernorm [4096, 4096] bf16 with gain and bias (the prefill hidden size)
+      geglu     [4096, 14336] bf16, erf and tanh forms (the prefill FFN size)
+    Algorithmic bytes: each input read once, each output written once."""
+    out = {}
+
+    def record(name, workload, nbytes, t, kernels):
+        avg = float(np.mean(t))
+        gbps = nbytes / (avg * 1e-3) / 1e9
+        out[name] = {"workload": workload, "bytes": nbytes, "avg_us": round(avg * 1e3, 2),
+                     "median_us": round(float(np.median(t)) * 1e3, 2), "samples": len(t),
+                     "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_GBPS, 4),
+                     "kernels": kernels}
+
+    lg, _ = wl.gen_argmax(wl.WORKLOADS[3])
+    rows, n = lg.shape
+    xs = [torch.from_numpy(lg).cuda() for _ in range(sets)]
+    ys = [torch.empty_like(x) for x in xs]
+    ws = torch.zeros(max(et.softmax_workspace_bytes(rows, n), 16), dtype=torch.uint8, device="cuda")
+    t = _time_launches(stream, lambda i: et.softmax(xs[i % sets], 0.7, out=ys[i % sets], workspace=ws),
+                       sets, launches)
+    record("softmax", "decode logits [256,128256] f32, temperature 0.7", 2 * rows * n * 4, t,
+           "softmax_chunks (one launch)")
+    del xs, ys, ws
+
+    g = np.random.default_rng([1002, 40])
+    d = 4096
+    xs = [torch.from_numpy(g.standard_normal((4096, d)).astype(np.float32)).to("cuda", torch.bfloat16)
+          for _ in range(sets)]
+    ys = [torch.empty_like(x) for x in xs]
+    gam = torch.from_numpy(g.uniform(0.5, 1.5, d).astype(np.float32)).to("cuda", torch.bfloat16)
+    bet = torch.from_numpy(g.standard_normal(d).astype(np.float32)).to("cuda", torch.bfloat16)
+    t = _time_launches(stream, lambda i: et.layernorm(xs[i % sets], gam, bet, 1e-5, out=ys[i % sets]),
+                       sets, launches)
+    record("layernorm", "[4096,4096] bf16 with gain and bias, eps 1e-5", 2 * 4096 * d * 2 + 2 * d * 2, t,
+           "layernorm_rows")
+    del xs, ys
+
+    g = np.random.default_rng([1002, 41])
+    shape = (4096, 14336)
+    gs = [torch.from_numpy(g.standard_normal(shape).astype(np.float32)).to("cuda", torch.bfloat16)
+          for _ in range(sets)]
+    us = [torch.from_numpy(g.standard_normal(shape).astype(np.float32)).to("cuda", torch.bfloat16)
+          for _ in range(sets)]
+    ys = [torch.empty_like(x) for x in gs]
+    for form, name in ((et.GELU_ERF, "geglu_erf"), (et.GELU_TANH, "geglu_tanh")):
+        t = _time_launches(stream, lambda i: et.geglu(gs[i % sets], us[i % sets], form, out=ys[i % sets]),
+                           sets, launches)
+        record(name, f"[4096,14336] bf16, {'erf' if form == 0 else 'tanh'} form", 3 * 4096 * 14336 * 2, t,
+               "eltwise_vec")
+    return out
 
 
 def cpu_baseline(w, min_seconds):

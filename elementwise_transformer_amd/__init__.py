@@ -58,6 +58,8 @@ _SIGS = {
     "embedding": [_vp, _i64, _vp, _vp, _i64, _i64, _vp],
     "argmax": [_vp, _i64, _i64, _vp, _vp, _sz, _vp],
     "softmax": [_vp, _vp, _i64, _i64, _f32, _vp, _sz, _vp],
+    "layernorm": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp],
+    "geglu": [_vp, _vp, _vp, _i64, _int, _vp],
 }
 for _op, _args in _SIGS.items():
     for _sfx in ("f32", "bf16"):
@@ -132,6 +134,20 @@ def rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float,
     _same(x, w, out)
     rows = math.prod(x.shape[:-1])
     _call(f"et_rmsnorm_{_sfx(x)}", _ptr(x), _ptr(w), _ptr(out), rows, d, float(eps), _stream(x))
+    return out
+
+
+def layernorm(x: torch.Tensor, gamma: torch.Tensor, beta: Optional[torch.Tensor], eps: float,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = (x - mean) / sqrt(var + eps) * gamma + beta over the last axis
+    (et_layernorm_*); beta may be None.  ``out`` may be ``x`` (in place)."""
+    d = x.shape[-1]
+    out = torch.empty_like(x) if out is None else out
+    _dev(x, gamma, beta, out)
+    _same(x, gamma, beta, out)
+    rows = math.prod(x.shape[:-1])
+    _call(f"et_layernorm_{_sfx(x)}", _ptr(x), _ptr(gamma), _ptr(beta), _ptr(out), rows, d, float(eps),
+          _stream(x))
     return out
 
 
@@ -214,6 +230,22 @@ def rmsnorm_rope_qk(q: torch.Tensor, gq: torch.Tensor, k: Optional[torch.Tensor]
 
 
 # ------------------------------------------------------- flat ops, gather
+
+GELU_ERF = 0
+GELU_TANH = 1
+
+
+def geglu(gate: torch.Tensor, up: torch.Tensor, approximate: int = GELU_ERF,
+          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = gelu(gate) * up elementwise (et_geglu_*); approximate GELU_ERF
+    (exact) or GELU_TANH.  ``out`` may be gate or up."""
+    out = torch.empty_like(gate) if out is None else out
+    _dev(gate, up, out)
+    _same(gate, up, out)
+    _call(f"et_geglu_{_sfx(gate)}", _ptr(gate), _ptr(up), _ptr(out), gate.numel(), int(approximate),
+          _stream(gate))
+    return out
+
 
 def silu_mul(gate: torch.Tensor, up: torch.Tensor,
              out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -22,6 +22,7 @@
 //   * Unaligned buffers or d not a multiple of the vector width take the same
 //     kernels with scalar loads (same ownership, same sums).
 #include "et_common.hpp"
+#include "norm_common.hpp"
 
 namespace et {
 namespace {
@@ -29,65 +30,6 @@ namespace {
 #ifndef ET_POL_NORM
 #define ET_POL_NORM 1  // 0: by size, 1: non-temporal, 2: device scope
 #endif
-
-// 16-byte vectors per thread in the register path: 4 for rows of 1024..4096
-// vectors (256..1024 threads per row), 8 otherwise.
-constexpr int kVPTMax = 8;
-constexpr int kLargeTPR = 1024;  // threads per row in the two-pass path
-// Issue the gain loads right after the row loads when a row spans several
-// waves (its cross-wave reduction is long enough to hide them); for one-wave
-// rows the extra registers cost more occupancy than they save.
-#ifndef ET_NORM_W_EARLY_MIN_TPR
-#define ET_NORM_W_EARLY_MIN_TPR 128
-#endif
-
-#ifndef ET_NORM_VPT4_MIN
-#define ET_NORM_VPT4_MIN 1024
-#endif
-
-#ifndef ET_NORM_BLOCK
-#define ET_NORM_BLOCK 128
-#endif
-
-template <int TPR>
-struct NormShape {
-  static constexpr int kBlock = TPR < ET_NORM_BLOCK ? ET_NORM_BLOCK : TPR;
-  static constexpr int kRowsPerBlock = kBlock / TPR;
-  static constexpr int kGroup = TPR < 64 ? TPR : 64;  // lanes of one row inside a wave
-  static constexpr int kWavesPerRow = TPR > 64 ? TPR / 64 : 1;
-};
-
-// Reduce a per-thread partial over the TPR threads that own one row.
-template <int TPR>
-__device__ inline float row_sum(float part, float* lds, int row_in_block, int lane_in_row) {
-  using Sh = NormShape<TPR>;
-  float s = group_sum<Sh::kGroup>(part);
-  if constexpr (Sh::kWavesPerRow > 1) {
-    const int wave_in_row = lane_in_row / 64;
-    if ((lane_in_row & 63) == 0) lds[row_in_block * Sh::kWavesPerRow + wave_in_row] = s;
-    __syncthreads();
-    s = 0.0f;
-#pragma unroll
-    for (int w = 0; w < Sh::kWavesPerRow; ++w) s += lds[row_in_block * Sh::kWavesPerRow + w];
-  }
-  return s;
-}
-
-#ifndef ET_NORM_WAVE
-#define ET_NORM_WAVE 1
-#endif
-
-// Vector slot k of thread t in its row.  Rows of one wave or less: slot k is
-// the k-th TPR-vector stripe.  Longer rows: each wave owns a contiguous run of
-// 64 * VPT vectors, slot k of lane l at k * 64 + l inside it.
-template <int TPR, int VPT>
-__device__ inline int own(int k, int t) {
-  if constexpr (TPR > 64 && ET_NORM_WAVE) {
-    return (t / 64) * (64 * VPT) + k * 64 + (t % 64);
-  } else {
-    return k * TPR + t;
-  }
-}
 
 __device__ inline float inv_rms(float ss, int d, float eps) {
   return 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
@@ -294,23 +236,6 @@ __global__ __launch_bounds__(kLargeTPR) void rmsnorm_rows_large(
       }
     }
   }
-}
-
-// Launch shape from the row length alone: vectors per thread (4 for rows of
-// 1024..4096 vectors, else 8) and threads per row (the smallest power of two
-// with TPR * VPT >= number of vectors); TPR 0 selects the two-pass path.
-inline void pick_shape(int64_t nvec, int* tpr_out, int* vpt_out) {
-  const int vpt = (nvec >= ET_NORM_VPT4_MIN && nvec <= 4096) ? 4 : kVPTMax;
-  int tpr = 1;
-  while (static_cast<int64_t>(tpr) * vpt < nvec) {
-    tpr <<= 1;
-    if (tpr > 1024) {
-      tpr = 0;
-      break;
-    }
-  }
-  *tpr_out = tpr;
-  *vpt_out = vpt;
 }
 
 template <typename S, int TPR, int VPT, bool FUSED, bool VEC>

@@ -4,7 +4,8 @@
  *
  * Ops and the passages that define them (web pages, by section):
  *   [OPS] "Operations" (op spec of the glia runtime): 2 Normalization /
- *         RmsNorm; 3 Position encoding / Rope; 4 Activation / Silu, SwiGlu;
+ *         RmsNorm, LayerNorm; 3 Position encoding / Rope; 4 Activation /
+ *         Silu, SwiGlu, Gelu, GeGlu, Softmax;
  *         5 Attention / QK-norm; 8 Sampling / Greedy; 10 Fused ops
  *         (FusedSkipNorm, and fused = unfused within tolerance).
  *   [ELT] "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding,
@@ -200,6 +201,34 @@ et_status et_argmax_f32(const float* x, int64_t rows, int64_t n, int32_t* out,
 et_status et_argmax_bf16(const et_bf16* x, int64_t rows, int64_t n,
                          int32_t* out, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* ------------------------------------------------------------------------
+ * LayerNorm  ([OPS] 2 Normalization / LayerNorm; [DNN] 7)
+ *   per row of d: mu = mean(x), var = mean((x - mu)^2) (the two-pass
+ *   variance), y = (x - mu) / sqrt(var + eps) * gamma + beta.
+ *   x, y: [rows, d]; gamma, beta: [d] in the storage type; beta may be NULL
+ *   (no bias).  y may be x (in place).  eps finite and >= 0 (else
+ *   ET_ERR_BAD_ARG); d == 0 with rows > 0 is ET_ERR_BAD_SIZE.
+ */
+et_status et_layernorm_f32(const float* x, const float* gamma, const float* beta,
+                           float* y, int64_t rows, int64_t d, float eps,
+                           void* stream);
+et_status et_layernorm_bf16(const et_bf16* x, const et_bf16* gamma,
+                            const et_bf16* beta, et_bf16* y, int64_t rows,
+                            int64_t d, float eps, void* stream);
+
+/* ------------------------------------------------------------------------
+ * GELU-gated multiply, GeGLU  ([OPS] 4 Activation / Gelu, GeGlu)
+ *   y = Gelu(gate) * up elementwise, with approximate = ET_GELU_ERF:
+ *   Gelu(x) = x/2 (1 + erf(x/sqrt 2)), or ET_GELU_TANH:
+ *   Gelu(x) = x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))); any other value
+ *   is ET_ERR_BAD_ARG.  gate, up, y: [n]; y may be gate or up.
+ */
+enum { ET_GELU_ERF = 0, ET_GELU_TANH = 1 };
+et_status et_geglu_f32(const float* gate, const float* up, float* y, int64_t n,
+                       int approximate, void* stream);
+et_status et_geglu_bf16(const et_bf16* gate, const et_bf16* up, et_bf16* y,
+                        int64_t n, int approximate, void* stream);
 
 /* ------------------------------------------------------------------------
  * Softmax over the last axis with a temperature  ([OPS] 4 Activation /

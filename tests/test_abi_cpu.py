@@ -27,7 +27,7 @@ def _declared():
 def test_header_declares_the_ops():
     names = _declared()
     for op in ("rmsnorm", "add_rmsnorm", "rope", "rope_qk", "rmsnorm_rope_qk", "silu_mul", "add",
-               "embedding", "argmax", "softmax"):
+               "embedding", "argmax", "softmax", "layernorm", "geglu"):
         for sfx in ("f32", "bf16"):
             assert f"et_{op}_{sfx}" in names
     assert "et_argmax_workspace_bytes" in names and "et_status_string" in names
@@ -190,6 +190,30 @@ def test_softmax_validation(sfx):
     assert f(A, B, 256, 128256, 1.0, P(G + 64), need, S) == 4   # workspace inside x
     assert f(NULL, NULL, 0, 8, 1.0, NULL, 0, S) == 0
     assert f(A, B, 4, 0, 1.0, NULL, 0, S) == 0
+
+
+@gpu_visible
+@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+def test_layernorm_and_geglu_validation(sfx):
+    import elementwise_transformer_amd as et
+    f = getattr(et.lib, f"et_layernorm_{sfx}")
+    assert f(A, B, C, D, -1, 8, 1e-5, S) == 2
+    assert f(A, B, C, D, 4, 0, 1e-5, S) == 2                    # nonempty final axis
+    assert f(A, B, C, D, 4, 8, -1.0, S) == 3                    # eps >= 0
+    assert f(A, B, C, D, 4, 8, float("nan"), S) == 3
+    assert f(NULL, B, C, D, 4, 8, 1e-5, S) == 1
+    assert f(A, NULL, C, D, 4, 8, 1e-5, S) == 1
+    assert f(A, B, C, P(G + 4), 4, 8, 1e-5, S) == 4             # y overlaps x partially
+    assert f(A, B, C, B, 4, 8, 1e-5, S) == 4                    # y over the gain
+    assert f(A, B, C, C, 4, 8, 1e-5, S) == 4                    # y over the bias
+    assert f(NULL, NULL, NULL, NULL, 0, 8, 1e-5, S) == 0
+    g = getattr(et.lib, f"et_geglu_{sfx}")
+    assert g(A, B, C, -1, 0, S) == 2
+    assert g(A, B, C, 8, 2, S) == 3                             # approximate must be 0 or 1
+    assert g(A, B, C, 8, -1, S) == 3
+    assert g(NULL, B, C, 8, 1, S) == 1
+    assert g(A, B, P(G + 4), 64, 0, S) == 4
+    assert g(NULL, NULL, NULL, 0, 1, S) == 0
 
 
 def test_softmax_workspace_sizes():
