@@ -70,6 +70,9 @@ class Oracle:
         lib.orc_softmax.argtypes = [_int, _vp, _i64, _i64, _f32, _vp, _vp]
         lib.orc_layernorm.argtypes = [_int, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp]
         lib.orc_geglu.argtypes = [_int, _vp, _vp, _i64, _int, _vp, _vp]
+        lib.orc_rope_cache.argtypes = [_vp, _i64, _i64, _vp, _vp]
+        lib.orc_rope_cached.argtypes = [_int, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _f32,
+                                        _int, _vp]
         lib.orc_add_rmsnorm.argtypes = [_int, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp, _vp]
         lib.orc_rope.argtypes = [_int, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _f32, _int, _vp]
         lib.orc_rmsnorm_rope.argtypes = [_int, _vp, _vp, _f32, _vp, _i64, _i64, _i64, _i64,
@@ -221,6 +224,27 @@ class Oracle:
         y64 = np.empty(gate.shape, np.float64)
         self.lib.orc_geglu(dt, _p(gate), _p(up), gate.size, form, _p(y64), _p(y))
         return y, y64
+
+    def rope_cache(self, inv_freq: np.ndarray, max_pos: int, r: int):
+        """(cos, sin) f32 [max_pos, r/2] of the RoPE angles."""
+        inv = np.ascontiguousarray(inv_freq, dtype=np.float32)
+        c = np.empty((max_pos, r // 2), np.float32)
+        s = np.empty((max_pos, r // 2), np.float32)
+        self.lib.orc_rope_cache(_p(inv), max_pos, r, _p(c), _p(s))
+        return c, s
+
+    def rope_cached(self, x: np.ndarray, pos: np.ndarray, r: int, cos_c: np.ndarray, sin_c: np.ndarray,
+                    mu: float, layout: int):
+        """x [T, H, D] (not modified) -> (rotated copy, y64), rotation from the cache."""
+        out = np.array(x, copy=True, order="C")
+        T, H, D = out.shape
+        y64 = np.empty(out.shape, np.float64)
+        pos = np.ascontiguousarray(pos, dtype=np.int32)
+        cos_c = np.ascontiguousarray(cos_c, dtype=np.float32)
+        sin_c = np.ascontiguousarray(sin_c, dtype=np.float32)
+        self.lib.orc_rope_cached(_dt(out), _p(out), _p(pos), T, H, D, r, _p(cos_c), _p(sin_c),
+                                 cos_c.shape[0], mu, layout, _p(y64))
+        return out, y64
 
 
 _default: Optional[Oracle] = None

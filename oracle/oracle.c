@@ -8,7 +8,8 @@
  * leg do.  It shares no source with the HIP kernels.
  *
  * Also the next rows built after those: softmax over the last axis with a
- * temperature; LayerNorm; GELU-gated multiply (GeGLU, erf and tanh forms).
+ * temperature; LayerNorm; GELU-gated multiply (GeGLU, erf and tanh forms);
+ * RoPE from a precomputed cos/sin cache.
  *
  * Sources (web pages; sections named, never line numbers):
  *   [OPS]  "Operations" (glia runtime op spec): 2 Normalization / RmsNorm,
@@ -423,5 +424,63 @@ void orc_geglu(int dt, const void* gate, const void* up, int64_t n, int form,
         const double v = gl * ld(dt, up, i);
         if (y64) y64[i] = v;
         if (y) st(dt, y, i, v);
+    }
+}
+
+/* ------------------------------------------------------------ RoPE cache */
+
+/* [OPS] 3 Rope, "Cos/sin cache": cos[p, i] and sin[p, i] for every position
+ * p < max_pos and pair i < r/2, of the angle [ELT] 2.2 defines (the f32
+ * product, R1), in f64 and rounded once to f32.  Layout [max_pos, r/2]. */
+void orc_rope_cache(const float* inv_freq, int64_t max_pos, int64_t r,
+                    float* cos_c, float* sin_c) {
+    const int64_t half = r / 2;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < max_pos; ++p)
+        for (int64_t i = 0; i < half; ++i) {
+            const double ang = (double)orc_rope_angle((int32_t)p, inv_freq[i]);
+            cos_c[p * half + i] = (float)cos(ang);
+            sin_c[p * half + i] = (float)sin(ang);
+        }
+}
+
+/* RoPE with the rotation read from a cache instead of computed: for pair i
+ * of token t, c = cos[pos[t], i] and s = sin[pos[t], i] as given (f32,
+ * widened), then a' = mu (a c - b s), b' = mu (a s + b c) in f64.  A
+ * position outside [0, max_pos) (the pages make it an error: no angle is
+ * defined for it) is never looked up; that token's rotated entries become
+ * quiet NaN, its other entries stay as given. */
+void orc_rope_cached(int dt, void* x, const int32_t* pos, int64_t T,
+                     int64_t H, int64_t D, int64_t r, const float* cos_c,
+                     const float* sin_c, int64_t max_pos, float mu_f,
+                     int layout, double* y64) {
+    const int64_t half = r / 2;
+    const double mu = (double)mu_f;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t base = t * H * D;
+        const int32_t p = pos[t];
+        const int ok = p >= 0 && (int64_t)p < max_pos;
+        double* v = row_buffer(H * D);
+        for (int64_t j = 0; j < H * D; ++j) v[j] = ld(dt, x, base + j);
+        for (int64_t i = 0; i < half; ++i) {
+            const double c = ok ? (double)cos_c[(int64_t)p * half + i] : NAN;
+            const double sn = ok ? (double)sin_c[(int64_t)p * half + i] : NAN;
+            int64_t ia, ib;
+            rope_pair(layout, r, i, &ia, &ib);
+            for (int64_t h = 0; h < H; ++h) {
+                double* w = v + h * D;
+                const double a = w[ia];
+                const double b = w[ib];
+                w[ia] = mu * (a * c - b * sn);
+                w[ib] = mu * (a * sn + b * c);
+            }
+        }
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t j = 0; j < D; ++j) {
+                if (j < r) st(dt, x, base + h * D + j, v[h * D + j]);
+                if (y64) y64[base + h * D + j] = v[h * D + j];
+            }
+        free(v);
     }
 }

@@ -57,6 +57,12 @@ void orc_layernorm(int dt, const void* x, const void* g, const void* b,
                    int64_t rows, int64_t d, float eps, double* y64, void* y);
 void orc_geglu(int dt, const void* gate, const void* up, int64_t n, int form,
                double* y64, void* y);
+void orc_rope_cache(const float* inv_freq, int64_t max_pos, int64_t r,
+                    float* cos_c, float* sin_c);
+void orc_rope_cached(int dt, void* x, const int32_t* pos, int64_t T,
+                     int64_t H, int64_t D, int64_t r, const float* cos_c,
+                     const float* sin_c, int64_t max_pos, float mu_f,
+                     int layout, double* y64);
 
 #ifdef __cplusplus
 }

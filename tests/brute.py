@@ -195,3 +195,29 @@ def layernorm_row_exact(x: Sequence[float], g: Sequence[float], b, eps: float) -
                 val += Decimal(b[i])
             out.append(float(val))
         return out
+
+
+def sincos_decimal(x: float, digits: int = 50):
+    """(sin x, cos x) of a double x: reduction by pi/2 with pi from Machin's
+    formula and the Taylor series, all in decimal."""
+    from decimal import Decimal, localcontext
+    with localcontext() as ctx:
+        ctx.prec = digits + 20
+        pi = _dec_pi(digits + 20)
+        xx = Decimal(x)
+        k = (xx / (pi / 2)).to_integral_value()
+        r = xx - k * (pi / 2)
+        s, c = Decimal(0), Decimal(0)
+        term, n = r, 1
+        while abs(term) > Decimal(10) ** (-(digits + 5)):
+            s += term
+            term = -term * r * r / ((n + 1) * (n + 2))
+            n += 2
+        term, n = Decimal(1), 0
+        while abs(term) > Decimal(10) ** (-(digits + 5)):
+            c += term
+            term = -term * r * r / ((n + 1) * (n + 2))
+            n += 2
+        q = int(k) % 4
+        sv, cv = [(s, c), (c, -s), (-s, -c), (-c, s)][q]
+        return float(sv), float(cv)

@@ -589,6 +589,64 @@ def pin_softmax_matches_library(orc):
                 np.max(np.abs(y.astype(np.int32) - _bf16(ref.astype(np.float32)).astype(np.int32))) <= 1
 
 
+# ------------------------------------------------------------ RoPE cache
+
+def pin_rope_cache_values(orc):
+    """[OPS] Rope, cos/sin cache: entry (p, i) is cos and sin of the f32 angle
+    of [ELT] 2.2 rounded to f32 -- position 0 gives exactly (1, 0); against a
+    decimal evaluation (pi by Machin's formula, Taylor series) for positions
+    up to 2^20."""
+    r = 64
+    inv = np.power(np.float64(1e4), -2.0 * np.arange(r // 2) / r).astype(np.float32)
+    c, s_ = orc.rope_cache(inv, 2000, r)
+    assert np.all(c[0] == 1.0) and np.all(s_[0] == 0.0)
+    assert np.all(np.abs(c.astype(np.float64) ** 2 + s_.astype(np.float64) ** 2 - 1.0) <= 2.0 ** -22)
+    for p in (1, 7, 1999):
+        for i in (0, 5, 31):
+            ang = float(np.float32(np.float64(p) * np.float64(inv[i])))
+            sd, cd = brute.sincos_decimal(ang)
+            assert c[p, i] == np.float32(cd) and s_[p, i] == np.float32(sd), (p, i)
+    big = np.array([1.0], np.float32)
+    cb, sb = orc.rope_cache(big, 3, 2)
+    for p in range(3):
+        sd, cd = brute.sincos_decimal(float(p))
+        assert cb[p, 0] == np.float32(cd) and sb[p, 0] == np.float32(sd)
+
+
+def pin_rope_cached_rotation(orc):
+    """The cached rotation is RoPE with (cos, sin) read instead of computed:
+    with the cache built from the same angles it matches the computed oracle
+    to the f32 rounding of cos and sin; a cache of quarter turns maps each
+    pair (a, b) to mu (-b, a) in both layouts; a position outside the cache
+    gives NaN in that token's rotated entries and leaves the rest."""
+    g = np.random.default_rng(101)
+    T, H, D, r = 6, 3, 16, 12
+    x = g.standard_normal((T, H, D)).astype(np.float32)
+    pos = np.array([0, 3, 9, 1, 9, 4], np.int32)
+    inv = np.power(np.float64(500.0), -2.0 * np.arange(r // 2) / r).astype(np.float32)
+    c, s_ = orc.rope_cache(inv, 10, r)
+    for layout in (0, 1):
+        _, y64 = orc.rope_cached(x, pos, r, c, s_, 1.3, layout)
+        _, ref64 = orc.rope(x, pos, r, inv, 1.3, layout)
+        pair = np.abs(x.astype(np.float64)).max()
+        assert np.max(np.abs(y64 - ref64)) <= 1.3 * 2 * pair * 2.0 ** -24, layout
+        q = np.zeros((10, r // 2), np.float32)
+        one = np.ones((10, r // 2), np.float32)
+        _, y64 = orc.rope_cached(x, pos, r, q, one, 1.25, layout)
+        for i in range(r // 2):
+            ia, ib = _pair_index(layout, r, i)
+            assert np.array_equal(y64[..., ia], -1.25 * x[..., ib].astype(np.float64))
+            assert np.array_equal(y64[..., ib], 1.25 * x[..., ia].astype(np.float64))
+        bad = pos.copy()
+        bad[2], bad[4] = 10, -1
+        out, y64 = orc.rope_cached(x, bad, r, c, s_, 1.0, layout)
+        for t in (2, 4):
+            assert np.all(np.isnan(y64[t, :, :r])) and np.array_equal(y64[t, :, r:], x[t, :, r:])
+        ok = [0, 1, 3, 5]
+        _, good64 = orc.rope_cached(x, pos, r, c, s_, 1.0, layout)
+        assert np.array_equal(y64[ok], good64[ok])
+
+
 # -------------------------------------------------------------- LayerNorm
 
 def pin_layernorm_closed_forms(orc):

@@ -4,9 +4,9 @@ Each mutant is a copy of ``oracle/oracle.c`` with one plausible mistake
 planted by text substitution, built into a temporary library.  The pins must
 fail on every mutant.  s01-s15 are the mistakes listed in the Pitfalls table
 (section 5) of "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding,
-add, argmax", each with the test the page says catches it; x01-x25 are further
+add, argmax", each with the test the page says catches it; x01-x29 are further
 slips (a wrong sign, index, dropped term or rounding) in the same code, x11-x16
-in the softmax, x17-x20 in LayerNorm, x21-x25 in the GELU-gated multiply.
+in the softmax, x17-x20 in LayerNorm, x21-x25 in the GELU-gated multiply, x26-x29 in the RoPE cache.
 """
 import os
 import tempfile
@@ -38,7 +38,8 @@ MUTANTS = {
     "s07_rotate_all_D": ("rope_partial_rotary_and_scaling",
                          [("const int64_t rr = r;", "const int64_t rr = D;")]),
     "s08_ignore_mu": ("rope_partial_rotary_and_scaling",
-                      [("const double mu = (double)mu_f;", "const double mu = 1.0;")]),
+                      [("const int64_t rr = r;\n    const double mu = (double)mu_f;",
+                        "const int64_t rr = r;\n    const double mu = 1.0;")]),
     "s09_silu_as_sigmoid": ("silu_mul_saturates_without_nan",
                             [("const double s = gv / (1.0 + e);", "const double s = 1.0 / (1.0 + e);")]),
     "s10_exp_plus_g": ("silu_mul_saturates_without_nan",
@@ -92,6 +93,17 @@ MUTANTS = {
     "x23_geglu_up_ignored": ("gelu_symmetry_and_limits",
                              [("const double v = gl * ld(dt, up, i);", "const double v = gl;")]),
     "x24_gelu_forms_swapped": ("gelu_brute", [("if (form == 0) {", "if (form == 1) {")]),
+    "x26_cache_transposed": ("rope_cached_rotation",
+                             [("? (double)cos_c[(int64_t)p * half + i] : NAN;", "? (double)cos_c[i * max_pos + p] : NAN;")]),
+    "x27_cached_rotation_sign": ("rope_cached_rotation",
+                                 [("w[ia] = mu * (a * c - b * sn);", "w[ia] = mu * (a * c + b * sn);")]),
+    "x28_cache_bad_position_zero": ("rope_cached_rotation",
+                                    [("? (double)sin_c[(int64_t)p * half + i] : NAN;",
+                                      "? (double)sin_c[(int64_t)p * half + i] : 0.0;"),
+                                     ("? (double)cos_c[(int64_t)p * half + i] : NAN;",
+                                      "? (double)cos_c[(int64_t)p * half + i] : 1.0;")]),
+    "x29_cache_uses_cos_for_sin": ("rope_cache_values",
+                                   [("sin_c[p * half + i] = (float)sin(ang);", "sin_c[p * half + i] = (float)cos(ang);")]),
     "x25_gelu_tanh_no_f32_limit": ("gelu_symmetry_and_limits",
                                    [("if (e > FLT_MAX) e = INFINITY;  /* the f32", "/* the f32")]),
 }
