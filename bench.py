@@ -238,6 +238,9 @@ def time_next_ops(et, torch, wl, stream, sets=3, launches=60):
       softmax   temperature 0.7 over the decode logits [256, 128256] f32
       layernorm [4096, 4096] bf16 with gain and bias (the prefill hidden size)
       geglu     [4096, 14336] bf16, erf and tanh forms (the prefill FFN size)
+      rope_cached  the prefill RoPE (q [4096,32,128], k [4096,8,128] bf16,
+                positions 0..4095) with the rotation read from a cos/sin
+                cache [4096, 64] f32 built by the library
     Algorithmic bytes: each input read once, each output written once."""
     out = {}
 
@@ -285,6 +288,21 @@ def time_next_ops(et, torch, wl, stream, sets=3, launches=60):
                            sets, launches)
         record(name, f"[4096,14336] bf16, {'erf' if form == 0 else 'tanh'} form", 3 * 4096 * 14336 * 2, t,
                "eltwise_vec")
+    del gs, us, ys
+
+    w = wl.WORKLOADS[2]
+    s = w.rope
+    q, k, pos, inv = wl.gen_rope(w)
+    qs = [torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda() for _ in range(sets)]
+    ks = [torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).cuda() for _ in range(sets)]
+    pt = torch.from_numpy(pos).cuda()
+    cc, sc = et.rope_cache(torch.from_numpy(inv).cuda(), s.T, s.r)
+    t = _time_launches(stream, lambda i: et.rope_qk_cached(qs[i % sets], ks[i % sets], pt, cc, sc,
+                                                           d_rot=s.r, attn_scaling=s.mu,
+                                                           layout=s.layout), sets, launches)
+    heads = s.Hq + s.Hk
+    record("rope_cached", "prefill RoPE q [4096,32,128] k [4096,8,128] bf16, cache [4096,64] f32",
+           2 * s.T * heads * s.r * 2 + 4 * s.T + 2 * s.T * (s.r // 2) * 4, t, "rope_qk_kernel (cached)")
     return out
 
 

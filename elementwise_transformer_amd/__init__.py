@@ -19,7 +19,7 @@ from typing import Optional, Tuple
 import torch  # loaded first so libet.so binds to the HIP runtime torch uses
 
 __all__ = ["rmsnorm", "add_rmsnorm", "rope", "rope_qk", "rmsnorm_rope_qk", "silu_mul", "add",
-           "embedding", "argmax", "argmax_workspace_bytes", "ETError", "lib", "LIB_PATH",
+           "rope_cache", "rope_qk_cached", "embedding", "argmax", "argmax_workspace_bytes", "ETError", "lib", "LIB_PATH",
            "ROPE_HALF", "ROPE_INTERLEAVED", "abi_version"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libet.so")
@@ -60,6 +60,8 @@ _SIGS = {
     "softmax": [_vp, _vp, _i64, _i64, _f32, _vp, _sz, _vp],
     "layernorm": [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _vp],
     "geglu": [_vp, _vp, _vp, _i64, _int, _vp],
+    "rope_qk_cached": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _f32, _int,
+                       _vp],
 }
 for _op, _args in _SIGS.items():
     for _sfx in ("f32", "bf16"):
@@ -70,6 +72,8 @@ lib.et_argmax_workspace_bytes.argtypes = [_i64, _i64]
 lib.et_argmax_workspace_bytes.restype = _sz
 lib.et_softmax_workspace_bytes.argtypes = [_i64, _i64]
 lib.et_softmax_workspace_bytes.restype = _sz
+lib.et_rope_cache_f32.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
+lib.et_rope_cache_f32.restype = ctypes.c_int
 lib.et_status_string.argtypes = [ctypes.c_int]
 lib.et_status_string.restype = ctypes.c_char_p
 lib.et_abi_version.argtypes = []
@@ -206,6 +210,56 @@ def rope_qk(q: torch.Tensor, k: Optional[torch.Tensor], pos: torch.Tensor, inv_f
     _rope_common(pos, inv_freq)
     _call(f"et_rope_qk_{_sfx(q)}", _ptr(q), Hq, _ptr(k), Hk, _ptr(pos), T, D, d_rot, _ptr(inv_freq),
           float(attn_scaling), int(layout), _stream(q))
+    return q, k
+
+
+def rope_cache(inv_freq: torch.Tensor, max_pos: int, d_rot: Optional[int] = None,
+               out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
+               ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(cos, sin) f32 [max_pos, d_rot/2] of the angles et_rope_* uses
+    (et_rope_cache_f32); d_rot defaults to 2 * len(inv_freq)."""
+    _dev(inv_freq)
+    if inv_freq.dtype != torch.float32:
+        raise TypeError("inv_freq must be float32")
+    d_rot = 2 * inv_freq.numel() if d_rot is None else int(d_rot)
+    if inv_freq.numel() < d_rot // 2:
+        raise ValueError("inv_freq needs d_rot/2 entries")
+    shape = (int(max_pos), d_rot // 2)
+    if out is None:
+        out = (torch.empty(shape, dtype=torch.float32, device=inv_freq.device),
+               torch.empty(shape, dtype=torch.float32, device=inv_freq.device))
+    cos_c, sin_c = out
+    _dev(cos_c, sin_c)
+    for c in (cos_c, sin_c):
+        if c.dtype != torch.float32 or tuple(c.shape) != shape:
+            raise ValueError(f"cache buffers must be float32 {shape}")
+    _call("et_rope_cache_f32", _ptr(inv_freq), shape[0], d_rot, _ptr(cos_c), _ptr(sin_c),
+          _stream(inv_freq))
+    return cos_c, sin_c
+
+
+def rope_qk_cached(q: torch.Tensor, k: Optional[torch.Tensor], pos: torch.Tensor,
+                   cos_cache: torch.Tensor, sin_cache: torch.Tensor, d_rot: Optional[int] = None,
+                   attn_scaling: float = 1.0,
+                   layout: int = ROPE_HALF) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """In-place rotary embedding of q [T, Hq, D] and k [T, Hk, D] with the
+    rotation read from cos_cache / sin_cache f32 [max_pos, d_rot/2]
+    (et_rope_qk_cached_*); returns (q, k)."""
+    T, Hq, D = q.shape
+    Hk = 0 if k is None else k.shape[1]
+    if k is not None and (k.shape[0] != T or k.shape[2] != D):
+        raise ValueError("k must be [T, Hk, D] with q's T and D")
+    d_rot = D if d_rot is None else int(d_rot)
+    _dev(q, k, cos_cache, sin_cache)
+    _same(q, k)
+    _rope_common(pos, cos_cache)
+    if sin_cache.dtype != torch.float32 or sin_cache.shape != cos_cache.shape:
+        raise ValueError("sin_cache must match cos_cache (float32)")
+    if cos_cache.dim() != 2 or cos_cache.shape[1] != d_rot // 2:
+        raise ValueError("caches must be [max_pos, d_rot/2]")
+    _call(f"et_rope_qk_cached_{_sfx(q)}", _ptr(q), Hq, _ptr(k), Hk, _ptr(pos), T, D, d_rot,
+          _ptr(cos_cache), _ptr(sin_cache), cos_cache.shape[0], float(attn_scaling), int(layout),
+          _stream(q))
     return q, k
 
 

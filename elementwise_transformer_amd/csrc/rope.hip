@@ -56,6 +56,13 @@ struct RopeArgs {
   FastDiv fd_sph;     // divide by slots per head row
   FastDiv fd_half;    // divide by r/2
   int ntok_max;       // tokens one workgroup can touch (table rows)
+  // Cos/sin cache ("Operations" 3 Rope): when cached is set, the table
+  // reads (cos, sin) of pair i at position p from cos_c / sin_c[p * half + i]
+  // instead of computing them; positions outside [0, max_pos) give NaN.
+  int cached;
+  int max_pos;
+  const float* cos_c;
+  const float* sin_c;
 };
 
 // Angle of pair i of position p: the f64 product rounded once to f32.
@@ -125,15 +132,41 @@ __device__ inline TabIn table_inputs(int64_t t0, int ntok, const RopeArgs& a,
     if (idx >= n) idx = n - 1;  // clamped, never guarded (see above)
     const uint32_t tl = fdiv(idx, a.fd_half);
     in.p[k] = pos[t0 + tl];
-    in.w[k] = inv_freq[idx - tl * a.half];
+    in.w[k] = a.cached ? 0.0f : inv_freq[idx - tl * a.half];  // (uniform branch)
   }
   return in;
+}
+
+// Cached (mu cos, mu sin) of pair i at position p; NaN outside the cache.
+__device__ inline float2 cached_cs(int32_t p, uint32_t i, const RopeArgs& a) {
+  // Out-of-range positions load nothing (the cache may even be empty).
+  float cn = __builtin_nanf(""), sn = cn;
+  if (p >= 0 && p < a.max_pos) {
+    const int64_t ci = static_cast<int64_t>(p) * a.half + i;
+    cn = a.cos_c[ci];
+    sn = a.sin_c[ci];
+  }
+  return make_float2(a.mu * cn, a.mu * sn);
 }
 
 __device__ inline void table_fill(float2* cs, const TabIn& in, int64_t t0, int ntok,
                                   const RopeArgs& a, const int32_t* __restrict__ pos,
                                   const float* __restrict__ inv_freq) {
   const uint32_t n = static_cast<uint32_t>(ntok) * a.half;
+  if (a.cached) {
+    // The cache loads depend on the positions, so they are issued here,
+    // after the row loads; the table is a copy, no trigonometry.
+#pragma unroll
+    for (int k = 0; k < kTabPre; ++k) {
+      const uint32_t idx = threadIdx.x + k * kBlock;
+      if (idx < n) cs[idx] = cached_cs(in.p[k], idx - fdiv(idx, a.fd_half) * a.half, a);
+    }
+    for (uint32_t idx = threadIdx.x + kTabPre * kBlock; idx < n; idx += kBlock) {
+      const uint32_t tl = fdiv(idx, a.fd_half);
+      cs[idx] = cached_cs(pos[t0 + tl], idx - tl * a.half, a);
+    }
+    return;
+  }
 #pragma unroll
   for (int k = 0; k < kTabPre; ++k) {
     const uint32_t idx = threadIdx.x + k * kBlock;
@@ -531,7 +564,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_wave_kernel(
 template <typename S>
 et_status check_rope(const S* q, int64_t hq, const S* k, int64_t hk, const int32_t* pos,
                      int64_t T, int64_t D, int64_t r, const float* inv_freq, float mu, int layout,
-                     int64_t* qbytes, int64_t* kbytes) {
+                     int64_t* qbytes, int64_t* kbytes, bool need_freq = true) {
   if (T < 0 || hq < 0 || hk < 0 || D < 0) return ET_ERR_BAD_SIZE;
   if (r < 0 || r > D || (r & 1)) return ET_ERR_BAD_ARG;
   if (layout != ET_ROPE_HALF && layout != ET_ROPE_INTERLEAVED) return ET_ERR_BAD_ARG;
@@ -542,7 +575,8 @@ et_status check_rope(const S* q, int64_t hq, const S* k, int64_t hk, const int32
     return ET_ERR_BAD_SIZE;
   if (D > INT32_MAX / 2 || hq + hk > INT32_MAX / 2) return ET_ERR_BAD_SIZE;
   if ((*qbytes > 0 && !q) || (*kbytes > 0 && !k)) return ET_ERR_NULL_POINTER;
-  if (T > 0 && (hq + hk) > 0 && r > 0 && (!pos || !inv_freq)) return ET_ERR_NULL_POINTER;
+  if (T > 0 && (hq + hk) > 0 && r > 0 && (!pos || (need_freq && !inv_freq)))
+    return ET_ERR_NULL_POINTER;
   if (!ranges_ok(q, *qbytes, k, *kbytes, false)) return ET_ERR_OVERLAP;
   const int64_t pbytes = T * int64_t(sizeof(int32_t)), fbytes = (r / 2) * int64_t(sizeof(float));
   if (!ranges_ok(q, *qbytes, pos, pbytes, false) || !ranges_ok(k, *kbytes, pos, pbytes, false) ||
@@ -597,12 +631,33 @@ inline int pick_u(int64_t spt, int64_t half, int64_t per_u, int umax) {
   return 0;
 }
 
+// A cos/sin cache of max_pos rows of r/2 f32 each, read instead of the
+// frequencies.
+struct RopeCache {
+  const float* cos_c;
+  const float* sin_c;
+  int64_t max_pos;
+};
+
 template <typename S>
 et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int64_t T, int64_t D,
-                     int64_t r, const float* inv_freq, float mu, int layout, void* stream) {
+                     int64_t r, const float* inv_freq, float mu, int layout, void* stream,
+                     const RopeCache* cache = nullptr) {
   int64_t qb = 0, kb = 0;
-  const et_status st = check_rope(q, hq, k, hk, pos, T, D, r, inv_freq, mu, layout, &qb, &kb);
+  // With a cache the frequencies are not read; the cache is checked below.
+  const et_status st = check_rope(q, hq, k, hk, pos, T, D, r, cache ? nullptr : inv_freq, mu,
+                                  layout, &qb, &kb, !cache);
   if (st != ET_OK) return st;
+  if (cache) {
+    if (cache->max_pos < 0 || cache->max_pos > INT32_MAX) return ET_ERR_BAD_SIZE;
+    int64_t cb = 0;
+    if (!mul_ok(cache->max_pos, (r / 2) * int64_t(sizeof(float)), &cb)) return ET_ERR_BAD_SIZE;
+    if (T > 0 && hq + hk > 0 && cb > 0 && (!cache->cos_c || !cache->sin_c))
+      return ET_ERR_NULL_POINTER;
+    if (!ranges_ok(q, qb, cache->cos_c, cb, false) || !ranges_ok(q, qb, cache->sin_c, cb, false) ||
+        !ranges_ok(k, kb, cache->cos_c, cb, false) || !ranges_ok(k, kb, cache->sin_c, cb, false))
+      return ET_ERR_OVERLAP;
+  }
   if (T == 0 || hq + hk == 0 || r == 0) return ET_OK;
   constexpr int V = Elem<S>::V;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -611,6 +666,14 @@ et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int
   if (a.spt > (1u << 30)) return ET_ERR_BAD_SIZE;
   int u = pick_u(a.spt, a.half, kBlock, ET_ROPE_UMAX);
   if (u == 0) return ET_ERR_BAD_SIZE;
+  auto set_cache = [&](RopeArgs& ra) {
+    if (!cache) return;
+    ra.cached = 1;
+    ra.cos_c = cache->cos_c;
+    ra.sin_c = cache->sin_c;
+    ra.max_pos = static_cast<int>(cache->max_pos);
+  };
+  set_cache(a);
   if (vec) {
     // The vector path stores at byte offsets below (head rows a workgroup
     // touches) * D * sizeof(S); past 2^31 take the scalar path.
@@ -618,6 +681,7 @@ et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int
     if (rows_blk * D * int64_t(sizeof(S)) >= (int64_t{1} << 31)) {
       vec = false;
       a = make_args(T, hq, hk, D, r, mu, layout, 1);
+      set_cache(a);
       if (a.spt > (1u << 30)) return ET_ERR_BAD_SIZE;
       u = pick_u(a.spt, a.half, kBlock, ET_ROPE_UMAX);
       if (u == 0) return ET_ERR_BAD_SIZE;
@@ -748,6 +812,45 @@ et_status qknorm_entry(S* q, const S* gq, int64_t hq, S* k, const S* gk, int64_t
   return launch_status();
 }
 
+// cos_c / sin_c[p * half + i] of the angle rope_angle(p, inv_freq[i]), with
+// the same sin/cos the computed tables use, so a cached rotation equals the
+// computed one bit for bit.
+__global__ __launch_bounds__(kBlock) void rope_cache_kernel(const float* __restrict__ inv_freq,
+                                                            int64_t total, FastDiv fd_half,
+                                                            int half, float* cos_c, float* sin_c) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (idx >= total) return;
+  const uint32_t p = fdiv(static_cast<uint32_t>(idx), fd_half);
+  const uint32_t i = static_cast<uint32_t>(idx) - p * static_cast<uint32_t>(half);
+  float sn, cn;
+  sincos_angle(rope_angle(static_cast<int32_t>(p), inv_freq[i]), &sn, &cn);
+  cos_c[idx] = cn;
+  sin_c[idx] = sn;
+}
+
+et_status rope_cache_entry(const float* inv_freq, int64_t max_pos, int64_t r, float* cos_c,
+                           float* sin_c, void* stream) {
+  if (max_pos < 0 || r < 0) return ET_ERR_BAD_SIZE;
+  if (r & 1) return ET_ERR_BAD_ARG;
+  const int64_t half = r / 2;
+  int64_t total = 0, bytes = 0;
+  if (!mul_ok(max_pos, half, &total) || !mul_ok(total, int64_t(sizeof(float)), &bytes))
+    return ET_ERR_BAD_SIZE;
+  if (total == 0) return ET_OK;
+  if (total > UINT32_MAX || max_pos > INT32_MAX) return ET_ERR_BAD_SIZE;
+  if (!inv_freq || !cos_c || !sin_c) return ET_ERR_NULL_POINTER;
+  const int64_t fb = half * int64_t(sizeof(float));
+  if (!ranges_ok(cos_c, bytes, sin_c, bytes, false) || !ranges_ok(cos_c, bytes, inv_freq, fb, false) ||
+      !ranges_ok(sin_c, bytes, inv_freq, fb, false))
+    return ET_ERR_OVERLAP;
+  (void)hipGetLastError();
+  const int64_t grid = (total + kBlock - 1) / kBlock;
+  rope_cache_kernel<<<static_cast<unsigned>(grid), kBlock, 0, static_cast<hipStream_t>(stream)>>>(
+      inv_freq, total, make_fastdiv(static_cast<uint32_t>(half)), static_cast<int>(half), cos_c,
+      sin_c);
+  return launch_status();
+}
+
 }  // namespace
 }  // namespace et
 
@@ -797,6 +900,29 @@ et_status et_rmsnorm_rope_qk_bf16(et_bf16* q, const et_bf16* gq, int64_t Hq, et_
   return et::qknorm_entry<Bf16>(reinterpret_cast<Bf16*>(q), reinterpret_cast<const Bf16*>(gq), Hq,
                                 reinterpret_cast<Bf16*>(k), reinterpret_cast<const Bf16*>(gk), Hk,
                                 eps, pos, T, D, d_rot, inv_freq, attn_scaling, layout, stream);
+}
+
+et_status et_rope_cache_f32(const float* inv_freq, int64_t max_pos, int64_t d_rot,
+                            float* cos_cache, float* sin_cache, void* stream) {
+  return et::rope_cache_entry(inv_freq, max_pos, d_rot, cos_cache, sin_cache, stream);
+}
+
+et_status et_rope_qk_cached_f32(float* q, int64_t Hq, float* k, int64_t Hk, const int32_t* pos,
+                                int64_t T, int64_t D, int64_t d_rot, const float* cos_cache,
+                                const float* sin_cache, int64_t max_pos, float attn_scaling,
+                                int layout, void* stream) {
+  const et::RopeCache c{cos_cache, sin_cache, max_pos};
+  return et::rope_entry<float>(q, Hq, k, Hk, pos, T, D, d_rot, nullptr, attn_scaling, layout,
+                               stream, &c);
+}
+
+et_status et_rope_qk_cached_bf16(et_bf16* q, int64_t Hq, et_bf16* k, int64_t Hk,
+                                 const int32_t* pos, int64_t T, int64_t D, int64_t d_rot,
+                                 const float* cos_cache, const float* sin_cache, int64_t max_pos,
+                                 float attn_scaling, int layout, void* stream) {
+  const et::RopeCache c{cos_cache, sin_cache, max_pos};
+  return et::rope_entry<Bf16>(reinterpret_cast<Bf16*>(q), Hq, reinterpret_cast<Bf16*>(k), Hk, pos,
+                              T, D, d_rot, nullptr, attn_scaling, layout, stream, &c);
 }
 
 }  // extern "C"

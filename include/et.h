@@ -123,6 +123,42 @@ et_status et_rope_qk_bf16(et_bf16* q, int64_t Hq, et_bf16* k, int64_t Hk,
                           float attn_scaling, int layout, void* stream);
 
 /* ------------------------------------------------------------------------
+ * RoPE cos/sin cache  ([OPS] 3 Rope, cos/sin cache)
+ *   Fills cos_cache[p * d_rot/2 + i] and sin_cache[p * d_rot/2 + i] (f32,
+ *   device, [max_pos, d_rot/2], caller-owned) with the cosine and sine of
+ *   the angle et_rope_* uses for position p and pair i, for 0 <= p < max_pos.
+ *   Bit for bit the values et_rope_* computes, so a rotation from this cache
+ *   equals the computed one.  d_rot even; max_pos <= 2^31 - 1 and
+ *   max_pos * d_rot/2 < 2^32; the three buffers must not overlap.
+ */
+et_status et_rope_cache_f32(const float* inv_freq, int64_t max_pos,
+                            int64_t d_rot, float* cos_cache, float* sin_cache,
+                            void* stream);
+
+/* RoPE on q and k with the rotation read from a cos/sin cache instead of
+ * computed ([OPS] 3 Rope, cos/sin cache): for token t the pair i uses
+ * c = cos_cache[pos[t] * d_rot/2 + i], s = sin_cache[same] (any values;
+ * et_rope_cache_f32 makes the standard ones), then
+ *   a' = mu (a c - b s),  b' = mu (a s + b c)
+ * as et_rope_qk_*.  A position outside [0, max_pos) reads nothing from the
+ * cache; that token's rotated entries become NaN (its other entries are
+ * left alone).  0 <= max_pos <= 2^31 - 1; with max_pos == 0 the caches may
+ * be NULL.  The caches must not overlap q or k.  inv_freq is not used.
+ * Other rules as et_rope_qk_*.
+ */
+et_status et_rope_qk_cached_f32(float* q, int64_t Hq, float* k, int64_t Hk,
+                                const int32_t* pos, int64_t T, int64_t D,
+                                int64_t d_rot, const float* cos_cache,
+                                const float* sin_cache, int64_t max_pos,
+                                float attn_scaling, int layout, void* stream);
+et_status et_rope_qk_cached_bf16(et_bf16* q, int64_t Hq, et_bf16* k,
+                                 int64_t Hk, const int32_t* pos, int64_t T,
+                                 int64_t D, int64_t d_rot,
+                                 const float* cos_cache,
+                                 const float* sin_cache, int64_t max_pos,
+                                 float attn_scaling, int layout, void* stream);
+
+/* ------------------------------------------------------------------------
  * Fused RMSNorm + RoPE on Q and K, in place  ([OPS] 5 QK-norm)
  *   Each (token, head) row of length D is normalised over all D entries
  *   with the gain gq [D] (query heads) or gk [D] (key heads) and eps, then

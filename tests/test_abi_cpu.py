@@ -32,6 +32,9 @@ def test_header_declares_the_ops():
             assert f"et_{op}_{sfx}" in names
     assert "et_argmax_workspace_bytes" in names and "et_status_string" in names
     assert "et_softmax_workspace_bytes" in names
+    assert "et_rope_cache_f32" in names
+    for sfx in ("f32", "bf16"):
+        assert f"et_rope_qk_cached_{sfx}" in names
 
 
 def test_library_exports_every_declared_symbol():
@@ -120,6 +123,41 @@ def test_rope_validation(sfx):
     q = getattr(et.lib, f"et_rope_qk_{sfx}")
     assert q(A, 2, P(G + 16), 2, B, 4, 8, 8, C, 1.0, 0, S) == 4   # q and k overlap
     assert q(A, 2, NULL, 3, B, 4, 8, 8, C, 1.0, 0, S) == 1          # k NULL with Hk > 0
+
+
+@gpu_visible
+def test_rope_cache_validation():
+    import elementwise_transformer_amd as et
+    f = et.lib.et_rope_cache_f32
+    assert f(A, 16, 7, B, C, S) == 3                         # odd d_rot
+    assert f(A, -1, 8, B, C, S) == 2
+    assert f(A, 16, -2, B, C, S) == 2
+    assert f(A, 1 << 31, 8, B, C, S) == 2                    # positions are int32
+    assert f(A, 1 << 30, 16, B, C, S) == 2                   # 2^33 entries
+    assert f(NULL, 16, 8, B, C, S) == 1
+    assert f(A, 16, 8, NULL, C, S) == 1
+    assert f(A, 16, 8, B, B, S) == 4                         # cos == sin
+    assert f(A, 16, 8, B, P(2 * G + 64), S) == 4             # sin inside cos
+    assert f(P(2 * G + 16), 16, 8, B, C, S) == 4             # inv_freq inside cos
+    assert f(NULL, 0, 8, NULL, NULL, S) == 0                 # empty cache: no-op
+
+
+@gpu_visible
+@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+def test_rope_cached_validation(sfx):
+    import elementwise_transformer_amd as et
+    f = getattr(et.lib, f"et_rope_qk_cached_{sfx}")
+    # q, Hq, k, Hk, pos, T, D, d_rot, cos, sin, max_pos, mu, layout, stream
+    assert f(A, 2, B, 2, C, 4, 8, 8, NULL, E5, 16, 1.0, 0, S) == 1   # cos NULL
+    assert f(A, 2, B, 2, C, 4, 8, 8, D, NULL, 16, 1.0, 0, S) == 1    # sin NULL
+    assert f(A, 2, B, 2, NULL, 4, 8, 8, D, E5, 16, 1.0, 0, S) == 1   # pos NULL
+    assert f(A, 2, B, 2, C, 4, 8, 8, D, E5, -1, 1.0, 0, S) == 2
+    assert f(A, 2, B, 2, C, 4, 8, 8, D, E5, 1 << 31, 1.0, 0, S) == 2
+    assert f(A, 2, B, 2, C, 4, 8, 7, D, E5, 16, 1.0, 0, S) == 3      # odd d_rot
+    assert f(A, 2, B, 2, C, 4, 8, 8, D, E5, 16, 1.0, 5, S) == 3      # bad layout
+    assert f(A, 2, B, 2, C, 4, 8, 8, P(G + 64), E5, 16, 1.0, 0, S) == 4   # cos inside q
+    assert f(A, 2, B, 2, C, 4, 8, 8, D, P(2 * G + 32), 16, 1.0, 0, S) == 4  # sin inside k
+    assert f(NULL, 0, NULL, 0, NULL, 4, 8, 8, NULL, NULL, 0, 1.0, 0, S) == 0  # no heads
 
 
 @gpu_visible
