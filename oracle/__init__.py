@@ -71,6 +71,8 @@ class Oracle:
         lib.orc_layernorm.argtypes = [_int, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp]
         lib.orc_geglu.argtypes = [_int, _vp, _vp, _i64, _int, _vp, _vp]
         lib.orc_rope_cache.argtypes = [_vp, _i64, _i64, _vp, _vp]
+        lib.orc_rope_multi.argtypes = [_int, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _f32, _int,
+                                       _vp]
         lib.orc_rope_cached.argtypes = [_int, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _f32,
                                         _int, _vp]
         lib.orc_add_rmsnorm.argtypes = [_int, _vp, _vp, _vp, _i64, _i64, _f32, _vp, _vp, _vp]
@@ -244,6 +246,23 @@ class Oracle:
         sin_c = np.ascontiguousarray(sin_c, dtype=np.float32)
         self.lib.orc_rope_cached(_dt(out), _p(out), _p(pos), T, H, D, r, _p(cos_c), _p(sin_c),
                                  cos_c.shape[0], mu, layout, _p(y64))
+        return out, y64
+
+
+    def rope_multi(self, x: np.ndarray, pos: np.ndarray, dims, inv_freq: np.ndarray, mu: float,
+                   layout: int):
+        """x [T, H, D] (not modified), pos int32 [T, A], dims [A] (even), inv_freq f32
+        [sum(dims)/2] (axis a's frequencies at offset sum(dims[:a])/2) -> (rotated copy, y64)."""
+        out = np.array(x, copy=True, order="C")
+        T, H, D = out.shape
+        pos = np.ascontiguousarray(pos, dtype=np.int32).reshape(T, -1)
+        dims = np.ascontiguousarray(dims, dtype=np.int64)
+        assert pos.shape[1] == dims.size and int(dims.sum()) <= D and not np.any(dims % 2)
+        inv = np.ascontiguousarray(inv_freq, dtype=np.float32)
+        assert inv.size >= int(dims.sum()) // 2
+        y64 = np.empty(out.shape, np.float64)
+        self.lib.orc_rope_multi(_dt(out), _p(out), _p(pos), T, H, D, dims.size, _p(dims), _p(inv),
+                                mu, layout, _p(y64))
         return out, y64
 
 

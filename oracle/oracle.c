@@ -9,7 +9,7 @@
  *
  * Also the next rows built after those: softmax over the last axis with a
  * temperature; LayerNorm; GELU-gated multiply (GeGLU, erf and tanh forms);
- * RoPE from a precomputed cos/sin cache.
+ * RoPE from a precomputed cos/sin cache; multi-axis RoPE.
  *
  * Sources (web pages; sections named, never line numbers):
  *   [OPS]  "Operations" (glia runtime op spec): 2 Normalization / RmsNorm,
@@ -479,6 +479,62 @@ void orc_rope_cached(int dt, void* x, const int32_t* pos, int64_t T,
         for (int64_t h = 0; h < H; ++h)
             for (int64_t j = 0; j < D; ++j) {
                 if (j < r) st(dt, x, base + h * D + j, v[h * D + j]);
+                if (y64) y64[base + h * D + j] = v[h * D + j];
+            }
+        free(v);
+    }
+}
+
+/* ------------------------------------------------------- multi-axis RoPE */
+
+/* [OPS] 3 Rope, multi-axis RoPE (3D, for video diffusion transformers):
+ * token t has a position vector pos[t * A + a], a < A.  The head is cut into
+ * consecutive sub-ranges of dims[a] entries (each even; they need not fill
+ * the head), axis a starting at o_a = dims[0] + ... + dims[a-1].  Axis a
+ * applies RoPE on its own sub-range, as if that were a whole head of
+ * dims[a] entries: its position pos[t * A + a], its own frequencies
+ * inv_freq[h_a + j], j < dims[a]/2, h_a = (dims[0] + ... + dims[a-1]) / 2
+ * (so each axis may have its own base), the angle of [ELT] 2.2 (R1), and
+ * the pairing of layout inside the sub-range: half (o_a + j, o_a + j +
+ * dims[a]/2) or interleaved (o_a + 2j, o_a + 2j + 1).  Entries past the last
+ * sub-range are not touched. */
+void orc_rope_multi(int dt, void* x, const int32_t* pos, int64_t T,
+                    int64_t H, int64_t D, int64_t A, const int64_t* dims,
+                    const float* inv_freq, float mu_f, int layout,
+                    double* y64) {
+    const double mu = (double)mu_f;
+    int64_t span = 0;
+    for (int64_t a = 0; a < A; ++a) span += dims[a];
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t base = t * H * D;
+        double* v = row_buffer(H * D);
+        for (int64_t j = 0; j < H * D; ++j) v[j] = ld(dt, x, base + j);
+        int64_t off = 0;    /* o_a: first entry of this axis's sub-range */
+        int64_t foff = 0;   /* h_a: first frequency of this axis */
+        for (int64_t a = 0; a < A; ++a) {
+            const int64_t da = dims[a];
+            const int32_t p = pos[t * A + a];
+            for (int64_t j = 0; j < da / 2; ++j) {
+                const double ang = (double)orc_rope_angle(p, inv_freq[foff + j]);
+                const double c = cos(ang);
+                const double sn = sin(ang);
+                int64_t ia, ib;
+                rope_pair(layout, da, j, &ia, &ib);
+                for (int64_t h = 0; h < H; ++h) {
+                    double* w = v + h * D + off;
+                    const double x1 = w[ia];
+                    const double x2 = w[ib];
+                    w[ia] = mu * (x1 * c - x2 * sn);
+                    w[ib] = mu * (x1 * sn + x2 * c);
+                }
+            }
+            off += da;
+            foff += da / 2;
+        }
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t j = 0; j < D; ++j) {
+                if (j < span) st(dt, x, base + h * D + j, v[h * D + j]);
                 if (y64) y64[base + h * D + j] = v[h * D + j];
             }
         free(v);

@@ -64,6 +64,11 @@ void orc_rope_cached(int dt, void* x, const int32_t* pos, int64_t T,
                      const float* sin_c, int64_t max_pos, float mu_f,
                      int layout, double* y64);
 
+void orc_rope_multi(int dt, void* x, const int32_t* pos, int64_t T,
+                    int64_t H, int64_t D, int64_t A, const int64_t* dims,
+                    const float* inv_freq, float mu_f, int layout,
+                    double* y64);
+
 #ifdef __cplusplus
 }
 #endif

@@ -647,6 +647,81 @@ def pin_rope_cached_rotation(orc):
         assert np.array_equal(y64[ok], good64[ok])
 
 
+# ------------------------------------------------------- multi-axis RoPE
+
+def _multi_brute(x, pos, dims, inv, mu, layout):
+    """[OPS] Rope, multi-axis: the page's loop written out in Python floats --
+    for each axis, its sub-range of the head is rotated as a whole head of
+    dims[a] entries with that axis's position and frequencies (angles per
+    [ELT] 2.2, the f64 product rounded to f32; sine and cosine in decimal)."""
+    T, H, D = x.shape
+    y = x.astype(np.float64)
+    off, foff = 0, 0
+    for a, da in enumerate(dims):
+        for t in range(T):
+            for j in range(da // 2):
+                ang = float(np.float32(np.float64(int(pos[t, a])) * np.float64(inv[foff + j])))
+                s, c = brute.sincos_decimal(ang, 30)
+                ia, ib = _pair_index(layout, da, j)
+                for h in range(H):
+                    x1, x2 = y[t, h, off + ia], y[t, h, off + ib]
+                    y[t, h, off + ia] = mu * (x1 * c - x2 * s)
+                    y[t, h, off + ib] = mu * (x1 * s + x2 * c)
+        off += da
+        foff += da // 2
+    return y
+
+
+def pin_rope_multi_brute_force(orc):
+    """[OPS] Rope, multi-axis (3D) RoPE on a tiny head: three axes of 4, 6
+    and 4 entries in a head of 16 (the last 2 pass through), each axis with
+    its own base, positions of both signs; both pairings.  Against the loop
+    of the page written out independently (decimal sine and cosine)."""
+    g = np.random.default_rng(303)
+    T, H, D = 3, 2, 16
+    dims = [4, 6, 4]
+    x = g.standard_normal((T, H, D)).astype(np.float32)
+    pos = np.array([[0, 5, -3], [7, 0, 2], [2, 9, 11]], np.int32)
+    inv = np.concatenate([np.power(np.float64(b), -2.0 * np.arange(d // 2) / d)
+                          for b, d in zip((10.0, 100.0, 1000.0), dims)]).astype(np.float32)
+    for layout in (0, 1):
+        out, y64 = orc.rope_multi(x, pos, dims, inv, 1.25, layout)
+        ref = _multi_brute(x, pos, dims, inv, 1.25, layout)
+        scale = np.abs(x.astype(np.float64)).max() * 1.25
+        assert np.max(np.abs(y64 - ref)) <= 4 * scale * 2.0 ** -52, layout
+        assert np.array_equal(out[..., 14:], x[..., 14:])
+        assert np.array_equal(y64[..., 14:], x[..., 14:].astype(np.float64))
+
+
+def pin_rope_multi_axes_decompose(orc):
+    """Each axis is RoPE on its own sub-range: the multi-axis result, cut at
+    the axis boundaries, equals the (separately pinned) single-axis RoPE of
+    each slice with that axis's positions and frequencies, in f64 bits; one
+    axis spanning r entries is partial RoPE with rotary width r; position
+    vectors of zeros scale by mu only."""
+    g = np.random.default_rng(304)
+    T, H, D = 5, 3, 40
+    dims = [8, 12, 16]
+    x = g.standard_normal((T, H, D)).astype(np.float32)
+    pos = g.integers(-5000, 5000, (T, 3)).astype(np.int32)
+    inv = np.concatenate([np.power(np.float64(b), -2.0 * np.arange(d // 2) / d)
+                          for b, d in zip((1e4, 5e3, 7e2), dims)]).astype(np.float32)
+    for layout in (0, 1):
+        _, y64 = orc.rope_multi(x, pos, dims, inv, 0.75, layout)
+        off, foff = 0, 0
+        for a, da in enumerate(dims):
+            sl = np.ascontiguousarray(x[..., off:off + da])
+            _, r64 = orc.rope(sl, pos[:, a].copy(), da, inv[foff:foff + da // 2].copy(), 0.75, layout)
+            assert np.array_equal(y64[..., off:off + da], r64), (layout, a)
+            off += da
+            foff += da // 2
+        _, one64 = orc.rope_multi(x, pos[:, 1:2], [24], inv[:12], 0.75, layout)
+        _, p64 = orc.rope(x, pos[:, 1].copy(), 24, inv[:12].copy(), 0.75, layout)
+        assert np.array_equal(one64, p64)
+        _, z64 = orc.rope_multi(x, np.zeros((T, 3), np.int32), dims, inv, 0.75, layout)
+        assert np.array_equal(z64[..., :36], 0.75 * x[..., :36].astype(np.float64))
+
+
 # -------------------------------------------------------------- LayerNorm
 
 def pin_layernorm_closed_forms(orc):

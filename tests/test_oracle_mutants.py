@@ -4,9 +4,10 @@ Each mutant is a copy of ``oracle/oracle.c`` with one plausible mistake
 planted by text substitution, built into a temporary library.  The pins must
 fail on every mutant.  s01-s15 are the mistakes listed in the Pitfalls table
 (section 5) of "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding,
-add, argmax", each with the test the page says catches it; x01-x29 are further
+add, argmax", each with the test the page says catches it; x01-x34 are further
 slips (a wrong sign, index, dropped term or rounding) in the same code, x11-x16
-in the softmax, x17-x20 in LayerNorm, x21-x25 in the GELU-gated multiply, x26-x29 in the RoPE cache.
+in the softmax, x17-x20 in LayerNorm, x21-x25 in the GELU-gated multiply, x26-x29
+in the RoPE cache, x30-x34 in multi-axis RoPE.
 """
 import os
 import tempfile
@@ -104,6 +105,18 @@ MUTANTS = {
                                       "? (double)cos_c[(int64_t)p * half + i] : 1.0;")]),
     "x29_cache_uses_cos_for_sin": ("rope_cache_values",
                                    [("sin_c[p * half + i] = (float)sin(ang);", "sin_c[p * half + i] = (float)cos(ang);")]),
+    "x30_multi_axis_offset_stuck": ("rope_multi_brute_force",
+                                    [("            off += da;\n            foff += da / 2;",
+                                      "            foff += da / 2;")]),
+    "x31_multi_freq_offset_stuck": ("rope_multi_brute_force",
+                                    [("            foff += da / 2;", "            foff += 0;")]),
+    "x32_multi_axis0_position": ("rope_multi_brute_force",
+                                 [("const int32_t p = pos[t * A + a];", "const int32_t p = pos[t * A];")]),
+    "x33_multi_half_of_first_axis": ("rope_multi_brute_force",
+                                     [("rope_pair(layout, da, j, &ia, &ib);",
+                                       "rope_pair(layout, dims[0], j, &ia, &ib);")]),
+    "x34_multi_rotation_sign": ("rope_multi_axes_decompose",
+                                [("w[ib] = mu * (x1 * sn + x2 * c);", "w[ib] = mu * (x2 * c - x1 * sn);")]),
     "x25_gelu_tanh_no_f32_limit": ("gelu_symmetry_and_limits",
                                    [("if (e > FLT_MAX) e = INFINITY;  /* the f32", "/* the f32")]),
 }
