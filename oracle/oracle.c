@@ -517,16 +517,16 @@ void orc_rope_multi(int dt, void* x, const int32_t* pos, int64_t T,
             const int32_t p = pos[t * A + a];
             for (int64_t j = 0; j < da / 2; ++j) {
                 const double ang = (double)orc_rope_angle(p, inv_freq[foff + j]);
-                const double c = cos(ang);
-                const double sn = sin(ang);
+                const double ca = cos(ang);
+                const double sa = sin(ang);
                 int64_t ia, ib;
                 rope_pair(layout, da, j, &ia, &ib);
                 for (int64_t h = 0; h < H; ++h) {
                     double* w = v + h * D + off;
                     const double x1 = w[ia];
                     const double x2 = w[ib];
-                    w[ia] = mu * (x1 * c - x2 * sn);
-                    w[ib] = mu * (x1 * sn + x2 * c);
+                    w[ia] = mu * (x1 * ca - x2 * sa);
+                    w[ib] = mu * (x1 * sa + x2 * ca);
                 }
             }
             off += da;

@@ -116,7 +116,7 @@ MUTANTS = {
                                      [("rope_pair(layout, da, j, &ia, &ib);",
                                        "rope_pair(layout, dims[0], j, &ia, &ib);")]),
     "x34_multi_rotation_sign": ("rope_multi_axes_decompose",
-                                [("w[ib] = mu * (x1 * sn + x2 * c);", "w[ib] = mu * (x2 * c - x1 * sn);")]),
+                                [("w[ib] = mu * (x1 * sa + x2 * ca);", "w[ib] = mu * (x2 * ca - x1 * sa);")]),
     "x25_gelu_tanh_no_f32_limit": ("gelu_symmetry_and_limits",
                                    [("if (e > FLT_MAX) e = INFINITY;  /* the f32", "/* the f32")]),
 }
