@@ -241,6 +241,8 @@ def time_next_ops(et, torch, wl, stream, sets=3, launches=60):
       rope_cached  the prefill RoPE (q [4096,32,128], k [4096,8,128] bf16,
                 positions 0..4095) with the rotation read from a cos/sin
                 cache [4096, 64] f32 built by the library
+      rope_multi  3D RoPE of a video DiT: q and k [19200, 24, 128] bf16 over a
+                16 x 30 x 40 latent grid, axis widths 16 / 56 / 56
     Algorithmic bytes: each input read once, each output written once."""
     out = {}
 
@@ -303,6 +305,20 @@ def time_next_ops(et, torch, wl, stream, sets=3, launches=60):
     heads = s.Hq + s.Hk
     record("rope_cached", "prefill RoPE q [4096,32,128] k [4096,8,128] bf16, cache [4096,64] f32",
            2 * s.T * heads * s.r * 2 + 4 * s.T + 2 * s.T * (s.r // 2) * 4, t, "rope_qk_kernel (cached)")
+    del qs, ks
+
+    w = wl.WORKLOADS[6]
+    m = w.rope_multi
+    q, k, pos, inv = wl.gen_rope_multi(w)
+    qs = [torch.from_numpy(q.view(np.int16)).view(torch.bfloat16).cuda() for _ in range(sets)]
+    ks = [torch.from_numpy(k.view(np.int16)).view(torch.bfloat16).cuda() for _ in range(sets)]
+    pt = torch.from_numpy(pos).cuda()
+    ft = torch.from_numpy(inv).cuda()
+    t = _time_launches(stream, lambda i: et.rope_multi(qs[i % sets], ks[i % sets], pt, m.dims, ft,
+                                                       attn_scaling=m.mu, layout=m.layout), sets, launches)
+    span = sum(m.dims)
+    record("rope_multi", "video DiT 3D RoPE q,k [19200,24,128] bf16, grid 16x30x40, widths 16/56/56",
+           2 * m.T * (m.Hq + m.Hk) * span * 2 + 4 * 3 * m.T + 4 * (span // 2), t, "rope_multi_kernel")
     return out
 
 

@@ -19,7 +19,7 @@ from typing import Optional, Tuple
 import torch  # loaded first so libet.so binds to the HIP runtime torch uses
 
 __all__ = ["rmsnorm", "add_rmsnorm", "rope", "rope_qk", "rmsnorm_rope_qk", "silu_mul", "add",
-           "rope_cache", "rope_qk_cached", "embedding", "argmax", "argmax_workspace_bytes", "ETError", "lib", "LIB_PATH",
+           "rope_cache", "rope_qk_cached", "rope_multi", "embedding", "argmax", "argmax_workspace_bytes", "ETError", "lib", "LIB_PATH",
            "ROPE_HALF", "ROPE_INTERLEAVED", "abi_version"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libet.so")
@@ -62,6 +62,7 @@ _SIGS = {
     "geglu": [_vp, _vp, _vp, _i64, _int, _vp],
     "rope_qk_cached": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _f32, _int,
                        _vp],
+    "rope_multi": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp, _f32, _int, _vp],
 }
 for _op, _args in _SIGS.items():
     for _sfx in ("f32", "bf16"):
@@ -259,6 +260,31 @@ def rope_qk_cached(q: torch.Tensor, k: Optional[torch.Tensor], pos: torch.Tensor
         raise ValueError("caches must be [max_pos, d_rot/2]")
     _call(f"et_rope_qk_cached_{_sfx(q)}", _ptr(q), Hq, _ptr(k), Hk, _ptr(pos), T, D, d_rot,
           _ptr(cos_cache), _ptr(sin_cache), cos_cache.shape[0], float(attn_scaling), int(layout),
+          _stream(q))
+    return q, k
+
+
+def rope_multi(q: torch.Tensor, k: Optional[torch.Tensor], pos: torch.Tensor, dims,
+               inv_freq: torch.Tensor, attn_scaling: float = 1.0,
+               layout: int = ROPE_HALF) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """In-place multi-axis RoPE of q [T, Hq, D] and k [T, Hk, D]: pos int32
+    [T, len(dims)], dims the per-axis widths (even), inv_freq f32
+    [sum(dims)/2] (axis a's frequencies from sum(dims[:a])/2)
+    (et_rope_multi_*); returns (q, k)."""
+    T, Hq, D = q.shape
+    Hk = 0 if k is None else k.shape[1]
+    if k is not None and (k.shape[0] != T or k.shape[2] != D):
+        raise ValueError("k must be [T, Hk, D] with q's T and D")
+    dims_arr = (ctypes.c_int64 * len(dims))(*[int(d) for d in dims])
+    _dev(q, k)
+    _same(q, k)
+    _rope_common(pos, inv_freq)
+    if pos.dim() != 2 or pos.shape[0] != T or pos.shape[1] != len(dims):
+        raise ValueError("pos must be [T, len(dims)]")
+    if inv_freq.numel() < sum(int(d) for d in dims) // 2:
+        raise ValueError("inv_freq needs sum(dims)/2 entries")
+    _call(f"et_rope_multi_{_sfx(q)}", _ptr(q), Hq, _ptr(k), Hk, _ptr(pos), T, D, len(dims),
+          ctypes.cast(dims_arr, ctypes.c_void_p), _ptr(inv_freq), float(attn_scaling), int(layout),
           _stream(q))
     return q, k
 

@@ -851,6 +851,299 @@ et_status rope_cache_entry(const float* inv_freq, int64_t max_pos, int64_t r, fl
   return launch_status();
 }
 
+
+// --------------------------------------------------------- multi-axis RoPE
+//
+// "Operations" 3 Rope, multi-axis RoPE: the first `span` entries of a head
+// are cut into consecutive sub-ranges, one per axis of the token's position
+// vector, and each is rotated as a whole head of its own width, with its own
+// position and frequencies.  A sub-range's pairs may sit anywhere relative
+// to the 16-byte vectors (half widths need not be multiples of V), so a
+// workgroup stages its head rows in LDS and every element reads its partner
+// from there:
+//   * a workgroup owns rpb consecutive head rows (token-major: a token's q
+//     heads, then its k heads), loads their first span entries once, 16
+//     bytes at a time (scalars on the scalar path), and copies them to LDS;
+//   * a column table gives each of the span columns its partner column, its
+//     pair index and whether it is the pair's first member;
+//   * an angle table holds (mu cos, mu sin) per (token, pair), built as the
+//     RoPE kernel builds its own.
+// Each element is then rotated exactly as the RoPE kernel rotates it, so a
+// single axis of width r gives that kernel's bits.  In place: a workgroup
+// reads all of its rows before the barrier and writes after it, each
+// element by the thread that loaded it.
+
+constexpr int kMaxAxes = 8;
+constexpr int kMultiU = 4;
+constexpr int kMultiMaxSpan = 1024;
+
+struct MultiArgs {
+  RopeArgs ra;              // T, hq, hk, D and mu, as for the RoPE kernel
+  int A;                    // axes
+  int span;                 // rotated entries per head row (sum of the widths)
+  int np;                   // pairs per head row (span / 2)
+  int off[kMaxAxes + 1];    // first entry of axis a; off[A] = span
+  int foff[kMaxAxes + 1];   // first pair (frequency) of axis a
+  uint32_t rows;            // head rows in this launch
+  int rpb;                  // head rows per workgroup
+  int nv;                   // vectors (or scalars) per head row: span / PS
+  int ntok_max;             // tokens one workgroup can touch
+  int heads;                // hq + hk
+  FastDiv fd_heads, fd_nv, fd_np;
+  uint32_t col_off, xs_off; // byte offsets of the column table and the rows in LDS
+};
+
+// The axis a pair index i belongs to (zero-width axes are skipped: a later
+// axis with the same start wins).
+__device__ inline int axis_of_pair(int i, const MultiArgs& a) {
+  int ax = 0;
+#pragma unroll
+  for (int b = 1; b < kMaxAxes; ++b)
+    if (b < a.A && i >= a.foff[b]) ax = b;
+  return ax;
+}
+
+// Column entry: partner column (bits 0-15), pair index (16-30), first
+// member of its pair (bit 31).
+__device__ inline uint32_t column_info(int c, const MultiArgs& a) {
+  int o = 0, w = a.off[1], h = 0;
+#pragma unroll
+  for (int b = 1; b < kMaxAxes; ++b) {
+    if (b < a.A && c >= a.off[b]) {
+      o = a.off[b];
+      w = a.off[b + 1] - a.off[b];
+      h = a.foff[b];
+    }
+  }
+  const int l = c - o;
+  int partner, j;
+  bool first;
+  if (a.ra.layout == ET_ROPE_HALF) {
+    const int hd = w / 2;
+    first = l < hd;
+    j = first ? l : l - hd;
+    partner = first ? c + hd : c - hd;
+  } else {
+    first = (l & 1) == 0;  // sub-ranges start at even entries
+    j = l >> 1;
+    partner = c ^ 1;
+  }
+  return static_cast<uint32_t>(partner) | (static_cast<uint32_t>(h + j) << 16) |
+         (first ? 0x80000000u : 0u);
+}
+
+template <typename S>
+__device__ inline float lds_elem(const S* xs, int i) {
+  if constexpr (sizeof(S) == 2) {
+    return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(xs)[i]) << 16);
+  } else {
+    return xs[i];
+  }
+}
+
+template <typename S, int PS, int U, int POL>
+__global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
+                                                           const int32_t* __restrict__ pos,
+                                                           const float* __restrict__ inv_freq,
+                                                           MultiArgs a) {
+  using E = Elem<S>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float2* cs = reinterpret_cast<float2*>(smem);
+  uint32_t* col = reinterpret_cast<uint32_t*>(smem + a.col_off);
+  S* xs = reinterpret_cast<S*>(smem + a.xs_off);
+
+  const uint32_t row0 = blockIdx.x * static_cast<uint32_t>(a.rpb);
+  uint32_t row_end = row0 + a.rpb;
+  if (row_end > a.rows) row_end = a.rows;
+  const uint32_t t0 = fdiv(row0, a.fd_heads);
+  const int ntok = static_cast<int>(fdiv(row_end - 1, a.fd_heads) - t0 + 1);
+  const int nslot = static_cast<int>(row_end - row0) * a.nv;
+  const int ntab = ntok * a.np;
+
+  // Phase 0: positions and frequencies of this thread's first angle-table
+  // entries, fetched before the row loads (loads complete in issue order).
+  int32_t tp[kTabPre];
+  float tw[kTabPre];
+#pragma unroll
+  for (int kk = 0; kk < kTabPre; ++kk) {
+    int idx = threadIdx.x + kk * kBlock;
+    if (idx >= ntab) idx = ntab - 1;  // clamped: loaded, never used
+    const int tl = static_cast<int>(fdiv(static_cast<uint32_t>(idx), a.fd_np));
+    const int i = idx - tl * a.np;
+    tp[kk] = pos[static_cast<int64_t>(t0 + tl) * a.A + axis_of_pair(i, a)];
+    tw[kk] = inv_freq[i];
+  }
+
+  // Phase 1: every row load of this thread.
+  const QkOut<S, POL> out(q, k, t0, static_cast<int>(row0 - t0 * a.heads), a.ra);
+  int sl[U], cv[U], tl[U], rel[U];
+  bool isq[U];
+  S* rowp[U];
+  u32x4 v[U];
+  float sv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    int s = static_cast<int>(rope_slot<U>(0, threadIdx.x, u));
+    if (s >= nslot) s = nslot - 1;  // clamped: loaded, never stored
+    const int r = static_cast<int>(fdiv(static_cast<uint32_t>(s), a.fd_nv));
+    sl[u] = r;
+    cv[u] = s - r * a.nv;
+    const uint32_t g = row0 + r;
+    const uint32_t t = fdiv(g, a.fd_heads);
+    const int hh = static_cast<int>(g - t * a.heads);
+    tl[u] = static_cast<int>(t - t0);
+    isq[u] = hh < a.ra.hq;
+    rowp[u] = isq[u] ? q + (static_cast<int64_t>(t) * a.ra.hq + hh) * a.ra.D
+                     : k + (static_cast<int64_t>(t) * a.ra.hk + (hh - a.ra.hq)) * a.ra.D;
+    rel[u] = out.rel(t, hh, a.ra);
+    if constexpr (PS == 1) sv[u] = E::ld(rowp[u], cv[u]);
+    else v[u] = ld16(rowp[u], static_cast<int64_t>(cv[u]) * PS);
+  }
+#if ET_ROPE_SCHED_BARRIER
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+
+  // Phase 2: angle table, column table, rows to LDS.
+#pragma unroll
+  for (int kk = 0; kk < kTabPre; ++kk) {
+    const int idx = threadIdx.x + kk * kBlock;
+    if (idx < ntab) {
+      float sn, cn;
+      sincos_angle(rope_angle(tp[kk], tw[kk]), &sn, &cn);
+      cs[idx] = make_float2(a.ra.mu * cn, a.ra.mu * sn);
+    }
+  }
+  for (int idx = threadIdx.x + kTabPre * kBlock; idx < ntab; idx += kBlock) {
+    const int t = static_cast<int>(fdiv(static_cast<uint32_t>(idx), a.fd_np));
+    const int i = idx - t * a.np;
+    float sn, cn;
+    sincos_angle(rope_angle(pos[static_cast<int64_t>(t0 + t) * a.A + axis_of_pair(i, a)],
+                            inv_freq[i]), &sn, &cn);
+    cs[idx] = make_float2(a.ra.mu * cn, a.ra.mu * sn);
+  }
+  for (int c = threadIdx.x; c < a.span; c += kBlock) col[c] = column_info(c, a);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int s = static_cast<int>(rope_slot<U>(0, threadIdx.x, u));
+    if (s >= nslot) continue;
+    S* dst = xs + sl[u] * a.span + cv[u] * PS;
+    if constexpr (PS == 1) E::st(dst, 0, sv[u]);
+    else *reinterpret_cast<u32x4*>(dst) = v[u];
+  }
+  __syncthreads();
+
+  // Phase 3: rotate and store.
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int s = static_cast<int>(rope_slot<U>(0, threadIdx.x, u));
+    if (s >= nslot) continue;
+    const S* xr = xs + sl[u] * a.span;
+    const float2* tab = cs + tl[u] * a.np;
+    float y[PS];
+#pragma unroll
+    for (int e = 0; e < PS; ++e) {
+      const float x = PS == 1 ? sv[u] : E::get(v[u], e);
+      const uint32_t info = col[cv[u] * PS + e];
+      const float xp = lds_elem(xr, static_cast<int>(info & 0xFFFFu));
+      const float2 c = tab[(info >> 16) & 0x7FFFu];
+      y[e] = (info >> 31) ? __builtin_fmaf(x, c.x, -(xp * c.y)) : __builtin_fmaf(xp, c.y, x * c.x);
+    }
+    if constexpr (PS == 1) {
+      E::st(rowp[u], cv[u], y[0]);
+    } else {
+      out.store(isq[u], rel[u] + cv[u] * PS, E::pack(y));
+    }
+  }
+}
+
+// LDS bytes of a workgroup of rpb rows: angle table, column table, rows.
+inline void multi_lds(MultiArgs& a, int es, size_t* bytes) {
+  a.ntok_max = (a.rpb + a.heads - 1) / a.heads + 1;
+  if (a.ntok_max > a.rpb) a.ntok_max = a.rpb;
+  const uint32_t tab = static_cast<uint32_t>(a.ntok_max) * a.np * sizeof(float2);
+  a.col_off = (tab + 15u) & ~15u;
+  a.xs_off = (a.col_off + static_cast<uint32_t>(a.span) * 4u + 15u) & ~15u;
+  *bytes = a.xs_off + static_cast<size_t>(a.rpb) * a.span * es;
+}
+
+template <typename S, int PS, int POL>
+void launch_multi(S* q, S* k, const int32_t* pos, const float* inv_freq, MultiArgs a, int64_t T,
+                  size_t shmem, hipStream_t s) {
+  const int64_t tok_per_launch = (int64_t{1} << 30) / a.heads;
+  for (int64_t t0 = 0; t0 < T; t0 += tok_per_launch) {
+    const int64_t m = T - t0 < tok_per_launch ? T - t0 : tok_per_launch;
+    a.ra.T = m;
+    a.rows = static_cast<uint32_t>(m * a.heads);
+    const unsigned grid = (a.rows + a.rpb - 1) / a.rpb;
+    rope_multi_kernel<S, PS, kMultiU, POL><<<grid, kBlock, shmem, s>>>(
+        q + t0 * a.ra.hq * a.ra.D, a.ra.hk ? k + t0 * a.ra.hk * a.ra.D : k, pos + t0 * a.A,
+        inv_freq, a);
+  }
+}
+
+template <typename S>
+et_status rope_multi_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int64_t T,
+                           int64_t D, int64_t A, const int64_t* dims, const float* inv_freq,
+                           float mu, int layout, void* stream) {
+  if (A < 1 || A > kMaxAxes) return ET_ERR_BAD_ARG;
+  if (!dims) return ET_ERR_NULL_POINTER;
+  int64_t span = 0;
+  for (int64_t ax = 0; ax < A; ++ax) {
+    if (dims[ax] < 0 || (dims[ax] & 1) || dims[ax] > D) return ET_ERR_BAD_ARG;
+    span += dims[ax];
+  }
+  int64_t qb = 0, kb = 0;
+  const et_status st = check_rope(q, hq, k, hk, pos, T, D, span, inv_freq, mu, layout, &qb, &kb);
+  if (st != ET_OK) return st;
+  if (span > kMultiMaxSpan) return ET_ERR_BAD_SIZE;
+  int64_t pb = 0;
+  if (!mul_ok(T, A * int64_t(sizeof(int32_t)), &pb)) return ET_ERR_BAD_SIZE;
+  if (!ranges_ok(q, qb, pos, pb, false) || !ranges_ok(k, kb, pos, pb, false)) return ET_ERR_OVERLAP;
+  if (T == 0 || hq + hk == 0 || span == 0) return ET_OK;
+
+  constexpr int V = Elem<S>::V;
+  const bool vec = span % V == 0 && D % V == 0 && aligned16(q) && (hk == 0 || aligned16(k));
+  const int ps = vec ? V : 1;
+  MultiArgs a{};
+  a.ra.hq = static_cast<int>(hq);
+  a.ra.hk = static_cast<int>(hk);
+  a.ra.D = static_cast<int>(D);
+  a.ra.layout = layout;
+  a.ra.mu = mu;
+  a.A = static_cast<int>(A);
+  a.span = static_cast<int>(span);
+  a.np = a.span / 2;
+  int o = 0;
+  for (int ax = 0; ax <= kMaxAxes; ++ax) {
+    a.off[ax] = o;
+    a.foff[ax] = o / 2;
+    if (ax < A) o += static_cast<int>(dims[ax]);
+  }
+  a.heads = static_cast<int>(hq + hk);
+  a.nv = a.span / ps;
+  a.rpb = (kBlock * kMultiU) / a.nv;
+  size_t shmem = 0;
+  for (;;) {
+    multi_lds(a, static_cast<int>(sizeof(S)), &shmem);
+    if (shmem <= static_cast<size_t>(kMaxTableBytes) || a.rpb == 1) break;
+    a.rpb /= 2;
+  }
+  if (a.rpb < 1 || shmem > static_cast<size_t>(kMaxTableBytes)) return ET_ERR_BAD_SIZE;
+  a.fd_heads = make_fastdiv(static_cast<uint32_t>(a.heads));
+  a.fd_nv = make_fastdiv(static_cast<uint32_t>(a.nv));
+  a.fd_np = make_fastdiv(static_cast<uint32_t>(a.np));
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (vec && store_policy(T * (hq + hk) * span * int64_t(sizeof(S)), ET_POL_ROPE) == kStoreDevice)
+    launch_multi<S, V, kStoreDevice>(q, k, pos, inv_freq, a, T, shmem, s);
+  else if (vec)
+    launch_multi<S, V, kStoreStream>(q, k, pos, inv_freq, a, T, shmem, s);
+  else
+    launch_multi<S, 1, kStoreStream>(q, k, pos, inv_freq, a, T, shmem, s);
+  return launch_status();
+}
+
 }  // namespace
 }  // namespace et
 
@@ -923,6 +1216,20 @@ et_status et_rope_qk_cached_bf16(et_bf16* q, int64_t Hq, et_bf16* k, int64_t Hk,
   const et::RopeCache c{cos_cache, sin_cache, max_pos};
   return et::rope_entry<Bf16>(reinterpret_cast<Bf16*>(q), Hq, reinterpret_cast<Bf16*>(k), Hk, pos,
                               T, D, d_rot, nullptr, attn_scaling, layout, stream, &c);
+}
+
+et_status et_rope_multi_f32(float* q, int64_t Hq, float* k, int64_t Hk, const int32_t* pos,
+                            int64_t T, int64_t D, int64_t n_axes, const int64_t* dims,
+                            const float* inv_freq, float attn_scaling, int layout, void* stream) {
+  return et::rope_multi_entry<float>(q, Hq, k, Hk, pos, T, D, n_axes, dims, inv_freq, attn_scaling,
+                                     layout, stream);
+}
+
+et_status et_rope_multi_bf16(et_bf16* q, int64_t Hq, et_bf16* k, int64_t Hk, const int32_t* pos,
+                             int64_t T, int64_t D, int64_t n_axes, const int64_t* dims,
+                             const float* inv_freq, float attn_scaling, int layout, void* stream) {
+  return et::rope_multi_entry<Bf16>(reinterpret_cast<Bf16*>(q), Hq, reinterpret_cast<Bf16*>(k), Hk,
+                                    pos, T, D, n_axes, dims, inv_freq, attn_scaling, layout, stream);
 }
 
 }  // extern "C"

@@ -159,6 +159,33 @@ et_status et_rope_qk_cached_bf16(et_bf16* q, int64_t Hq, et_bf16* k,
                                  float attn_scaling, int layout, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Multi-axis RoPE on Q and K, in place  ([OPS] 3 Rope, multi-axis RoPE)
+ *   Token t has a position vector pos[t * n_axes + a] (int32, device,
+ *   [T, n_axes]).  The first span = dims[0] + ... + dims[n_axes-1] entries
+ *   of every head are cut into consecutive sub-ranges, axis a owning the
+ *   dims[a] entries from o_a = dims[0] + ... + dims[a-1].  Axis a rotates its
+ *   sub-range as et_rope_qk_* rotates a whole head of dims[a] entries
+ *   (same angle rule, same pairing per layout, relative to o_a), with
+ *   position pos[t * n_axes + a] and frequencies inv_freq[h_a + j],
+ *   j < dims[a]/2, h_a = o_a / 2 (inv_freq: f32, device, [span / 2]; each
+ *   axis may have its own base).  Entries span..D-1 are not touched.
+ *   dims: a HOST array of n_axes int64, each even and >= 0;
+ *   1 <= n_axes <= 8; span <= D and span <= 1024 (else ET_ERR_BAD_SIZE).
+ *   q: [T, Hq, D]; k: [T, Hk, D] (NULL with Hk == 0).  One axis of width r
+ *   gives the bits of et_rope_qk_* with d_rot = r.
+ */
+et_status et_rope_multi_f32(float* q, int64_t Hq, float* k, int64_t Hk,
+                            const int32_t* pos, int64_t T, int64_t D,
+                            int64_t n_axes, const int64_t* dims,
+                            const float* inv_freq, float attn_scaling,
+                            int layout, void* stream);
+et_status et_rope_multi_bf16(et_bf16* q, int64_t Hq, et_bf16* k, int64_t Hk,
+                             const int32_t* pos, int64_t T, int64_t D,
+                             int64_t n_axes, const int64_t* dims,
+                             const float* inv_freq, float attn_scaling,
+                             int layout, void* stream);
+
+/* ------------------------------------------------------------------------
  * Fused RMSNorm + RoPE on Q and K, in place  ([OPS] 5 QK-norm)
  *   Each (token, head) row of length D is normalised over all D entries
  *   with the gain gq [D] (query heads) or gk [D] (key heads) and eps, then

@@ -35,6 +35,7 @@ def test_header_declares_the_ops():
     assert "et_rope_cache_f32" in names
     for sfx in ("f32", "bf16"):
         assert f"et_rope_qk_cached_{sfx}" in names
+        assert f"et_rope_multi_{sfx}" in names
 
 
 def test_library_exports_every_declared_symbol():
@@ -158,6 +159,32 @@ def test_rope_cached_validation(sfx):
     assert f(A, 2, B, 2, C, 4, 8, 8, P(G + 64), E5, 16, 1.0, 0, S) == 4   # cos inside q
     assert f(A, 2, B, 2, C, 4, 8, 8, D, P(2 * G + 32), 16, 1.0, 0, S) == 4  # sin inside k
     assert f(NULL, 0, NULL, 0, NULL, 4, 8, 8, NULL, NULL, 0, 1.0, 0, S) == 0  # no heads
+
+
+@gpu_visible
+@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+def test_rope_multi_validation(sfx):
+    import elementwise_transformer_amd as et
+    f = getattr(et.lib, f"et_rope_multi_{sfx}")
+
+    def dims(*d):
+        return ctypes.cast((ctypes.c_int64 * len(d))(*d), P)
+
+    # q, Hq, k, Hk, pos, T, D, n_axes, dims (host), inv_freq, mu, layout, stream
+    assert f(A, 2, B, 2, C, 4, 16, 0, dims(4), D, 1.0, 0, S) == 3                 # no axes
+    assert f(A, 2, B, 2, C, 4, 16, 9, dims(*[2] * 9), D, 1.0, 0, S) == 3          # more than 8
+    assert f(A, 2, B, 2, C, 4, 16, 3, NULL, D, 1.0, 0, S) == 1                    # dims NULL
+    assert f(A, 2, B, 2, C, 4, 16, 3, dims(4, 5, 4), D, 1.0, 0, S) == 3           # odd width
+    assert f(A, 2, B, 2, C, 4, 16, 2, dims(4, -2), D, 1.0, 0, S) == 3             # negative width
+    assert f(A, 2, B, 2, C, 4, 16, 3, dims(8, 6, 4), D, 1.0, 0, S) == 3           # span > D
+    assert f(A, 2, B, 2, C, 4, 2048, 2, dims(1100, 900), D, 1.0, 0, S) == 2       # span > 1024
+    assert f(A, 2, B, 2, NULL, 4, 16, 3, dims(4, 6, 4), D, 1.0, 0, S) == 1        # pos NULL
+    assert f(A, 2, B, 2, C, 4, 16, 3, dims(4, 6, 4), NULL, 1.0, 0, S) == 1        # inv_freq NULL
+    assert f(A, 2, B, 2, C, 4, 16, 3, dims(4, 6, 4), D, 1.0, 3, S) == 3           # bad layout
+    assert f(A, 2, B, 2, C, 4, 16, 3, dims(4, 6, 4), D, float("nan"), 0, S) == 3  # attn_scaling
+    assert f(A, 2, B, 2, P(G + 64), 4, 16, 3, dims(4, 6, 4), D, 1.0, 0, S) == 4   # pos inside q
+    assert f(A, 2, P(G + 32), 2, C, 4, 16, 3, dims(4, 6, 4), D, 1.0, 0, S) == 4   # q and k overlap
+    assert f(NULL, 0, NULL, 0, NULL, 4, 16, 3, dims(4, 6, 4), NULL, 1.0, 0, S) == 0  # no heads
 
 
 @gpu_visible

@@ -22,7 +22,7 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 
 # Group ids (the second seed word).
-G_EMBED, G_ADD, G_RMSNORM, G_ADD_RMSNORM, G_ROPE, G_QKNORM, G_SILU, G_ARGMAX = range(8)
+G_EMBED, G_ADD, G_RMSNORM, G_ADD_RMSNORM, G_ROPE, G_QKNORM, G_SILU, G_ARGMAX, G_ROPE_MULTI = range(9)
 
 
 def rng(workload: int, group: int) -> np.random.Generator:
@@ -82,6 +82,26 @@ class RopeShape:
 
 
 @dataclass(frozen=True)
+class MultiRopeShape:
+    """Multi-axis RoPE over a latent video grid: one token per (frame, row,
+    column), frame-major; the position vector of a token is its grid index."""
+    frames: int
+    height: int
+    width: int
+    Hq: int
+    Hk: int
+    D: int
+    dims: Tuple[int, ...]      # per-axis widths (frame, row, column)
+    thetas: Tuple[float, ...]  # per-axis bases
+    layout: int
+    mu: float
+
+    @property
+    def T(self) -> int:
+        return self.frames * self.height * self.width
+
+
+@dataclass(frozen=True)
 class Workload:
     number: int
     name: str
@@ -94,6 +114,7 @@ class Workload:
     silu: Optional[Tuple[int, int, float]] = None          # (rows, cols, std)
     argmax: Optional[Tuple[int, int]] = None               # [rows, n]
     argmax_dtype: str = "f32"
+    rope_multi: Optional[MultiRopeShape] = None
     extra: Dict[str, object] = field(default_factory=dict)
 
 
@@ -123,6 +144,12 @@ WORKLOADS: Dict[int, Workload] = {
                 add_rmsnorm=(8192, 8192, 1e-5, True),
                 rope=RopeShape(8192, 64, 8, 128, 128, 0, 1e6, 1.0, "arange", 1e-5),
                 silu=(8192, 28672, 2.0)),
+    # Multi-axis (3D) RoPE of a video diffusion transformer, bf16: a latent
+    # grid of 16 frames x 30 x 40 (19,200 tokens), 24 query and 24 key heads
+    # of 128, axis widths 16 / 56 / 56, base 256 on every axis.
+    6: Workload(6, "video-dit-3d-rope-bf16-T19200", "bf16",
+                rope_multi=MultiRopeShape(16, 30, 40, 24, 24, 128, (16, 56, 56), (256.0, 256.0, 256.0),
+                                          0, 1.0)),
 }
 
 
@@ -186,6 +213,29 @@ def gen_rope(w: Workload):
     pos = positions(s.pos, s.T, g)
     return (store(q, w.dtype), None if k is None else store(k, w.dtype), pos,
             inv_freq(s.theta, s.r))
+
+
+def grid_positions(frames: int, height: int, width: int) -> np.ndarray:
+    """int32 [frames * height * width, 3]: (frame, row, column) of each token,
+    frame-major."""
+    f, h, c = np.meshgrid(np.arange(frames), np.arange(height), np.arange(width), indexing="ij")
+    return np.stack([f.ravel(), h.ravel(), c.ravel()], axis=1).astype(np.int32)
+
+
+def multi_inv_freq(dims, thetas) -> np.ndarray:
+    """Per-axis frequency tables w = theta_a^(-2j/d_a), j < d_a/2, concatenated."""
+    return np.concatenate([inv_freq(t, d) for d, t in zip(dims, thetas)]).astype(np.float32)
+
+
+def gen_rope_multi(w: Workload):
+    """Q, K, positions [T, 3], concatenated inv_freq for the multi-axis RoPE."""
+    s = w.rope_multi
+    g = rng(w.number, G_ROPE_MULTI)
+    q = normal(g, (s.T, s.Hq, s.D))
+    k = normal(g, (s.T, s.Hk, s.D)) if s.Hk else None
+    pos = grid_positions(s.frames, s.height, s.width)
+    return (store(q, w.dtype), None if k is None else store(k, w.dtype), pos,
+            multi_inv_freq(s.dims, s.thetas))
 
 
 def gen_qknorm(w: Workload):
