@@ -24,6 +24,9 @@
 //     lane); the sum of squares is per-lane then an xor butterfly over the G
 //     lanes -- fixed by D, so rows are batch-invariant.  Shapes without that
 //     vector layout use a one-wave-per-row kernel.
+#include <algorithm>
+#include <vector>
+
 #include "et_common.hpp"
 
 namespace et {
@@ -859,26 +862,33 @@ et_status rope_cache_entry(const float* inv_freq, int64_t max_pos, int64_t r, fl
 // vector, and each is rotated as a whole head of its own width, with its own
 // position and frequencies.  A sub-range's pairs may sit anywhere relative
 // to the 16-byte vectors (half widths need not be multiples of V), so a
-// workgroup stages its head rows in LDS and every element reads its partner
-// from there:
+// workgroup stages its head rows in LDS and every element of the half
+// pairing reads its partner from there (interleaved partners sit in the same
+// vector):
 //   * a workgroup owns rpb consecutive head rows (token-major: a token's q
 //     heads, then its k heads), loads their first span entries once, 16
 //     bytes at a time (scalars on the scalar path), and copies them to LDS;
-//   * a column table gives each of the span columns its partner column, its
-//     pair index and whether it is the pair's first member;
+//   * a descriptor per vector of a row: its elements form at most two runs
+//     (split where an axis or, for the half pairing, a half begins), and in a
+//     run the partner column and the pair index advance with the element,
+//     so a run is its first element's partner and pair, and its member flag;
 //   * an angle table holds (mu cos, mu sin) per (token, pair), built as the
 //     RoPE kernel builds its own.
 // Each element is then rotated exactly as the RoPE kernel rotates it, so a
 // single axis of width r gives that kernel's bits.  In place: a workgroup
 // reads all of its rows before the barrier and writes after it, each
-// element by the thread that loaded it.
+// element by the thread that loaded it.  The host takes the scalar path when
+// some vector would hold more than two runs (axes narrower than a vector).
 
 constexpr int kMaxAxes = 8;
-constexpr int kMultiU = 4;
+#ifndef ET_MULTI_U
+#define ET_MULTI_U 4
+#endif
+constexpr int kMultiU = ET_MULTI_U;
 constexpr int kMultiMaxSpan = 1024;
 
 struct MultiArgs {
-  RopeArgs ra;              // T, hq, hk, D and mu, as for the RoPE kernel
+  RopeArgs ra;              // T, hq, hk, D, layout and mu, as for the RoPE kernel
   int A;                    // axes
   int span;                 // rotated entries per head row (sum of the widths)
   int np;                   // pairs per head row (span / 2)
@@ -890,7 +900,7 @@ struct MultiArgs {
   int ntok_max;             // tokens one workgroup can touch
   int heads;                // hq + hk
   FastDiv fd_heads, fd_nv, fd_np;
-  uint32_t col_off, xs_off; // byte offsets of the column table and the rows in LDS
+  uint32_t d4_off, d1_off, xs_off;  // LDS byte offsets of the descriptors and the rows
 };
 
 // The axis a pair index i belongs to (zero-width axes are skipped: a later
@@ -903,9 +913,10 @@ __device__ inline int axis_of_pair(int i, const MultiArgs& a) {
   return ax;
 }
 
-// Column entry: partner column (bits 0-15), pair index (16-30), first
-// member of its pair (bit 31).
-__device__ inline uint32_t column_info(int c, const MultiArgs& a) {
+// Partner column, pair index and first-member flag of column c; *next is the
+// first column after c where the axis or (half pairing) the half changes.
+__device__ inline void column_of(int c, const MultiArgs& a, int* partner, int* pair, bool* first,
+                                 int* next) {
   int o = 0, w = a.off[1], h = 0;
 #pragma unroll
   for (int b = 1; b < kMaxAxes; ++b) {
@@ -916,20 +927,41 @@ __device__ inline uint32_t column_info(int c, const MultiArgs& a) {
     }
   }
   const int l = c - o;
-  int partner, j;
-  bool first;
   if (a.ra.layout == ET_ROPE_HALF) {
     const int hd = w / 2;
-    first = l < hd;
-    j = first ? l : l - hd;
-    partner = first ? c + hd : c - hd;
+    *first = l < hd;
+    *pair = h + (*first ? l : l - hd);
+    *partner = *first ? c + hd : c - hd;
+    *next = *first ? o + hd : o + w;
   } else {
-    first = (l & 1) == 0;  // sub-ranges start at even entries
-    j = l >> 1;
-    partner = c ^ 1;
+    *first = (l & 1) == 0;  // sub-ranges start at even entries
+    *pair = h + (l >> 1);
+    *partner = c ^ 1;
+    *next = o + w;
   }
-  return static_cast<uint32_t>(partner) | (static_cast<uint32_t>(h + j) << 16) |
-         (first ? 0x80000000u : 0u);
+}
+
+// Descriptor of vector cv (elements cv*PS .. cv*PS + PS-1): runs A = [0, k)
+// and B = [k, PS); element e of run X has partner column pX + e and pair
+// iX + e (half pairing) or iX + e/2 (interleaved).  d1 = k | fA << 8 | fB << 9.
+template <int PS>
+__device__ inline void vector_desc(int cv, const MultiArgs& a, int4* d4, int* d1) {
+  const int c0 = cv * PS;
+  int pa, ia, nx, pb, ib, nx2;
+  bool fa, fb;
+  column_of(c0, a, &pa, &ia, &fa, &nx);
+  int k = nx - c0;
+  if (k >= PS) k = PS;
+  if (k < PS) {
+    column_of(c0 + k, a, &pb, &ib, &fb, &nx2);
+  } else {
+    pb = pa + k;
+    ib = ia + (a.ra.layout == ET_ROPE_HALF ? k : k / 2);
+    fb = fa;
+  }
+  const bool half = a.ra.layout == ET_ROPE_HALF;
+  *d4 = make_int4(pa, pb - k, ia, half ? ib - k : ib - k / 2);
+  *d1 = k | (fa ? 0x100 : 0) | (fb ? 0x200 : 0);
 }
 
 template <typename S>
@@ -941,6 +973,57 @@ __device__ inline float lds_elem(const S* xs, int i) {
   }
 }
 
+#ifndef ET_MULTI_WIDE
+#define ET_MULTI_WIDE 1
+#endif
+
+// W consecutive entries of a staged row from column p (p a multiple of W).
+template <typename S, int W>
+__device__ inline void lds_run(const S* xr, int p, float (&o)[W]) {
+  if constexpr (W == 1) {
+    o[0] = lds_elem(xr, p);
+  } else if constexpr (sizeof(S) == 2) {
+    if constexpr (W == 4) {
+      const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(xr) + p);
+      o[0] = bf16_lo(w.x); o[1] = bf16_hi(w.x); o[2] = bf16_lo(w.y); o[3] = bf16_hi(w.y);
+    } else {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(xr) + p);
+      o[0] = bf16_lo(w); o[1] = bf16_hi(w);
+    }
+  } else {
+    if constexpr (W == 4) {
+      const float4 w = *reinterpret_cast<const float4*>(xr + p);
+      o[0] = w.x; o[1] = w.y; o[2] = w.z; o[3] = w.w;
+    } else {
+      const float2 w = *reinterpret_cast<const float2*>(xr + p);
+      o[0] = w.x; o[1] = w.y;
+    }
+  }
+}
+
+// Half pairing (or the scalar path): element e of the vector belongs to run
+// A (e < kr) or B; its partner is read from the staged row, its angle from
+// the table, and it is rotated as the RoPE kernel's rotate() rotates it.
+template <typename S, int PS, int W>
+__device__ inline void rotate_runs(const S* xr, const float (&x)[PS], float (&y)[PS], int4 d, int d1,
+                                   int kr, const float2* tab) {
+#pragma unroll
+  for (int e0 = 0; e0 < PS; e0 += W) {
+    const bool in_a = e0 < kr;  // the W entries share a run (kr is a multiple of W)
+    float xp[W];
+    lds_run<S, W>(xr, (in_a ? d.x : d.y) + e0, xp);
+    const float2* tr = tab + (in_a ? d.z : d.w) + e0;
+    const bool first = (d1 & (in_a ? 0x100 : 0x200)) != 0;
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      const float2 c = tr[j];
+      const float y0 = __builtin_fmaf(x[e0 + j], c.x, -(xp[j] * c.y));
+      const float y1 = __builtin_fmaf(xp[j], c.y, x[e0 + j] * c.x);
+      y[e0 + j] = first ? y0 : y1;
+    }
+  }
+}
+
 template <typename S, int PS, int U, int POL>
 __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
                                                            const int32_t* __restrict__ pos,
@@ -949,7 +1032,8 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
   using E = Elem<S>;
   extern __shared__ __align__(16) unsigned char smem[];
   float2* cs = reinterpret_cast<float2*>(smem);
-  uint32_t* col = reinterpret_cast<uint32_t*>(smem + a.col_off);
+  int4* d4s = reinterpret_cast<int4*>(smem + a.d4_off);
+  int* d1s = reinterpret_cast<int*>(smem + a.d1_off);
   S* xs = reinterpret_cast<S*>(smem + a.xs_off);
 
   const uint32_t row0 = blockIdx.x * static_cast<uint32_t>(a.rpb);
@@ -1003,7 +1087,7 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
   __builtin_amdgcn_sched_barrier(0);
 #endif
 
-  // Phase 2: angle table, column table, rows to LDS.
+  // Phase 2: angle table, vector descriptors, rows to LDS.
 #pragma unroll
   for (int kk = 0; kk < kTabPre; ++kk) {
     const int idx = threadIdx.x + kk * kBlock;
@@ -1021,14 +1105,19 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
                             inv_freq[i]), &sn, &cn);
     cs[idx] = make_float2(a.ra.mu * cn, a.ra.mu * sn);
   }
-  for (int c = threadIdx.x; c < a.span; c += kBlock) col[c] = column_info(c, a);
+  for (int c = threadIdx.x; c < a.nv; c += kBlock) vector_desc<PS>(c, a, &d4s[c], &d1s[c]);
+  // Partners come from LDS for the half pairing, and on the scalar path for
+  // both; interleaved partners of a vector sit in the vector itself.
+  const bool via_lds = PS == 1 || a.ra.layout == ET_ROPE_HALF;
+  if (via_lds) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int s = static_cast<int>(rope_slot<U>(0, threadIdx.x, u));
-    if (s >= nslot) continue;
-    S* dst = xs + sl[u] * a.span + cv[u] * PS;
-    if constexpr (PS == 1) E::st(dst, 0, sv[u]);
-    else *reinterpret_cast<u32x4*>(dst) = v[u];
+    for (int u = 0; u < U; ++u) {
+      const int s = static_cast<int>(rope_slot<U>(0, threadIdx.x, u));
+      if (s >= nslot) continue;
+      S* dst = xs + sl[u] * a.span + cv[u] * PS;
+      if constexpr (PS == 1) E::st(dst, 0, sv[u]);
+      else *reinterpret_cast<u32x4*>(dst) = v[u];
+    }
   }
   __syncthreads();
 
@@ -1037,16 +1126,34 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
   for (int u = 0; u < U; ++u) {
     const int s = static_cast<int>(rope_slot<U>(0, threadIdx.x, u));
     if (s >= nslot) continue;
-    const S* xr = xs + sl[u] * a.span;
+    const int4 d = d4s[cv[u]];
+    const int d1 = d1s[cv[u]];
+    const int kr = d1 & 0xFF;
     const float2* tab = cs + tl[u] * a.np;
-    float y[PS];
+    float x[PS], y[PS];
 #pragma unroll
-    for (int e = 0; e < PS; ++e) {
-      const float x = PS == 1 ? sv[u] : E::get(v[u], e);
-      const uint32_t info = col[cv[u] * PS + e];
-      const float xp = lds_elem(xr, static_cast<int>(info & 0xFFFFu));
-      const float2 c = tab[(info >> 16) & 0x7FFFu];
-      y[e] = (info >> 31) ? __builtin_fmaf(x, c.x, -(xp * c.y)) : __builtin_fmaf(xp, c.y, x * c.x);
+    for (int e = 0; e < PS; ++e) x[e] = PS == 1 ? sv[u] : E::get(v[u], e);
+    if (via_lds) {
+      const S* xr = xs + sl[u] * a.span;
+      // Partners are read W entries at a time when both runs' partner
+      // columns and the split are multiples of W (the usual case: half
+      // widths even), else one entry at a time.
+      const int al = kr | d.x | d.y;
+      if (PS >= 4 && ET_MULTI_WIDE && (al & 3) == 0) {
+        rotate_runs<S, PS, (PS >= 4 ? 4 : 1)>(xr, x, y, d, d1, kr, tab);
+      } else if (PS >= 2 && ET_MULTI_WIDE && (al & 1) == 0) {
+        rotate_runs<S, PS, (PS >= 2 ? 2 : 1)>(xr, x, y, d, d1, kr, tab);
+      } else {
+        rotate_runs<S, PS, 1>(xr, x, y, d, d1, kr, tab);
+      }
+    } else if constexpr (PS > 1) {
+      // Interleaved pairs (e, e + 1) lie inside the vector.
+#pragma unroll
+      for (int e = 0; e < PS; e += 2) {
+        const float2 c = tab[(e < kr ? d.z : d.w) + e / 2];
+        y[e] = __builtin_fmaf(x[e], c.x, -(x[e + 1] * c.y));
+        y[e + 1] = __builtin_fmaf(x[e], c.y, x[e + 1] * c.x);
+      }
     }
     if constexpr (PS == 1) {
       E::st(rowp[u], cv[u], y[0]);
@@ -1056,14 +1163,35 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
   }
 }
 
-// LDS bytes of a workgroup of rpb rows: angle table, column table, rows.
+// LDS bytes of a workgroup of rpb rows: angle table, descriptors, rows.
 inline void multi_lds(MultiArgs& a, int es, size_t* bytes) {
   a.ntok_max = (a.rpb + a.heads - 1) / a.heads + 1;
   if (a.ntok_max > a.rpb) a.ntok_max = a.rpb;
   const uint32_t tab = static_cast<uint32_t>(a.ntok_max) * a.np * sizeof(float2);
-  a.col_off = (tab + 15u) & ~15u;
-  a.xs_off = (a.col_off + static_cast<uint32_t>(a.span) * 4u + 15u) & ~15u;
+  a.d4_off = (tab + 15u) & ~15u;
+  a.d1_off = a.d4_off + static_cast<uint32_t>(a.nv) * 16u;
+  a.xs_off = (a.d1_off + static_cast<uint32_t>(a.nv) * 4u + 15u) & ~15u;
   *bytes = a.xs_off + static_cast<size_t>(a.rpb) * a.span * es;
+}
+
+// Whether every vector of ps entries holds at most two runs: at most one
+// place inside it where an axis or (half pairing) a half begins.
+inline bool runs_fit(const int64_t* dims, int64_t A, int layout, int ps) {
+  std::vector<int64_t> b;
+  int64_t o = 0;
+  for (int64_t ax = 0; ax < A; ++ax) {
+    b.push_back(o);
+    if (layout == ET_ROPE_HALF) b.push_back(o + dims[ax] / 2);
+    o += dims[ax];
+  }
+  std::sort(b.begin(), b.end());
+  b.erase(std::unique(b.begin(), b.end()), b.end());
+  for (int64_t c0 = 0; c0 < o; c0 += ps) {
+    int inside = 0;
+    for (int64_t x : b) inside += (x > c0 && x < c0 + ps) ? 1 : 0;
+    if (inside > 1) return false;
+  }
+  return true;
 }
 
 template <typename S, int PS, int POL>
@@ -1102,7 +1230,8 @@ et_status rope_multi_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* po
   if (T == 0 || hq + hk == 0 || span == 0) return ET_OK;
 
   constexpr int V = Elem<S>::V;
-  const bool vec = span % V == 0 && D % V == 0 && aligned16(q) && (hk == 0 || aligned16(k));
+  const bool vec = span % V == 0 && D % V == 0 && aligned16(q) && (hk == 0 || aligned16(k)) &&
+                   runs_fit(dims, A, layout, V);
   const int ps = vec ? V : 1;
   MultiArgs a{};
   a.ra.hq = static_cast<int>(hq);
