@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 
 CFLAGS = ["-std=c11", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
           "-fPIC", "-shared", "-Wall", "-Wextra"]
@@ -40,7 +40,9 @@ def _dt(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError(f"oracle storage must be float32 or uint16 (bf16 bits), got {a.dtype}")
+    if a.dtype == np.float16:
+        return F16
+    raise TypeError(f"oracle storage must be float32, uint16 (bf16 bits) or float16, got {a.dtype}")
 
 
 def _p(a: Optional[np.ndarray]):
@@ -64,6 +66,9 @@ class Oracle:
         lib.orc_get_threads.restype = _int
         lib.orc_bf16_from_f64.argtypes = [ctypes.c_double]
         lib.orc_bf16_from_f64.restype = ctypes.c_uint16
+        lib.orc_f16_from_f64.argtypes = [ctypes.c_double]
+        lib.orc_f16_from_f64.restype = ctypes.c_uint16
+        lib.orc_round_to.argtypes = [_int, _vp, _i64, _vp]
         lib.orc_rope_angle.argtypes = [ctypes.c_int32, _f32]
         lib.orc_rope_angle.restype = _f32
         lib.orc_rmsnorm.argtypes = [_int, _vp, _vp, _i64, _i64, _f32, _vp, _vp]
@@ -97,6 +102,17 @@ class Oracle:
 
     def bf16_from_f64(self, v: float) -> int:
         return int(self.lib.orc_bf16_from_f64(float(v)))
+
+    def f16_from_f64(self, v: float) -> int:
+        return int(self.lib.orc_f16_from_f64(float(v)))
+
+    def round_to(self, v: np.ndarray, dtype: str) -> np.ndarray:
+        """The storage rounding every op applies: f64 values -> "f32" (float32),
+        "bf16" (uint16 bits) or "f16" (float16)."""
+        v = np.ascontiguousarray(v, dtype=np.float64)
+        out = np.empty(v.shape, {"f32": np.float32, "bf16": np.uint16, "f16": np.float16}[dtype])
+        self.lib.orc_round_to({"f32": F32, "bf16": BF16, "f16": F16}[dtype], _p(v), v.size, _p(out))
+        return out
 
     def rope_angle(self, p: int, w: float) -> np.float32:
         return np.float32(self.lib.orc_rope_angle(int(p), float(w)))

@@ -22,6 +22,8 @@
  *          2.4 Embedding, add, argmax; 4 The interface.
  *   [DNN]  "ruDNN User Guide": 7 LayerNorm, RMSNorm, and Softmax.
  *
+ * Storage: f32, bf16 or IEEE f16 ([OPS] gives F16 tolerances).
+ *
  * Arithmetic: every input is widened exactly to f64; all math is IEEE f64
  * with libm sqrt/exp/sin/cos; every stored output is rounded once (RNE),
  * straight from f64 to the storage type.  Build with
@@ -61,7 +63,22 @@ int orc_get_threads(void) {
 
 /* ---------------------------------------------------------------- storage */
 
-/* Widen element i of a dt-typed array to f64 (exact for f32 and bf16). */
+/* IEEE binary16 bits to f64, exactly: sign, 5-bit biased exponent (bias
+ * 15), 10-bit fraction; exponent 0 holds the subnormals f * 2^-24, exponent
+ * 31 infinity (f = 0) and NaN. */
+static double f16_to_f64(uint16_t h) {
+    const int sgn = h >> 15, ex = (h >> 10) & 0x1F, fr = h & 0x3FF;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)fr, -24);
+    else if (ex == 31)
+        v = fr ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + fr), ex - 25);
+    return sgn ? -v : v;
+}
+
+/* Widen element i of a dt-typed array to f64 (exact for all three types). */
 static double ld(int dt, const void* p, int64_t i) {
     if (dt == ORC_BF16) {
         uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
@@ -69,6 +86,7 @@ static double ld(int dt, const void* p, int64_t i) {
         memcpy(&f, &u, sizeof f);
         return (double)f;
     }
+    if (dt == ORC_F16) return f16_to_f64(((const uint16_t*)p)[i]);
     return (double)((const float*)p)[i];
 }
 
@@ -92,18 +110,53 @@ uint16_t orc_bf16_from_f64(double v) {
     return (uint16_t)(u >> 16);
 }
 
+/* Round-to-nearest-even from f64 straight to IEEE binary16 (11 significant
+ * bits, normal exponents -14..15).  A value in binade e is rounded to a
+ * multiple of 2^(e-10); below 2^-14 the spacing stays 2^-24 (subnormals).
+ * A result of 2^16 or more (|v| >= 65520, halfway past the largest finite
+ * 65504, rounds up) is infinite. */
+uint16_t orc_f16_from_f64(double v) {
+    if (isnan(v)) return signbit(v) ? 0xFE00u : 0x7E00u;
+    const uint16_t sign = signbit(v) ? 0x8000u : 0x0000u;
+    const double a = fabs(v);
+    if (isinf(a)) return sign | 0x7C00u;
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                 /* a = m * 2^e with 0.5 <= m < 1 */
+    int binade = e - 1;
+    if (binade < -14) binade = -14;
+    const double q = ldexp(1.0, binade - 10);
+    const double r = nearbyint(a / q) * q;   /* ties to even (default mode) */
+    if (r >= 65536.0) return sign | 0x7C00u;
+    if (r < ldexp(1.0, -14))                 /* subnormal: r = k * 2^-24, k < 1024 */
+        return sign | (uint16_t)ldexp(r, 24);
+    frexp(r, &e);
+    const int ex = e - 1;                    /* binade of the rounded value */
+    const int fr = (int)(ldexp(r, 10 - ex) - 1024.0);
+    return sign | (uint16_t)(((ex + 15) << 10) | fr);
+}
+
 /* Store v into element i, rounded once to the storage type. */
 static void st(int dt, void* p, int64_t i, double v) {
     if (dt == ORC_BF16)
         ((uint16_t*)p)[i] = orc_bf16_from_f64(v);
+    else if (dt == ORC_F16)
+        ((uint16_t*)p)[i] = orc_f16_from_f64(v);
     else
         ((float*)p)[i] = (float)v;           /* C conversion: RNE */
+}
+
+/* The storage rounding of n values, exported for the tests. */
+void orc_round_to(int dt, const double* v, int64_t n, void* out) {
+    for (int64_t i = 0; i < n; ++i) st(dt, out, i, v[i]);
 }
 
 /* Quiet NaN in the storage type (the row an out-of-range id produces). */
 static void st_nan(int dt, void* p, int64_t i) {
     if (dt == ORC_BF16) {
         ((uint16_t*)p)[i] = 0x7FC0u;
+    } else if (dt == ORC_F16) {
+        ((uint16_t*)p)[i] = 0x7E00u;
     } else {
         const uint32_t u = 0x7FC00000u;
         memcpy((float*)p + i, &u, sizeof u);
@@ -294,7 +347,7 @@ void orc_add(int dt, const void* a, const void* b, int64_t n, void* y) {
  * a row of quiet NaN (the kernels' documented behaviour for bad ids). */
 void orc_embedding(int dt, const void* table, int64_t V, const int32_t* ids,
                    int64_t n, int64_t d, void* out) {
-    const size_t es = (dt == ORC_BF16) ? 2 : 4;
+    const size_t es = (dt == ORC_F32) ? 4 : 2;
 #pragma omp parallel for schedule(static)
     for (int64_t t = 0; t < n; ++t) {
         char* dst = (char*)out + (size_t)t * (size_t)d * es;

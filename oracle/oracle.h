@@ -6,8 +6,9 @@
  * of the benchmark do.  It shares no source with the HIP kernels.
  *
  * Conventions
- *   dt      storage type of every tensor argument: ORC_F32 (float) or
- *           ORC_BF16 (uint16_t holding bfloat16 bits).
+ *   dt      storage type of every tensor argument: ORC_F32 (float),
+ *           ORC_BF16 (uint16_t holding bfloat16 bits) or ORC_F16 (uint16_t
+ *           holding IEEE binary16 bits).
  *   y64     optional (may be NULL) f64 buffer receiving the unrounded result
  *           of each output element; tolerance checks use it.
  *   All arithmetic is IEEE f64 (libm sqrt/exp/sin/cos); inputs are widened
@@ -21,7 +22,7 @@
 extern "C" {
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_F16 = 2 };
 
 /* Threads used by the row/element loops (OpenMP); <= 0 leaves the default. */
 void     orc_set_threads(int n);
@@ -29,6 +30,10 @@ int      orc_get_threads(void);
 
 /* f64 -> bfloat16 bits, one round-to-nearest-even (no pass through f32). */
 uint16_t orc_bf16_from_f64(double v);
+/* f64 -> IEEE binary16 bits, one round-to-nearest-even. */
+uint16_t orc_f16_from_f64(double v);
+/* The storage rounding (as every op stores) of n f64 values into out. */
+void     orc_round_to(int dt, const double* v, int64_t n, void* out);
 /* The RoPE angle of position p and frequency w: the f64 product rounded once
  * to f32. */
 float    orc_rope_angle(int32_t p, float w);

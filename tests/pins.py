@@ -722,6 +722,108 @@ def pin_rope_multi_axes_decompose(orc):
         assert np.array_equal(z64[..., :36], 0.75 * x[..., :36].astype(np.float64))
 
 
+# ------------------------------------------------------------ f16 storage
+
+def _f16_all_finite():
+    """Every non-negative finite binary16 value: bits and exact f64 values
+    (numpy widens float16 exactly)."""
+    bits = np.arange(0x7C00, dtype=np.uint16)
+    return bits, bits.view(np.float16).astype(np.float64)
+
+
+def pin_f16_rounding_exhaustive(orc):
+    """[OPS] F16 storage: f64 -> binary16 rounds to nearest, ties to even,
+    once.  Over every finite value: exact values map to themselves; the
+    midpoint of each pair of neighbours goes to the one with an even
+    significand, the doubles just below and above it to the lower and upper
+    neighbour; 65520 (halfway past 65504) and above overflow to infinity;
+    negatives mirror; NaN and infinity keep their class.  Then the library's
+    float64 -> float16 cast (numpy) on values across the whole range."""
+    bits, v = _f16_all_finite()
+    assert np.array_equal(orc.round_to(v, "f16").view(np.uint16), bits)
+    assert np.array_equal(orc.round_to(-v, "f16").view(np.uint16), bits | 0x8000)
+    lo, hi = v[:-1], v[1:]
+    mid = (lo + hi) / 2                                   # exact in f64
+    even = np.where(bits[:-1] % 2 == 0, bits[:-1], bits[1:])
+    assert np.array_equal(orc.round_to(mid, "f16").view(np.uint16), even)
+    assert np.array_equal(orc.round_to(np.nextafter(mid, 0), "f16").view(np.uint16), bits[:-1])
+    assert np.array_equal(orc.round_to(np.nextafter(mid, np.inf), "f16").view(np.uint16), bits[1:])
+    top = orc.round_to(np.array([65519.999, 65520.0, 1e6, np.inf, -65520.0, -np.inf]), "f16")
+    assert top.view(np.uint16).tolist() == [0x7BFF, 0x7C00, 0x7C00, 0x7C00, 0xFC00, 0xFC00]
+    tiny = orc.round_to(np.array([2.0 ** -25, np.nextafter(2.0 ** -25, 1), 2.0 ** -26, -2.0 ** -25]), "f16")
+    assert tiny.view(np.uint16).tolist() == [0x0000, 0x0001, 0x0000, 0x8000]
+    n = orc.round_to(np.array([np.nan, -np.nan]), "f16").view(np.uint16)
+    assert np.all((n & 0x7C00) == 0x7C00) and np.all((n & 0x03FF) != 0)
+    g = np.random.default_rng(505)
+    r = g.standard_normal(200000) * np.exp(g.uniform(-21, 12, 200000))
+    with np.errstate(over="ignore"):
+        ref = r.astype(np.float16)
+    assert np.array_equal(orc.round_to(r, "f16").view(np.uint16), ref.view(np.uint16))
+
+
+def pin_f16_storage_through_ops(orc):
+    """Every op reads f16 storage exactly and rounds each result once: adding
+    -0 returns every finite value, infinity and NaN as given; on f16
+    inputs each op's f64 result equals its result on the same values held in
+    f32 storage, and the stored output is that f64 result rounded by the
+    library's float16 cast; the embedding copies bits; argmax picks the same
+    index as on the f32 copy."""
+    bits, v = _f16_all_finite()
+    x = np.concatenate([bits, bits | 0x8000, [0x7C00, 0xFC00, 0x7E00]]).astype(np.uint16).view(np.float16)
+    y = orc.add(x, np.full_like(x, -0.0))                  # x + (-0) == x for every x, signed zeros too
+    assert np.array_equal(y.view(np.uint16)[:-1], x.view(np.uint16)[:-1])
+    assert np.isnan(y[-1])
+    g = np.random.default_rng(506)
+
+    def h(shape, scale=1.0):
+        return (g.standard_normal(shape) * scale).astype(np.float16)
+
+    def same(out16, y16, y32, what):
+        assert np.array_equal(y16, y32, equal_nan=True), f"{what}: f64 results differ"
+        with np.errstate(over="ignore", invalid="ignore"):
+            ref = y16.astype(np.float16)
+        assert np.array_equal(out16.view(np.uint16), ref.view(np.uint16)), f"{what}: rounding"
+
+    x16, w16, b16 = h((5, 96), 3), (g.uniform(0.5, 1.5, 96)).astype(np.float16), h(96)
+    x16[0, :4] = [3e-6, -6e-8, 0, 6e4]                     # f16 subnormals and a large value
+    f32 = lambda a: a.astype(np.float32)
+    o, y1 = orc.rmsnorm(x16, w16, 1e-5)
+    _, y2 = orc.rmsnorm(f32(x16), f32(w16), 1e-5)
+    same(o, y1, y2, "rmsnorm")
+    o, y1 = orc.layernorm(x16, w16, b16, 1e-5)
+    _, y2 = orc.layernorm(f32(x16), f32(w16), f32(b16), 1e-5)
+    same(o, y1, y2, "layernorm")
+    o, y1 = orc.softmax(x16, 0.7)
+    _, y2 = orc.softmax(f32(x16), 0.7)
+    same(o, y1, y2, "softmax")
+    u16 = h((5, 96))
+    o, y1 = orc.silu_mul(x16, u16)
+    _, y2 = orc.silu_mul(f32(x16), f32(u16))
+    same(o, y1, y2, "silu_mul")
+    for form in (0, 1):
+        o, y1 = orc.geglu(x16, u16, form)
+        _, y2 = orc.geglu(f32(x16), f32(u16), form)
+        same(o, y1, y2, f"geglu {form}")
+    q16 = h((4, 3, 32))
+    pos = np.array([0, 5, 100, 4095], np.int32)
+    inv = np.power(1e4, -2.0 * np.arange(16) / 32).astype(np.float32)
+    for layout in (0, 1):
+        o, y1 = orc.rope(q16, pos, 32, inv, 1.0, layout)
+        _, y2 = orc.rope(f32(q16), pos, 32, inv, 1.0, layout)
+        same(o, y1, y2, f"rope {layout}")
+        o, y1 = orc.rope_multi(q16, np.stack([pos, pos + 1], 1), [16, 12], inv[:14], 1.0, layout)
+        _, y2 = orc.rope_multi(f32(q16), np.stack([pos, pos + 1], 1), [16, 12], inv[:14], 1.0, layout)
+        same(o, y1, y2, f"rope_multi {layout}")
+    tab = h((50, 40))
+    ids = np.array([3, 49, 0, 7, 50, -1], np.int32)
+    e = orc.embedding(tab, ids)
+    assert np.array_equal(e[:4].view(np.uint16), tab[ids[:4]].view(np.uint16))
+    assert np.all(np.isnan(e[4:].astype(np.float32)))
+    lg = h((6, 300), 3)
+    lg[2, 7] = np.nan
+    assert np.array_equal(orc.argmax(lg), orc.argmax(f32(lg)))
+
+
 # -------------------------------------------------------------- LayerNorm
 
 def pin_layernorm_closed_forms(orc):

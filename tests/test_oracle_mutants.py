@@ -4,10 +4,10 @@ Each mutant is a copy of ``oracle/oracle.c`` with one plausible mistake
 planted by text substitution, built into a temporary library.  The pins must
 fail on every mutant.  s01-s15 are the mistakes listed in the Pitfalls table
 (section 5) of "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding,
-add, argmax", each with the test the page says catches it; x01-x34 are further
+add, argmax", each with the test the page says catches it; x01-x40 are further
 slips (a wrong sign, index, dropped term or rounding) in the same code, x11-x16
 in the softmax, x17-x20 in LayerNorm, x21-x25 in the GELU-gated multiply, x26-x29
-in the RoPE cache, x30-x34 in multi-axis RoPE.
+in the RoPE cache, x30-x34 in multi-axis RoPE, x35-x40 in the f16 storage.
 """
 import os
 import tempfile
@@ -117,6 +117,18 @@ MUTANTS = {
                                        "rope_pair(layout, dims[0], j, &ia, &ib);")]),
     "x34_multi_rotation_sign": ("rope_multi_axes_decompose",
                                 [("w[ib] = mu * (x1 * sa + x2 * ca);", "w[ib] = mu * (x2 * ca - x1 * sa);")]),
+    "x35_f16_truncates": ("f16_rounding_exhaustive",
+                          [("const double r = nearbyint(a / q) * q;", "const double r = floor(a / q) * q;")]),
+    "x36_f16_subnormal_spacing": ("f16_rounding_exhaustive",
+                                  [("if (binade < -14) binade = -14;", "if (binade < -15) binade = -15;")]),
+    "x37_f16_read_without_subnormals": ("f16_storage_through_ops",
+                                        [("v = ldexp((double)fr, -24);", "v = ldexp((double)(1024 + fr), -25);")]),
+    "x38_f16_read_bias": ("f16_storage_through_ops",
+                          [("v = ldexp((double)(1024 + fr), ex - 25);", "v = ldexp((double)(1024 + fr), ex - 24);")]),
+    "x39_f16_nan_read_as_inf": ("f16_storage_through_ops",
+                                [("v = fr ? NAN : INFINITY;", "v = INFINITY;")]),
+    "x40_f16_stored_as_bf16": ("f16_rounding_exhaustive",
+                               [("((uint16_t*)p)[i] = orc_f16_from_f64(v);", "((uint16_t*)p)[i] = orc_bf16_from_f64(v);")]),
     "x25_gelu_tanh_no_f32_limit": ("gelu_symmetry_and_limits",
                                    [("if (e > FLT_MAX) e = INFINITY;  /* the f32", "/* the f32")]),
 }
