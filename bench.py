@@ -120,7 +120,7 @@ def build_ops(w, et, torch):
     import workloads as wl
     from_np = lambda a: (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
                          if a.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(a))).cuda()
-    es = 2 if w.dtype == "bf16" else 4
+    es = 4 if w.dtype == "f32" else 2
     ops = []
     if w.embed:
         V, d, n, _ = w.embed
@@ -243,6 +243,8 @@ def time_next_ops(et, torch, wl, stream, sets=3, launches=60):
                 cache [4096, 64] f32 built by the library
       rope_multi  3D RoPE of a video DiT: q and k [19200, 24, 128] bf16 over a
                 16 x 30 x 40 latent grid, axis widths 16 / 56 / 56
+      f16_step  the whole prefill step (every op of it, same shapes and
+                inputs) with f16 storage, one event pair per step
     Algorithmic bytes: each input read once, each output written once."""
     out = {}
 
@@ -319,6 +321,14 @@ def time_next_ops(et, torch, wl, stream, sets=3, launches=60):
     span = sum(m.dims)
     record("rope_multi", "video DiT 3D RoPE q,k [19200,24,128] bf16, grid 16x30x40, widths 16/56/56",
            2 * m.T * (m.Hq + m.Hk) * span * 2 + 4 * 3 * m.T + 4 * (span // 2), t, "rope_multi_kernel")
+    del qs, ks
+
+    import dataclasses
+    wf = dataclasses.replace(wl.WORKLOADS[2], dtype="f16")
+    ops = build_ops(wf, et, torch)
+    t = _time_launches(stream, lambda i: [op.fn() for op in ops], 1, 40)
+    record("f16_step", "the prefill step of llama3-8b-prefill-T4096 with f16 storage",
+           sum(op.nbytes for op in ops), t, "the step's eight kernels, f16 instances")
     return out
 
 

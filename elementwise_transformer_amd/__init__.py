@@ -2,12 +2,12 @@
 
 A thin ctypes binding over ``libet.so`` (C ABI in ``include/et.h``).  Every
 function here only checks tensor placement, derives sizes and pointers, and
-calls the matching ``et_*_f32`` / ``et_*_bf16`` entry point on the current
-torch stream; all arithmetic runs in the library's HIP kernels.  There is no
+calls the matching ``et_*_f32`` / ``et_*_bf16`` / ``et_*_f16`` entry point on
+the current torch stream; all arithmetic runs in the library's HIP kernels.  There is no
 other implementation: if the library is missing, importing this package
 raises.
 
-Tensors must be CUDA (ROCm) tensors, contiguous, float32 or bfloat16.
+Tensors must be CUDA (ROCm) tensors, contiguous, float32, bfloat16 or float16.
 """
 from __future__ import annotations
 
@@ -65,7 +65,7 @@ _SIGS = {
     "rope_multi": [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp, _f32, _int, _vp],
 }
 for _op, _args in _SIGS.items():
-    for _sfx in ("f32", "bf16"):
+    for _sfx in ("f32", "bf16", "f16"):
         _f = getattr(lib, f"et_{_op}_{_sfx}")
         _f.argtypes = _args
         _f.restype = ctypes.c_int
@@ -94,7 +94,9 @@ def _sfx(t: torch.Tensor) -> str:
         return "f32"
     if t.dtype == torch.bfloat16:
         return "bf16"
-    raise TypeError(f"expected float32 or bfloat16, got {t.dtype}")
+    if t.dtype == torch.float16:
+        return "f16"
+    raise TypeError(f"expected float32, bfloat16 or float16, got {t.dtype}")
 
 
 def _dev(*ts: Optional[torch.Tensor]) -> None:

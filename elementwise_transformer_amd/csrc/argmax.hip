@@ -310,6 +310,7 @@ et_status argmax_entry(const S* x, int64_t rows, int64_t n, int32_t* out, void* 
 }  // namespace et
 
 using et::Bf16;
+using et::F16;
 
 extern "C" {
 
@@ -337,6 +338,12 @@ et_status et_argmax_f32(const float* x, int64_t rows, int64_t n, int32_t* out, v
 et_status et_argmax_bf16(const et_bf16* x, int64_t rows, int64_t n, int32_t* out, void* workspace,
                          size_t workspace_bytes, void* stream) {
   return et::argmax_entry<Bf16>(reinterpret_cast<const Bf16*>(x), rows, n, out, workspace,
+                                workspace_bytes, stream);
+}
+
+et_status et_argmax_f16(const et_f16* x, int64_t rows, int64_t n, int32_t* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return et::argmax_entry<F16>(reinterpret_cast<const F16*>(x), rows, n, out, workspace,
                                 workspace_bytes, stream);
 }
 

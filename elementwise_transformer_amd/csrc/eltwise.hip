@@ -49,11 +49,12 @@ __device__ inline int64_t slot_index(int64_t b, int tid, int u) {
 enum Op { kAdd = 0, kSiluMul = 1, kGeluErfMul = 2, kGeluTanhMul = 3 };
 
 // silu(g) = g / (1 + e^-g).  f32 storage: library expf and IEEE division.
-// bf16 storage: the f32 value only has to be within ~1e-5 relative before the
-// final rounding to 8 significant bits, so the hardware exp2 and reciprocal
-// (quarter-rate transcendental instructions) replace the library calls -- at
-// bf16 the op moves 6 bytes per element and the accurate sequence would make
-// it ALU-bound.  The reciprocal flushes denormal results, so a 1 + e^-g above
+// 2-byte storage (bf16, f16): the f32 value only has to be within ~1e-5
+// relative before the final rounding to 8 or 11 significant bits, so the
+// hardware exp2 and reciprocal (quarter-rate transcendental instructions,
+// about 1 ulp of f32 each) replace the library calls -- at 2 bytes the op
+// moves 6 bytes per element and the accurate sequence would make it
+// ALU-bound.  The reciprocal flushes denormal results, so a 1 + e^-g above
 // 2^64 is scaled by 2^-64 together with g (both exact); e^-g overflowing to
 // +inf still gives g * 0 = -0 for very negative g.
 template <typename S>
@@ -102,7 +103,7 @@ __device__ inline float gelu_erf(float x) {
 // GELU, tanh form: (1 + tanh u) / 2 = 1 / (1 + e^(-2u)) with
 // u = sqrt(2/pi) (x + 0.044715 x^3), so it is x / (1 + e^(-2u)) -- the SiLU
 // shape, computed the same way (library expf and IEEE division in f32; the
-// hardware exp2 and reciprocal with the 2^-64 rescale for bf16).
+// hardware exp2 and reciprocal with the 2^-64 rescale for 2-byte storage).
 template <typename S>
 __device__ inline float gelu_tanh(float x) {
   const float u2 = -1.59576912160573071176f * __builtin_fmaf(0.044715f * x, x * x, x);  // -2u
@@ -231,6 +232,7 @@ et_status eltwise_entry(const S* a, const S* b, S* y, int64_t n, void* stream) {
 }  // namespace et
 
 using et::Bf16;
+using et::F16;
 
 extern "C" {
 
@@ -244,6 +246,12 @@ et_status et_add_bf16(const et_bf16* a, const et_bf16* b, et_bf16* y, int64_t n,
                                            reinterpret_cast<Bf16*>(y), n, stream);
 }
 
+et_status et_add_f16(const et_f16* a, const et_f16* b, et_f16* y, int64_t n, void* stream) {
+  return et::eltwise_entry<F16, et::kAdd>(reinterpret_cast<const F16*>(a),
+                                           reinterpret_cast<const F16*>(b),
+                                           reinterpret_cast<F16*>(y), n, stream);
+}
+
 et_status et_silu_mul_f32(const float* gate, const float* up, float* y, int64_t n, void* stream) {
   return et::eltwise_entry<float, et::kSiluMul>(gate, up, y, n, stream);
 }
@@ -253,6 +261,13 @@ et_status et_silu_mul_bf16(const et_bf16* gate, const et_bf16* up, et_bf16* y, i
   return et::eltwise_entry<Bf16, et::kSiluMul>(reinterpret_cast<const Bf16*>(gate),
                                                reinterpret_cast<const Bf16*>(up),
                                                reinterpret_cast<Bf16*>(y), n, stream);
+}
+
+et_status et_silu_mul_f16(const et_f16* gate, const et_f16* up, et_f16* y, int64_t n,
+                           void* stream) {
+  return et::eltwise_entry<F16, et::kSiluMul>(reinterpret_cast<const F16*>(gate),
+                                               reinterpret_cast<const F16*>(up),
+                                               reinterpret_cast<F16*>(y), n, stream);
 }
 
 }  // extern "C"
@@ -273,6 +288,16 @@ et_status et_geglu_bf16(const et_bf16* gate, const et_bf16* up, et_bf16* y, int6
   auto* o = reinterpret_cast<Bf16*>(y);
   if (approximate == ET_GELU_ERF) return et::eltwise_entry<Bf16, et::kGeluErfMul>(g, u, o, n, stream);
   if (approximate == ET_GELU_TANH) return et::eltwise_entry<Bf16, et::kGeluTanhMul>(g, u, o, n, stream);
+  return n < 0 ? ET_ERR_BAD_SIZE : ET_ERR_BAD_ARG;
+}
+
+et_status et_geglu_f16(const et_f16* gate, const et_f16* up, et_f16* y, int64_t n,
+                        int approximate, void* stream) {
+  const auto* g = reinterpret_cast<const F16*>(gate);
+  const auto* u = reinterpret_cast<const F16*>(up);
+  auto* o = reinterpret_cast<F16*>(y);
+  if (approximate == ET_GELU_ERF) return et::eltwise_entry<F16, et::kGeluErfMul>(g, u, o, n, stream);
+  if (approximate == ET_GELU_TANH) return et::eltwise_entry<F16, et::kGeluTanhMul>(g, u, o, n, stream);
   return n < 0 ? ET_ERR_BAD_SIZE : ET_ERR_BAD_ARG;
 }
 

@@ -13,9 +13,12 @@
 namespace et {
 
 // ---------------------------------------------------------------- storage
-// Kernels are templated on the storage type: float (f32) or Bf16 (raw
-// bfloat16 bits).  Arithmetic is always f32.
+// Kernels are templated on the storage type: float (f32), Bf16 (raw
+// bfloat16 bits) or F16 (raw IEEE binary16 bits).  Arithmetic is always f32.
 struct Bf16 {
+  uint16_t bits;
+};
+struct F16 {
   uint16_t bits;
 };
 
@@ -86,6 +89,67 @@ struct Elem<Bf16> {
     return (e & 1) ? bf16_hi(u[e >> 1]) : bf16_lo(u[e >> 1]);
   }
   static constexpr uint32_t kQuietNaN = 0x7FC07FC0u;  // two bf16 quiet NaNs
+  // The entries of one 32-bit word (entry 0 in the low half).
+  __device__ static inline float lo(uint32_t w) { return bf16_lo(w); }
+  __device__ static inline float hi(uint32_t w) { return bf16_hi(w); }
+};
+
+// f16 -> f32 is exact (every binary16 value, subnormals included, is an f32
+// normal); f32 -> f16 rounds to nearest even (v_cvt_f16_f32), overflowing to
+// infinity past 65504 and keeping subnormals.  An f32 result rounded once to
+// f16 is the correctly rounded f16 of the exact result whenever the f32 one
+// was, and for a sum or product of two f16 values it always is: f32 carries
+// 24 >= 2 * 11 + 2 significant bits, so the double rounding is harmless.
+__device__ inline float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
+}
+__device__ inline float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+#ifndef ET_F16_OPAQUE
+#define ET_F16_OPAQUE 1
+#endif
+__device__ inline uint32_t f16_bits(float v) {
+  // The f32 value is formed first: left alone, the compiler may fold the last
+  // multiply or multiply-add into a mixed-precision FMA that rounds straight
+  // to f16 (v_fma_mixlo_f16) in one code path and not in another, so the
+  // vector and scalar paths of a kernel could differ in the last bit.  The
+  // empty asm makes v opaque; the conversion is then v_cvt_f16_f32 alone.
+#if ET_F16_OPAQUE
+  __asm__("" : "+v"(v));
+#endif
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v)));
+}
+__device__ inline uint32_t f16_pack2(float lo, float hi) { return f16_bits(lo) | (f16_bits(hi) << 16); }
+
+template <>
+struct Elem<F16> {
+  static constexpr int V = 8;
+  __device__ static inline float ld(const F16* p, int64_t i) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, p[i].bits));
+  }
+  __device__ static inline void st(F16* p, int64_t i, float v) {
+    p[i].bits = static_cast<uint16_t>(f16_bits(v));
+  }
+  __device__ static inline void unpack(const u32x4& u, float (&f)[8]) {
+    f[0] = f16_lo(u.x); f[1] = f16_hi(u.x);
+    f[2] = f16_lo(u.y); f[3] = f16_hi(u.y);
+    f[4] = f16_lo(u.z); f[5] = f16_hi(u.z);
+    f[6] = f16_lo(u.w); f[7] = f16_hi(u.w);
+  }
+  __device__ static inline u32x4 pack(const float (&f)[8]) {
+    return u32x4{f16_pack2(f[0], f[1]), f16_pack2(f[2], f[3]), f16_pack2(f[4], f[5]),
+                 f16_pack2(f[6], f[7])};
+  }
+  __device__ static inline float round(float v) {  // to storage precision (RNE)
+    return static_cast<float>(static_cast<_Float16>(v));
+  }
+  __device__ static inline float get(const u32x4& u, int e) {
+    return (e & 1) ? f16_hi(u[e >> 1]) : f16_lo(u[e >> 1]);
+  }
+  static constexpr uint32_t kQuietNaN = 0x7E007E00u;  // two f16 quiet NaNs
+  __device__ static inline float lo(uint32_t w) { return f16_lo(w); }
+  __device__ static inline float hi(uint32_t w) { return f16_hi(w); }
 };
 
 // 16-byte vector access; the caller guarantees 16-byte alignment.

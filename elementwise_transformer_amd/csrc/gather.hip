@@ -132,6 +132,7 @@ et_status embedding_entry(const S* table, int64_t vocab, const int32_t* ids, S* 
 }  // namespace et
 
 using et::Bf16;
+using et::F16;
 
 extern "C" {
 
@@ -144,6 +145,12 @@ et_status et_embedding_bf16(const et_bf16* table, int64_t V, const int32_t* ids,
                             int64_t n, int64_t d, void* stream) {
   return et::embedding_entry<Bf16>(reinterpret_cast<const Bf16*>(table), V, ids,
                                    reinterpret_cast<Bf16*>(out), n, d, stream);
+}
+
+et_status et_embedding_f16(const et_f16* table, int64_t V, const int32_t* ids, et_f16* out,
+                            int64_t n, int64_t d, void* stream) {
+  return et::embedding_entry<F16>(reinterpret_cast<const F16*>(table), V, ids,
+                                   reinterpret_cast<F16*>(out), n, d, stream);
 }
 
 }  // extern "C"

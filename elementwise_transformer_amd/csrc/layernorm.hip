@@ -293,6 +293,7 @@ et_status layernorm_entry(const S* x, const S* w, const S* b, S* y, int64_t rows
 }  // namespace et
 
 using et::Bf16;
+using et::F16;
 
 extern "C" {
 
@@ -306,6 +307,14 @@ et_status et_layernorm_bf16(const et_bf16* x, const et_bf16* gamma, const et_bf1
   return et::layernorm_entry<Bf16>(reinterpret_cast<const Bf16*>(x),
                                    reinterpret_cast<const Bf16*>(gamma),
                                    reinterpret_cast<const Bf16*>(beta), reinterpret_cast<Bf16*>(y),
+                                   rows, d, eps, stream);
+}
+
+et_status et_layernorm_f16(const et_f16* x, const et_f16* gamma, const et_f16* beta,
+                            et_f16* y, int64_t rows, int64_t d, float eps, void* stream) {
+  return et::layernorm_entry<F16>(reinterpret_cast<const F16*>(x),
+                                   reinterpret_cast<const F16*>(gamma),
+                                   reinterpret_cast<const F16*>(beta), reinterpret_cast<F16*>(y),
                                    rows, d, eps, stream);
 }
 

@@ -342,6 +342,7 @@ et_status norm_entry(const S* x, const S* res, const S* w, S* y, S* h, int64_t r
 }  // namespace et
 
 using et::Bf16;
+using et::F16;
 
 extern "C" {
 
@@ -357,6 +358,13 @@ et_status et_rmsnorm_bf16(const et_bf16* x, const et_bf16* w, et_bf16* y, int64_
                                      nullptr, rows, d, eps, stream);
 }
 
+et_status et_rmsnorm_f16(const et_f16* x, const et_f16* w, et_f16* y, int64_t rows,
+                          int64_t d, float eps, void* stream) {
+  return et::norm_entry<F16, false>(reinterpret_cast<const F16*>(x), nullptr,
+                                     reinterpret_cast<const F16*>(w), reinterpret_cast<F16*>(y),
+                                     nullptr, rows, d, eps, stream);
+}
+
 et_status et_add_rmsnorm_f32(const float* x, const float* residual, const float* w, float* y,
                              float* h, int64_t rows, int64_t d, float eps, void* stream) {
   return et::norm_entry<float, true>(x, residual, w, y, h, rows, d, eps, stream);
@@ -368,6 +376,15 @@ et_status et_add_rmsnorm_bf16(const et_bf16* x, const et_bf16* residual, const e
   return et::norm_entry<Bf16, true>(
       reinterpret_cast<const Bf16*>(x), reinterpret_cast<const Bf16*>(residual),
       reinterpret_cast<const Bf16*>(w), reinterpret_cast<Bf16*>(y), reinterpret_cast<Bf16*>(h),
+      rows, d, eps, stream);
+}
+
+et_status et_add_rmsnorm_f16(const et_f16* x, const et_f16* residual, const et_f16* w,
+                              et_f16* y, et_f16* h, int64_t rows, int64_t d, float eps,
+                              void* stream) {
+  return et::norm_entry<F16, true>(
+      reinterpret_cast<const F16*>(x), reinterpret_cast<const F16*>(residual),
+      reinterpret_cast<const F16*>(w), reinterpret_cast<F16*>(y), reinterpret_cast<F16*>(h),
       rows, d, eps, stream);
 }
 

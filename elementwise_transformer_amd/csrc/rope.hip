@@ -967,7 +967,7 @@ __device__ inline void vector_desc(int cv, const MultiArgs& a, int4* d4, int* d1
 template <typename S>
 __device__ inline float lds_elem(const S* xs, int i) {
   if constexpr (sizeof(S) == 2) {
-    return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(xs)[i]) << 16);
+    return Elem<S>::lo(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(xs)[i]));
   } else {
     return xs[i];
   }
@@ -985,10 +985,11 @@ __device__ inline void lds_run(const S* xr, int p, float (&o)[W]) {
   } else if constexpr (sizeof(S) == 2) {
     if constexpr (W == 4) {
       const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(xr) + p);
-      o[0] = bf16_lo(w.x); o[1] = bf16_hi(w.x); o[2] = bf16_lo(w.y); o[3] = bf16_hi(w.y);
+      using E = Elem<S>;
+      o[0] = E::lo(w.x); o[1] = E::hi(w.x); o[2] = E::lo(w.y); o[3] = E::hi(w.y);
     } else {
       const uint32_t w = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint16_t*>(xr) + p);
-      o[0] = bf16_lo(w); o[1] = bf16_hi(w);
+      o[0] = Elem<S>::lo(w); o[1] = Elem<S>::hi(w);
     }
   } else {
     if constexpr (W == 4) {
@@ -1277,6 +1278,7 @@ et_status rope_multi_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* po
 }  // namespace et
 
 using et::Bf16;
+using et::F16;
 
 extern "C" {
 
@@ -1290,6 +1292,13 @@ et_status et_rope_bf16(et_bf16* x, const int32_t* pos, int64_t T, int64_t H, int
                        int64_t d_rot, const float* inv_freq, float attn_scaling, int layout,
                        void* stream) {
   return et::rope_entry<Bf16>(reinterpret_cast<Bf16*>(x), H, nullptr, 0, pos, T, D, d_rot,
+                              inv_freq, attn_scaling, layout, stream);
+}
+
+et_status et_rope_f16(et_f16* x, const int32_t* pos, int64_t T, int64_t H, int64_t D,
+                       int64_t d_rot, const float* inv_freq, float attn_scaling, int layout,
+                       void* stream) {
+  return et::rope_entry<F16>(reinterpret_cast<F16*>(x), H, nullptr, 0, pos, T, D, d_rot,
                               inv_freq, attn_scaling, layout, stream);
 }
 
@@ -1307,6 +1316,13 @@ et_status et_rope_qk_bf16(et_bf16* q, int64_t Hq, et_bf16* k, int64_t Hk, const 
                               T, D, d_rot, inv_freq, attn_scaling, layout, stream);
 }
 
+et_status et_rope_qk_f16(et_f16* q, int64_t Hq, et_f16* k, int64_t Hk, const int32_t* pos,
+                          int64_t T, int64_t D, int64_t d_rot, const float* inv_freq,
+                          float attn_scaling, int layout, void* stream) {
+  return et::rope_entry<F16>(reinterpret_cast<F16*>(q), Hq, reinterpret_cast<F16*>(k), Hk, pos,
+                              T, D, d_rot, inv_freq, attn_scaling, layout, stream);
+}
+
 et_status et_rmsnorm_rope_qk_f32(float* q, const float* gq, int64_t Hq, float* k, const float* gk,
                                  int64_t Hk, float eps, const int32_t* pos, int64_t T, int64_t D,
                                  int64_t d_rot, const float* inv_freq, float attn_scaling,
@@ -1321,6 +1337,15 @@ et_status et_rmsnorm_rope_qk_bf16(et_bf16* q, const et_bf16* gq, int64_t Hq, et_
                                   float attn_scaling, int layout, void* stream) {
   return et::qknorm_entry<Bf16>(reinterpret_cast<Bf16*>(q), reinterpret_cast<const Bf16*>(gq), Hq,
                                 reinterpret_cast<Bf16*>(k), reinterpret_cast<const Bf16*>(gk), Hk,
+                                eps, pos, T, D, d_rot, inv_freq, attn_scaling, layout, stream);
+}
+
+et_status et_rmsnorm_rope_qk_f16(et_f16* q, const et_f16* gq, int64_t Hq, et_f16* k,
+                                  const et_f16* gk, int64_t Hk, float eps, const int32_t* pos,
+                                  int64_t T, int64_t D, int64_t d_rot, const float* inv_freq,
+                                  float attn_scaling, int layout, void* stream) {
+  return et::qknorm_entry<F16>(reinterpret_cast<F16*>(q), reinterpret_cast<const F16*>(gq), Hq,
+                                reinterpret_cast<F16*>(k), reinterpret_cast<const F16*>(gk), Hk,
                                 eps, pos, T, D, d_rot, inv_freq, attn_scaling, layout, stream);
 }
 
@@ -1347,6 +1372,15 @@ et_status et_rope_qk_cached_bf16(et_bf16* q, int64_t Hq, et_bf16* k, int64_t Hk,
                               T, D, d_rot, nullptr, attn_scaling, layout, stream, &c);
 }
 
+et_status et_rope_qk_cached_f16(et_f16* q, int64_t Hq, et_f16* k, int64_t Hk,
+                                 const int32_t* pos, int64_t T, int64_t D, int64_t d_rot,
+                                 const float* cos_cache, const float* sin_cache, int64_t max_pos,
+                                 float attn_scaling, int layout, void* stream) {
+  const et::RopeCache c{cos_cache, sin_cache, max_pos};
+  return et::rope_entry<F16>(reinterpret_cast<F16*>(q), Hq, reinterpret_cast<F16*>(k), Hk, pos,
+                              T, D, d_rot, nullptr, attn_scaling, layout, stream, &c);
+}
+
 et_status et_rope_multi_f32(float* q, int64_t Hq, float* k, int64_t Hk, const int32_t* pos,
                             int64_t T, int64_t D, int64_t n_axes, const int64_t* dims,
                             const float* inv_freq, float attn_scaling, int layout, void* stream) {
@@ -1358,6 +1392,13 @@ et_status et_rope_multi_bf16(et_bf16* q, int64_t Hq, et_bf16* k, int64_t Hk, con
                              int64_t T, int64_t D, int64_t n_axes, const int64_t* dims,
                              const float* inv_freq, float attn_scaling, int layout, void* stream) {
   return et::rope_multi_entry<Bf16>(reinterpret_cast<Bf16*>(q), Hq, reinterpret_cast<Bf16*>(k), Hk,
+                                    pos, T, D, n_axes, dims, inv_freq, attn_scaling, layout, stream);
+}
+
+et_status et_rope_multi_f16(et_f16* q, int64_t Hq, et_f16* k, int64_t Hk, const int32_t* pos,
+                             int64_t T, int64_t D, int64_t n_axes, const int64_t* dims,
+                             const float* inv_freq, float attn_scaling, int layout, void* stream) {
+  return et::rope_multi_entry<F16>(reinterpret_cast<F16*>(q), Hq, reinterpret_cast<F16*>(k), Hk,
                                     pos, T, D, n_axes, dims, inv_freq, attn_scaling, layout, stream);
 }
 

@@ -625,6 +625,7 @@ et_status softmax_entry(const S* x, S* y, int64_t rows, int64_t n, float tempera
 }  // namespace et
 
 using et::Bf16;
+using et::F16;
 
 extern "C" {
 
@@ -644,6 +645,13 @@ et_status et_softmax_bf16(const et_bf16* x, et_bf16* y, int64_t rows, int64_t n,
                           float temperature, void* workspace, size_t workspace_bytes,
                           void* stream) {
   return et::softmax_entry<Bf16>(reinterpret_cast<const Bf16*>(x), reinterpret_cast<Bf16*>(y), rows,
+                                 n, temperature, workspace, workspace_bytes, stream);
+}
+
+et_status et_softmax_f16(const et_f16* x, et_f16* y, int64_t rows, int64_t n,
+                          float temperature, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return et::softmax_entry<F16>(reinterpret_cast<const F16*>(x), reinterpret_cast<F16*>(y), rows,
                                  n, temperature, workspace, workspace_bytes, stream);
 }
 

@@ -17,8 +17,11 @@
  *
  * Common rules for every entry point
  *   - Types: the _f32 variant stores float; the _bf16 variant stores
- *     bfloat16 bits (et_bf16) and computes in f32, rounding each stored
- *     result once to nearest-even.  inv_freq and scalars are f32 in both.
+ *     bfloat16 bits (et_bf16) and the _f16 variant IEEE binary16 bits
+ *     (et_f16, [OPS] gives F16 tolerances); both compute in f32, rounding
+ *     each stored result once to nearest-even (f16 overflows to infinity
+ *     past 65504 and keeps subnormals).  inv_freq, caches and scalars are
+ *     f32 in every variant.
  *   - Pointers are DEVICE pointers of the current HIP device, except scalars
  *     passed by value.  The caller owns every buffer; the library allocates
  *     nothing, keeps no state and is reentrant.
@@ -52,6 +55,8 @@ extern "C" {
 
 /* Raw bfloat16 bits (sign, 8-bit exponent, 7-bit fraction). */
 typedef uint16_t et_bf16;
+/* Raw IEEE binary16 bits (sign, 5-bit exponent, 10-bit fraction). */
+typedef uint16_t et_f16;
 
 typedef enum {
     ET_OK = 0,
@@ -77,6 +82,8 @@ et_status et_rmsnorm_f32(const float* x, const float* w, float* y,
                          int64_t rows, int64_t d, float eps, void* stream);
 et_status et_rmsnorm_bf16(const et_bf16* x, const et_bf16* w, et_bf16* y,
                           int64_t rows, int64_t d, float eps, void* stream);
+et_status et_rmsnorm_f16(const et_f16* x, const et_f16* w, et_f16* y,
+                         int64_t rows, int64_t d, float eps, void* stream);
 
 /* ------------------------------------------------------------------------
  * Fused residual add + RMSNorm  ([OPS] 10 Fused ops, FusedSkipNorm)
@@ -92,6 +99,9 @@ et_status et_add_rmsnorm_f32(const float* x, const float* residual,
 et_status et_add_rmsnorm_bf16(const et_bf16* x, const et_bf16* residual,
                               const et_bf16* w, et_bf16* y, et_bf16* h,
                               int64_t rows, int64_t d, float eps, void* stream);
+et_status et_add_rmsnorm_f16(const et_f16* x, const et_f16* residual,
+                             const et_f16* w, et_f16* y, et_f16* h,
+                             int64_t rows, int64_t d, float eps, void* stream);
 
 /* ------------------------------------------------------------------------
  * RoPE, in place  ([OPS] Rope; [ELT] 2.2 and 4, tl_rope_f32)
@@ -109,6 +119,9 @@ et_status et_rope_f32(float* x, const int32_t* pos, int64_t T, int64_t H,
 et_status et_rope_bf16(et_bf16* x, const int32_t* pos, int64_t T, int64_t H,
                        int64_t D, int64_t d_rot, const float* inv_freq,
                        float attn_scaling, int layout, void* stream);
+et_status et_rope_f16(et_f16* x, const int32_t* pos, int64_t T, int64_t H,
+                      int64_t D, int64_t d_rot, const float* inv_freq,
+                      float attn_scaling, int layout, void* stream);
 
 /* RoPE on a query and a key tensor in one launch (one angle per (token,
  * pair) serves all Hq + Hk heads).  q: [T, Hq, D]; k: [T, Hk, D] (k may be
@@ -121,6 +134,10 @@ et_status et_rope_qk_bf16(et_bf16* q, int64_t Hq, et_bf16* k, int64_t Hk,
                           const int32_t* pos, int64_t T, int64_t D,
                           int64_t d_rot, const float* inv_freq,
                           float attn_scaling, int layout, void* stream);
+et_status et_rope_qk_f16(et_f16* q, int64_t Hq, et_f16* k, int64_t Hk,
+                         const int32_t* pos, int64_t T, int64_t D,
+                         int64_t d_rot, const float* inv_freq,
+                         float attn_scaling, int layout, void* stream);
 
 /* ------------------------------------------------------------------------
  * RoPE cos/sin cache  ([OPS] 3 Rope, cos/sin cache)
@@ -157,6 +174,12 @@ et_status et_rope_qk_cached_bf16(et_bf16* q, int64_t Hq, et_bf16* k,
                                  const float* cos_cache,
                                  const float* sin_cache, int64_t max_pos,
                                  float attn_scaling, int layout, void* stream);
+et_status et_rope_qk_cached_f16(et_f16* q, int64_t Hq, et_f16* k,
+                                int64_t Hk, const int32_t* pos, int64_t T,
+                                int64_t D, int64_t d_rot,
+                                const float* cos_cache,
+                                const float* sin_cache, int64_t max_pos,
+                                float attn_scaling, int layout, void* stream);
 
 /* ------------------------------------------------------------------------
  * Multi-axis RoPE on Q and K, in place  ([OPS] 3 Rope, multi-axis RoPE)
@@ -184,6 +207,11 @@ et_status et_rope_multi_bf16(et_bf16* q, int64_t Hq, et_bf16* k, int64_t Hk,
                              int64_t n_axes, const int64_t* dims,
                              const float* inv_freq, float attn_scaling,
                              int layout, void* stream);
+et_status et_rope_multi_f16(et_f16* q, int64_t Hq, et_f16* k, int64_t Hk,
+                            const int32_t* pos, int64_t T, int64_t D,
+                            int64_t n_axes, const int64_t* dims,
+                            const float* inv_freq, float attn_scaling,
+                            int layout, void* stream);
 
 /* ------------------------------------------------------------------------
  * Fused RMSNorm + RoPE on Q and K, in place  ([OPS] 5 QK-norm)
@@ -205,6 +233,12 @@ et_status et_rmsnorm_rope_qk_bf16(et_bf16* q, const et_bf16* gq, int64_t Hq,
                                   int64_t D, int64_t d_rot,
                                   const float* inv_freq, float attn_scaling,
                                   int layout, void* stream);
+et_status et_rmsnorm_rope_qk_f16(et_f16* q, const et_f16* gq, int64_t Hq,
+                                 et_f16* k, const et_f16* gk, int64_t Hk,
+                                 float eps, const int32_t* pos, int64_t T,
+                                 int64_t D, int64_t d_rot,
+                                 const float* inv_freq, float attn_scaling,
+                                 int layout, void* stream);
 
 /* ------------------------------------------------------------------------
  * SiLU-gated multiply  ([OPS] Silu, SwiGlu; [ELT] 2.3, tl_silu_mul_f32)
@@ -216,6 +250,8 @@ et_status et_silu_mul_f32(const float* gate, const float* up, float* y,
                           int64_t n, void* stream);
 et_status et_silu_mul_bf16(const et_bf16* gate, const et_bf16* up, et_bf16* y,
                            int64_t n, void* stream);
+et_status et_silu_mul_f16(const et_f16* gate, const et_f16* up, et_f16* y,
+                          int64_t n, void* stream);
 
 /* ------------------------------------------------------------------------
  * Residual add  ([OPS] Add; [ELT] 2.4, tl_add_f32)
@@ -227,6 +263,8 @@ et_status et_add_f32(const float* a, const float* b, float* y, int64_t n,
                      void* stream);
 et_status et_add_bf16(const et_bf16* a, const et_bf16* b, et_bf16* y,
                       int64_t n, void* stream);
+et_status et_add_f16(const et_f16* a, const et_f16* b, et_f16* y,
+                     int64_t n, void* stream);
 
 /* ------------------------------------------------------------------------
  * Embedding gather  ([OPS] TokenEmbed; [ELT] 2.4, tl_embedding_f32)
@@ -241,6 +279,9 @@ et_status et_embedding_f32(const float* table, int64_t V, const int32_t* ids,
 et_status et_embedding_bf16(const et_bf16* table, int64_t V,
                             const int32_t* ids, et_bf16* out, int64_t n,
                             int64_t d, void* stream);
+et_status et_embedding_f16(const et_f16* table, int64_t V,
+                           const int32_t* ids, et_f16* out, int64_t n,
+                           int64_t d, void* stream);
 
 /* ------------------------------------------------------------------------
  * Greedy argmax per row  ([OPS] Argmax, 8 Sampling / Greedy; [ELT] 2.4)
@@ -264,6 +305,9 @@ et_status et_argmax_f32(const float* x, int64_t rows, int64_t n, int32_t* out,
 et_status et_argmax_bf16(const et_bf16* x, int64_t rows, int64_t n,
                          int32_t* out, void* workspace, size_t workspace_bytes,
                          void* stream);
+et_status et_argmax_f16(const et_f16* x, int64_t rows, int64_t n,
+                        int32_t* out, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* ------------------------------------------------------------------------
  * LayerNorm  ([OPS] 2 Normalization / LayerNorm; [DNN] 7)
@@ -279,6 +323,9 @@ et_status et_layernorm_f32(const float* x, const float* gamma, const float* beta
 et_status et_layernorm_bf16(const et_bf16* x, const et_bf16* gamma,
                             const et_bf16* beta, et_bf16* y, int64_t rows,
                             int64_t d, float eps, void* stream);
+et_status et_layernorm_f16(const et_f16* x, const et_f16* gamma,
+                           const et_f16* beta, et_f16* y, int64_t rows,
+                           int64_t d, float eps, void* stream);
 
 /* ------------------------------------------------------------------------
  * GELU-gated multiply, GeGLU  ([OPS] 4 Activation / Gelu, GeGlu)
@@ -292,6 +339,8 @@ et_status et_geglu_f32(const float* gate, const float* up, float* y, int64_t n,
                        int approximate, void* stream);
 et_status et_geglu_bf16(const et_bf16* gate, const et_bf16* up, et_bf16* y,
                         int64_t n, int approximate, void* stream);
+et_status et_geglu_f16(const et_f16* gate, const et_f16* up, et_f16* y,
+                       int64_t n, int approximate, void* stream);
 
 /* ------------------------------------------------------------------------
  * Softmax over the last axis with a temperature  ([OPS] 4 Activation /
@@ -319,6 +368,9 @@ et_status et_softmax_f32(const float* x, float* y, int64_t rows, int64_t n,
 et_status et_softmax_bf16(const et_bf16* x, et_bf16* y, int64_t rows,
                           int64_t n, float temperature, void* workspace,
                           size_t workspace_bytes, void* stream);
+et_status et_softmax_f16(const et_f16* x, et_f16* y, int64_t rows,
+                         int64_t n, float temperature, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Library information. */

@@ -28,12 +28,12 @@ def test_header_declares_the_ops():
     names = _declared()
     for op in ("rmsnorm", "add_rmsnorm", "rope", "rope_qk", "rmsnorm_rope_qk", "silu_mul", "add",
                "embedding", "argmax", "softmax", "layernorm", "geglu"):
-        for sfx in ("f32", "bf16"):
+        for sfx in ("f32", "bf16", "f16"):
             assert f"et_{op}_{sfx}" in names
     assert "et_argmax_workspace_bytes" in names and "et_status_string" in names
     assert "et_softmax_workspace_bytes" in names
     assert "et_rope_cache_f32" in names
-    for sfx in ("f32", "bf16"):
+    for sfx in ("f32", "bf16", "f16"):
         assert f"et_rope_qk_cached_{sfx}" in names
         assert f"et_rope_multi_{sfx}" in names
 
@@ -73,7 +73,7 @@ S = P(0)             # default stream
 
 
 @gpu_visible
-@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+@pytest.mark.parametrize("sfx", ["f32", "bf16", "f16"])
 def test_rmsnorm_validation(sfx):
     import elementwise_transformer_amd as et
     f = getattr(et.lib, f"et_rmsnorm_{sfx}")
@@ -93,7 +93,7 @@ def test_rmsnorm_validation(sfx):
 
 
 @gpu_visible
-@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+@pytest.mark.parametrize("sfx", ["f32", "bf16", "f16"])
 def test_add_rmsnorm_validation(sfx):
     import elementwise_transformer_amd as et
     f = getattr(et.lib, f"et_add_rmsnorm_{sfx}")
@@ -106,7 +106,7 @@ def test_add_rmsnorm_validation(sfx):
 
 
 @gpu_visible
-@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+@pytest.mark.parametrize("sfx", ["f32", "bf16", "f16"])
 def test_rope_validation(sfx):
     import elementwise_transformer_amd as et
     f = getattr(et.lib, f"et_rope_{sfx}")
@@ -144,7 +144,7 @@ def test_rope_cache_validation():
 
 
 @gpu_visible
-@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+@pytest.mark.parametrize("sfx", ["f32", "bf16", "f16"])
 def test_rope_cached_validation(sfx):
     import elementwise_transformer_amd as et
     f = getattr(et.lib, f"et_rope_qk_cached_{sfx}")
@@ -162,7 +162,7 @@ def test_rope_cached_validation(sfx):
 
 
 @gpu_visible
-@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+@pytest.mark.parametrize("sfx", ["f32", "bf16", "f16"])
 def test_rope_multi_validation(sfx):
     import elementwise_transformer_amd as et
     f = getattr(et.lib, f"et_rope_multi_{sfx}")
@@ -188,7 +188,7 @@ def test_rope_multi_validation(sfx):
 
 
 @gpu_visible
-@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+@pytest.mark.parametrize("sfx", ["f32", "bf16", "f16"])
 def test_rmsnorm_rope_validation(sfx):
     import elementwise_transformer_amd as et
     f = getattr(et.lib, f"et_rmsnorm_rope_qk_{sfx}")
@@ -200,7 +200,7 @@ def test_rmsnorm_rope_validation(sfx):
 
 
 @gpu_visible
-@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+@pytest.mark.parametrize("sfx", ["f32", "bf16", "f16"])
 def test_flat_validation(sfx):
     import elementwise_transformer_amd as et
     for op in ("add", "silu_mul"):
@@ -213,7 +213,7 @@ def test_flat_validation(sfx):
 
 
 @gpu_visible
-@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+@pytest.mark.parametrize("sfx", ["f32", "bf16", "f16"])
 def test_embedding_and_argmax_validation(sfx):
     import elementwise_transformer_amd as et
     e = getattr(et.lib, f"et_embedding_{sfx}")
@@ -235,7 +235,7 @@ def test_embedding_and_argmax_validation(sfx):
 
 
 @gpu_visible
-@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+@pytest.mark.parametrize("sfx", ["f32", "bf16", "f16"])
 def test_softmax_validation(sfx):
     import elementwise_transformer_amd as et
     f = getattr(et.lib, f"et_softmax_{sfx}")
@@ -258,7 +258,7 @@ def test_softmax_validation(sfx):
 
 
 @gpu_visible
-@pytest.mark.parametrize("sfx", ["f32", "bf16"])
+@pytest.mark.parametrize("sfx", ["f32", "bf16", "f16"])
 def test_layernorm_and_geglu_validation(sfx):
     import elementwise_transformer_amd as et
     f = getattr(et.lib, f"et_layernorm_{sfx}")

@@ -17,7 +17,7 @@ from gpu_util import assert_bits, dev, host, pair_norms, widen
 
 pytestmark = pytest.mark.gpu
 
-DTS = ["f32", "bf16"]
+DTS = ["f32", "bf16", "f16"]
 
 
 @pytest.fixture(scope="module")

@@ -11,7 +11,8 @@ give none for these ops:
         root and reciprocal < 64 u relative; the gain, bias and output
         roundings 2u.  The bound is absolute per element, because x - mu and
         + b cancel.
-  LayerNorm bf16 |got - y| <= (the f32 bound) + one bf16 ulp of y.
+  LayerNorm bf16, f16  |got - y| <= (the f32 bound) + one ulp of y in the
+        storage type.
   GeGLU f32  erf form:  |got - y| <= u (2 x^2 + 64) |y| + 2^-140: the
         argument -x/sqrt(2) carries 1.5 u, which erfc magnifies by up to
         2 z^2 = x^2 in the lower tail, plus the erfc fit (fractional error
@@ -19,14 +20,14 @@ give none for these ops:
         tanh form: u (3 |v| + 64) |y| + 2^-140, v = -2u(x) the exponent,
         carrying 3 u (its polynomial), which exp turns into a relative error
         of up to 3 |v| u.
-  GeGLU bf16  1 bf16 ulp of the oracle's correctly rounded value.
+  GeGLU bf16, f16  1 ulp of the oracle's correctly rounded value.
 """
 import numpy as np
 import pytest
 import torch
 
 import workloads as wl
-from gpu_util import assert_bf16_ulp, assert_bits, dev, host, widen
+from gpu_util import assert_bf16_ulp, assert_bits, dev, host, ulp16, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -52,12 +53,6 @@ def _misaligned(t):
     return v
 
 
-def _bf16_ulp(v):
-    a = np.abs(v)
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    return np.where(a >= 2.0 ** -126, 2.0 ** (e - 7), 2.0 ** -133)
-
-
 def _check_ln(got, xs, gs, bs, eps, y, y64, what):
     x = widen(xs)
     g = widen(gs)
@@ -68,7 +63,7 @@ def _check_ln(got, xs, gs, bs, eps, y, y64, what):
     tol = U * inv * np.abs(g) * (np.abs(x) + 64 * np.abs(x).mean(axis=1, keepdims=True) + 64 * np.abs(c)) \
         + 2 * U * (np.abs(b) + np.abs(y64)) + 2.0 ** -140
     if got.dtype != np.float32:
-        tol = tol + _bf16_ulp(y64)
+        tol = tol + ulp16(y64, got.dtype)
     gw = widen(got)
     gn, rn = np.isnan(gw), np.isnan(y64)
     assert np.array_equal(gn, rn), f"{what}: NaN positions differ"
@@ -111,7 +106,7 @@ LN_SHAPES = [(1, 1), (3, 3), (5, 7), (4, 64), (33, 100), (7, 1000), (9, 4096), (
              (2, 14336), (2, 40000), (2, 70001)]
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("shape", LN_SHAPES)
 def test_layernorm_matches_oracle(et, orc, dt, shape):
     rows, d = shape
@@ -125,7 +120,7 @@ def test_layernorm_matches_oracle(et, orc, dt, shape):
         _check_ln(got, xs, gs, b, 1e-5, y, y64, f"{dt} {shape} bias={b is not None}")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("d", [7, 1000, 4100, 40003])
 def test_layernorm_scalar_path_and_in_place(et, orc, dt, d):
     g = _rng(d, 2)
@@ -141,7 +136,7 @@ def test_layernorm_scalar_path_and_in_place(et, orc, dt, d):
     assert_bits(host(xd), ref, f"{dt} d={d} in place")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("d", [64, 4096, 8192, 40000])
 def test_layernorm_batch_invariance_and_constant_rows(et, dt, d):
     rows = 64 if d <= 4096 else 9
@@ -177,7 +172,7 @@ def test_layernorm_prefill_full_size(et, orc):
 GEGLU_N = [1, 7, 100, 4099, (1 << 20) + 5]
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("form", [0, 1])
 @pytest.mark.parametrize("n", GEGLU_N)
 def test_geglu_matches_oracle(et, orc, dt, form, n):
@@ -192,7 +187,7 @@ def test_geglu_matches_oracle(et, orc, dt, form, n):
     _check_geglu(got, gs, form, y, y64, f"{dt} form={form} n={n}")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("form", [0, 1])
 def test_geglu_special_values_in_place_and_scalar(et, orc, dt, form):
     x = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 1.0, -1.0, 5.0] * 13, np.float32)

@@ -14,7 +14,7 @@ from gpu_util import (assert_bits, assert_close, assert_f32_rel, assert_pair, de
 
 pytestmark = pytest.mark.gpu
 
-DTS = ["f32", "bf16"]
+DTS = ["f32", "bf16", "f16"]
 
 
 @pytest.fixture(scope="module")
@@ -34,7 +34,8 @@ def _store(a, dt):
 
 def _misaligned(t: torch.Tensor) -> torch.Tensor:
     """A contiguous copy of t whose data pointer is 4 bytes (f32) or 2 bytes
-    (bf16) past a 16-byte boundary: the kernels must take their scalar path."""
+    (bf16, f16) past a 16-byte boundary: the kernels must take their scalar
+    path."""
     flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
     v = flat[1:1 + t.numel()].view(t.shape)
     v.copy_(t)
@@ -156,7 +157,7 @@ def test_rmsnorm_rope_qk(et, orc, dt, ci):
     gq = _store(g.uniform(0.5, 1.5, D).astype(np.float32), dt)
     gk = _store(g.uniform(0.5, 1.5, D).astype(np.float32), dt)
     if T > 1:
-        q[1, 0, :] = 0 if dt == "f32" else np.uint16(0)   # a zero head row -> 0
+        q[1, 0, :] = 0                                   # a zero head row -> 0
     mu = float(np.float32(mu))
     qt, kt = dev(q), (dev(k) if k is not None else None)
     et.rmsnorm_rope_qk(qt, dev(gq), kt, dev(gk) if k is not None else None, 1e-6, dev(pos),
@@ -271,7 +272,8 @@ def test_argmax(et, orc, dt, rows, n, split):
 
 @pytest.mark.parametrize("dt", DTS)
 def test_argmax_empty_rows(et, dt):
-    x = torch.empty((3, 0), dtype=torch.float32 if dt == "f32" else torch.bfloat16, device="cuda")
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    x = torch.empty((3, 0), dtype=tdt, device="cuda")
     assert host(et.argmax(x)).tolist() == [-1, -1, -1]
 
 

@@ -22,7 +22,7 @@ from gpu_util import assert_bits, assert_pair, dev, host, widen
 
 pytestmark = pytest.mark.gpu
 
-DTS = ["f32", "bf16"]
+DTS = ["f32", "bf16", "f16"]
 CACHE_ABS = 1.5e-7
 
 

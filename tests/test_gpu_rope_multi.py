@@ -16,7 +16,7 @@ from gpu_util import assert_bits, assert_pair, dev, host
 
 pytestmark = pytest.mark.gpu
 
-DTS = ["f32", "bf16"]
+DTS = ["f32", "bf16", "f16"]
 
 
 @pytest.fixture(scope="module")

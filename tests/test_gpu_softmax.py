@@ -13,8 +13,8 @@ Tolerances, derived from the f32 arithmetic of the kernels (u = 2^-24):
         wave partials and the chunk combine -- well under 128 u in all.
         Results below 2^-126 may come out as 0 (the hardware exp2 returns no
         subnormals).
-  bf16  at most 1 bf16 ulp from the oracle's correctly rounded value (the
-        f32 result above is far inside half a bf16 ulp); results below
+  bf16, f16  at most 1 ulp from the oracle's correctly rounded value (the
+        f32 result above is far inside half an ulp of either); results below
         2^-126 may also come out as 0.
 """
 import numpy as np
@@ -77,7 +77,7 @@ SHAPES = [(1, 1), (3, 5), (4, 64), (7, 100), (5, 1000), (3, 4096), (2, 8191), (2
           (2, 32769), (3, 40000), (2, 128256)]
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_softmax_matches_oracle(et, orc, dt, shape):
     for t in (1.0, 0.7):
@@ -88,7 +88,7 @@ def test_softmax_matches_oracle(et, orc, dt, shape):
         assert np.all(np.abs(y64.sum(axis=1) - 1.0) < 1e-12)
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("n", [40000, 128256])
 def test_softmax_workspace_and_single_block_agree(et, dt, n):
     """Long rows: the single-launch split (workspace) and one workgroup per
@@ -99,7 +99,7 @@ def test_softmax_workspace_and_single_block_agree(et, dt, n):
     assert_bits(a, b, f"{dt} n={n}")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("n", [40000, 128256])
 def test_softmax_bounded_wait_fallback_same_bits(et, dt, n, monkeypatch):
     """Forced from the host: with a spin limit of 0 no workgroup waits for the
@@ -123,7 +123,7 @@ def test_softmax_bounded_wait_fallback_same_bits(et, dt, n, monkeypatch):
     assert_bits(d, a, f"{dt} n={n} reuse")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("n", [100, 4096, 32768, 40000, 128256])
 def test_softmax_batch_invariance_and_in_place(et, dt, n):
     """A row's bits do not depend on the rows beside it; y == x works."""
@@ -139,7 +139,7 @@ def test_softmax_batch_invariance_and_in_place(et, dt, n):
     assert_bits(host(inplace), full, f"{dt} n={n} in place")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("n", [7, 1001, 40003])
 def test_softmax_scalar_path(et, orc, dt, n):
     """Misaligned buffers and lengths that are not whole vectors take the
@@ -155,7 +155,7 @@ def test_softmax_scalar_path(et, orc, dt, n):
     _check(got, xs, 0.8, y, y64, f"{dt} n={n} misaligned")
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("n", [16, 5000, 40000])
 def test_softmax_special_values(et, orc, dt, n):
     """NaN anywhere, all -inf, a +inf entry: NaN rows; a single -inf entry

@@ -4,7 +4,7 @@ This module only draws random inputs and describes workload shapes; it holds
 none of the ops' arithmetic.  Both the HIP path (through the tests and the
 benchmark) and the CPU oracle are fed from it, and it imports neither.
 
-Storage: f32 tensors are ``numpy.float32``; bf16 tensors are ``numpy.uint16``
+Storage: f32 tensors are ``numpy.float32``; f16 tensors ``numpy.float16``; bf16 tensors are ``numpy.uint16``
 arrays of bfloat16 bits, drawn in f32 and converted by torch's CPU cast
 (round to nearest even).
 
@@ -42,8 +42,15 @@ def from_bf16_bits(b: np.ndarray) -> np.ndarray:
 
 
 def store(a: np.ndarray, dtype: str) -> np.ndarray:
+    """f32 values -> storage form: float32, bf16 bits (uint16) or float16
+    (numpy's cast, round to nearest even; past 65504 infinite)."""
     a = np.asarray(a, dtype=np.float32)
-    return to_bf16_bits(a) if dtype == "bf16" else np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return to_bf16_bits(a)
+    if dtype == "f16":
+        with np.errstate(over="ignore"):
+            return np.ascontiguousarray(a.astype(np.float16))
+    return np.ascontiguousarray(a)
 
 
 def normal(g: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
