@@ -18,9 +18,10 @@ from typing import Optional, Tuple
 
 import torch  # loaded first so libet.so binds to the HIP runtime torch uses
 
-__all__ = ["rmsnorm", "add_rmsnorm", "rope", "rope_qk", "rmsnorm_rope_qk", "silu_mul", "add",
-           "rope_cache", "rope_qk_cached", "rope_multi", "embedding", "argmax", "argmax_workspace_bytes", "ETError", "lib", "LIB_PATH",
-           "ROPE_HALF", "ROPE_INTERLEAVED", "abi_version"]
+__all__ = ["rmsnorm", "add_rmsnorm", "layernorm", "rope", "rope_qk", "rmsnorm_rope_qk", "rope_cache",
+           "rope_qk_cached", "rope_multi", "silu_mul", "geglu", "add", "embedding", "argmax",
+           "argmax_workspace_bytes", "softmax", "softmax_workspace_bytes", "ETError", "lib", "LIB_PATH",
+           "ROPE_HALF", "ROPE_INTERLEAVED", "GELU_ERF", "GELU_TANH", "abi_version"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libet.so")
 ROPE_HALF, ROPE_INTERLEAVED = 0, 1
