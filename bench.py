@@ -339,7 +339,7 @@ def cpu_baseline(w, min_seconds):
     import workloads as wl
     orc = oracle.load()
     calls = []            # (bytes, closure)
-    es = 2 if w.dtype == "bf16" else 4
+    es = 4 if w.dtype == "f32" else 2
     if w.embed:
         V, d, n, _ = w.embed
         table, ids = wl.gen_embedding(w)
@@ -399,6 +399,69 @@ def cpu_baseline(w, min_seconds):
             "cores": orc.threads(), "cpu": cpu, "kind": "oracle", "seconds": round(t_total, 2),
             "sample": f"{reps} whole steps of the same workload ({step_bytes} algorithmic bytes "
                       f"each), all ops at full size"}
+
+
+def cpu_next_ops(next_ops, min_seconds):
+    """The CPU oracle as it stands on a bounded sample of each next op's
+    workload (same generators, shapes and distributions, fewer rows or
+    tokens), timed like cpu_baseline: GB/s of algorithmic bytes, added to
+    that op's record as cpu_GBps with the sample named."""
+    import dataclasses
+    import oracle
+    import workloads as wl
+    orc = oracle.load()
+
+    def put(name, fn, nbytes, sample):
+        if name not in next_ops:
+            return
+        reps, t = 0, 0.0
+        while t < min_seconds or reps == 0:
+            t0 = time.perf_counter()
+            fn()
+            t += time.perf_counter() - t0
+            reps += 1
+        next_ops[name]["cpu_GBps"] = round(reps * nbytes / t / 1e9, 3)
+        next_ops[name]["cpu_sample"] = sample
+
+    lg, _ = wl.gen_argmax(wl.WORKLOADS[3])
+    lg = np.ascontiguousarray(lg[:32])
+    put("softmax", lambda: orc.softmax(lg, 0.7), 2 * lg.size * 4, "32 of the 256 rows")
+    g = np.random.default_rng([1002, 40])
+    x = wl.store(g.standard_normal((512, 4096)).astype(np.float32), "bf16")
+    gm = wl.store(g.uniform(0.5, 1.5, 4096).astype(np.float32), "bf16")
+    bt = wl.store(g.standard_normal(4096).astype(np.float32), "bf16")
+    put("layernorm", lambda: orc.layernorm(x, gm, bt, 1e-5), 2 * x.size * 2 + 2 * 4096 * 2,
+        "512 of the 4096 rows")
+    g = np.random.default_rng([1002, 41])
+    ga = wl.store(g.standard_normal((512, 14336)).astype(np.float32), "bf16")
+    ua = wl.store(g.standard_normal((512, 14336)).astype(np.float32), "bf16")
+    for form, name in ((0, "geglu_erf"), (1, "geglu_tanh")):
+        put(name, lambda: orc.geglu(ga, ua, form), 3 * ga.size * 2, "512 of the 4096 rows")
+    w2 = wl.WORKLOADS[2]
+    s = w2.rope
+    q, k, pos, inv = wl.gen_rope(w2)
+    q, k, pos = np.ascontiguousarray(q[:512]), np.ascontiguousarray(k[:512]), pos[:512].copy()
+    oc, osn = orc.rope_cache(inv, s.T, s.r)
+
+    def cached():
+        orc.rope_cached(q, pos, s.r, oc, osn, s.mu, s.layout)
+        orc.rope_cached(k, pos, s.r, oc, osn, s.mu, s.layout)
+    put("rope_cached", cached, 2 * 512 * (s.Hq + s.Hk) * s.r * 2 + 4 * 512 + 2 * 512 * (s.r // 2) * 4,
+        "512 of the 4096 tokens")
+    w6 = wl.WORKLOADS[6]
+    m = w6.rope_multi
+    q, k, pos, inv = wl.gen_rope_multi(w6)
+    q, k, pos = np.ascontiguousarray(q[:2400]), np.ascontiguousarray(k[:2400]), pos[:2400].copy()
+
+    def multi():
+        orc.rope_multi(q, pos, m.dims, inv, m.mu, m.layout)
+        orc.rope_multi(k, pos, m.dims, inv, m.mu, m.layout)
+    put("rope_multi", multi, 2 * 2400 * (m.Hq + m.Hk) * sum(m.dims) * 2 + 12 * 2400,
+        "2400 of the 19200 tokens (two frames)")
+    if "f16_step" in next_ops:
+        c = cpu_baseline(dataclasses.replace(w2, dtype="f16"), min_seconds)
+        next_ops["f16_step"]["cpu_GBps"] = c["value"]
+        next_ops["f16_step"]["cpu_sample"] = c["sample"]
 
 
 def main():
@@ -525,6 +588,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
+        if next_ops:
+            cpu_next_ops(next_ops, 1.0)
 
     s = w.rope
     line = {
