@@ -7,7 +7,10 @@ Workloads (shapes of Llama-style prefill and decode):
   3  decode, f32, 256 sequences of one token
   4  partial (r = 64 of 128) interleaved RoPE, f32, T = 16384, mu = 1.1
   5  large hidden, bf16, T = 8192, hidden 8192, in-place fused add + RMSNorm
+  2 in f16: the prefill step with f16 storage (the benchmark's f16 step)
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -137,4 +140,14 @@ FN = {"embedding": _check_embedding, "add": _check_add, "rmsnorm": _check_norm,
 def test_workload(et, orc, number, op):
     print(f"workload {number} {op}", flush=True)
     FN[op](et, orc, wl.WORKLOADS[number])
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("op", CHECKS[2])
+def test_prefill_f16(et, orc, op):
+    """The prefill step's ops at full size with f16 storage, as the benchmark
+    times them: sampled rows against the oracle (1 f16 ulp; bits where the
+    op is exact)."""
+    print(f"prefill f16 {op}", flush=True)
+    FN[op](et, orc, dataclasses.replace(wl.WORKLOADS[2], dtype="f16"))
     torch.cuda.synchronize()
