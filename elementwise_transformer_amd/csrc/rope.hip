@@ -208,11 +208,14 @@ __device__ inline void slot_offsets(int kk, const RopeArgs& a, int* ea, int* eb)
   }
 }
 
-// Rotate one pair with the pre-scaled (mu cos, mu sin).
+// Rotate one pair with the pre-scaled (mu cos, mu sin).  Each member is
+// formed the same way, fma(own, mu cos, partner * (-+ mu sin)), so a kernel
+// that holds only one member of a pair per lane (multi-axis RoPE) gives the
+// same bits as one that holds both.
 __device__ inline void rotate(float& x0, float& x1, float2 c) {
   const float a = x0, b = x1;
-  x0 = __builtin_fmaf(a, c.x, -(b * c.y));
-  x1 = __builtin_fmaf(a, c.y, b * c.x);
+  x0 = __builtin_fmaf(a, c.x, b * -c.y);
+  x1 = __builtin_fmaf(b, c.x, a * c.y);
 }
 
 // ------------------------------------------------------------------ RoPE
@@ -1018,9 +1021,7 @@ __device__ inline void rotate_runs(const S* xr, const float (&x)[PS], float (&y)
 #pragma unroll
     for (int j = 0; j < W; ++j) {
       const float2 c = tr[j];
-      const float y0 = __builtin_fmaf(x[e0 + j], c.x, -(xp[j] * c.y));
-      const float y1 = __builtin_fmaf(xp[j], c.y, x[e0 + j] * c.x);
-      y[e0 + j] = first ? y0 : y1;
+      y[e0 + j] = __builtin_fmaf(x[e0 + j], c.x, xp[j] * (first ? -c.y : c.y));
     }
   }
 }
@@ -1152,8 +1153,8 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
 #pragma unroll
       for (int e = 0; e < PS; e += 2) {
         const float2 c = tab[(e < kr ? d.z : d.w) + e / 2];
-        y[e] = __builtin_fmaf(x[e], c.x, -(x[e + 1] * c.y));
-        y[e + 1] = __builtin_fmaf(x[e], c.y, x[e + 1] * c.x);
+        y[e] = __builtin_fmaf(x[e], c.x, x[e + 1] * -c.y);
+        y[e + 1] = __builtin_fmaf(x[e + 1], c.x, x[e] * c.y);
       }
     }
     if constexpr (PS == 1) {
