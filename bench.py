@@ -190,26 +190,41 @@ def build_ops(w, et, torch):
 COUNTER_SUMMARY = {2: "prefill_bf16_T4096_hbm_counters.md"}
 
 
+# The kernel sources each step op is built from (relative to csrc/): a
+# counter record stays valid while these files are unchanged.
+OP_SOURCES = {
+    "silu_mul": ["eltwise.hip", "et_common.hpp"], "add": ["eltwise.hip", "et_common.hpp"],
+    "rmsnorm": ["norm.hip", "norm_common.hpp", "et_common.hpp"],
+    "add_rmsnorm": ["norm.hip", "norm_common.hpp", "et_common.hpp"],
+    "rope": ["rope.hip", "et_common.hpp"], "rmsnorm_rope": ["rope.hip", "et_common.hpp"],
+    "embedding": ["gather.hip", "et_common.hpp"], "argmax": ["argmax.hip", "et_common.hpp"],
+}
+
+
+def op_sources_sha256(op):
+    src = os.path.join(ROOT, "elementwise_transformer_amd", "csrc")
+    h = hashlib.sha256()
+    for f in OP_SOURCES[op]:
+        with open(os.path.join(src, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def traffic_record(workload, op):
     """HBM bytes per launch of `op` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size),
-    if that summary covers this workload and was taken on the current kernel
-    sources; else None."""
+    if that summary covers this workload and was taken on the current sources
+    of that op's kernel; else None."""
     name = COUNTER_SUMMARY.get(workload)
     path = os.path.join(ROOT, "profiles", name) if name else ""
-    if not name or not os.path.exists(path):
+    if not name or not os.path.exists(path) or op not in OP_SOURCES:
         return None
     text = open(path).read()
-    m_src = re.search(r"source sha256:\s*([0-9a-f]{64})", text)
-    m_b = re.search(r"traffic bytes per launch:\s*" + re.escape(op) + r"\s+([0-9.eE+]+)", text)
-    if not (m_src and m_b):
+    m = re.search(r"traffic bytes per launch:\s*" + re.escape(op) + r"\s+([0-9.eE+]+)\s+sources sha256\s+"
+                  r"([0-9a-f]{64})", text)
+    if not m:
         return None
-    src = os.path.join(ROOT, "elementwise_transformer_amd", "csrc")
-    h = hashlib.sha256()
-    for f in sorted(os.listdir(src)):
-        with open(os.path.join(src, f), "rb") as fh:
-            h.update(fh.read())
-    return float(m_b.group(1)) if h.hexdigest() == m_src.group(1) else None
+    return float(m.group(1)) if op_sources_sha256(op) == m.group(2) else None
 
 
 def _time_launches(stream, fn, sets, launches):
