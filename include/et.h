@@ -174,10 +174,9 @@ et_status et_rope_qk_cached_bf16(et_bf16* q, int64_t Hq, et_bf16* k,
                                  const float* cos_cache,
                                  const float* sin_cache, int64_t max_pos,
                                  float attn_scaling, int layout, void* stream);
-et_status et_rope_qk_cached_f16(et_f16* q, int64_t Hq, et_f16* k,
-                                int64_t Hk, const int32_t* pos, int64_t T,
-                                int64_t D, int64_t d_rot,
-                                const float* cos_cache,
+et_status et_rope_qk_cached_f16(et_f16* q, int64_t Hq, et_f16* k, int64_t Hk,
+                                const int32_t* pos, int64_t T, int64_t D,
+                                int64_t d_rot, const float* cos_cache,
                                 const float* sin_cache, int64_t max_pos,
                                 float attn_scaling, int layout, void* stream);
 
@@ -294,10 +293,10 @@ et_status et_embedding_f16(const et_f16* table, int64_t V,
  *   workspace_bytes == 0 (one workgroup per row, no scratch), or
  *   workspace != NULL with workspace_bytes >= et_argmax_workspace_bytes(rows,
  *   n) and 16-byte aligned, else ET_ERR_WORKSPACE (ET_ERR_NULL_POINTER for
- *   NULL with a nonzero size).  The caller owns the workspace.  It must be zero-filled before its
- *   first use; every call leaves it zero-filled again, so it can be reused as
- *   is.  Calls that share a workspace must not run concurrently.  The result
- *   is the same with or without a workspace.
+ *   NULL with a nonzero size).  The caller owns the workspace.  It must be
+ *   zero-filled before its first use; every call leaves it zero-filled
+ *   again, so it can be reused as is.  Calls that share a workspace must not
+ *   run concurrently.  The result is the same with or without a workspace.
  */
 size_t et_argmax_workspace_bytes(int64_t rows, int64_t n);
 et_status et_argmax_f32(const float* x, int64_t rows, int64_t n, int32_t* out,
