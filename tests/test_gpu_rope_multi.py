@@ -161,3 +161,42 @@ def test_rope_multi_video_full_size(et, orc):
         sub = np.ascontiguousarray(src[toks])
         ref, y64 = orc.rope_multi(sub, pos[toks], s.dims, inv, s.mu, s.layout)
         assert_multi(host(t)[toks], y64, ref, s.dims, s.layout, f"video {name}")
+
+
+def _random_case(g):
+    """Random even widths (some zero, some narrower than a vector), a head
+    at least as wide as their sum, either pairing, mixed signs of positions."""
+    A = int(g.integers(1, 9))
+    dims = [int(2 * g.integers(0, 40)) for _ in range(A)]
+    if sum(dims) == 0:
+        dims[0] = 2
+    span = sum(dims)
+    D = span + int(g.choice([0, 0, 2, 8, 16]))
+    if D > 1024:
+        return None
+    T, Hq, Hk = int(g.integers(1, 40)), int(g.integers(1, 6)), int(g.integers(0, 4))
+    return T, Hq, Hk, D, tuple(dims), int(g.integers(0, 2)), float(g.choice([1.0, 0.75])), int(g.integers(2, 1 << 16))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_rope_multi_random_geometry(et, orc, seed):
+    """Seeded random axis geometries in every storage type: oracle parity
+    (per-axis PAIR tolerance, tail bits kept) and the scalar path's bits
+    equal to the vector path's."""
+    g = np.random.default_rng([4747, seed])
+    case = None
+    while case is None:
+        case = _random_case(g)
+    T, Hq, Hk, D, dims, layout, mu, pos_hi = case
+    for dt in DTS:
+        q, k, pos, inv = _inputs(case, dt, 1000 + seed)
+        qt, kt = dev(q), (dev(k) if k is not None else None)
+        et.rope_multi(qt, kt, dev(pos), dims, dev(inv), attn_scaling=mu, layout=layout)
+        for name, src, t in (("q", q, qt), ("k", k, kt)):
+            if src is None:
+                continue
+            ref, y64 = orc.rope_multi(src, pos, dims, inv, mu, layout)
+            assert_multi(host(t), y64, ref, dims, layout, f"random {seed} {dt} {case} {name}")
+        qm = _misaligned(dev(q))
+        et.rope_multi(qm, None, dev(pos), dims, dev(inv), attn_scaling=mu, layout=layout)
+        assert_bits(host(qm), host(qt), f"random {seed} {dt} {case} misaligned")
