@@ -13,6 +13,8 @@
 // done by the last block with scalar accesses.  Misaligned buffers use the
 // scalar kernel.  y may equal a or b: every element is read by the thread
 // that writes it, before it writes it.
+#include <type_traits>
+
 #include "et_common.hpp"
 
 namespace et {
@@ -69,16 +71,14 @@ __device__ inline float silu(float g) {
   }
 }
 
-// erfc(z), branch free: the Chebyshev-fitted form of Press, Teukolsky,
-// Vetterling and Flannery, Numerical Recipes (2nd ed.), section 6.2:
-// for a = |z|, t = 1 / (1 + a/2) and erfc(a) = t exp(-a^2 + P(t)) with P
-// of degree 9, fractional error below 1.2e-7 for every a >= 0 (checked here
+// erfc, branch free: the Chebyshev-fitted form of Press, Teukolsky,
+// Vetterling and Flannery, Numerical Recipes (2nd ed.), section 6.2: for
+// a = |z|, t = 1 / (1 + a/2) and erfc(a) = t exp(-a^2 + P(t)), fractional
+// error below 1.2e-7 for every a >= 0 with P of degree 9 (checked here
 // against scipy to 1.05e-7); erfc(-a) = 2 - erfc(a).  The library erfcf
 // branches by range, so a wave of mixed arguments runs every branch: it made
 // the bf16 GELU-gated multiply ALU-bound (103 us where 57 us moves the bytes).
-__device__ inline float erfc_fit(float z) {
-  const float a = __builtin_fabsf(z);
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, a, 1.0f));
+__device__ inline float erfc_poly9(float t) {
   float p = 0.17087277f;
   p = __builtin_fmaf(p, t, -0.82215223f);
   p = __builtin_fmaf(p, t, 1.48851587f);
@@ -88,38 +88,53 @@ __device__ inline float erfc_fit(float z) {
   p = __builtin_fmaf(p, t, 0.09678418f);
   p = __builtin_fmaf(p, t, 0.37409196f);
   p = __builtin_fmaf(p, t, 1.00002368f);
-  p = __builtin_fmaf(p, t, -1.26551223f);
-  // exp(p - a^2) as the hardware exp2; the exponent is <= p(t) < 0.
-  const float y = t * __builtin_amdgcn_exp2f(__builtin_fmaf(-a, a, p) * 1.44269504088896340736f);
-  return z >= 0.0f ? y : 2.0f - y;
+  return __builtin_fmaf(p, t, -1.26551223f);
 }
 
-// erfc(z) for 2-byte storage, whose results keep 8 or 11 significant bits:
-// the same form with P of degree 5 instead of 9, fitted here to
-// log(erfc(a) e^(a^2) / t) over 0 <= a <= 12 (Chebyshev nodes in t,
-// weighted least squares iterated toward the minimax fit, coefficients
-// rounded to f32).  Relative error below 1.3e-5 in f32 arithmetic against
-// scipy's erfc, inside 3 % of half an f16 ulp; four fused multiply-adds
-// fewer per element in a kernel whose 2-byte form is close to ALU-bound.
-__device__ inline float erfc_fit5(float z) {
-  const float a = __builtin_fabsf(z);
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, a, 1.0f));
+// The same form for 2-byte storage, whose results keep 8 or 11 significant
+// bits: P of degree 5, fitted here to log(erfc(a) e^(a^2) / t) over
+// 0 <= a <= 12 (Chebyshev nodes in t, weighted least squares iterated toward
+// the minimax fit, coefficients rounded to f32).  Relative error below
+// 1.3e-5 in f32 arithmetic against scipy's erfc, inside 3 % of half an f16
+// ulp; four fused multiply-adds fewer per element in a kernel whose 2-byte
+// form is close to ALU-bound.
+__device__ inline float erfc_poly5(float t) {
   float p = 0x1.d141fp-3f;
   p = __builtin_fmaf(p, t, -0x1.68beacp-1f);
   p = __builtin_fmaf(p, t, 0x1.e0c8f6p-2f);
   p = __builtin_fmaf(p, t, 0x1.071e78p-2f);
   p = __builtin_fmaf(p, t, 0x1.04764ap+0f);
-  p = __builtin_fmaf(p, t, -0x1.4438d8p+0f);
-  const float y = t * __builtin_amdgcn_exp2f(__builtin_fmaf(-a, a, p) * 1.44269504088896340736f);
-  return z >= 0.0f ? y : 2.0f - y;
+  return __builtin_fmaf(p, t, -0x1.4438d8p+0f);
 }
 
-// GELU, exact form: x * Phi(x) = x * erfc(-x / sqrt 2) / 2 (the identity
-// 1 + erf(z) = erfc(-z) keeps the tail of negative x, where 1 + erf cancels).
+// GELU-gated product, exact form: x Phi(x) u = x erfc(-x / sqrt 2) u / 2 (the
+// identity 1 + erf(z) = erfc(-z) keeps the tail of negative x, where 1 + erf
+// cancels), with erfc(a) = t 2^k, k = (P(t) - a^2) log2 e <= 0.
+// The hardware exp2 returns no subnormals, so 2^k alone would flush every
+// erfc below 2^-126 -- results x Phi(x) u down to 2^-149 in f32 and bf16
+// storage, from x near -13 on.  There k is split into its floor n and a
+// fraction, and 2^n is applied last with ldexp, which rounds a subnormal
+// result once and correctly; k is held above -320, where every product
+// of f32 values times 2^k is below the smallest subnormal.  f16 storage
+// flushes results below 2^-25 in its own rounding, so the plain 2^k is kept.
 template <typename S>
-__device__ inline float gelu_erf(float x) {
-  if constexpr (sizeof(S) == 4) return 0.5f * x * erfc_fit(x * -0.70710678118654752440f);
-  else return 0.5f * x * erfc_fit5(x * -0.70710678118654752440f);
+__device__ inline float gelu_erf_mul(float x, float u) {
+  const float z = x * -0.70710678118654752440f;
+  const float a = __builtin_fabsf(z);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, a, 1.0f));
+  const float p = sizeof(S) == 4 ? erfc_poly9(t) : erfc_poly5(t);
+  const float k = __builtin_fmaf(-a, a, p) * 1.44269504088896340736f;
+  if constexpr (std::is_same<S, F16>::value) {
+    const float y = t * __builtin_amdgcn_exp2f(k);
+    return 0.5f * x * (z >= 0.0f ? y : 2.0f - y) * u;
+  } else {
+    const float kc = __builtin_fmaxf(k, -320.0f);
+    const float n = __builtin_floorf(kc);
+    const int ni = static_cast<int>(n);
+    const float h = 0.5f * t * __builtin_amdgcn_exp2f(kc - n);  // erfc(a) / 2 = h 2^n
+    if (z >= 0.0f) return __builtin_ldexpf(x * h * u, ni);       // x <= 0: Phi(x) = h 2^n
+    return x * (1.0f - __builtin_ldexpf(h, ni)) * u;             // x > 0: 1 - h 2^n
+  }
 }
 
 // GELU, tanh form: (1 + tanh u) / 2 = 1 / (1 + e^(-2u)) with
@@ -146,7 +161,7 @@ __device__ inline float apply(float a, float b) {
   } else if constexpr (OP == kSiluMul) {
     return silu<S>(a) * b;
   } else if constexpr (OP == kGeluErfMul) {
-    return gelu_erf<S>(a) * b;
+    return gelu_erf_mul<S>(a, b);
   } else {
     return gelu_tanh<S>(a) * b;
   }
