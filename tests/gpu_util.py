@@ -156,3 +156,87 @@ def assert_pair(got: np.ndarray, y64: np.ndarray, ref: np.ndarray, r: int, layou
         ud = np.abs(bf16_key(got[..., :r]) - bf16_key(ref[..., :r]))
         bad = np.flatnonzero(~((ud <= 1) | (err <= BF16_PAIR * pn)))
         assert bad.size == 0, f"{what}: {bad.size} rotated 2-byte entries over 1 ulp and 2^-16 |pair|"
+
+
+U = 2.0 ** -24
+
+
+def check_softmax(got, x_store, t, y, y64, what=""):
+    """Softmax bound: f32 derived relative bound, 2-byte 1 ulp; results
+    below 2^-126 may come out as 0 (see the softmax tests)."""
+    if got.dtype == np.float32:
+        z = widen(x_store) / np.float64(np.float32(t))
+        with np.errstate(invalid="ignore"):
+            m = np.max(z, axis=-1, keepdims=True)
+            tol = U * (2 * np.abs(z) + 3 * np.abs(m) + 3 * np.abs(z - m) + 128.0)
+        g = got.astype(np.float64)
+        gn, rn = np.isnan(g), np.isnan(y64)
+        assert np.array_equal(gn, rn), f"{what}: NaN positions differ"
+        fin = ~rn
+        err = np.abs(g[fin] - y64[fin])
+        # an exact 0 (the exponential of -inf) must come out as 0 (+ the floor)
+        with np.errstate(invalid="ignore"):
+            lim = np.where(y64[fin] == 0, 0.0, tol[fin] * np.abs(y64[fin])) + 2.0 ** -140
+        flushed = (np.abs(y64[fin]) < 2.0 ** -126) & (g[fin] == 0)
+        lim = np.where(flushed, np.inf, lim)
+        bad = np.flatnonzero(~(err <= lim))
+        if bad.size:
+            i = bad[np.argmax(err[bad] / lim[bad])]
+            raise AssertionError(f"{what}: {bad.size} over tolerance; worst got={g[fin][i]!r} "
+                                 f"ref={y64[fin][i]!r} rel={err[i] / max(abs(y64[fin][i]), 1e-300):.3g} "
+                                 f"tol={tol[fin][i]:.3g}")
+    else:
+        flushed = (np.abs(y64) < 2.0 ** -126) & (got == 0)
+        g = np.where(flushed, y, got)
+        assert_bf16_ulp(g, y, what)
+
+
+def check_layernorm(got, xs, gs, bs, eps, y, y64, what=""):
+    """LayerNorm absolute bound of the f32 arithmetic, plus one ulp in 2-byte
+    storage (see the LayerNorm tests)."""
+    x = widen(xs)
+    g = widen(gs)
+    b = np.zeros_like(g) if bs is None else widen(bs)
+    mu = x.mean(axis=1, keepdims=True)
+    c = x - mu
+    inv = 1.0 / np.sqrt((c * c).mean(axis=1, keepdims=True) + float(np.float32(eps)))
+    tol = U * inv * np.abs(g) * (np.abs(x) + 64 * np.abs(x).mean(axis=1, keepdims=True) + 64 * np.abs(c)) \
+        + 2 * U * (np.abs(b) + np.abs(y64)) + 2.0 ** -140
+    if got.dtype != np.float32:
+        tol = tol + ulp16(y64, got.dtype)
+    gw = widen(got)
+    gn, rn = np.isnan(gw), np.isnan(y64)
+    assert np.array_equal(gn, rn), f"{what}: NaN positions differ"
+    err = np.abs(gw - y64)
+    bad = np.flatnonzero(~(err[~rn] <= tol[~rn]))
+    if bad.size:
+        i = bad[np.argmax((err[~rn] / tol[~rn])[bad])]
+        raise AssertionError(f"{what}: {bad.size} over tolerance; worst got={gw[~rn][i]!r} "
+                             f"ref={y64[~rn][i]!r} tol={tol[~rn][i]:.3g}")
+
+
+def check_geglu(got, gate_s, form, y, y64, what=""):
+    """GeGLU: f32 relative bound of the form's arithmetic, 2-byte 1 ulp (see
+    the GeGLU tests)."""
+    if got.dtype != np.float32:
+        assert_bf16_ulp(got, y, what)
+        return
+    x = widen(gate_s)
+    with np.errstate(over="ignore", invalid="ignore"):
+        if form == 0:
+            rel = U * (2 * x * x + 64)
+        else:
+            v = 1.5957691216057308 * (x + 0.044715 * x ** 3)
+            rel = U * (3 * np.abs(v) + 64)
+    g = got.astype(np.float64)
+    gn, rn = np.isnan(g), np.isnan(y64)
+    assert np.array_equal(gn, rn), f"{what}: NaN positions differ"
+    fin = ~rn & np.isfinite(y64)
+    assert np.array_equal(g[~rn & ~fin], y64[~rn & ~fin]), f"{what}: infinities differ"
+    err = np.abs(g[fin] - y64[fin])
+    lim = rel[fin] * np.abs(y64[fin]) + 2.0 ** -140
+    bad = np.flatnonzero(~(err <= lim))
+    if bad.size:
+        i = bad[np.argmax(err[bad] / lim[bad])]
+        raise AssertionError(f"{what}: {bad.size} over tolerance; worst got={g[fin][i]!r} "
+                             f"ref={y64[fin][i]!r} x={x[fin][i]!r}")

@@ -1,0 +1,170 @@
+"""Seeded random shapes for every op, in every storage type, against the
+CPU oracle through the C ABI.
+
+The fixed-shape tests pick sizes around known launch boundaries; these draw
+row lengths, row counts, head geometries, flat lengths and buffer alignment
+at random (row lengths log-uniform up to about 140,000, half of them whole
+16-byte vectors), so the launch-shape choices -- threads per row, vectors
+per thread, long-row and chunked paths, ragged tails, the scalar path for
+misaligned buffers -- are reached from points nobody picked.  Each result is
+held to its op's own tolerance (gpu_util), and the ops whose kernels do no
+reduction (add, embedding, argmax, RoPE pass-through, the fused sum h) to
+equal bits.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_util import (assert_bits, assert_close, assert_pair, check_geglu, check_layernorm,
+                      check_softmax, dev, host)
+
+pytestmark = pytest.mark.gpu
+
+DTS = ["f32", "bf16", "f16"]
+SEEDS = range(8)
+
+
+@pytest.fixture(scope="module")
+def et():
+    import elementwise_transformer_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return m
+
+
+def _length(g, lo, hi):
+    """Log-uniform in [lo, hi]; half the draws rounded down to a multiple of 8."""
+    n = int(np.exp(g.uniform(np.log(lo), np.log(hi + 1))))
+    n = min(max(n, lo), hi)
+    return max(lo, n - n % 8) if g.uniform() < 0.5 else n
+
+
+def _rows(g, n, budget=1 << 21):
+    """A row count from 1 to 40, capped so rows * n stays near the budget."""
+    return int(max(1, min(int(g.integers(1, 41)), budget // max(n, 1))))
+
+
+def _dev_maybe_misaligned(a, misalign):
+    """To the device, at an address 16-byte aligned or (misalign) not."""
+    t = dev(a)
+    if not misalign:
+        return t
+    flat = torch.empty(t.numel() + 8, dtype=t.dtype, device=t.device)
+    v = flat[1:1 + t.numel()].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 != 0
+    return v
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_norms(et, orc, dt, seed):
+    g = np.random.default_rng([4848, seed, DTS.index(dt)])
+    d = _length(g, 1, 70000)
+    rows = _rows(g, d)
+    mis = bool(g.uniform() < 0.25)
+    x = wl.store((g.standard_normal((rows, d)) * 2).astype(np.float32), dt)
+    r = wl.store(g.standard_normal((rows, d)).astype(np.float32), dt)
+    w = wl.store(g.uniform(0.5, 1.5, d).astype(np.float32), dt)
+    b = wl.store(g.standard_normal(d).astype(np.float32), dt)
+    what = f"{dt} rows={rows} d={d} misaligned={mis}"
+    xt = _dev_maybe_misaligned(x, mis)
+    yr, y64 = orc.rmsnorm(x, w, 1e-5)
+    assert_close(host(et.rmsnorm(xt, dev(w), 1e-5)), y64, yr, "rmsnorm " + what)
+    yt, ht = et.add_rmsnorm(xt, dev(r), dev(w), 1e-5)
+    oy, oh, oy64 = orc.add_rmsnorm(x, r, w, 1e-5)
+    assert_bits(host(ht), oh, "add_rmsnorm h " + what)
+    assert_close(host(yt), oy64, oy, "add_rmsnorm y " + what)
+    y, ly64 = orc.layernorm(x, w, b, 1e-5)
+    check_layernorm(host(et.layernorm(xt, dev(w), dev(b), 1e-5)), x, w, b, 1e-5, y, ly64,
+                    "layernorm " + what)
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_softmax(et, orc, dt, seed):
+    g = np.random.default_rng([4949, seed, DTS.index(dt)])
+    n = _length(g, 1, 140000)
+    rows = _rows(g, n)
+    mis = bool(g.uniform() < 0.25)
+    x = wl.store((g.standard_normal((rows, n)) * 3).astype(np.float32), dt)
+    t = float(np.float32(g.choice([0.5, 0.7, 1.0, 1.7])))
+    y, y64 = orc.softmax(x, t)
+    got = host(et.softmax(_dev_maybe_misaligned(x, mis), t))
+    check_softmax(got, x, t, y, y64, f"softmax {dt} rows={rows} n={n} t={t} misaligned={mis}")
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_rope(et, orc, dt, seed):
+    g = np.random.default_rng([5050, seed, DTS.index(dt)])
+    D = int(2 * g.integers(1, 161))
+    r = int(2 * g.integers(0, D // 2 + 1))
+    T, Hq, Hk = int(g.integers(1, 50)), int(g.integers(1, 9)), int(g.integers(0, 5))
+    layout = int(g.integers(0, 2))
+    mu = float(np.float32(g.choice([1.0, 1.1, 0.5])))
+    q = wl.store(g.standard_normal((T, Hq, D)).astype(np.float32), dt)
+    k = wl.store(g.standard_normal((T, Hk, D)).astype(np.float32), dt) if Hk else None
+    pos = g.integers(0, 1 << 20, T).astype(np.int32)
+    inv = wl.inv_freq(1e4, r) if r else np.zeros(1, np.float32)
+    gq = wl.store(g.uniform(0.5, 1.5, D).astype(np.float32), dt)
+    gk = wl.store(g.uniform(0.5, 1.5, D).astype(np.float32), dt)
+    what = f"{dt} T={T} Hq={Hq} Hk={Hk} D={D} r={r} layout={layout}"
+    qt, kt = dev(q), (dev(k) if k is not None else None)
+    et.rope_qk(qt, kt, dev(pos), dev(inv), d_rot=r, attn_scaling=mu, layout=layout)
+    q2, k2 = dev(q), (dev(k) if k is not None else None)
+    et.rmsnorm_rope_qk(q2, dev(gq), k2, dev(gk) if k is not None else None, 1e-6, dev(pos),
+                       dev(inv), d_rot=r, attn_scaling=mu, layout=layout)
+    for name, src, gain, t1, t2 in (("q", q, gq, qt, q2), ("k", k, gk, kt, k2)):
+        if src is None:
+            continue
+        ref, y64 = orc.rope(src, pos, r, inv, mu, layout)
+        got = host(t1)
+        assert_pair(got, y64, ref, r, layout, f"rope {name} {what}")
+        assert_bits(got[..., r:], src[..., r:], f"rope pass-through {name} {what}")
+        ref, y64 = orc.rmsnorm_rope(src, gain, 1e-6, pos, r, inv, mu, layout)
+        got = host(t2)
+        assert_pair(got, y64, ref, r, layout, f"rmsnorm_rope {name} {what}")
+        assert_close(got[..., r:], y64[..., r:], ref[..., r:], f"rmsnorm_rope tail {name} {what}")
+    # the scalar path (misaligned q) gives the vector path's bits
+    qm = _dev_maybe_misaligned(q, True)
+    et.rope_qk(qm, None, dev(pos), dev(inv), d_rot=r, attn_scaling=mu, layout=layout)
+    assert_bits(host(qm), host(qt), f"rope misaligned {what}")
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_flat(et, orc, dt, seed):
+    g = np.random.default_rng([5151, seed, DTS.index(dt)])
+    n = _length(g, 1, 1 << 21)
+    mis = bool(g.uniform() < 0.25)
+    a = wl.store((g.standard_normal(n) * 3).astype(np.float32), dt)
+    b = wl.store(g.standard_normal(n).astype(np.float32), dt)
+    what = f"{dt} n={n} misaligned={mis}"
+    at, bt = _dev_maybe_misaligned(a, mis), dev(b)
+    assert_bits(host(et.add(at, bt)), orc.add(a, b), "add " + what)
+    yr, y64 = orc.silu_mul(a, b)
+    assert_close(host(et.silu_mul(at, bt)), y64, yr, "silu_mul " + what)
+    for form in (0, 1):
+        y, gy64 = orc.geglu(a, b, form)
+        check_geglu(host(et.geglu(at, bt, form)), a, form, y, gy64, f"geglu form={form} {what}")
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_embedding_argmax(et, orc, dt, seed):
+    g = np.random.default_rng([5252, seed, DTS.index(dt)])
+    V, d, nid = int(g.integers(1, 3000)), _length(g, 1, 9000), int(g.integers(1, 60))
+    mis = bool(g.uniform() < 0.25)
+    table = wl.store(g.standard_normal((V, d)).astype(np.float32), dt)
+    ids = g.integers(-2, V + 2, nid).astype(np.int32)            # some out of range
+    got = host(et.embedding(_dev_maybe_misaligned(table, mis), dev(ids)))
+    assert_bits(got, orc.embedding(table, ids), f"embedding {dt} V={V} d={d} n={nid} misaligned={mis}")
+    n = _length(g, 1, 140000)
+    rows = _rows(g, n)
+    # integer-valued logits: many ties, so the lowest-index rule is exercised
+    x = wl.store(np.round(g.standard_normal((rows, n)) * 6).astype(np.float32), dt)
+    ref = orc.argmax(x)
+    for split in (True, False):
+        got = host(et.argmax(_dev_maybe_misaligned(x, mis), split=split))
+        assert_bits(got, ref, f"argmax {dt} rows={rows} n={n} split={split} misaligned={mis}")

@@ -22,11 +22,9 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_util import assert_bf16_ulp, assert_bits, dev, host, widen
+from gpu_util import assert_bits, check_softmax, dev, host, widen
 
 pytestmark = pytest.mark.gpu
-
-U = 2.0 ** -24
 
 
 @pytest.fixture(scope="module")
@@ -38,34 +36,6 @@ def et():
 
 def _rng(*key):
     return np.random.default_rng([4343, *key])
-
-
-def _check(got, x_store, t, y, y64, what):
-    if got.dtype == np.float32:
-        z = widen(x_store) / np.float64(np.float32(t))
-        with np.errstate(invalid="ignore"):
-            m = np.max(z, axis=-1, keepdims=True)
-            tol = U * (2 * np.abs(z) + 3 * np.abs(m) + 3 * np.abs(z - m) + 128.0)
-        g = got.astype(np.float64)
-        gn, rn = np.isnan(g), np.isnan(y64)
-        assert np.array_equal(gn, rn), f"{what}: NaN positions differ"
-        fin = ~rn
-        err = np.abs(g[fin] - y64[fin])
-        # an exact 0 (the exponential of -inf) must come out as 0 (+ the floor)
-        with np.errstate(invalid="ignore"):
-            lim = np.where(y64[fin] == 0, 0.0, tol[fin] * np.abs(y64[fin])) + 2.0 ** -140
-        flushed = (np.abs(y64[fin]) < 2.0 ** -126) & (g[fin] == 0)
-        lim = np.where(flushed, np.inf, lim)
-        bad = np.flatnonzero(~(err <= lim))
-        if bad.size:
-            i = bad[np.argmax(err[bad] / lim[bad])]
-            raise AssertionError(f"{what}: {bad.size} over tolerance; worst got={g[fin][i]!r} "
-                                 f"ref={y64[fin][i]!r} rel={err[i] / max(abs(y64[fin][i]), 1e-300):.3g} "
-                                 f"tol={tol[fin][i]:.3g}")
-    else:
-        flushed = (np.abs(y64) < 2.0 ** -126) & (got == 0)
-        g = np.where(flushed, y, got)
-        assert_bf16_ulp(g, y, what)
 
 
 def _logits(shape, dt, key, scale=3.0):
@@ -84,7 +54,7 @@ def test_softmax_matches_oracle(et, orc, dt, shape):
         xs = _logits(shape, dt, (shape[1], 1 if dt == "f32" else 2))
         y, y64 = orc.softmax(xs, t)
         got = host(et.softmax(dev(xs), t))
-        _check(got, xs, t, y, y64, f"{dt} {shape} t={t}")
+        check_softmax(got, xs, t, y, y64, f"{dt} {shape} t={t}")
         assert np.all(np.abs(y64.sum(axis=1) - 1.0) < 1e-12)
 
 
@@ -152,7 +122,7 @@ def test_softmax_scalar_path(et, orc, dt, n):
     mis.copy_(t)
     assert mis.data_ptr() % 16 != 0
     got = host(et.softmax(mis, 0.8))
-    _check(got, xs, 0.8, y, y64, f"{dt} n={n} misaligned")
+    check_softmax(got, xs, 0.8, y, y64, f"{dt} n={n} misaligned")
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
@@ -173,7 +143,7 @@ def test_softmax_special_values(et, orc, dt, n):
     assert np.all(np.isnan(widen(got[:3])))
     assert widen(got[3:4])[0, n - 1] == 0.0
     assert np.all(np.isfinite(widen(got[3:])))
-    _check(got[3:], xs[3:], 1.0, y[3:], y64[3:], f"{dt} n={n} special")
+    check_softmax(got[3:], xs[3:], 1.0, y[3:], y64[3:], f"{dt} n={n} special")
 
 
 def test_softmax_empty_and_degenerate(et):
@@ -203,4 +173,4 @@ def test_softmax_decode_logits_full_size(et, orc):
     rows = sorted(set([0, 1, 127, 255] + list(np.flatnonzero(nan_rows)[:2])))
     sub = np.ascontiguousarray(lg[rows])
     y, y64 = orc.softmax(sub, 0.7)
-    _check(got[rows], sub, 0.7, y, y64, "decode logits")
+    check_softmax(got[rows], sub, 0.7, y, y64, "decode logits")
