@@ -12,7 +12,10 @@ Prints ONE JSON line: whole-step throughput in GB/s of algorithmic HBM
 traffic (each input read once, each output written once; in-place RoPE counts
 only rotated entries), per-op GB/s and fraction of the 8 TB/s peak from HIP
 events on the launch stream, rows/s for the fused RMSNorm+RoPE, the roofline
-record of the dominant kernel and the CPU oracle timed on a sample.
+record of the dominant kernel and the CPU oracle timed on a sample.  After the
+timed region it also times plain HBM streams (libet_probe.so: loads and stores
+only, at the step's operand sizes and store policies) and reports each op's
+fraction of the stream of its own shape.
 
     python bench.py [--steps K] [--warmup W] [--workload 2|3|4|5]
 """
@@ -46,6 +49,8 @@ def parse():
                         "plain copy kernel of known size, to scale HBM traffic counters)")
     p.add_argument("--no-next-ops", action="store_true",
                    help="skip timing the ops beyond the step (softmax, LayerNorm, GeGLU)")
+    p.add_argument("--no-stream-ceiling", action="store_true",
+                   help="skip timing the plain-stream probe (libet_probe.so)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="least CPU time spent timing the oracle on whole steps")
     return p.parse_args()
@@ -245,6 +250,73 @@ def _time_launches(stream, fn, sets, launches):
     for ev in evs:
         ev.close()
     return t
+
+
+# Plain streams the kernels are measured against: (name, operand bytes,
+# reads, writes, device-scope stores).  32 MiB is one [4096, 4096] bf16
+# operand of the prefill row ops (RMSNorm and the gather read one and write
+# one, add reads two and writes one, fused add+RMSNorm reads two and writes
+# two); 112 MiB one [4096, 14336] bf16 operand of the prefill SiLU-mul (two
+# reads, one write).  Non-temporal and device-scope stores are the two
+# policies the kernels choose between by output size.
+CEILING_CASES = [
+    ("read_32MiB", 32 << 20, 1, 0, 0),
+    ("write_32MiB", 32 << 20, 0, 1, 0),
+    ("1R1W_32MiB", 32 << 20, 1, 1, 0),
+    ("1R1W_32MiB_dev", 32 << 20, 1, 1, 1),
+    ("2R1W_32MiB", 32 << 20, 2, 1, 0),
+    ("2R1W_32MiB_dev", 32 << 20, 2, 1, 1),
+    ("2R2W_32MiB", 32 << 20, 2, 2, 0),
+    ("2R1W_112MiB", 4096 * 14336 * 2, 2, 1, 0),
+    ("2R1W_112MiB_dev", 4096 * 14336 * 2, 2, 1, 1),
+]
+
+
+# The plain stream of each prefill-step op's shape and store policy (the
+# policy its kernel picks at that output size); RoPE's in-place rotation of
+# q (32 MiB) and k (8 MiB) is a 1-read 1-write stream of about that size.
+OP_CEILING = {2: {"rmsnorm": "1R1W_32MiB", "embedding": "1R1W_32MiB", "add": "2R1W_32MiB_dev",
+                  "add_rmsnorm": "2R2W_32MiB", "rope": "1R1W_32MiB_dev",
+                  "rmsnorm_rope": "1R1W_32MiB_dev", "silu_mul": "2R1W_112MiB_dev"}}
+
+
+def stream_ceiling(torch, stream, launches=40):
+    """Per-launch HIP-event times of plain HBM streams (libet_probe.so: 16-byte
+    non-temporal loads, stores by the given policy, nothing computed between),
+    each case over rotating buffer sets whose footprint is several times the
+    256 MB Infinity Cache, so every launch streams from HBM.  Algorithmic
+    bytes = (reads + writes) x operand bytes; the best of 4 and 8 vectors
+    per lane is kept."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "elementwise_transformer_amd", "libet_probe.so"))
+    f = lib.et_probe_stream
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, vp]
+    f.restype = ctypes.c_int
+    out = {}
+    for name, nb, nr, nw, dev in CEILING_CASES:
+        sets = max(4, -(-(1 << 30) // (4 * nb)))
+        bufs = [[torch.randint(0, 256, (nb,), dtype=torch.uint8, device="cuda") for _ in range(4)]
+                for _ in range(sets)]
+        best = None
+        for u in (4, 8):
+            def fn(i, u=u):
+                a, b, y, h = bufs[i % sets]
+                rc = f(a.data_ptr(), b.data_ptr(), y.data_ptr(), h.data_ptr(), nb, nr, nw, u, dev,
+                       stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"et_probe_stream failed ({rc}) on {name}")
+            t = _time_launches(stream, fn, sets, launches)
+            avg = float(np.mean(t))
+            if best is None or avg < best[0]:
+                best = (avg, float(np.median(t)), u)
+        gbps = (nr + nw) * nb / (best[0] * 1e-3) / 1e9
+        out[name] = {"bytes": (nr + nw) * nb, "avg_us": round(best[0] * 1e3, 2),
+                     "median_us": round(best[1] * 1e3, 2), "vectors_per_lane": best[2],
+                     "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_GBPS, 4)}
+        del bufs
+    return out
 
 
 def time_next_ops(et, torch, wl, stream, sets=3, launches=60):
@@ -539,6 +611,7 @@ def main():
     # its own workload after the timed region, as back-to-back launches over
     # rotating buffer sets with one pair of events per launch.
     next_ops = None if args.no_next_ops else time_next_ops(et, torch, wl, stream)
+    ceiling = None if args.no_stream_ceiling else stream_ceiling(torch, stream)
 
     # Attainable-bandwidth context: a plain device-to-device copy as large as
     # the dominant op's largest operand (read once, written once), timed the
@@ -587,6 +660,10 @@ def main():
                "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_GBPS, 4)}
         if op.rows:
             rec["rows_per_s"] = float(f"{op.rows / (avg * 1e-3):.4g}")
+        case = OP_CEILING.get(args.workload, {}).get(op.name)
+        if ceiling and case:
+            rec["stream_ceiling"] = case
+            rec["frac_of_ceiling"] = round(gbps / ceiling[case]["GBps"], 4)
         per_op[op.name] = rec
     dom = ops[dom]
     dom_avg_s = float(np.mean(dom.ms)) * 1e-3
@@ -599,6 +676,21 @@ def main():
                         "device-scope stores; the cache writes part of their output back to HBM "
                         "after the kernel ends, so their per-kernel figures exclude that part, "
                         "while the whole-step value includes it"}
+    case = OP_CEILING.get(args.workload, {}).get(dom.name)
+    if ceiling and case:
+        roofline["stream_ceiling"] = {"case": case, "GBps": ceiling[case]["GBps"],
+                                      "frac_of_ceiling": round(achieved / ceiling[case]["GBps"], 4)}
+
+    # The step as plain streams: each op's bytes at the measured rate of the
+    # stream of its shape and store policy (an op with no such stream, the
+    # latency-bound argmax, at its own time), against the measured step.
+    step_ceiling = None
+    cases = OP_CEILING.get(args.workload, {})
+    if ceiling and cases:
+        eq_s = sum(op.nbytes / (ceiling[cases[op.name]]["GBps"] * 1e9) if op.name in cases
+                   else float(np.mean(op.ms)) * 1e-3 for op in ops)
+        step_ceiling = {"stream_step_us": round(eq_s * 1e6, 2), "step_us": round(ms_step * 1e3, 2),
+                        "frac": round(eq_s * 1e3 / ms_step, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -626,6 +718,8 @@ def main():
         "ops": per_op,
         "roofline": roofline,
         "copy_context": copy_ctx,
+        "stream_ceiling": ceiling,
+        "step_vs_stream_ceiling": step_ceiling,
         "next_ops": next_ops,
         "cpu_baseline": cpu,
     }

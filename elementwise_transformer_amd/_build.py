@@ -1,7 +1,9 @@
 """Build libet.so: the gfx950 HIP kernels and their C-ABI entry points.
 
 Each ``csrc/*.hip`` file is compiled with hipcc for gfx950 into an object
-under ``_build/``, then linked into ``libet.so`` next to this file.
+under ``_build/``, then linked into ``libet.so`` next to this file.  The
+plain-stream probe the benchmark measures the kernels against
+(``probe/*.hip``) is linked apart, into ``libet_probe.so``.
 Usage: ``python elementwise_transformer_amd/_build.py`` (the package itself
 refuses to import until the library exists).
 """
@@ -18,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libet.so")
+PROBE_SRC = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PKG, "libet_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -O3, IEEE f32 division and square root (HIP's default), denormals kept, no
@@ -40,21 +44,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libet.so; returns its path."""
-    os.makedirs(OBJ, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source, link libet.so and libet_probe.so; returns
+    the path of libet.so."""
+    os.makedirs(OBJ, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probes = sorted(glob.glob(os.path.join(PROBE_SRC, "*.hip")))
+    jobs = min(len(srcs) + len(probes), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs + probes))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} from {len(srcs)} sources and {PROBE_LIB} from {len(probes)}")
     return LIB
 
 

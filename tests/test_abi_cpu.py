@@ -338,3 +338,35 @@ int main() {
         if r.returncode != 0:
             pytest.fail(r.stderr[-3000:])
         assert subprocess.run([exe]).returncode == 0
+
+
+@gpu_visible
+def test_stream_probe_validation():
+    """The plain-stream probe the benchmark measures against (libet_probe.so)
+    rejects bad sizes, stream shapes, vector counts, NULL and misaligned
+    buffers before any HIP call."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "elementwise_transformer_amd", "libet_probe.so"))
+    f = lib.et_probe_stream
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, vp]
+    f.restype = ctypes.c_int
+    A, B, Y, H = 0x100000, 0x200000, 0x300000, 0x400000   # fake, never dereferenced
+    bad = [
+        (A, B, Y, H, 0, 1, 1, 4, 0),          # empty
+        (A, B, Y, H, 24, 1, 1, 4, 0),         # not whole 16-byte words
+        (A, B, Y, H, 1 << 31, 1, 1, 4, 0),    # past 32-bit buffer offsets
+        (A, B, Y, H, 64, 0, 0, 4, 0),         # nothing streamed
+        (A, B, Y, H, 64, 3, 1, 4, 0),         # three reads
+        (A, B, Y, H, 64, 0, 2, 4, 0),         # a shape not offered
+        (A, B, Y, H, 64, 2, 0, 4, 0),
+        (A, B, Y, H, 64, 1, 1, 5, 0),         # vectors per lane
+        (None, B, Y, H, 64, 1, 1, 4, 0),      # missing read buffer
+        (A, None, Y, H, 64, 2, 1, 4, 0),
+        (A, B, None, H, 64, 1, 0, 4, 0),      # y is needed even for a pure read
+        (A, B, Y, None, 64, 2, 2, 4, 1),
+        (A + 4, B, Y, H, 64, 1, 1, 4, 0),     # misaligned
+        (A, B, Y + 8, H, 64, 1, 1, 8, 1),
+    ]
+    for args in bad:
+        assert f(*args, None) == 1, args
