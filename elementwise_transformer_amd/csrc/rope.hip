@@ -1005,24 +1005,40 @@ __device__ inline void lds_run(const S* xr, int p, float (&o)[W]) {
   }
 }
 
+// The angles of the PS entries of a vector with descriptor (d, d1), from the
+// token's row tab of the angle table: entry e's (mu cos, +-mu sin), the sine
+// negated for the first member of its pair, so that every entry rotates as
+// y = x mu cos + x_partner (+-mu sin), the form of the RoPE kernel's rotate()
+// (negation is exact: the bits are those of applying the sign afterwards).
+template <int PS>
+__device__ inline void entry_angles(const float2* tab, int4 d, int d1, bool half,
+                                    float2 (&ang)[PS]) {
+  const int kr = d1 & 0xFF;
+#pragma unroll
+  for (int e = 0; e < PS; ++e) {
+    const bool in_a = e < kr;
+    const float2 c = tab[(in_a ? d.z : d.w) + (half ? e : e / 2)];
+    // a vector of PS > 1 starts at an even column, so for the interleaved
+    // pairing the parity of e is the column's; a single entry (the scalar
+    // path) takes its run's flag, as the half pairing does
+    const bool first = (half || PS == 1) ? (d1 & (in_a ? 0x100 : 0x200)) != 0 : (e & 1) == 0;
+    ang[e] = make_float2(c.x, first ? -c.y : c.y);
+  }
+}
+
 // Half pairing (or the scalar path): element e of the vector belongs to run
-// A (e < kr) or B; its partner is read from the staged row, its angle from
-// the table, and it is rotated as the RoPE kernel's rotate() rotates it.
+// A (e < kr) or B; its partner is read from the staged row W entries at a
+// time (the W entries share a run: kr is a multiple of W).
 template <typename S, int PS, int W>
-__device__ inline void rotate_runs(const S* xr, const float (&x)[PS], float (&y)[PS], int4 d, int d1,
-                                   int kr, const float2* tab) {
+__device__ inline void rotate_runs(const S* xr, const float (&x)[PS], float (&y)[PS], int4 d, int kr,
+                                   const float2 (&ang)[PS]) {
 #pragma unroll
   for (int e0 = 0; e0 < PS; e0 += W) {
-    const bool in_a = e0 < kr;  // the W entries share a run (kr is a multiple of W)
     float xp[W];
-    lds_run<S, W>(xr, (in_a ? d.x : d.y) + e0, xp);
-    const float2* tr = tab + (in_a ? d.z : d.w) + e0;
-    const bool first = (d1 & (in_a ? 0x100 : 0x200)) != 0;
+    lds_run<S, W>(xr, (e0 < kr ? d.x : d.y) + e0, xp);
 #pragma unroll
-    for (int j = 0; j < W; ++j) {
-      const float2 c = tr[j];
-      y[e0 + j] = __builtin_fmaf(x[e0 + j], c.x, xp[j] * (first ? -c.y : c.y));
-    }
+    for (int j = 0; j < W; ++j)
+      y[e0 + j] = __builtin_fmaf(x[e0 + j], ang[e0 + j].x, xp[j] * ang[e0 + j].y);
   }
 }
 
@@ -1123,15 +1139,29 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
   }
   __syncthreads();
 
-  // Phase 3: rotate and store.
+  // Phase 3: rotate and store.  A thread's slots usually share one column
+  // (the row length divides the slot stride) and advance through one token
+  // or a few, so the descriptor is read again only when the column changes
+  // and the angles are kept in registers until the token or column changes.
+  const bool half = a.ra.layout == ET_ROPE_HALF;
+  int4 d = make_int4(0, 0, 0, 0);
+  int d1 = 0, kr = 0, cur_cv = -1, cur_tl = -1;
+  float2 ang[PS];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int s = static_cast<int>(rope_slot<U>(0, threadIdx.x, u));
     if (s >= nslot) continue;
-    const int4 d = d4s[cv[u]];
-    const int d1 = d1s[cv[u]];
-    const int kr = d1 & 0xFF;
-    const float2* tab = cs + tl[u] * a.np;
+    if (cv[u] != cur_cv) {
+      d = d4s[cv[u]];
+      d1 = d1s[cv[u]];
+      kr = d1 & 0xFF;
+      cur_cv = cv[u];
+      cur_tl = -1;
+    }
+    if (tl[u] != cur_tl) {
+      entry_angles<PS>(cs + tl[u] * a.np, d, d1, half, ang);
+      cur_tl = tl[u];
+    }
     float x[PS], y[PS];
 #pragma unroll
     for (int e = 0; e < PS; ++e) x[e] = PS == 1 ? sv[u] : E::get(v[u], e);
@@ -1142,20 +1172,16 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
       // widths even), else one entry at a time.
       const int al = kr | d.x | d.y;
       if (PS >= 4 && ET_MULTI_WIDE && (al & 3) == 0) {
-        rotate_runs<S, PS, (PS >= 4 ? 4 : 1)>(xr, x, y, d, d1, kr, tab);
+        rotate_runs<S, PS, (PS >= 4 ? 4 : 1)>(xr, x, y, d, kr, ang);
       } else if (PS >= 2 && ET_MULTI_WIDE && (al & 1) == 0) {
-        rotate_runs<S, PS, (PS >= 2 ? 2 : 1)>(xr, x, y, d, d1, kr, tab);
+        rotate_runs<S, PS, (PS >= 2 ? 2 : 1)>(xr, x, y, d, kr, ang);
       } else {
-        rotate_runs<S, PS, 1>(xr, x, y, d, d1, kr, tab);
+        rotate_runs<S, PS, 1>(xr, x, y, d, kr, ang);
       }
     } else if constexpr (PS > 1) {
-      // Interleaved pairs (e, e + 1) lie inside the vector.
+      // Interleaved pairs (e, e ^ 1) lie inside the vector.
 #pragma unroll
-      for (int e = 0; e < PS; e += 2) {
-        const float2 c = tab[(e < kr ? d.z : d.w) + e / 2];
-        y[e] = __builtin_fmaf(x[e], c.x, x[e + 1] * -c.y);
-        y[e + 1] = __builtin_fmaf(x[e + 1], c.x, x[e] * c.y);
-      }
+      for (int e = 0; e < PS; ++e) y[e] = __builtin_fmaf(x[e], ang[e].x, x[e ^ 1] * ang[e].y);
     }
     if constexpr (PS == 1) {
       E::st(rowp[u], cv[u], y[0]);
