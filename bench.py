@@ -257,7 +257,9 @@ def _time_launches(stream, fn, sets, launches):
 # operand of the prefill row ops (RMSNorm and the gather read one and write
 # one, add reads two and writes one, fused add+RMSNorm reads two and writes
 # two); 112 MiB one [4096, 14336] bf16 operand of the prefill SiLU-mul (two
-# reads, one write).  Non-temporal and device-scope stores are the two
+# reads, one write) and GeGLU; 125 MiB the decode logits [256, 128256] f32
+# softmax reads and writes; 225 MiB the q and k [19200, 24, 128] bf16 the
+# multi-axis RoPE rotates.  Non-temporal and device-scope stores are the two
 # policies the kernels choose between by output size.
 CEILING_CASES = [
     ("read_32MiB", 32 << 20, 1, 0, 0),
@@ -269,6 +271,8 @@ CEILING_CASES = [
     ("2R2W_32MiB", 32 << 20, 2, 2, 0),
     ("2R1W_112MiB", 4096 * 14336 * 2, 2, 1, 0),
     ("2R1W_112MiB_dev", 4096 * 14336 * 2, 2, 1, 1),
+    ("1R1W_125MiB", 256 * 128256 * 4, 1, 1, 0),
+    ("1R1W_225MiB", 19200 * 48 * 128 * 2, 1, 1, 0),
 ]
 
 
@@ -278,6 +282,14 @@ CEILING_CASES = [
 OP_CEILING = {2: {"rmsnorm": "1R1W_32MiB", "embedding": "1R1W_32MiB", "add": "2R1W_32MiB_dev",
                   "add_rmsnorm": "2R2W_32MiB", "rope": "1R1W_32MiB_dev",
                   "rmsnorm_rope": "1R1W_32MiB_dev", "silu_mul": "2R1W_112MiB_dev"}}
+
+
+# The same for the ops timed beyond the step (their kernels' store policies:
+# non-temporal for softmax, LayerNorm and the multi-axis RoPE, device scope
+# for GeGLU and the cached RoPE at these sizes).
+NEXT_CEILING = {"softmax": "1R1W_125MiB", "layernorm": "1R1W_32MiB", "geglu_erf": "2R1W_112MiB_dev",
+                "geglu_tanh": "2R1W_112MiB_dev", "rope_cached": "1R1W_32MiB_dev",
+                "rope_multi": "1R1W_225MiB"}
 
 
 def stream_ceiling(torch, stream, launches=40):
@@ -691,6 +703,16 @@ def main():
                    else float(np.mean(op.ms)) * 1e-3 for op in ops)
         step_ceiling = {"stream_step_us": round(eq_s * 1e6, 2), "step_us": round(ms_step * 1e3, 2),
                         "frac": round(eq_s * 1e3 / ms_step, 4)}
+    if ceiling and next_ops:
+        for name, rec in next_ops.items():
+            case = NEXT_CEILING.get(name)
+            if case:
+                rec["stream_ceiling"] = case
+                rec["frac_of_ceiling"] = round(rec["GBps"] / ceiling[case]["GBps"], 4)
+            elif name == "f16_step" and step_ceiling and args.workload == 2:
+                # the f16 step moves the bf16 step's bytes in the same shapes
+                rec["stream_step_us"] = step_ceiling["stream_step_us"]
+                rec["frac_of_ceiling"] = round(step_ceiling["stream_step_us"] / rec["avg_us"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
