@@ -171,13 +171,30 @@ static double* row_buffer(int64_t n) {
 
 /* ---------------------------------------------------------------- RMSNorm */
 
+/* The pages' normalisation statistics are single-precision sums ([ELT] 2.1
+ * accumulates the squares in a float; [DNN] 7 keeps its statistics in F32).
+ * Where such a sum, or LayerNorm's deviation x - mu, passes the f32 range
+ * the single-precision value is +-inf, and so is it here: f32_range maps an
+ * f64 value to +-inf from 2^128 - 2^103 on, where round-to-nearest f32
+ * overflows.  Below that the f64 value stands (the order of the f32 partial
+ * sums is the kernels' own, and a sum whose terms have mixed signs may
+ * overflow in a partial sum first: no single value is right there). */
+static double f32_range(double v) {
+    if (v >= 0x1.ffffffp127) return INFINITY;
+    if (v <= -0x1.ffffffp127) return -INFINITY;
+    return v;
+}
+
 /* [OPS] RmsNorm; [ELT] 2.1: y_i = x_i / sqrt(mean(x^2) + eps) * w_i, with eps
  * inside the root and the mean taken over the row's d entries.  The row is
- * given in f64 and normalised in place. */
+ * given in f64 and normalised in place; a sum of squares past the f32 range
+ * is +inf (f32_range), so the row then maps to x * 0 (NaN where x is
+ * infinite). */
 static void normalize_row(double* v, int64_t d, int dt, const void* w,
                           float eps) {
     double ss = 0.0;
     for (int64_t i = 0; i < d; ++i) ss += v[i] * v[i];
+    ss = f32_range(ss);
     const double ms = ss / (double)d;
     const double inv = 1.0 / sqrt(ms + (double)eps);
     for (int64_t i = 0; i < d; ++i) v[i] = v[i] * inv * ld(dt, w, i);
@@ -425,23 +442,26 @@ void orc_softmax(int dt, const void* x, int64_t rows, int64_t n, float t,
 /* [OPS] 2 Normalization / LayerNorm; [DNN] 7: mu = mean(x),
  * var = mean((x - mu)^2), y = (x - mu) / sqrt(var + eps) * g + b over the
  * last axis (the two-pass variance, as written).  b may be NULL (no bias,
- * [DNN] 7's optional beta). */
+ * [DNN] 7's optional beta).  The sum of x, each deviation x - mu and the sum
+ * of squared deviations are taken to +-inf past the f32 range (f32_range):
+ * a row whose squared deviations overflow maps to the bias, one whose sum
+ * overflows to NaN. */
 void orc_layernorm(int dt, const void* x, const void* g, const void* b,
                    int64_t rows, int64_t d, float eps, double* y64, void* y) {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
         double sum = 0.0;
         for (int64_t i = 0; i < d; ++i) sum += ld(dt, x, r * d + i);
-        const double mu = sum / (double)d;
+        const double mu = f32_range(sum) / (double)d;
         double ss = 0.0;
         for (int64_t i = 0; i < d; ++i) {
-            const double c = ld(dt, x, r * d + i) - mu;
+            const double c = f32_range(ld(dt, x, r * d + i) - mu);
             ss += c * c;
         }
-        const double var = ss / (double)d;
+        const double var = f32_range(ss) / (double)d;
         const double inv = 1.0 / sqrt(var + (double)eps);
         for (int64_t i = 0; i < d; ++i) {
-            double v = (ld(dt, x, r * d + i) - mu) * inv * ld(dt, g, i);
+            double v = f32_range(ld(dt, x, r * d + i) - mu) * inv * ld(dt, g, i);
             if (b) v += ld(dt, b, i);
             if (y64) y64[r * d + i] = v;
             if (y) st(dt, y, r * d + i, v);

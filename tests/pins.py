@@ -898,6 +898,90 @@ def pin_layernorm_brute_and_library(orc):
     assert np.array_equal(y, np.array([brute.bf16_bits_exact(v) for v in y64.ravel()], np.uint16).reshape(y.shape))
 
 
+def _page_rmsnorm_f32(x, w, eps):
+    """[ELT] 2.1's routine in single precision: a float sum of squares in
+    increasing i, then x * (1 / sqrt(ss / d + eps)) * w, every step in f32."""
+    f = np.float32
+    ss = f(0.0)
+    with np.errstate(over="ignore", invalid="ignore"):
+        for v in x:
+            ss = f(ss + f(v) * f(v))
+        inv = f(1.0) / np.sqrt(f(ss / f(len(x))) + f(eps))
+        return np.array([f(f(v) * inv) * f(g) for v, g in zip(x, w)], np.float32)
+
+
+def _page_layernorm_f32(x, g, b, eps):
+    """[DNN] 7's two-pass statistics kept in f32: mean as a float sum / d,
+    variance as a float sum of (x - mean)^2 / d, then
+    (x - mean) * (1 / sqrt(var + eps)) * g + b, every step in f32."""
+    f = np.float32
+    with np.errstate(over="ignore", invalid="ignore"):
+        s = f(0.0)
+        for v in x:
+            s = f(s + f(v))
+        mu = f(s / f(len(x)))
+        ss = f(0.0)
+        for v in x:
+            c = f(f(v) - mu)
+            ss = f(ss + c * c)
+        inv = f(1.0) / np.sqrt(f(ss / f(len(x))) + f(eps))
+        return np.array([f(f(f(f(v) - mu) * inv) * f(gv)) + f(bv) for v, gv, bv in zip(x, g, b)],
+                        np.float32)
+
+
+def pin_norm_statistics_beyond_f32(orc):
+    """The normalisation statistics are single-precision sums on the pages
+    ([ELT] 2.1's float sum of squares, [DNN] 7's F32 statistics): a row
+    whose sum of squares passes the f32 range normalises to x * 0 (signed
+    zeros, NaN at an infinite entry), a LayerNorm row whose squared
+    deviations pass it gives exactly the bias, and one whose (one-signed) sum
+    passes it gives NaN.  Rows of the same shape that stay inside the range
+    keep the f64 formula.  Checked bit for bit against the pages' routines
+    run in numpy float32, in f32 and bf16 storage (all values here are bf16
+    numbers)."""
+    d = 16
+    rms_rows = [
+        [2.0 ** 65] * d,                             # every square already past the range
+        [2.0 ** 63, -(2.0 ** 63)] * (d // 2),        # squares 2^126: the sum passes at the 4th term
+        [2.0 ** 64] + [1.0] * (d - 1),               # one square of 2^128
+        [float("inf")] + [3.0] * (d - 1),            # an infinite entry
+    ]
+    ln_rows = [
+        [2.0 ** 65, -(2.0 ** 65)] * (d // 2),        # mean 0, squared deviations past the range
+        [2.0 ** 126] * d,                            # a one-signed sum of 2^130
+        [2.0 ** 120] * (d // 2) + [-(2.0 ** 120)] * (d // 2),  # mean 0, squares 2^240
+    ]
+    w = np.linspace(0.5, 1.5, d).astype(np.float32)
+    b = np.linspace(-1.0, 1.0, d).astype(np.float32)
+    for dt in ("f32", "bf16"):
+        cvt = (lambda a: np.asarray(a, np.float32)) if dt == "f32" else (lambda a: _bf16(np.asarray(a, np.float32)))
+        wide = (lambda a: a) if dt == "f32" else _wide
+        ws, bs = cvt(w), cvt(b)
+        x = cvt(np.array(rms_rows, np.float32))
+        y, _ = orc.rmsnorm(x, ws, 1e-5)
+        for r in range(len(rms_rows)):
+            page = _page_rmsnorm_f32(wide(x[r]), wide(ws), 1e-5)
+            assert np.array_equal(np.isnan(page), np.isnan(wide(y[r]))), (dt, r)
+            ok = ~np.isnan(page)
+            assert np.array_equal(np.signbit(page[ok]), np.signbit(wide(y[r])[ok])), (dt, r)
+            assert np.all(page[ok] == 0) and np.all(wide(y[r])[ok] == 0), (dt, r)
+        x = cvt(np.array(ln_rows, np.float32))
+        y, _ = orc.layernorm(x, ws, bs, 1e-5)
+        for r in range(len(ln_rows)):
+            page = _page_layernorm_f32(wide(x[r]), wide(ws), wide(bs), 1e-5)
+            got = wide(y[r])
+            assert np.array_equal(np.isnan(page), np.isnan(got)), (dt, r)
+            assert np.array_equal(page[~np.isnan(page)], got[~np.isnan(page)]), (dt, r)
+        assert np.all(np.isnan(wide(y[1]))) and np.array_equal(wide(y[0]), wide(bs))
+    # inside the range the f64 formula stands: squares summing to 2^126
+    x = np.full((1, d), 2.0 ** 61, np.float32)
+    _, y64 = orc.rmsnorm(x, np.ones(d, np.float32), 1e-5)
+    assert np.allclose(y64, 1.0, rtol=1e-12)
+    x = np.array([[2.0 ** 61, -(2.0 ** 61)] * (d // 2)], np.float32)
+    _, y64 = orc.layernorm(x, np.ones(d, np.float32), None, 1e-5)
+    assert np.allclose(np.abs(y64), 1.0, rtol=1e-12)
+
+
 # ------------------------------------------------------------------ GeGLU
 
 def pin_gelu_symmetry_and_limits(orc):

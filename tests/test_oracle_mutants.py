@@ -4,10 +4,11 @@ Each mutant is a copy of ``oracle/oracle.c`` with one plausible mistake
 planted by text substitution, built into a temporary library.  The pins must
 fail on every mutant.  s01-s15 are the mistakes listed in the Pitfalls table
 (section 5) of "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding,
-add, argmax", each with the test the page says catches it; x01-x40 are further
+add, argmax", each with the test the page says catches it; x01-x44 are further
 slips (a wrong sign, index, dropped term or rounding) in the same code, x11-x16
 in the softmax, x17-x20 in LayerNorm, x21-x25 in the GELU-gated multiply, x26-x29
-in the RoPE cache, x30-x34 in multi-axis RoPE, x35-x40 in the f16 storage.
+in the RoPE cache, x30-x34 in multi-axis RoPE, x35-x40 in the f16 storage,
+x41-x44 in the f32 range of the normalisation statistics.
 """
 import os
 import tempfile
@@ -82,13 +83,14 @@ MUTANTS = {
     "x16_softmax_exp_sign": ("softmax_temperature",
                              [("z[i] = exp(z[i] - m);", "z[i] = exp(m - z[i]);")]),
     "x17_layernorm_not_centred": ("layernorm_closed_forms",
-                                  [("double v = (ld(dt, x, r * d + i) - mu) * inv * ld(dt, g, i);",
-                                    "double v = ld(dt, x, r * d + i) * inv * ld(dt, g, i);")]),
+                                  [("double v = f32_range(ld(dt, x, r * d + i) - mu) * inv * ld(dt, g, i);",
+                                    "double v = f32_range(ld(dt, x, r * d + i)) * inv * ld(dt, g, i);")]),
     "x18_layernorm_eps_outside_root": ("layernorm_closed_forms",
                                        [("1.0 / sqrt(var + (double)eps);", "1.0 / (sqrt(var) + (double)eps);")]),
     "x19_layernorm_bias_dropped": ("layernorm_closed_forms", [("if (b) v += ld(dt, b, i);", "")]),
     "x20_variance_over_d_minus_1": ("layernorm_invariants",
-                                    [("const double var = ss / (double)d;", "const double var = ss / (double)(d - 1);")]),
+                                    [("const double var = f32_range(ss) / (double)d;",
+                                      "const double var = f32_range(ss) / (double)(d - 1);")]),
     "x21_gelu_no_sqrt2": ("gelu_brute", [("erfc(-x / sqrt(2.0))", "erfc(-x)")]),
     "x22_gelu_tanh_cubic_coefficient": ("gelu_brute", [("0.044715 * x * x * x", "0.44715 * x * x * x")]),
     "x23_geglu_up_ignored": ("gelu_symmetry_and_limits",
@@ -131,6 +133,17 @@ MUTANTS = {
                                [("((uint16_t*)p)[i] = orc_f16_from_f64(v);", "((uint16_t*)p)[i] = orc_bf16_from_f64(v);")]),
     "x25_gelu_tanh_no_f32_limit": ("gelu_symmetry_and_limits",
                                    [("if (e > FLT_MAX) e = INFINITY;  /* the f32", "/* the f32")]),
+    "x41_rms_sum_of_squares_in_f64_range": ("norm_statistics_beyond_f32",
+                                            [("    ss = f32_range(ss);\n", "")]),
+    "x42_layernorm_variance_in_f64_range": ("norm_statistics_beyond_f32",
+                                            [("const double var = f32_range(ss) / (double)d;",
+                                              "const double var = ss / (double)d;")]),
+    "x43_layernorm_sum_in_f64_range": ("norm_statistics_beyond_f32",
+                                       [("const double mu = f32_range(sum) / (double)d;",
+                                         "const double mu = sum / (double)d;")]),
+    "x44_f32_range_threshold_at_flt_max_squared": ("norm_statistics_beyond_f32",
+                                                   [("if (v >= 0x1.ffffffp127) return INFINITY;",
+                                                     "if (v >= 0x1.ffffffp254) return INFINITY;")]),
 }
 
 
@@ -159,9 +172,12 @@ def test_mutant_is_caught(name, tmpdir_mut):
     m = _build_mutant(name, subs, tmpdir_mut)
     m.set_threads(1)              # s15's shared accumulator must not race
     failed = []
-    for pin_name, pin in PINS.items():
+    # the page's catcher runs first: a mutant with state (s15's accumulator
+    # shared across calls) must meet it before other pins have moved that state
+    order = ([named] if named is not None else []) + [p for p in PINS if p != named]
+    for pin_name in order:
         try:
-            pin(m)
+            PINS[pin_name](m)
         except AssertionError:
             failed.append(pin_name)
     assert failed, f"mutant {name} survived every pin"
