@@ -344,3 +344,77 @@ def test_rope_extreme_positions(et, orc, dt, layout):
     et.rope(xt, dev(pos), dev(inv), d_rot=r, layout=layout)
     ref, y64 = orc.rope(x, pos, r, inv, 1.0, layout)
     assert_pair(host(xt), y64, ref, r, layout, f"extreme positions {dt}")
+
+
+# ------------------------------------------- statistics past the f32 range
+
+def _big_rows(d, g):
+    """Rows of d entries for the norms: squares past the f32 range (every
+    square; adjacent +-2^63 pairs), an infinite entry, squares just inside the
+    range, a plain row.  Only same-signed sums or pairs that cancel exactly
+    inside a lane, so no order of f32 partial sums decides the result."""
+    safe = 2.0 ** (63 - int(np.ceil(np.log2(d) / 2)) - 1)
+    rows = [np.full(d, 2.0 ** 65), np.tile([2.0 ** 63, -(2.0 ** 63)], d // 2) if d % 2 == 0 else np.full(d, 2.0 ** 64),
+            np.concatenate([[np.inf], np.full(d - 1, 3.0)]), np.full(d, safe) * np.sign(g.standard_normal(d)),
+            g.standard_normal(d)]
+    return np.array(rows, np.float32)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [16, 4096, 70000])
+def test_norms_past_the_f32_range(et, orc, dt, d):
+    """A row whose f32 sum of squares overflows normalises to x * 0 (signed
+    zeros, NaN at an infinite entry), as the oracle's reading of the pages'
+    single-precision statistics gives; rows just inside the range keep the
+    f64 formula within the usual tolerance.  RMSNorm, fused add+RMSNorm (h =
+    x + 0) and LayerNorm (squared deviations past the range give the bias, a
+    one-signed sum past it NaN)."""
+    from gpu_util import check_layernorm
+    g = _rng(40, d, DTS.index(dt))
+    x = _store(_big_rows(d, g), dt)
+    w = _store(g.uniform(0.5, 1.5, d).astype(np.float32), dt)
+    yr, y64 = orc.rmsnorm(x, w, 1e-5)
+    assert_close(host(et.rmsnorm(dev(x), dev(w), 1e-5)), y64, yr, f"rmsnorm {dt} d={d}")
+    z = _store(np.zeros(x.shape, np.float32), dt)
+    yt, ht = et.add_rmsnorm(dev(x), dev(z), dev(w), 1e-5)
+    oy, oh, oy64 = orc.add_rmsnorm(x, z, w, 1e-5)
+    assert_bits(host(ht), oh, f"add_rmsnorm h {dt} d={d}")
+    assert_close(host(yt), oy64, oy, f"add_rmsnorm y {dt} d={d}")
+    assert np.all(widen(host(yt))[:2] == 0)
+    b = _store(g.standard_normal(d).astype(np.float32), dt)
+    safe = 2.0 ** (63 - int(np.ceil(np.log2(d) / 2)) - 1)
+    lx = np.array([np.tile([2.0 ** 65, -(2.0 ** 65)], d // 2) if d % 2 == 0 else np.full(d, 2.0 ** 65),
+                   np.full(d, 2.0 ** 126), np.tile([safe, -safe], d // 2), g.standard_normal(d)], np.float32)
+    lx = _store(lx, dt)
+    y, ly64 = orc.layernorm(lx, w, b, 1e-5)
+    got = host(et.layernorm(dev(lx), dev(w), dev(b), 1e-5))
+    check_layernorm(got, lx, w, b, 1e-5, y, ly64, f"layernorm {dt} d={d}")
+    assert np.all(np.isnan(widen(got[1])))
+    if d % 2 == 0:
+        assert_bits(got[0], b, f"layernorm {dt} d={d}: squared deviations past the range give the bias")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_rmsnorm_rope_past_the_f32_range(et, orc, dt, layout):
+    """Per-head RMSNorm+RoPE: heads whose sum of squares overflows rotate
+    zeros (NaN where an entry is infinite), the others as usual."""
+    g = _rng(41, layout, DTS.index(dt))
+    T, H, D, r = 3, 5, 128, 64
+    heads = _big_rows(D, g)                                  # 5 rows of 128
+    q = _store(np.broadcast_to(heads, (T, H, D)).copy(), dt)
+    gq = _store(g.uniform(0.5, 1.5, D).astype(np.float32), dt)
+    pos = np.array([0, 7, 4095], np.int32)
+    inv = wl.inv_freq(5e5, r)
+    qt = dev(q)
+    et.rmsnorm_rope_qk(qt, dev(gq), None, None, 1e-6, dev(pos), dev(inv), d_rot=r, layout=layout)
+    ref, y64 = orc.rmsnorm_rope(q, gq, 1e-6, pos, r, inv, 1.0, layout)
+    got = host(qt)
+    # head 2 holds an infinite entry: x * 0 is NaN there, and so is its
+    # rotation partner; NaN positions first, then the other heads
+    assert np.array_equal(np.isnan(widen(got)), np.isnan(y64)), f"{dt} layout={layout}: NaN positions"
+    assert np.isnan(y64[:, 2]).sum() == 2 * T
+    fin = [0, 1, 3, 4]
+    assert_pair(got[:, fin], y64[:, fin], ref[:, fin], r, layout, f"{dt} layout={layout}")
+    assert_close(got[..., r:], y64[..., r:], ref[..., r:], f"{dt} tail")
+    assert np.all(widen(got[:, :2]) == 0)
