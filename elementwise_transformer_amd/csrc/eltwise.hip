@@ -13,8 +13,6 @@
 // done by the last block with scalar accesses.  Misaligned buffers use the
 // scalar kernel.  y may equal a or b: every element is read by the thread
 // that writes it, before it writes it.
-#include <type_traits>
-
 #include "et_common.hpp"
 
 namespace et {
@@ -74,67 +72,82 @@ __device__ inline float silu(float g) {
 // erfc, branch free: the Chebyshev-fitted form of Press, Teukolsky,
 // Vetterling and Flannery, Numerical Recipes (2nd ed.), section 6.2: for
 // a = |z|, t = 1 / (1 + a/2) and erfc(a) = t exp(-a^2 + P(t)), fractional
-// error below 1.2e-7 for every a >= 0 with P of degree 9 (checked here
-// against scipy to 1.05e-7); erfc(-a) = 2 - erfc(a).  The library erfcf
+// error below 1.2e-7 for every a >= 0 with P of degree 9.  The library erfcf
 // branches by range, so a wave of mixed arguments runs every branch: it made
 // the bf16 GELU-gated multiply ALU-bound (103 us where 57 us moves the bytes).
-__device__ inline float erfc_poly9(float t) {
-  float p = 0.17087277f;
-  p = __builtin_fmaf(p, t, -0.82215223f);
-  p = __builtin_fmaf(p, t, 1.48851587f);
-  p = __builtin_fmaf(p, t, -1.13520398f);
-  p = __builtin_fmaf(p, t, 0.27886807f);
-  p = __builtin_fmaf(p, t, -0.18628806f);
-  p = __builtin_fmaf(p, t, 0.09678418f);
-  p = __builtin_fmaf(p, t, 0.37409196f);
-  p = __builtin_fmaf(p, t, 1.00002368f);
-  return __builtin_fmaf(p, t, -1.26551223f);
+// For 2-byte storage, whose results keep 8 or 11 significant bits, P has
+// degree 5 instead, fitted here to log(erfc(a) e^(a^2) / t) over 0 <= a <= 12
+// (Chebyshev nodes in t, weighted least squares iterated toward the minimax
+// fit, coefficients rounded to f32): relative error below 1.3e-5 against
+// scipy's erfc (1.2e-4 out to a = 20), four fused multiply-adds fewer in a
+// kernel whose 2-byte form is close to ALU-bound.
+//
+// Both are evaluated in base 2 and at t8 = t / 8:
+//   Phi(-|x|) = erfc(a) / 2 = t8 2^K,  K = P'(t8) - a'^2,
+//   a' = a sqrt(log2 e),  t8 = 1 / (8 + (4 / sqrt(log2 e)) a'),
+//   P'(t8) = (P(8 t8) + 2 ln 2) log2 e,
+// so coefficient i of P' is P's times 8^i log2 e (the power of 8 is exact)
+// and its constant term is (c0 + 2 ln 2) log2 e.  The factor 1/8 in t8 keeps
+// |x| t8 2^(K - floor K) below 2^-1.5 for every x.
+constexpr double kLog2eD = 1.44269504088896340736;
+constexpr double kLn2D = 0.69314718055994530942;
+#define ET_ERFC_C(c, i) static_cast<float>((c) * (i) * kLog2eD)
+#define ET_ERFC_C0(c) static_cast<float>(((c) + 2.0 * kLn2D) * kLog2eD)
+
+__device__ inline float erfc_exp2_poly9(float t8) {
+  float p = ET_ERFC_C(0.17087277, 134217728.0);
+  p = __builtin_fmaf(p, t8, ET_ERFC_C(-0.82215223, 16777216.0));
+  p = __builtin_fmaf(p, t8, ET_ERFC_C(1.48851587, 2097152.0));
+  p = __builtin_fmaf(p, t8, ET_ERFC_C(-1.13520398, 262144.0));
+  p = __builtin_fmaf(p, t8, ET_ERFC_C(0.27886807, 32768.0));
+  p = __builtin_fmaf(p, t8, ET_ERFC_C(-0.18628806, 4096.0));
+  p = __builtin_fmaf(p, t8, ET_ERFC_C(0.09678418, 512.0));
+  p = __builtin_fmaf(p, t8, ET_ERFC_C(0.37409196, 64.0));
+  p = __builtin_fmaf(p, t8, ET_ERFC_C(1.00002368, 8.0));
+  return __builtin_fmaf(p, t8, ET_ERFC_C0(-1.26551223));
 }
 
-// The same form for 2-byte storage, whose results keep 8 or 11 significant
-// bits: P of degree 5, fitted here to log(erfc(a) e^(a^2) / t) over
-// 0 <= a <= 12 (Chebyshev nodes in t, weighted least squares iterated toward
-// the minimax fit, coefficients rounded to f32).  Relative error below
-// 1.3e-5 in f32 arithmetic against scipy's erfc, inside 3 % of half an f16
-// ulp; four fused multiply-adds fewer per element in a kernel whose 2-byte
-// form is close to ALU-bound.
-__device__ inline float erfc_poly5(float t) {
-  float p = 0x1.d141fp-3f;
-  p = __builtin_fmaf(p, t, -0x1.68beacp-1f);
-  p = __builtin_fmaf(p, t, 0x1.e0c8f6p-2f);
-  p = __builtin_fmaf(p, t, 0x1.071e78p-2f);
-  p = __builtin_fmaf(p, t, 0x1.04764ap+0f);
-  return __builtin_fmaf(p, t, -0x1.4438d8p+0f);
+__device__ inline float erfc_exp2_poly5(float t8) {
+  float p = ET_ERFC_C(0x1.d141fp-3, 32768.0);
+  p = __builtin_fmaf(p, t8, ET_ERFC_C(-0x1.68beacp-1, 4096.0));
+  p = __builtin_fmaf(p, t8, ET_ERFC_C(0x1.e0c8f6p-2, 512.0));
+  p = __builtin_fmaf(p, t8, ET_ERFC_C(0x1.071e78p-2, 64.0));
+  p = __builtin_fmaf(p, t8, ET_ERFC_C(0x1.04764ap+0, 8.0));
+  return __builtin_fmaf(p, t8, ET_ERFC_C0(-0x1.4438d8p+0));
 }
+#undef ET_ERFC_C
+#undef ET_ERFC_C0
 
-// GELU-gated product, exact form: x Phi(x) u = x erfc(-x / sqrt 2) u / 2 (the
-// identity 1 + erf(z) = erfc(-z) keeps the tail of negative x, where 1 + erf
-// cancels), with erfc(a) = t 2^k, k = (P(t) - a^2) log2 e <= 0.
-// The hardware exp2 returns no subnormals, so 2^k alone would flush every
-// erfc below 2^-126 -- results x Phi(x) u down to 2^-149 in f32 and bf16
-// storage, from x near -13 on.  There k is split into its floor n and a
-// fraction, and 2^n is applied last with ldexp, which rounds a subnormal
-// result once and correctly; k is held above -320, where every product
-// of f32 values times 2^k is below the smallest subnormal.  f16 storage
-// flushes results below 2^-25 in its own rounding, so the plain 2^k is kept.
+// GELU-gated product, exact form: x Phi(x) u, with Phi(x) = erfc(-x/sqrt 2) / 2
+// (the identity 1 + erf(z) = erfc(-z) keeps the tail of negative x, where
+// 1 + erf cancels), Phi(-|x|) = t8 2^K as above and Phi(|x|) = 1 - Phi(-|x|).
+// The hardware exp2 returns no subnormals, so 2^K alone would flush every
+// Phi below 2^-126 -- results x Phi(x) u down to 2^-149 from x near -13 on in
+// f32 and bf16 storage, and every product with a large or infinite up beyond
+// that.  So K (held above -320, where every product of f32 values times 2^K
+// is below the smallest subnormal) is split into its floor n and a fraction:
+// q = t8 2^(K - n) and Phi(-|x|) = q 2^n, with |x q| < 2^-1.5, so x q u is
+// finite for every finite u and ldexp(x q u, n) rounds a subnormal result
+// once and correctly.  a' is held at 2^100 in t8 (whose reciprocal would
+// flush from 2^127 on), so q is never 0 for a finite x: x Phi(x) is nonzero
+// for every finite x, and its product with an infinite u is an infinity.
+// Phi(-inf) is 0 and -inf * 0 has no value: NaN.  Both signs are computed
+// and one is selected, so a wave of mixed signs runs no branch.
 template <typename S>
 __device__ inline float gelu_erf_mul(float x, float u) {
-  const float z = x * -0.70710678118654752440f;
-  const float a = __builtin_fabsf(z);
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, a, 1.0f));
-  const float p = sizeof(S) == 4 ? erfc_poly9(t) : erfc_poly5(t);
-  const float k = __builtin_fmaf(-a, a, p) * 1.44269504088896340736f;
-  if constexpr (std::is_same<S, F16>::value) {
-    const float y = t * __builtin_amdgcn_exp2f(k);
-    return 0.5f * x * (z >= 0.0f ? y : 2.0f - y) * u;
-  } else {
-    const float kc = __builtin_fmaxf(k, -320.0f);
-    const float n = __builtin_floorf(kc);
-    const int ni = static_cast<int>(n);
-    const float h = 0.5f * t * __builtin_amdgcn_exp2f(kc - n);  // erfc(a) / 2 = h 2^n
-    if (z >= 0.0f) return __builtin_ldexpf(x * h * u, ni);       // x <= 0: Phi(x) = h 2^n
-    return x * (1.0f - __builtin_ldexpf(h, ni)) * u;             // x > 0: 1 - h 2^n
-  }
+  constexpr float kA = 0x1.b2da4ep-1f;   // sqrt(log2(e) / 2): a' = |x| kA
+  constexpr float kT = 0x1.aa449ap+1f;   // 4 / sqrt(log2 e): 8 + 4a = 8 + kT a'
+  const float ap = __builtin_fabsf(x) * kA;
+  const float t8 = __builtin_amdgcn_rcpf(__builtin_fmaf(kT, __builtin_fminf(ap, 0x1p100f), 8.0f));
+  const float p = sizeof(S) == 4 ? erfc_exp2_poly9(t8) : erfc_exp2_poly5(t8);
+  const float kc = __builtin_fmaxf(__builtin_fmaf(-ap, ap, p), -320.0f);
+  const float n = __builtin_floorf(kc);
+  const int ni = static_cast<int>(n);
+  const float q = t8 * __builtin_amdgcn_exp2f(kc - n);         // Phi(-|x|) = q 2^n
+  const float neg = __builtin_ldexpf(x * q * u, ni);            // x <= 0
+  const float pos = x * (1.0f - __builtin_ldexpf(q, ni)) * u;   // x > 0
+  const float r = x <= 0.0f ? neg : pos;
+  return x == -__builtin_inff() ? __builtin_nanf("") : r;
 }
 
 // GELU, tanh form: (1 + tanh u) / 2 = 1 / (1 + e^(-2u)) with

@@ -494,7 +494,14 @@ void orc_geglu(int dt, const void* gate, const void* up, int64_t n, int form,
             if (e > FLT_MAX) e = INFINITY;  /* the f32 exponential's limit, as for SiLU */
             gl = x / (1.0 + e);
         }
-        const double v = gl * ld(dt, up, i);
+        const double u = ld(dt, up, i);
+        double v = gl * u;
+        /* Phi(x) > 0 for every finite x, so x Phi(x) is nonzero, with the sign
+         * of x, also where erfc underflows f64 (x below about -38.6): its
+         * product with an infinite up is the infinity of that sign, not
+         * 0 * inf.  (x = +-0 and x = -inf, where Phi is 0, stay NaN.) */
+        if (form == 0 && isinf(u) && isfinite(x) && x != 0.0)
+            v = ((x > 0.0) == (u > 0.0)) ? INFINITY : -INFINITY;
         if (y64) y64[i] = v;
         if (y) st(dt, y, i, v);
     }

@@ -1002,6 +1002,18 @@ def pin_gelu_symmetry_and_limits(orc):
     _, z64 = orc.geglu(_f32([-10.0, -10.5]), _f32([1.0, 1.0]), 1)
     assert z64[0] < 0 and abs(z64[0] - brute.gelu_tanh_decimal(-10.0)) <= 1e-13 * abs(z64[0])
     assert z64[1] == 0.0 and math.copysign(1.0, z64[1]) < 0
+    # erf form with an infinite up: Phi(x) lies in (0, 1] for every finite x,
+    # so the product is the infinity of sign(x) sign(up), however far below
+    # zero x is (-60: x Phi(x) is below every float's range); Phi(0) x = 0 and
+    # Phi(-inf) = 0 leave 0 * inf, NaN; Phi(+inf) = 1.  The tanh form, whose
+    # value is -0 past the f32 limit above, gives NaN there.
+    inf = float("inf")
+    _, v64 = orc.geglu(_f32([-60.0, -60.0, -5.0, 3.0, 0.0, -inf, inf, -3e38]),
+                       _f32([inf, -inf, inf, -inf, inf, inf, -inf, inf]), 0)
+    assert list(v64[:4]) == [-inf, inf, -inf, -inf] and v64[6] == -inf and v64[7] == -inf
+    assert math.isnan(v64[4]) and math.isnan(v64[5])
+    _, w64 = orc.geglu(_f32([-60.0]), _f32([inf]), 1)
+    assert math.isnan(w64[0])
 
 
 def pin_gelu_brute(orc):

@@ -4,11 +4,12 @@ Each mutant is a copy of ``oracle/oracle.c`` with one plausible mistake
 planted by text substitution, built into a temporary library.  The pins must
 fail on every mutant.  s01-s15 are the mistakes listed in the Pitfalls table
 (section 5) of "Elementwise kernels in C: RMSNorm, RoPE, SiLU-mul, embedding,
-add, argmax", each with the test the page says catches it; x01-x44 are further
+add, argmax", each with the test the page says catches it; x01-x45 are further
 slips (a wrong sign, index, dropped term or rounding) in the same code, x11-x16
 in the softmax, x17-x20 in LayerNorm, x21-x25 in the GELU-gated multiply, x26-x29
 in the RoPE cache, x30-x34 in multi-axis RoPE, x35-x40 in the f16 storage,
-x41-x44 in the f32 range of the normalisation statistics.
+x41-x44 in the f32 range of the normalisation statistics, x45 in GELU's
+infinite limit.
 """
 import os
 import tempfile
@@ -94,7 +95,7 @@ MUTANTS = {
     "x21_gelu_no_sqrt2": ("gelu_brute", [("erfc(-x / sqrt(2.0))", "erfc(-x)")]),
     "x22_gelu_tanh_cubic_coefficient": ("gelu_brute", [("0.044715 * x * x * x", "0.44715 * x * x * x")]),
     "x23_geglu_up_ignored": ("gelu_symmetry_and_limits",
-                             [("const double v = gl * ld(dt, up, i);", "const double v = gl;")]),
+                             [("        double v = gl * u;\n", "        double v = gl;\n")]),
     "x24_gelu_forms_swapped": ("gelu_brute", [("if (form == 0) {", "if (form == 1) {")]),
     "x26_cache_transposed": ("rope_cached_rotation",
                              [("? (double)cos_c[(int64_t)p * half + i] : NAN;", "? (double)cos_c[i * max_pos + p] : NAN;")]),
@@ -141,6 +142,9 @@ MUTANTS = {
     "x43_layernorm_sum_in_f64_range": ("norm_statistics_beyond_f32",
                                        [("const double mu = f32_range(sum) / (double)d;",
                                          "const double mu = sum / (double)d;")]),
+    "x45_gelu_infinite_up_as_zero_times_inf": ("gelu_symmetry_and_limits",
+                                               [("        if (form == 0 && isinf(u) && isfinite(x) && x != 0.0)\n"
+                                                 "            v = ((x > 0.0) == (u > 0.0)) ? INFINITY : -INFINITY;\n", "")]),
     "x44_f32_range_threshold_at_flt_max_squared": ("norm_statistics_beyond_f32",
                                                    [("if (v >= 0x1.ffffffp127) return INFINITY;",
                                                      "if (v >= 0x1.ffffffp254) return INFINITY;")]),
