@@ -143,6 +143,23 @@ def test_geglu_matches_oracle(et, orc, dt, form, n):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("form", [0, 1])
+def test_geglu_large_up_and_deep_tail(et, orc, dt, form):
+    """Gates from -40 to 0 against ups near the f32 limit and far below it:
+    no intermediate may overflow where the product does not (x Phi(x) u for
+    x = -4.46, u = 3e38 is -5.6e33), and a GELU value below the f32 normal
+    range still gives its product with a large up in full precision."""
+    gates = np.concatenate([-np.linspace(0.0, 40.0, 81), [-1e-3, -0.5, -4.456161, -13.3, -15.9]])
+    ups = np.array([3e38, -3e38, 1e30, -1e30, 1.0, 1e-30], np.float64)
+    gg, uu = np.meshgrid(gates, ups)
+    gs, us = wl.store(gg.ravel().astype(np.float32), dt), wl.store(uu.ravel().astype(np.float32), dt)
+    y, y64 = orc.geglu(gs, us, form)
+    check_geglu(host(et.geglu(dev(gs), dev(us), form)), gs, form, y, y64, f"{dt} form={form} large up")
+    g2 = _misaligned(dev(gs))
+    check_geglu(host(et.geglu(g2, _misaligned(dev(us)), form)), gs, form, y, y64, f"{dt} form={form} scalar")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("form", [0, 1])
 def test_geglu_special_values_in_place_and_scalar(et, orc, dt, form):
     x = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 1.0, -1.0, 5.0] * 13, np.float32)
     u = np.array([1.0, 2.0, 0.5, np.nan, 3.0, -1.0, 1.0, np.inf] * 13, np.float32)

@@ -16,8 +16,8 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_util import (assert_bits, assert_close, assert_pair, check_geglu, check_layernorm,
-                      check_softmax, dev, host)
+from gpu_util import (assert_bits, assert_close, assert_f32_rel, assert_pair, check_geglu,
+                      check_layernorm, check_softmax, dev, host)
 
 pytestmark = pytest.mark.gpu
 
@@ -168,3 +168,83 @@ def test_random_embedding_argmax(et, orc, dt, seed):
     for split in (True, False):
         got = host(et.argmax(_dev_maybe_misaligned(x, mis), split=split))
         assert_bits(got, ref, f"argmax {dt} rows={rows} n={n} split={split} misaligned={mis}")
+
+
+# Special values planted at random positions: NaN, infinities, signed zeros,
+# values whose sums or products leave the f32 range, subnormals, values
+# beyond the f16 range (stored as infinities there).
+SPECIALS = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 3e38, -3e38, 1e-40, -1e-40, 7e4, 1.0],
+                    np.float32)
+
+
+def _plant(g, a, frac=0.02):
+    a = a.copy()
+    flat = a.reshape(-1)
+    m = max(1, int(flat.size * frac))
+    idx = g.choice(flat.size, size=min(m, flat.size), replace=False)
+    flat[idx] = g.choice(SPECIALS, size=idx.size)
+    return a
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("seed", range(6))
+def test_random_specials_flat(et, orc, dt, seed):
+    """add (equal bits), SiLU-mul and both GeGLU forms (their tolerances,
+    infinities exact) with special values planted in both operands."""
+    g = np.random.default_rng([5353, seed, DTS.index(dt)])
+    n = _length(g, 1, 300000)
+    a = wl.store(_plant(g, (g.standard_normal(n) * 3).astype(np.float32)), dt)
+    b = wl.store(_plant(g, g.standard_normal(n).astype(np.float32)), dt)
+    what = f"{dt} n={n}"
+    assert_bits(host(et.add(dev(a), dev(b))), orc.add(a, b), "add " + what)
+    # f32: a subnormal gate makes the activation an f32 subnormal, rounded to
+    # within 2^-150 in any single-precision order, and the product with up
+    # scales that by |up| (up to 3e38 here)
+    extra = 2.0 ** -149 * np.abs(b.astype(np.float64)) if dt == "f32" else None
+    yr, y64 = orc.silu_mul(a, b)
+    got = host(et.silu_mul(dev(a), dev(b)))
+    if dt == "f32":
+        assert_f32_rel(got, y64, "silu_mul " + what, abs_extra=extra)
+    else:
+        assert_close(got, y64, yr, "silu_mul " + what)
+    for form in (0, 1):
+        y, gy64 = orc.geglu(a, b, form)
+        check_geglu(host(et.geglu(dev(a), dev(b), form)), a, form, y, gy64, f"geglu form={form} {what}",
+                    abs_extra=extra)
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("seed", range(6))
+def test_random_specials_rows(et, orc, dt, seed):
+    """RMSNorm, fused add+RMSNorm, LayerNorm, softmax and argmax over rows
+    with special values planted in some of them (a NaN or an infinity
+    spreads over its row as the formula says; the other rows are unaffected).
+    Values whose sums overflow are kept to one sign per row here (R28 leaves
+    mixed-sign overflow to the order of the partial sums)."""
+    g = np.random.default_rng([5454, seed, DTS.index(dt)])
+    d = _length(g, 1, 20000)
+    rows = _rows(g, d, 1 << 19)
+    base = (g.standard_normal((rows, d)) * 2).astype(np.float32)
+    planted = _plant(g, base, frac=0.002)
+    # no +-3e38 of both signs in a row
+    for r in range(rows):
+        row = planted[r]
+        if np.any(row == np.float32(3e38)) and np.any(row == np.float32(-3e38)):
+            row[row == np.float32(-3e38)] = np.float32(-1.0)
+    x = wl.store(planted, dt)
+    res = wl.store(g.standard_normal((rows, d)).astype(np.float32), dt)
+    w = wl.store(g.uniform(0.5, 1.5, d).astype(np.float32), dt)
+    bias = wl.store(g.standard_normal(d).astype(np.float32), dt)
+    what = f"{dt} rows={rows} d={d}"
+    yr, y64 = orc.rmsnorm(x, w, 1e-5)
+    assert_close(host(et.rmsnorm(dev(x), dev(w), 1e-5)), y64, yr, "rmsnorm " + what)
+    yt, ht = et.add_rmsnorm(dev(x), dev(res), dev(w), 1e-5)
+    oy, oh, oy64 = orc.add_rmsnorm(x, res, w, 1e-5)
+    assert_bits(host(ht), oh, "add_rmsnorm h " + what)
+    assert_close(host(yt), oy64, oy, "add_rmsnorm y " + what)
+    y, ly64 = orc.layernorm(x, w, bias, 1e-5)
+    check_layernorm(host(et.layernorm(dev(x), dev(w), dev(bias), 1e-5)), x, w, bias, 1e-5, y, ly64,
+                    "layernorm " + what)
+    y, sy64 = orc.softmax(x, 0.7)
+    check_softmax(host(et.softmax(dev(x), 0.7)), x, 0.7, y, sy64, "softmax " + what)
+    assert_bits(host(et.argmax(dev(x))), orc.argmax(x), "argmax " + what)
