@@ -248,3 +248,70 @@ def test_random_specials_rows(et, orc, dt, seed):
     y, sy64 = orc.softmax(x, 0.7)
     check_softmax(host(et.softmax(dev(x), 0.7)), x, 0.7, y, sy64, "softmax " + what)
     assert_bits(host(et.argmax(dev(x))), orc.argmax(x), "argmax " + what)
+
+
+def _assert_pair_special(got, y64, ref, r, layout, what):
+    """The PAIR tolerance where a pair's two oracle values are finite; NaN
+    and infinite entries elsewhere must match in position (and sign)."""
+    from gpu_util import F32_FLOOR, F32_REL, BF16_PAIR, bf16_key, pair_norms, widen
+    g, y = widen(got), y64
+    assert np.array_equal(np.isnan(g), np.isnan(y)), f"{what}: NaN positions differ"
+    inf = np.isinf(y)
+    assert np.array_equal(g[inf], y[inf]), f"{what}: infinities differ"
+    pn = pair_norms(np.where(np.isfinite(y), y, np.nan), r, layout)[..., :r]
+    ok = np.isfinite(pn)
+    err = np.abs(g[..., :r] - y[..., :r])
+    if got.dtype == np.float32:
+        bad = ok & ~(err <= F32_REL * pn + F32_FLOOR)
+    else:
+        ud = np.abs(bf16_key(got[..., :r]) - bf16_key(ref[..., :r]))
+        bad = ok & ~((ud <= 1) | (err <= BF16_PAIR * pn))
+    assert not bad.any(), f"{what}: {int(bad.sum())} rotated entries over the pair tolerance"
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("seed", range(6))
+def test_random_specials_rope(et, orc, dt, seed):
+    """RoPE, fused RMSNorm+RoPE and multi-axis RoPE with special values
+    planted in q and k (a NaN or infinity spreads to its pair partner, or
+    through the norm to its head); pass-through entries keep their bits."""
+    g = np.random.default_rng([5555, seed, DTS.index(dt)])
+    D = int(2 * g.integers(4, 80))
+    r = int(2 * g.integers(1, D // 2 + 1))
+    T, Hq, Hk = int(g.integers(1, 30)), int(g.integers(1, 6)), int(g.integers(0, 4))
+    layout, mu = int(g.integers(0, 2)), float(np.float32(g.choice([1.0, 0.9])))
+    q = wl.store(_plant(g, g.standard_normal((T, Hq, D)).astype(np.float32), 0.01), dt)
+    k = wl.store(_plant(g, g.standard_normal((T, Hk, D)).astype(np.float32), 0.01), dt) if Hk else None
+    pos = g.integers(0, 1 << 16, T).astype(np.int32)
+    pos[0] = 0                                          # the identity rotation (sin 0) included
+    inv = wl.inv_freq(1e4, r)
+    gq = wl.store(g.uniform(0.5, 1.5, D).astype(np.float32), dt)
+    what = f"{dt} T={T} Hq={Hq} Hk={Hk} D={D} r={r} layout={layout}"
+    qt, kt = dev(q), (dev(k) if k is not None else None)
+    et.rope_qk(qt, kt, dev(pos), dev(inv), d_rot=r, attn_scaling=mu, layout=layout)
+    for name, src, t in (("q", q, qt), ("k", k, kt)):
+        if src is None:
+            continue
+        ref, y64 = orc.rope(src, pos, r, inv, mu, layout)
+        got = host(t)
+        _assert_pair_special(got, y64, ref, r, layout, f"rope {name} {what}")
+        assert_bits(got[..., r:], src[..., r:], f"rope pass-through {name} {what}")
+    q2 = dev(q)
+    et.rmsnorm_rope_qk(q2, dev(gq), None, None, 1e-6, dev(pos), dev(inv), d_rot=r, attn_scaling=mu,
+                       layout=layout)
+    ref, y64 = orc.rmsnorm_rope(q, gq, 1e-6, pos, r, inv, mu, layout)
+    _assert_pair_special(host(q2), y64, ref, r, layout, f"rmsnorm_rope {what}")
+    dims = (r // 2 - (r // 2) % 2, r - (r // 2 - (r // 2) % 2))     # two even widths summing to r
+    pm = np.stack([pos, pos[::-1]], axis=1).astype(np.int32)
+    inv2 = wl.multi_inv_freq(dims, [1e4, 1e3])
+    q3 = dev(q)
+    et.rope_multi(q3, None, dev(pm), dims, dev(inv2), attn_scaling=mu, layout=layout)
+    ref, y64 = orc.rope_multi(q, pm, dims, inv2, mu, layout)
+    got = host(q3)
+    o = 0
+    for a, dw in enumerate(dims):
+        if dw:
+            _assert_pair_special(np.ascontiguousarray(got[..., o:o + dw]), np.ascontiguousarray(y64[..., o:o + dw]),
+                                 np.ascontiguousarray(ref[..., o:o + dw]), dw, layout, f"multi axis {a} {what}")
+        o += dw
+    assert_bits(got[..., r:], q[..., r:], f"multi pass-through {what}")
