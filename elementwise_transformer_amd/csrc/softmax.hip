@@ -18,7 +18,10 @@
 //     the sum taken by the same fixed tree over c.  With a workspace, one
 //     launch does it all: each workgroup keeps its chunk in registers,
 //     publishes (m_c, s_c), waits (bounded) for the row's other chunks,
-//     combines and writes -- one read and one write of every element.
+//     combines and writes -- one read and one write of every element.  A
+//     row of more chunks than can be resident together (over 1024) takes
+//     two launches instead: chunk statistics, then combine and write (two
+//     reads, one write), so no workgroup waits for one that cannot start.
 //     Without one, a single workgroup per row recomputes every chunk's
 //     statistics itself and then writes (three reads); the bits are the same
 //     either way, and also when a bounded wait gives up and the workgroup
@@ -43,6 +46,10 @@ constexpr int kChunkElems = ET_SM_CHUNK;  // elements per chunk (256 threads x V
 constexpr int kChunkThreads = 256;
 constexpr int kRegMaxElems = 32768;   // register path up to this row length
 constexpr int kRegBlock = 128;        // threads per block for short rows
+// Chunks per row above which the workspace path takes two launches: the
+// one-launch exchange needs a row's chunk blocks resident together, and 256
+// CUs hold 2048 of them (eight each); half of that leaves room for other work.
+constexpr int64_t kMaxExchangeChunks = 1024;
 // Chunk kernels' reduction slots (kLdsSum floats each, one per wave): chunk
 // max, chunk sum, then the row max and row sum of row_stats_self, so that
 // no slot is written twice in a row without the other's barrier between.
@@ -467,6 +474,57 @@ __global__ __launch_bounds__(kChunkThreads) void softmax_chunks(const S* x, S* y
   }
 }
 
+// Rows of more chunks than can be resident at once (softmax_chunks needs
+// every chunk of a row resident together to end without its fallback): two
+// launches.  The first writes each chunk's (m_c, s_c) to the workspace; the
+// second reloads each chunk, combines its row's partials (written by the
+// previous launch, so plain loads see them) and writes -- two reads of the
+// row and one write, and no block waits for another.  chunk_exp and combine
+// are softmax_chunks', so the bits are the same.
+template <typename S, bool VEC>
+__global__ __launch_bounds__(kChunkThreads) void softmax_chunk_stats(const S* x, int n, int chunks,
+                                                                    float tt, float inv_t,
+                                                                    uint64_t* part) {
+  constexpr int VPT = Chunk<S>::kVPT;
+  __shared__ float lds[4 * kLdsSum];
+  const int64_t row = blockIdx.x / chunks;
+  const int c = blockIdx.x % chunks;
+  float ev[VPT][Elem<S>::V];
+  const float2 st = chunk_exp<S, VEC>(x + row * n, n, c, tt, inv_t, lds, ev);
+  if (threadIdx.x == 0) part[row * chunks + c] = partial_bits(st.x, st.y);
+}
+
+// The second launch.  cnt[2 row] counts the row's blocks done reading its
+// partials; the last one zeroes them and the counter with all its threads,
+// leaving the workspace as it was found.
+template <typename S, bool VEC>
+__global__ __launch_bounds__(kChunkThreads) void softmax_chunk_write(const S* x, S* y, int n,
+                                                                    int chunks, float tt,
+                                                                    float inv_t, uint64_t* part,
+                                                                    uint32_t* cnt) {
+  constexpr int VPT = Chunk<S>::kVPT;
+  __shared__ float lds[4 * kLdsSum];
+  __shared__ float res[2];
+  __shared__ int last;
+  const int64_t row = blockIdx.x / chunks;
+  const int c = blockIdx.x % chunks;
+  float ev[VPT][Elem<S>::V];
+  const float mc = chunk_exp<S, VEC>(x + row * n, n, c, tt, inv_t, lds, ev).x;
+  uint64_t* rp = part + row * chunks;
+  const auto get = [&](int k) { return __builtin_bit_cast(float2, rp[k]); };
+  const float2 ms = chunks <= 64 ? combine_wave<S>(get, chunks, res) : combine<S>(get, chunks, lds);
+  store_y<S, kChunkThreads, VPT, VEC>(y + row * n, n, c * Chunk<S>::kVec, threadIdx.x,
+                                      out_scale<S>(mc, ms), ev);
+  __syncthreads();  // every thread has read what it needs of the partials
+  if (threadIdx.x == 0)
+    last = atomicAdd(cnt + 2 * row, 1u) == static_cast<uint32_t>(chunks - 1) ? 1 : 0;
+  __syncthreads();
+  if (last) {
+    for (int k = threadIdx.x; k < chunks; k += kChunkThreads) rp[k] = 0;
+    if (threadIdx.x == 0) cnt[2 * row] = 0;
+  }
+}
+
 // Without a workspace: one block per row computes the row's statistics
 // itself (row_stats_self), then writes chunk by chunk -- three reads of the
 // row, the same bits as the workspace path.
@@ -571,6 +629,25 @@ void launch_chunks(const S* x, S* y, int64_t rows, int n, float tt, float inv_t,
 }
 
 template <typename S, bool VEC>
+void launch_two_pass(const S* x, S* y, int64_t rows, int n, float tt, float inv_t, void* ws,
+                     hipStream_t s) {
+  const int64_t chunks = chunks_of(n);
+  const int64_t rows_per_launch = kMaxGrid / chunks;
+  uint32_t* cnt = static_cast<uint32_t*>(ws);
+  uint64_t* part = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + counter_bytes(rows));
+  for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
+    const int64_t m = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
+    const unsigned grid = static_cast<unsigned>(m * chunks);
+    softmax_chunk_stats<S, VEC><<<grid, kChunkThreads, 0, s>>>(x + r0 * n, n,
+                                                               static_cast<int>(chunks), tt, inv_t,
+                                                               part + r0 * chunks);
+    softmax_chunk_write<S, VEC><<<grid, kChunkThreads, 0, s>>>(
+        x + r0 * n, y + r0 * n, n, static_cast<int>(chunks), tt, inv_t, part + r0 * chunks,
+        cnt + 2 * r0);
+  }
+}
+
+template <typename S, bool VEC>
 void launch_row_blocks(const S* x, S* y, int64_t rows, int n, float tt, float inv_t,
                        hipStream_t s) {
   const int64_t chunks = chunks_of(n);
@@ -612,8 +689,14 @@ et_status softmax_entry(const S* x, S* y, int64_t rows, int64_t n, float tempera
     if (!ranges_ok(ws, static_cast<int64_t>(ws_bytes), x, bytes, false) ||
         !ranges_ok(ws, static_cast<int64_t>(ws_bytes), y, bytes, false))
       return ET_ERR_OVERLAP;
-    if (vec) launch_chunks<S, true>(x, y, rows, static_cast<int>(n), temperature, inv_t, ws, s);
-    else launch_chunks<S, false>(x, y, rows, static_cast<int>(n), temperature, inv_t, ws, s);
+    if (chunks_of(n) > kMaxExchangeChunks) {
+      if (vec) launch_two_pass<S, true>(x, y, rows, static_cast<int>(n), temperature, inv_t, ws, s);
+      else launch_two_pass<S, false>(x, y, rows, static_cast<int>(n), temperature, inv_t, ws, s);
+    } else if (vec) {
+      launch_chunks<S, true>(x, y, rows, static_cast<int>(n), temperature, inv_t, ws, s);
+    } else {
+      launch_chunks<S, false>(x, y, rows, static_cast<int>(n), temperature, inv_t, ws, s);
+    }
     return launch_status();
   }
   if (vec) launch_row_blocks<S, true>(x, y, rows, static_cast<int>(n), temperature, inv_t, s);

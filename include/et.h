@@ -351,7 +351,9 @@ et_status et_geglu_f16(const et_f16* gate, const et_f16* up, et_f16* y,
  *   whose largest z is +-inf, gives a row of NaN.
  *   workspace: device scratch for rows longer than 32768 elements, which are
  *   then split over several workgroups in one launch (each element read
- *   once).  Either workspace == NULL with workspace_bytes == 0 (one workgroup
+ *   once; rows of more than 1024 chunks of 8192 elements, over 8388608
+ *   elements, in two launches, read twice).  Either workspace == NULL with
+ *   workspace_bytes == 0 (one workgroup
  *   per long row, reading the row three times), or workspace != NULL,
  *   16-byte aligned, with workspace_bytes >= et_softmax_workspace_bytes(rows,
  *   n) (0 for rows of at most 32768 elements), else ET_ERR_WORKSPACE.  The

@@ -93,6 +93,26 @@ def test_softmax_bounded_wait_fallback_same_bits(et, dt, n, monkeypatch):
     assert_bits(d, a, f"{dt} n={n} reuse")
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("rows,n", [(3, 1024 * 8192), (1, 1024 * 8192 + 3), (2, (1 << 24) + 5)])
+def test_softmax_very_long_rows(et, orc, dt, rows, n):
+    """Rows past 1024 chunks of 8192 take two launches (chunk statistics,
+    then combine and write): one launch would need all of a row's chunk
+    workgroups resident together.  At exactly 1024 chunks, the one-launch
+    exchange.  Against the oracle, the same bits as one workgroup per row
+    (no workspace), the same again on a reused workspace, which every call
+    leaves zero-filled."""
+    x = _logits((rows, n), dt, (n, 11))
+    xs = dev(x)
+    ws = torch.zeros(et.softmax_workspace_bytes(rows, n), dtype=torch.uint8, device="cuda")
+    a = host(et.softmax(xs, 0.8, workspace=ws))
+    assert int(torch.count_nonzero(ws)) == 0, "workspace not left zero-filled"
+    assert_bits(host(et.softmax(xs, 0.8, workspace=ws)), a, f"{dt} {rows}x{n} reused workspace")
+    assert_bits(host(et.softmax(xs, 0.8, split=False)), a, f"{dt} {rows}x{n} one workgroup per row")
+    y, y64 = orc.softmax(x, 0.8)
+    check_softmax(a, x, 0.8, y, y64, f"{dt} {rows}x{n}")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("n", [100, 4096, 32768, 40000, 128256])
 def test_softmax_batch_invariance_and_in_place(et, dt, n):
