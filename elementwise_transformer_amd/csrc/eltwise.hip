@@ -121,32 +121,50 @@ __device__ inline float erfc_exp2_poly5(float t8) {
 // GELU-gated product, exact form: x Phi(x) u, with Phi(x) = erfc(-x/sqrt 2) / 2
 // (the identity 1 + erf(z) = erfc(-z) keeps the tail of negative x, where
 // 1 + erf cancels), Phi(-|x|) = t8 2^K as above and Phi(|x|) = 1 - Phi(-|x|).
-// The hardware exp2 returns no subnormals, so 2^K alone would flush every
-// Phi below 2^-126 -- results x Phi(x) u down to 2^-149 from x near -13 on in
-// f32 and bf16 storage, and every product with a large or infinite up beyond
-// that.  So K (held above -320, where every product of f32 values times 2^K
-// is below the smallest subnormal) is split into its floor n and a fraction:
-// q = t8 2^(K - n) and Phi(-|x|) = q 2^n, with |x q| < 2^-1.5, so x q u is
-// finite for every finite u and ldexp(x q u, n) rounds a subnormal result
-// once and correctly.  a' is held at 2^100 in t8 (whose reciprocal would
-// flush from 2^127 on), so q is never 0 for a finite x: x Phi(x) is nonzero
-// for every finite x, and its product with an infinite u is an infinity.
-// Phi(-inf) is 0 and -inf * 0 has no value: NaN.  Both signs are computed
-// and one is selected, so a wave of mixed signs runs no branch.
+// While K >= -100 (|x| below about 12: every gate a model produces), 2^K is
+// a normal number, q = t8 2^K = Phi(-|x|) is at least 2^-105 and
+// |x q| <= max x Phi(-x) < 0.17, so x q u is finite for every finite u,
+// nonzero times an infinite one, and rounds once: one exp2 does.  Past that
+// (and for x = +-inf), the exact tail below; a wave runs it only when one of
+// its lanes needs it.
+template <typename S>
+__device__ inline float gelu_erf_tail(float x, float u, float ap);
+
 template <typename S>
 __device__ inline float gelu_erf_mul(float x, float u) {
   constexpr float kA = 0x1.b2da4ep-1f;   // sqrt(log2(e) / 2): a' = |x| kA
   constexpr float kT = 0x1.aa449ap+1f;   // 4 / sqrt(log2 e): 8 + 4a = 8 + kT a'
   const float ap = __builtin_fabsf(x) * kA;
+  const float t8 = __builtin_amdgcn_rcpf(__builtin_fmaf(kT, ap, 8.0f));
+  const float p = sizeof(S) == 4 ? erfc_exp2_poly9(t8) : erfc_exp2_poly5(t8);
+  const float k = __builtin_fmaf(-ap, ap, p);
+  if (k < -100.0f) return gelu_erf_tail<S>(x, u, ap);
+  const float q = t8 * __builtin_amdgcn_exp2f(k);              // Phi(-|x|)
+  return x <= 0.0f ? x * q * u : x * (1.0f - q) * u;
+}
+
+// The tail, K < -100.  The hardware exp2 returns no subnormals, so 2^K alone
+// would flush every Phi below 2^-126 -- results x Phi(x) u down to 2^-149
+// from x near -13 on in f32 and bf16 storage, and every product with a large
+// or infinite up beyond that.  So K (held above -320, where every product of
+// f32 values times 2^K is below the smallest subnormal) is split into its
+// floor n and a fraction: q = t8 2^(K - n), Phi(-|x|) = q 2^n, |x q| <
+// 2^-1.5, so x q u is finite for every finite u and ldexp(x q u, n) rounds a
+// subnormal result once and correctly.  a' is held at 2^100 in t8 (whose
+// reciprocal would flush from 2^127 on), so q is never 0 for a finite x: x
+// Phi(x) is nonzero for every finite x, and its product with an infinite u
+// is an infinity.  Phi(-inf) is 0 and -inf * 0 has no value: NaN.
+template <typename S>
+__device__ inline float gelu_erf_tail(float x, float u, float ap) {
+  constexpr float kT = 0x1.aa449ap+1f;
   const float t8 = __builtin_amdgcn_rcpf(__builtin_fmaf(kT, __builtin_fminf(ap, 0x1p100f), 8.0f));
   const float p = sizeof(S) == 4 ? erfc_exp2_poly9(t8) : erfc_exp2_poly5(t8);
   const float kc = __builtin_fmaxf(__builtin_fmaf(-ap, ap, p), -320.0f);
   const float n = __builtin_floorf(kc);
   const int ni = static_cast<int>(n);
   const float q = t8 * __builtin_amdgcn_exp2f(kc - n);         // Phi(-|x|) = q 2^n
-  const float neg = __builtin_ldexpf(x * q * u, ni);            // x <= 0
-  const float pos = x * (1.0f - __builtin_ldexpf(q, ni)) * u;   // x > 0
-  const float r = x <= 0.0f ? neg : pos;
+  const float r = x <= 0.0f ? __builtin_ldexpf(x * q * u, ni)
+                            : x * (1.0f - __builtin_ldexpf(q, ni)) * u;
   return x == -__builtin_inff() ? __builtin_nanf("") : r;
 }
 
