@@ -22,6 +22,7 @@ fraction of the stream of its own shape.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -233,18 +234,23 @@ def traffic_record(workload, op):
 
 
 def _time_launches(stream, fn, sets, launches):
-    """Per-launch HIP-event times (ms) of fn(i), i over rotating buffer sets."""
+    """Per-launch HIP-event times (ms) of fn(i), i over rotating buffer sets.
+    The events are created before the loop and Python's collector is paused
+    inside it, so no host pause lands between an event and its launch."""
+    import gc
     import torch
     for i in range(sets * 2):
         fn(i)
+    evs = [TimingEvents(stream) for _ in range(launches)]
     torch.cuda.synchronize()
-    evs = []
-    for i in range(launches):
-        ev = TimingEvents(stream)
-        ev.start()
-        fn(i)
-        ev.stop()
-        evs.append(ev)
+    gc.disable()
+    try:
+        for i, ev in enumerate(evs):
+            ev.start()
+            fn(i)
+            ev.stop()
+    finally:
+        gc.enable()
     torch.cuda.synchronize()
     t = [ev.elapsed_ms() for ev in evs]
     for ev in evs:
@@ -602,6 +608,7 @@ def main():
             pair[j] = TimingEvents(stream)
         plan.append(pair)
     torch.cuda.synchronize()
+    gc.disable()                      # no collector pause inside the timed region
     t0 = time.perf_counter()
     for s in range(args.steps):
         pair = plan[s]
@@ -614,6 +621,7 @@ def main():
                 ev.stop()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     for s in range(args.steps):
         for i, ev in plan[s].items():
             ops[i].ms.append(ev.elapsed_ms())
