@@ -1,0 +1,64 @@
+"""The plain-stream probe the benchmark measures the kernels against
+(libet_probe.so): each stream shape reads and writes what it says, in both
+store policies, so the ceiling it reports is the rate of real loads and
+stores of data.  Expected values are written out here from the probe's
+stated outputs (XOR and sum of the 16-byte words read, per 32-bit lane)."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def probe():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import elementwise_transformer_amd  # noqa: F401  (same runtime as the library)
+    lib = ctypes.CDLL(os.path.join(ROOT, "elementwise_transformer_amd", "libet_probe.so"))
+    f = lib.et_probe_stream
+    vp = ctypes.c_void_p
+    f.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_int, vp]
+    f.restype = ctypes.c_int
+    return f
+
+
+@pytest.mark.parametrize("nbytes", [16, 16 * 1000 + 16 * 37, 32 << 20])
+@pytest.mark.parametrize("u", [4, 8])
+@pytest.mark.parametrize("dev_scope", [0, 1])
+def test_stream_probe_outputs(probe, nbytes, u, dev_scope):
+    g = np.random.default_rng([7070, nbytes, u])
+    words = nbytes // 4
+    a = g.integers(0, 2 ** 32, words, dtype=np.uint64).astype(np.uint32)
+    b = g.integers(0, 2 ** 32, words, dtype=np.uint64).astype(np.uint32)
+    at = torch.from_numpy(a.view(np.int32)).cuda()
+    bt = torch.from_numpy(b.view(np.int32)).cuda()
+    s = torch.cuda.current_stream().cuda_stream
+
+    def run(nr, nw):
+        y = torch.full((words,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+        h = torch.full((words,), 0x3C3C3C3C, dtype=torch.int32, device="cuda")
+        assert probe(at.data_ptr(), bt.data_ptr(), y.data_ptr(), h.data_ptr(), nbytes, nr, nw, u,
+                     dev_scope, s) == 0
+        torch.cuda.synchronize()
+        return y.cpu().numpy().view(np.uint32), h.cpu().numpy().view(np.uint32)
+
+    pattern = np.tile(np.array([0x11, 0x22, 0x33, 0x44], np.uint32), words // 4)
+    y, h = run(2, 2)
+    assert np.array_equal(y, a ^ b) and np.array_equal(h, a + b)
+    y, h = run(2, 1)
+    assert np.array_equal(y, a ^ b) and np.all(h == 0x3C3C3C3C)
+    y, _ = run(1, 1)
+    assert np.array_equal(y, a ^ pattern)
+    y, _ = run(1, 0)
+    assert np.all(y == 0x5A5A5A5A)                     # a pure read stores nothing for real data
+    y, _ = run(0, 1)
+    i = np.arange(words // 4, dtype=np.uint64)
+    lane = np.stack([i.astype(np.uint32), np.full_like(i, 0x5bd1e995, dtype=np.uint32),
+                     (i >> 7).astype(np.uint32), np.full_like(i, 0x1b873593, dtype=np.uint32)], axis=1)
+    assert np.array_equal(y, (lane ^ np.array([0x11, 0x22, 0x33, 0x44], np.uint32)).ravel())
