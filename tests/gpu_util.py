@@ -23,9 +23,22 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+import functools
+
 F32_REL = 1e-6
 F32_FLOOR = 2.0 ** -140
 BF16_PAIR = 2.0 ** -16
+
+
+def _quiet(fn):
+    """Run a check with numpy's invalid/overflow warnings off: with special
+    values in the data, the tolerance arithmetic meets inf - inf and the
+    like; NaN positions and infinities are compared on their own."""
+    @functools.wraps(fn)
+    def wrapped(*args, **kwargs):
+        with np.errstate(invalid="ignore", over="ignore"):
+            return fn(*args, **kwargs)
+    return wrapped
 
 
 def dev(a: np.ndarray) -> torch.Tensor:
@@ -67,6 +80,7 @@ def assert_bits(got: np.ndarray, ref: np.ndarray, what: str = "") -> None:
 F32_OVERFLOW = 2.0 ** 128 - 2.0 ** 103   # round-to-nearest f32 gives +-inf from here on
 
 
+@_quiet
 def assert_f32_rel(got: np.ndarray, y64: np.ndarray, what: str = "", rel: float = F32_REL,
                    abs_extra=None) -> None:
     """F32_REL; where y is infinite, or rounds to infinity in f32, got must be
@@ -153,6 +167,7 @@ def pair_norms(y64: np.ndarray, r: int, layout: int) -> np.ndarray:
     return out
 
 
+@_quiet
 def assert_pair(got: np.ndarray, y64: np.ndarray, ref: np.ndarray, r: int, layout: int,
                 what: str = "") -> None:
     """PAIR tolerance on the first r entries of each head row."""
@@ -175,6 +190,7 @@ def assert_pair(got: np.ndarray, y64: np.ndarray, ref: np.ndarray, r: int, layou
 U = 2.0 ** -24
 
 
+@_quiet
 def check_softmax(got, x_store, t, y, y64, what=""):
     """Softmax bound: f32 derived relative bound, 2-byte 1 ulp; results
     below 2^-126 may come out as 0 (see the softmax tests)."""
@@ -205,6 +221,7 @@ def check_softmax(got, x_store, t, y, y64, what=""):
         assert_bf16_ulp(g, y, what)
 
 
+@_quiet
 def check_layernorm(got, xs, gs, bs, eps, y, y64, what=""):
     """LayerNorm absolute bound of the f32 arithmetic, plus one ulp in 2-byte
     storage (see the LayerNorm tests)."""
@@ -229,6 +246,7 @@ def check_layernorm(got, xs, gs, bs, eps, y, y64, what=""):
                              f"ref={y64[~rn][i]!r} tol={tol[~rn][i]:.3g}")
 
 
+@_quiet
 def check_geglu(got, gate_s, form, y, y64, what="", abs_extra=None):
     """GeGLU: f32 relative bound of the form's arithmetic, 2-byte 1 ulp (see
     the GeGLU tests)."""

@@ -16,8 +16,9 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_util import (assert_bits, assert_close, assert_f32_rel, assert_pair, check_geglu,
-                      check_layernorm, check_softmax, dev, host)
+from gpu_util import (BF16_PAIR, F32_FLOOR, F32_REL, assert_bits, assert_close, assert_f32_rel,
+                      assert_pair, bf16_key, check_geglu, check_layernorm, check_softmax, dev, host,
+                      pair_norms, widen)
 
 pytestmark = pytest.mark.gpu
 
@@ -253,19 +254,19 @@ def test_random_specials_rows(et, orc, dt, seed):
 def _assert_pair_special(got, y64, ref, r, layout, what):
     """The PAIR tolerance where a pair's two oracle values are finite; NaN
     and infinite entries elsewhere must match in position (and sign)."""
-    from gpu_util import F32_FLOOR, F32_REL, BF16_PAIR, bf16_key, pair_norms, widen
-    g, y = widen(got), y64
-    assert np.array_equal(np.isnan(g), np.isnan(y)), f"{what}: NaN positions differ"
-    inf = np.isinf(y)
-    assert np.array_equal(g[inf], y[inf]), f"{what}: infinities differ"
-    pn = pair_norms(np.where(np.isfinite(y), y, np.nan), r, layout)[..., :r]
-    ok = np.isfinite(pn)
-    err = np.abs(g[..., :r] - y[..., :r])
-    if got.dtype == np.float32:
-        bad = ok & ~(err <= F32_REL * pn + F32_FLOOR)
-    else:
-        ud = np.abs(bf16_key(got[..., :r]) - bf16_key(ref[..., :r]))
-        bad = ok & ~((ud <= 1) | (err <= BF16_PAIR * pn))
+    with np.errstate(invalid="ignore", over="ignore"):
+        g, y = widen(got), y64
+        assert np.array_equal(np.isnan(g), np.isnan(y)), f"{what}: NaN positions differ"
+        inf = np.isinf(y)
+        assert np.array_equal(g[inf], y[inf]), f"{what}: infinities differ"
+        pn = pair_norms(np.where(np.isfinite(y), y, np.nan), r, layout)[..., :r]
+        ok = np.isfinite(pn)
+        err = np.abs(g[..., :r] - y[..., :r])
+        if got.dtype == np.float32:
+            bad = ok & ~(err <= F32_REL * pn + F32_FLOOR)
+        else:
+            ud = np.abs(bf16_key(got[..., :r]) - bf16_key(ref[..., :r]))
+            bad = ok & ~((ud <= 1) | (err <= BF16_PAIR * pn))
     assert not bad.any(), f"{what}: {int(bad.sum())} rotated entries over the pair tolerance"
 
 
