@@ -131,6 +131,18 @@ def test_random_rope(et, orc, dt, seed):
     qm = _dev_maybe_misaligned(q, True)
     et.rope_qk(qm, None, dev(pos), dev(inv), d_rot=r, attn_scaling=mu, layout=layout)
     assert_bits(host(qm), host(qt), f"rope misaligned {what}")
+    # the rotation read from the library's own cos/sin cache: the same bits,
+    # on the vector and the scalar path
+    if r:
+        c, sn = et.rope_cache(dev(inv), int(pos.max()) + 1, r)
+        qc, kc = dev(q), (dev(k) if k is not None else None)
+        et.rope_qk_cached(qc, kc, dev(pos), c, sn, d_rot=r, attn_scaling=mu, layout=layout)
+        assert_bits(host(qc), host(qt), f"cached rope q {what}")
+        if k is not None:
+            assert_bits(host(kc), host(kt), f"cached rope k {what}")
+        qcm = _dev_maybe_misaligned(q, True)
+        et.rope_qk_cached(qcm, None, dev(pos), c, sn, d_rot=r, attn_scaling=mu, layout=layout)
+        assert_bits(host(qcm), host(qt), f"cached rope misaligned {what}")
 
 
 @pytest.mark.parametrize("dt", DTS)
