@@ -328,3 +328,32 @@ def test_random_specials_rope(et, orc, dt, seed):
                                  np.ascontiguousarray(ref[..., o:o + dw]), dw, layout, f"multi axis {a} {what}")
         o += dw
     assert_bits(got[..., r:], q[..., r:], f"multi pass-through {what}")
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_call_sequences_share_a_workspace(et, orc, seed):
+    """A seeded sequence of argmax and softmax calls of random shapes and
+    storage types, all through one caller-owned workspace sized for the
+    largest: each result against the oracle, and the workspace zero-filled
+    after every call (the contract that lets the next call reuse it)."""
+    g = np.random.default_rng([5656, seed])
+    shapes = []
+    for _ in range(10):
+        n = int(g.choice([_length(g, 2, 200000), (1024 * 8192) + int(g.integers(1, 9000))]))
+        if n > 200000:
+            rows = 1                                         # a row of more than 1024 chunks: two launches
+        else:
+            rows = _rows(g, n, 1 << 20)
+        shapes.append((rows, n, DTS[int(g.integers(0, 3))], bool(g.uniform() < 0.5)))
+    need = max(max(et.softmax_workspace_bytes(r, n), et.argmax_workspace_bytes(r, n)) for r, n, _, _ in shapes)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
+    for i, (rows, n, dt, soft) in enumerate(shapes):
+        x = wl.store(np.round(g.standard_normal((rows, n)) * 4).astype(np.float32), dt)
+        xt = dev(x)
+        what = f"call {i}: {'softmax' if soft else 'argmax'} {dt} {rows}x{n}"
+        if soft:
+            y, y64 = orc.softmax(x, 0.9)
+            check_softmax(host(et.softmax(xt, 0.9, workspace=ws)), x, 0.9, y, y64, what)
+        else:
+            assert_bits(host(et.argmax(xt, workspace=ws)), orc.argmax(x), what)
+        assert int(torch.count_nonzero(ws)) == 0, f"{what}: workspace not left zero-filled"
