@@ -265,7 +265,9 @@ def _time_launches(stream, fn, sets, launches):
 # two); 112 MiB one [4096, 14336] bf16 operand of the prefill SiLU-mul (two
 # reads, one write) and GeGLU; 125 MiB the decode logits [256, 128256] f32
 # softmax reads and writes; 225 MiB the q and k [19200, 24, 128] bf16 the
-# multi-axis RoPE rotates.  Non-temporal and device-scope stores are the two
+# multi-axis RoPE rotates in place; "inplace" cases write back over what they read
+# (the output buffer is the input), as RoPE does to q and k [4096, 32 + 8,
+# 128] bf16 (40 MiB).  Non-temporal and device-scope stores are the two
 # policies the kernels choose between by output size.
 CEILING_CASES = [
     ("read_32MiB", 32 << 20, 1, 0, 0),
@@ -278,24 +280,25 @@ CEILING_CASES = [
     ("2R1W_112MiB", 4096 * 14336 * 2, 2, 1, 0),
     ("2R1W_112MiB_dev", 4096 * 14336 * 2, 2, 1, 1),
     ("1R1W_125MiB", 256 * 128256 * 4, 1, 1, 0),
-    ("1R1W_225MiB", 19200 * 48 * 128 * 2, 1, 1, 0),
+    ("inplace_225MiB", 19200 * 48 * 128 * 2, 1, 1, 0),
+    ("inplace_40MiB_dev", 4096 * 40 * 128 * 2, 1, 1, 1),
 ]
 
 
 # The plain stream of each prefill-step op's shape and store policy (the
-# policy its kernel picks at that output size); RoPE's in-place rotation of
-# q (32 MiB) and k (8 MiB) is a 1-read 1-write stream of about that size.
+# policy its kernel picks at that output size); RoPE rotates q (32 MiB) and k
+# (8 MiB) in place, so its stream writes back over what it reads.
 OP_CEILING = {2: {"rmsnorm": "1R1W_32MiB", "embedding": "1R1W_32MiB", "add": "2R1W_32MiB_dev",
-                  "add_rmsnorm": "2R2W_32MiB", "rope": "1R1W_32MiB_dev",
-                  "rmsnorm_rope": "1R1W_32MiB_dev", "silu_mul": "2R1W_112MiB_dev"}}
+                  "add_rmsnorm": "2R2W_32MiB", "rope": "inplace_40MiB_dev",
+                  "rmsnorm_rope": "inplace_40MiB_dev", "silu_mul": "2R1W_112MiB_dev"}}
 
 
 # The same for the ops timed beyond the step (their kernels' store policies:
 # non-temporal for softmax, LayerNorm and the multi-axis RoPE, device scope
 # for GeGLU and the cached RoPE at these sizes).
 NEXT_CEILING = {"softmax": "1R1W_125MiB", "layernorm": "1R1W_32MiB", "geglu_erf": "2R1W_112MiB_dev",
-                "geglu_tanh": "2R1W_112MiB_dev", "rope_cached": "1R1W_32MiB_dev",
-                "rope_multi": "1R1W_225MiB"}
+                "geglu_tanh": "2R1W_112MiB_dev", "rope_cached": "inplace_40MiB_dev",
+                "rope_multi": "inplace_225MiB"}
 
 
 def stream_ceiling(torch, stream, launches=40):
@@ -321,6 +324,8 @@ def stream_ceiling(torch, stream, launches=40):
         for u in (4, 8):
             def fn(i, u=u):
                 a, b, y, h = bufs[i % sets]
+                if name.startswith("inplace"):
+                    y = a
                 rc = f(a.data_ptr(), b.data_ptr(), y.data_ptr(), h.data_ptr(), nb, nr, nw, u, dev,
                        stream.cuda_stream)
                 if rc != 0:
