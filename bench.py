@@ -283,6 +283,15 @@ CEILING_CASES = [
     ("inplace_225MiB", 19200 * 48 * 128 * 2, 1, 1, 0),
     ("inplace_40MiB_dev", 4096 * 40 * 128 * 2, 1, 1, 1),
 ]
+# Cases only the large-hidden chain (workload 5: T = 8192, hidden 8192, FFN
+# 28672, bf16) needs, measured when that workload runs: its in-place fused
+# add+RMSNorm (x and residual, 128 MiB each, written back), its RoPE's q and
+# k (144 MiB in place) and its SiLU-mul operands (448 MiB).
+WORKLOAD_CASES = {5: [
+    ("inplace_2R2W_128MiB", 8192 * 8192 * 2, 2, 2, 0),
+    ("inplace_144MiB", 8192 * 72 * 128 * 2, 1, 1, 0),
+    ("2R1W_448MiB", 8192 * 28672 * 2, 2, 1, 0),
+]}
 
 
 # The plain stream of each prefill-step op's shape and store policy (the
@@ -290,7 +299,9 @@ CEILING_CASES = [
 # (8 MiB) in place, so its stream writes back over what it reads.
 OP_CEILING = {2: {"rmsnorm": "1R1W_32MiB", "embedding": "1R1W_32MiB", "add": "2R1W_32MiB_dev",
                   "add_rmsnorm": "2R2W_32MiB", "rope": "inplace_40MiB_dev",
-                  "rmsnorm_rope": "inplace_40MiB_dev", "silu_mul": "2R1W_112MiB_dev"}}
+                  "rmsnorm_rope": "inplace_40MiB_dev", "silu_mul": "2R1W_112MiB_dev"},
+              5: {"add_rmsnorm": "inplace_2R2W_128MiB", "rope": "inplace_144MiB",
+                  "rmsnorm_rope": "inplace_144MiB", "silu_mul": "2R1W_448MiB"}}
 
 
 # The same for the ops timed beyond the step (their kernels' store policies:
@@ -301,7 +312,7 @@ NEXT_CEILING = {"softmax": "1R1W_125MiB", "layernorm": "1R1W_32MiB", "geglu_erf"
                 "rope_multi": "inplace_225MiB"}
 
 
-def stream_ceiling(torch, stream, launches=40):
+def stream_ceiling(torch, stream, workload, launches=40):
     """Per-launch HIP-event times of plain HBM streams (libet_probe.so: 16-byte
     non-temporal loads, stores by the given policy, nothing computed between),
     each case over rotating buffer sets whose footprint is several times the
@@ -316,7 +327,7 @@ def stream_ceiling(torch, stream, launches=40):
                   ctypes.c_int, vp]
     f.restype = ctypes.c_int
     out = {}
-    for name, nb, nr, nw, dev in CEILING_CASES:
+    for name, nb, nr, nw, dev in CEILING_CASES + WORKLOAD_CASES.get(workload, []):
         sets = max(4, -(-(1 << 30) // (4 * nb)))
         bufs = [[torch.randint(0, 256, (nb,), dtype=torch.uint8, device="cuda") for _ in range(4)]
                 for _ in range(sets)]
@@ -325,7 +336,7 @@ def stream_ceiling(torch, stream, launches=40):
             def fn(i, u=u):
                 a, b, y, h = bufs[i % sets]
                 if name.startswith("inplace"):
-                    y = a
+                    y, h = a, b
                 rc = f(a.data_ptr(), b.data_ptr(), y.data_ptr(), h.data_ptr(), nb, nr, nw, u, dev,
                        stream.cuda_stream)
                 if rc != 0:
@@ -636,7 +647,7 @@ def main():
     # its own workload after the timed region, as back-to-back launches over
     # rotating buffer sets with one pair of events per launch.
     next_ops = None if args.no_next_ops else time_next_ops(et, torch, wl, stream)
-    ceiling = None if args.no_stream_ceiling else stream_ceiling(torch, stream)
+    ceiling = None if args.no_stream_ceiling else stream_ceiling(torch, stream, args.workload)
 
     # Attainable-bandwidth context: a plain device-to-device copy as large as
     # the dominant op's largest operand (read once, written once), timed the
