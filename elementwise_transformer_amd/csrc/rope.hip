@@ -38,8 +38,15 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kMaxTableBytes = 48 * 1024;
+// Slots per lane of the RoPE kernel (plain and cached angles): at most
+// ET_ROPE_UMAX with non-temporal stores, ET_ROPE_UMAX_DEV with device-scope
+// ones (one slot per lane was 6 % faster there inside a prefill layer, and
+// slower with non-temporal stores at 144 MiB).
 #ifndef ET_ROPE_UMAX
 #define ET_ROPE_UMAX 2
+#endif
+#ifndef ET_ROPE_UMAX_DEV
+#define ET_ROPE_UMAX_DEV 1
 #endif
 #ifndef ET_QK_UMAX
 #define ET_QK_UMAX 2
@@ -670,7 +677,8 @@ et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int
   bool vec = (r % (2 * V)) == 0 && (D % V) == 0 && aligned16(q) && (hk == 0 || aligned16(k));
   RopeArgs a = make_args(T, hq, hk, D, r, mu, layout, vec ? V : 1);
   if (a.spt > (1u << 30)) return ET_ERR_BAD_SIZE;
-  int u = pick_u(a.spt, a.half, kBlock, ET_ROPE_UMAX);
+  const bool dev = store_policy(T * (hq + hk) * r * int64_t(sizeof(S)), ET_POL_ROPE) == kStoreDevice;
+  int u = pick_u(a.spt, a.half, kBlock, vec && dev ? ET_ROPE_UMAX_DEV : ET_ROPE_UMAX);
   if (u == 0) return ET_ERR_BAD_SIZE;
   auto set_cache = [&](RopeArgs& ra) {
     if (!cache) return;
@@ -694,7 +702,7 @@ et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int
     }
   }
   (void)hipGetLastError();
-  if (vec && store_policy(T * (hq + hk) * r * int64_t(sizeof(S)), ET_POL_ROPE) == kStoreDevice) {
+  if (vec && dev) {
     if (u == 4) launch_rope<S, V, 4, kStoreDevice>(q, k, pos, inv_freq, a, T, s);
     else if (u == 2) launch_rope<S, V, 2, kStoreDevice>(q, k, pos, inv_freq, a, T, s);
     else launch_rope<S, V, 1, kStoreDevice>(q, k, pos, inv_freq, a, T, s);
