@@ -74,6 +74,8 @@ lib.et_argmax_workspace_bytes.argtypes = [_i64, _i64]
 lib.et_argmax_workspace_bytes.restype = _sz
 lib.et_softmax_workspace_bytes.argtypes = [_i64, _i64]
 lib.et_softmax_workspace_bytes.restype = _sz
+lib.et_softmax_wait_limit.argtypes = [_int, _vp, _vp, _i64, _i64, _f32, _vp, _sz, _int, _vp]
+lib.et_softmax_wait_limit.restype = ctypes.c_int
 lib.et_rope_cache_f32.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]
 lib.et_rope_cache_f32.restype = ctypes.c_int
 lib.et_status_string.argtypes = [ctypes.c_int]
@@ -400,12 +402,18 @@ def softmax_workspace_bytes(rows: int, n: int) -> int:
     return int(lib.et_softmax_workspace_bytes(int(rows), int(n)))
 
 
+_STORAGE = {"f32": 0, "bf16": 1, "f16": 2}
+
+
 def softmax(x: torch.Tensor, temperature: float = 1.0, out: Optional[torch.Tensor] = None,
-            workspace: Optional[torch.Tensor] = None, split: bool = True) -> torch.Tensor:
+            workspace: Optional[torch.Tensor] = None, split: bool = True,
+            wait_limit: Optional[int] = None) -> torch.Tensor:
     """Softmax of x / temperature over the last axis (et_softmax_*); out may be
     x.  ``split`` lets rows longer than 32768 elements spread over several
     workgroups through a workspace: zero-filled here unless given; a given
-    one must be zero-filled before its first use (each call leaves it so)."""
+    one must be zero-filled before its first use (each call leaves it so).
+    ``wait_limit`` (tests of the bounded wait) calls et_softmax_wait_limit
+    with that many polls per thread instead."""
     n = x.shape[-1]
     rows = math.prod(x.shape[:-1])
     out = torch.empty_like(x) if out is None else out
@@ -419,6 +427,10 @@ def softmax(x: torch.Tensor, temperature: float = 1.0, out: Optional[torch.Tenso
                 workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
             _dev(workspace)
             ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
-    _call(f"et_softmax_{_sfx(x)}", _ptr(x), _ptr(out), rows, n, float(temperature), ws_ptr, ws_bytes,
-          _stream(x))
+    if wait_limit is None:
+        _call(f"et_softmax_{_sfx(x)}", _ptr(x), _ptr(out), rows, n, float(temperature), ws_ptr,
+              ws_bytes, _stream(x))
+    else:
+        _call("et_softmax_wait_limit", _STORAGE[_sfx(x)], _ptr(x), _ptr(out), rows, n,
+              float(temperature), ws_ptr, ws_bytes, int(wait_limit), _stream(x))
     return out

@@ -1,9 +1,7 @@
 """Build libet.so: the gfx950 HIP kernels and their C-ABI entry points.
 
 Each ``csrc/*.hip`` file is compiled with hipcc for gfx950 into an object
-under ``_build/``, then linked into ``libet.so`` next to this file.  The
-plain-stream probe the benchmark measures the kernels against
-(``probe/*.hip``) is linked apart, into ``libet_probe.so``.
+under ``_build/``, then linked into ``libet.so`` next to this file.
 Usage: ``python elementwise_transformer_amd/_build.py`` (the package itself
 refuses to import until the library exists).
 """
@@ -20,8 +18,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libet.so")
-PROBE_SRC = os.path.join(PKG, "probe")
-PROBE_LIB = os.path.join(PKG, "libet_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -O3, IEEE f32 division and square root (HIP's default), denormals kept, no
@@ -54,18 +50,15 @@ def _link(objs, lib: str) -> None:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source, link libet.so and libet_probe.so; returns
-    the path of libet.so."""
+    """Compile every HIP source and link libet.so; returns its path."""
     os.makedirs(OBJ, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    probes = sorted(glob.glob(os.path.join(PROBE_SRC, "*.hip")))
-    jobs = min(len(srcs) + len(probes), max(1, min(8, os.cpu_count() or 1)))
+    jobs = min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs + probes))
-    _link(objs[:len(srcs)], LIB)
-    _link(objs[len(srcs):], PROBE_LIB)
+        objs = list(ex.map(_compile, srcs))
+    _link(objs, LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources and {PROBE_LIB} from {len(probes)}")
+        print(f"built {LIB} from {len(srcs)} sources")
     return LIB
 
 

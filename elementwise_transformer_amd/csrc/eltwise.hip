@@ -18,32 +18,14 @@
 namespace et {
 namespace {
 
-#ifndef ET_POL_ELT
-#define ET_POL_ELT 0  // 0: by size, 1: non-temporal, 2: device scope
-#endif
-#ifndef ET_POL_ADD
-#define ET_POL_ADD 0  // 0: by size, 1: non-temporal, 2: device scope
-#endif
-
 constexpr int kBlock = 256;
-#ifndef ET_ELT_U
-#define ET_ELT_U 4
-#endif
-constexpr int kU = ET_ELT_U;  // vectors per thread per input
-#ifndef ET_ELT_WAVE
-#define ET_ELT_WAVE 1
-#endif
+constexpr int kU = 4;  // vectors per thread per input
 
 // Vector index of slot u of thread tid in block b.  A block covers
-// kBlock * kU consecutive vectors; with ET_ELT_WAVE each wave owns a
-// contiguous quarter of them (slot u of lane l at u * 64 + l), else slot u
-// of the block is one contiguous kBlock-vector stripe.
+// kBlock * kU consecutive vectors and each wave owns a contiguous quarter of
+// them (slot u of lane l at u * 64 + l).
 __device__ inline int64_t slot_index(int64_t b, int tid, int u) {
-  if constexpr (ET_ELT_WAVE) {
-    return b * (kBlock * kU) + (tid / 64) * (64 * kU) + u * 64 + (tid % 64);
-  } else {
-    return b * (kBlock * kU) + u * kBlock + tid;
-  }
+  return b * (kBlock * kU) + (tid / 64) * (64 * kU) + u * 64 + (tid % 64);
 }
 
 enum Op { kAdd = 0, kSiluMul = 1, kGeluErfMul = 2, kGeluTanhMul = 3 };
@@ -269,7 +251,7 @@ et_status eltwise_entry(const S* a, const S* b, S* y, int64_t n, void* stream) {
     // a vector boundary, only the last one has a tail.
     const int64_t per_launch = kMaxGrid * kBlock * kU;  // vectors
     const int64_t nvec_all = n / V;
-    const int pol = store_policy(bytes, OP == kAdd ? ET_POL_ADD : ET_POL_ELT);
+    const int pol = store_policy(bytes);
     for (int64_t v0 = 0;; v0 += per_launch) {
       const int64_t nvec = nvec_all - v0 < per_launch ? nvec_all - v0 : per_launch;
       const bool last = v0 + nvec >= nvec_all;

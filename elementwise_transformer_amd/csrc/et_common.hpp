@@ -106,18 +106,13 @@ __device__ inline float f16_lo(uint32_t w) {
 __device__ inline float f16_hi(uint32_t w) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
 }
-#ifndef ET_F16_OPAQUE
-#define ET_F16_OPAQUE 1
-#endif
 __device__ inline uint32_t f16_bits(float v) {
   // The f32 value is formed first: left alone, the compiler may fold the last
   // multiply or multiply-add into a mixed-precision FMA that rounds straight
   // to f16 (v_fma_mixlo_f16) in one code path and not in another, so the
   // vector and scalar paths of a kernel could differ in the last bit.  The
   // empty asm makes v opaque; the conversion is then v_cvt_f16_f32 alone.
-#if ET_F16_OPAQUE
   __asm__("" : "+v"(v));
-#endif
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(v)));
 }
 __device__ inline uint32_t f16_pack2(float lo, float hi) { return f16_bits(lo) | (f16_bits(hi) << 16); }
@@ -290,9 +285,7 @@ constexpr int64_t kMaxGrid = int64_t{1} << 30;
 // Device-scope stores while a launch writes at most this much, else
 // non-temporal ones (see StorePolicy).
 constexpr int64_t kDeviceStoreMaxBytes = int64_t{128} << 20;
-inline int store_policy(int64_t out_bytes, int force = 0) {
-  if (force == 1) return kStoreStream;
-  if (force == 2) return kStoreDevice;
+inline int store_policy(int64_t out_bytes) {
   return out_bytes <= kDeviceStoreMaxBytes ? kStoreDevice : kStoreStream;
 }
 

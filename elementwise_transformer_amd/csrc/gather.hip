@@ -13,18 +13,8 @@
 namespace et {
 namespace {
 
-#ifndef ET_POL_GATHER
-#define ET_POL_GATHER 1  // 0: by size, 1: non-temporal, 2: device scope
-#endif
-
-#ifndef ET_GATHER_BLOCK
-#define ET_GATHER_BLOCK 64
-#endif
-constexpr int kBlock = ET_GATHER_BLOCK;
-#ifndef ET_GATHER_U
-#define ET_GATHER_U 8
-#endif
-constexpr int kU = ET_GATHER_U;
+constexpr int kBlock = 64;  // one wave per workgroup
+constexpr int kU = 8;       // vectors per lane
 
 template <typename S, bool VEC, int POL>
 __global__ __launch_bounds__(kBlock) void embedding_kernel(const S* __restrict__ table,
@@ -113,12 +103,9 @@ et_status embedding_entry(const S* table, int64_t vocab, const int32_t* ids, S* 
   for (int64_t t0 = 0; t0 < n; t0 += rows_per_launch) {
     const int64_t m = n - t0 < rows_per_launch ? n - t0 : rows_per_launch;
     const unsigned grid = static_cast<unsigned>(m * cpr);
-    // Non-temporal stores by default: device-scope ones (see StorePolicy)
-    // made the measured eight-op step slower here.
-    if (vec && store_policy(obytes, ET_POL_GATHER) == kStoreDevice)
-      embedding_kernel<S, true, kStoreDevice><<<grid, kBlock, 0, s>>>(
-          table, vocab, ids + t0, out + t0 * d, static_cast<int>(d), static_cast<int>(cpr));
-    else if (vec)
+    // Non-temporal stores at every size: device-scope ones (see
+    // StorePolicy) made the measured eight-op step slower here.
+    if (vec)
       embedding_kernel<S, true, kStoreStream><<<grid, kBlock, 0, s>>>(
           table, vocab, ids + t0, out + t0 * d, static_cast<int>(d), static_cast<int>(cpr));
     else

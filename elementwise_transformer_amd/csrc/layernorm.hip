@@ -50,7 +50,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void layernorm_rows(
       const int j = own<TPR, VPT>(k, t);
       xr[k] = ld16(x, base + static_cast<int64_t>(j < nvec ? j : nvec - 1) * V);
     }
-    if constexpr (TPR >= ET_NORM_W_EARLY_MIN_TPR) {
+    if constexpr (TPR >= kWEarlyMinTPR) {
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int j = own<TPR, VPT>(k, t);
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void layernorm_rows(
     constexpr int kGroupV = VPT < 4 ? VPT : 4;
 #pragma unroll
     for (int k0 = 0; k0 < VPT; k0 += kGroupV) {
-      if constexpr (TPR < ET_NORM_W_EARLY_MIN_TPR) {
+      if constexpr (TPR < kWEarlyMinTPR) {
 #pragma unroll
         for (int k = k0; k < k0 + kGroupV; ++k) {
           const int j = own<TPR, VPT>(k, t);

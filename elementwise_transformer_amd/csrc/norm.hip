@@ -27,10 +27,6 @@
 namespace et {
 namespace {
 
-#ifndef ET_POL_NORM
-#define ET_POL_NORM 1  // 0: by size, 1: non-temporal, 2: device scope
-#endif
-
 __device__ inline float inv_rms(float ss, int d, float eps) {
   return 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
 }
@@ -77,7 +73,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
       xr[k] = ld16(x, off);
       if constexpr (FUSED) rr[k] = ld16(res, off);
     }
-    if constexpr (TPR >= ET_NORM_W_EARLY_MIN_TPR) {
+    if constexpr (TPR >= kWEarlyMinTPR) {
       // The gain is cached (every row reads it); issuing its loads now hides
       // their latency behind the row loads and the reduction.
 #pragma unroll
@@ -138,7 +134,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
   if (!live) return;
 
   if constexpr (VEC) {
-    if constexpr (TPR < ET_NORM_W_EARLY_MIN_TPR) {
+    if constexpr (TPR < kWEarlyMinTPR) {
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int j = own<TPR, VPT>(k, t);
@@ -244,20 +240,14 @@ void launch_rows(const S* x, const S* res, const S* w, S* y, S* h, int64_t rows,
   // Non-temporal stores at every size: device-scope ones here (see
   // StorePolicy) made the measured eight-op step 10 % slower, the cache's
   // write-backs of the norm outputs competing with the next kernels' reads.
-  const int64_t out_bytes = rows * d * static_cast<int64_t>(sizeof(S)) * (FUSED ? 2 : 1);
-  const bool dev = store_policy(out_bytes, ET_POL_NORM) == kStoreDevice;
   using Sh = NormShape<TPR>;
   for (int64_t r0 = 0; r0 < rows; r0 += kMaxGrid * Sh::kRowsPerBlock) {
     const int64_t n = rows - r0 < kMaxGrid * Sh::kRowsPerBlock ? rows - r0
                                                                 : kMaxGrid * Sh::kRowsPerBlock;
     const int64_t off = r0 * d;
     const unsigned grid = static_cast<unsigned>((n + Sh::kRowsPerBlock - 1) / Sh::kRowsPerBlock);
-    if (dev)
-      rmsnorm_rows<S, TPR, VPT, FUSED, VEC, kStoreDevice><<<grid, Sh::kBlock, 0, s>>>(
-          x + off, FUSED ? res + off : nullptr, w, y + off, FUSED ? h + off : nullptr, n, d, eps);
-    else
-      rmsnorm_rows<S, TPR, VPT, FUSED, VEC, kStoreStream><<<grid, Sh::kBlock, 0, s>>>(
-          x + off, FUSED ? res + off : nullptr, w, y + off, FUSED ? h + off : nullptr, n, d, eps);
+    rmsnorm_rows<S, TPR, VPT, FUSED, VEC, kStoreStream><<<grid, Sh::kBlock, 0, s>>>(
+        x + off, FUSED ? res + off : nullptr, w, y + off, FUSED ? h + off : nullptr, n, d, eps);
   }
 }
 
@@ -273,10 +263,7 @@ void dispatch_tpr(int tpr, int vpt, const S* x, const S* res, const S* w, S* y, 
     case 32: launch_rows<S, 32, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
     case 64: launch_rows<S, 64, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s); break;
     case 128:
-#if ET_NORM_VPT4_MIN <= 512
-      if (vpt == 4) launch_rows<S, 128, 4, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s);
-      else
-#endif
+      // (4 vectors per thread start at 1024 vectors, 256 threads)
       launch_rows<S, 128, kVPTMax, FUSED, VEC>(x, res, w, y, h, rows, d, eps, s);
       break;
     case 256:

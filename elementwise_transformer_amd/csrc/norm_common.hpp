@@ -16,21 +16,15 @@ constexpr int kLargeTPR = 1024;  // threads per row in the two-pass path
 // Issue the gain loads right after the row loads when a row spans several
 // waves (its cross-wave reduction is long enough to hide them); for one-wave
 // rows the extra registers cost more occupancy than they save.
-#ifndef ET_NORM_W_EARLY_MIN_TPR
-#define ET_NORM_W_EARLY_MIN_TPR 128
-#endif
-
-#ifndef ET_NORM_VPT4_MIN
-#define ET_NORM_VPT4_MIN 1024
-#endif
-
-#ifndef ET_NORM_BLOCK
-#define ET_NORM_BLOCK 128
-#endif
+constexpr int kWEarlyMinTPR = 128;
+// Rows of at least this many vectors (up to 4096) take 4 vectors per thread.
+constexpr int kVPT4MinVec = 1024;
+// Threads per block when a row takes fewer (several rows per block).
+constexpr int kNormBlock = 128;
 
 template <int TPR>
 struct NormShape {
-  static constexpr int kBlock = TPR < ET_NORM_BLOCK ? ET_NORM_BLOCK : TPR;
+  static constexpr int kBlock = TPR < kNormBlock ? kNormBlock : TPR;
   static constexpr int kRowsPerBlock = kBlock / TPR;
   static constexpr int kGroup = TPR < 64 ? TPR : 64;  // lanes of one row inside a wave
   static constexpr int kWavesPerRow = TPR > 64 ? TPR / 64 : 1;
@@ -52,16 +46,12 @@ __device__ inline float row_sum(float part, float* lds, int row_in_block, int la
   return s;
 }
 
-#ifndef ET_NORM_WAVE
-#define ET_NORM_WAVE 1
-#endif
-
 // Vector slot k of thread t in its row.  Rows of one wave or less: slot k is
 // the k-th TPR-vector stripe.  Longer rows: each wave owns a contiguous run of
 // 64 * VPT vectors, slot k of lane l at k * 64 + l inside it.
 template <int TPR, int VPT>
 __device__ inline int own(int k, int t) {
-  if constexpr (TPR > 64 && ET_NORM_WAVE) {
+  if constexpr (TPR > 64) {
     return (t / 64) * (64 * VPT) + k * 64 + (t % 64);
   } else {
     return k * TPR + t;
@@ -72,7 +62,7 @@ __device__ inline int own(int k, int t) {
 // 1024..4096 vectors, else 8) and threads per row (the smallest power of two
 // with TPR * VPT >= number of vectors); TPR 0 selects the two-pass path.
 inline void pick_shape(int64_t nvec, int* tpr_out, int* vpt_out) {
-  const int vpt = (nvec >= ET_NORM_VPT4_MIN && nvec <= 4096) ? 4 : kVPTMax;
+  const int vpt = (nvec >= kVPT4MinVec && nvec <= 4096) ? 4 : kVPTMax;
   int tpr = 1;
   while (static_cast<int64_t>(tpr) * vpt < nvec) {
     tpr <<= 1;

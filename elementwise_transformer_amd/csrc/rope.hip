@@ -32,28 +32,16 @@
 namespace et {
 namespace {
 
-#ifndef ET_POL_ROPE
-#define ET_POL_ROPE 0  // 0: by size, 1: non-temporal, 2: device scope
-#endif
-
 constexpr int kBlock = 256;
 constexpr int kMaxTableBytes = 48 * 1024;
 // Slots per lane of the RoPE kernel (plain and cached angles): at most
-// ET_ROPE_UMAX with non-temporal stores, ET_ROPE_UMAX_DEV with device-scope
-// ones (one slot per lane was 6 % faster there inside a prefill layer, and
-// slower with non-temporal stores at 144 MiB).
-#ifndef ET_ROPE_UMAX
-#define ET_ROPE_UMAX 2
-#endif
-#ifndef ET_ROPE_UMAX_DEV
-#define ET_ROPE_UMAX_DEV 1
-#endif
-#ifndef ET_QK_UMAX
-#define ET_QK_UMAX 2
-#endif
-#ifndef ET_ROPE_SCHED_BARRIER
-#define ET_ROPE_SCHED_BARRIER 1
-#endif
+// kRopeUMax with non-temporal stores, kRopeUMaxDev with device-scope ones
+// (one slot per lane was 6 % faster there inside a prefill layer, and slower
+// with non-temporal stores at 144 MiB).  Head rows per lane group of the
+// fused RMSNorm + RoPE: at most kQkUMax.
+constexpr int kRopeUMax = 2;
+constexpr int kRopeUMaxDev = 1;
+constexpr int kQkUMax = 2;
 
 struct RopeArgs {
   int64_t T;
@@ -227,24 +215,11 @@ __device__ inline void rotate(float& x0, float& x1, float2 c) {
 
 // ------------------------------------------------------------------ RoPE
 
-#ifndef ET_ROPE_WAVE
-#define ET_ROPE_WAVE 1
-#endif
-#ifndef ET_QK_WAVE
-#define ET_QK_WAVE 1
-#endif
-
-// Slot u of thread tid in a block whose slots start at base.  With
-// ET_ROPE_WAVE each wave owns a contiguous run of 64 * U slots (slot u of
-// lane l at u * 64 + l in it); else slot u of the block is a contiguous
-// kBlock-slot stripe.
+// Slot u of thread tid in a block whose slots start at base: each wave owns
+// a contiguous run of 64 * U slots (slot u of lane l at u * 64 + l in it).
 template <int U>
 __device__ inline uint32_t rope_slot(uint32_t base, int tid, int u) {
-  if constexpr (ET_ROPE_WAVE) {
-    return base + static_cast<uint32_t>((tid / 64) * (64 * U) + u * 64 + (tid % 64));
-  } else {
-    return base + static_cast<uint32_t>(u * kBlock + tid);
-  }
+  return base + static_cast<uint32_t>((tid / 64) * (64 * U) + u * 64 + (tid % 64));
 }
 
 // Vector stores of one workgroup go through two buffer resources, one based
@@ -322,11 +297,9 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32
     }
   }
 
-#if ET_ROPE_SCHED_BARRIER
   // Nothing below may be scheduled above this point: the table inputs must
   // not be consumed before every row load has been issued.
   __builtin_amdgcn_sched_barrier(0);
-#endif
 
   // Phase 2: the angle table of this block's tokens.
   table_fill(cs, tin, t0, ntok, a, pos, inv_freq);
@@ -398,11 +371,10 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
   const int heads = ra.hq + ra.hk;
   const int kk = threadIdx.x % G;
   const uint32_t base = blockIdx.x * static_cast<uint32_t>(kRowsPerPass * U);
-  // Head row of slot u of this lane group: with ET_QK_WAVE each wave owns a
-  // contiguous run of (64 / G) * U head rows, else slot u of the block is a
-  // contiguous kRowsPerPass-row stripe.
+  // Head row of slot u of this lane group: each wave owns a contiguous run
+  // of (64 / G) * U head rows (one row per lane group for G == 64).
   auto head_row = [&](int u) -> uint32_t {
-    if constexpr (ET_QK_WAVE && G < 64) {
+    if constexpr (G < 64) {
       constexpr int kRowsPerWave = 64 / G;
       const int wave = threadIdx.x / 64;
       return base + static_cast<uint32_t>(wave * kRowsPerWave * U + u * kRowsPerWave +
@@ -437,6 +409,13 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
   }
 
   const QkOut<S, POL> out(q, k, t0, static_cast<int>(base - t0 * heads), ra);
+  // The two gains (2G vectors each) go through LDS: thread t < 4G fetches
+  // vector t % 2G of gq (t < 2G) or gk, before the row loads so that its
+  // LDS write waits for nothing else.  (gk is gq when there are no key
+  // heads: the host passes it so.)
+  __shared__ u32x4 gsh[4 * G];
+  const int gi = threadIdx.x < 4 * G ? static_cast<int>(threadIdx.x) : 4 * G - 1;
+  const u32x4 gv = ld16_keep(gi < 2 * G ? gq : gk, (gi % (2 * G)) * V);
   S* rowp[U];
   int tl[U], rel[U];
   bool isq[U];
@@ -455,16 +434,11 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
     va[u] = ld16(rowp[u], ea);
     vb[u] = ld16(rowp[u], eb);
   }
-  // gk is gq when there are no key heads (the host passes it so), so both
-  // gains load unconditionally.
-  const u32x4 gqa = ld16_keep(gq, ea), gqb = ld16_keep(gq, eb);
-  const u32x4 gka = ld16_keep(gk, ea), gkb = ld16_keep(gk, eb);
   __builtin_amdgcn_sched_barrier(0);  // table inputs are used only below
 
-  if constexpr (ROT) {
-    table_fill(cs, tin, t0, ntok, ra, pos, inv_freq);
-    __syncthreads();
-  }
+  if (threadIdx.x < 4 * G) gsh[threadIdx.x] = gv;
+  if constexpr (ROT) table_fill(cs, tin, t0, ntok, ra, pos, inv_freq);
+  __syncthreads();
 
   // Sums of squares of all U rows first, so their butterflies interleave.
   float inv[U];
@@ -491,8 +465,8 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     float xa[V], xb[V];
-    const u32x4& ga = isq[u] ? gqa : gka;
-    const u32x4& gb = isq[u] ? gqb : gkb;
+    const u32x4 ga = gsh[(isq[u] ? 0 : 2 * G) + ea / V];
+    const u32x4 gb = gsh[(isq[u] ? 0 : 2 * G) + eb / V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
       xa[e] = E::get(va[u], e) * inv[u] * E::get(ga, e);
@@ -677,8 +651,8 @@ et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int
   bool vec = (r % (2 * V)) == 0 && (D % V) == 0 && aligned16(q) && (hk == 0 || aligned16(k));
   RopeArgs a = make_args(T, hq, hk, D, r, mu, layout, vec ? V : 1);
   if (a.spt > (1u << 30)) return ET_ERR_BAD_SIZE;
-  const bool dev = store_policy(T * (hq + hk) * r * int64_t(sizeof(S)), ET_POL_ROPE) == kStoreDevice;
-  int u = pick_u(a.spt, a.half, kBlock, vec && dev ? ET_ROPE_UMAX_DEV : ET_ROPE_UMAX);
+  const bool dev = store_policy(T * (hq + hk) * r * int64_t(sizeof(S))) == kStoreDevice;
+  int u = pick_u(a.spt, a.half, kBlock, vec && dev ? kRopeUMaxDev : kRopeUMax);
   if (u == 0) return ET_ERR_BAD_SIZE;
   auto set_cache = [&](RopeArgs& ra) {
     if (!cache) return;
@@ -697,7 +671,7 @@ et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int
       a = make_args(T, hq, hk, D, r, mu, layout, 1);
       set_cache(a);
       if (a.spt > (1u << 30)) return ET_ERR_BAD_SIZE;
-      u = pick_u(a.spt, a.half, kBlock, ET_ROPE_UMAX);
+      u = pick_u(a.spt, a.half, kBlock, kRopeUMax);
       if (u == 0) return ET_ERR_BAD_SIZE;
     }
   }
@@ -742,7 +716,7 @@ template <typename S, int G>
 void launch_qknorm_vec_u(int u, S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
                          const float* inv_freq, QkNormArgs a, int64_t T, hipStream_t s) {
   const bool rot = a.rope.half > 0;
-  const bool dev = store_policy(T * (a.rope.hq + a.rope.hk) * a.rope.D * int64_t(sizeof(S)), ET_POL_ROPE) ==
+  const bool dev = store_policy(T * (a.rope.hq + a.rope.hk) * a.rope.D * int64_t(sizeof(S))) ==
                    kStoreDevice;
   if (dev) {
     if (u == 4) {
@@ -800,7 +774,7 @@ et_status qknorm_entry(S* q, const S* gq, int64_t hq, S* k, const S* gk, int64_t
   if (vec) {
     a.rope = make_args(T, hq, hk, D, r, mu, layout, V);
     a.rsl = static_cast<int>(r / (2 * V));
-    const int u = pick_u(heads, a.rope.half, kBlock / g, ET_QK_UMAX);
+    const int u = pick_u(heads, a.rope.half, kBlock / g, kQkUMax);
     if (u == 0) return ET_ERR_BAD_SIZE;
     const S* gkk = hk > 0 ? gk : gq;
     switch (g) {
@@ -892,10 +866,7 @@ et_status rope_cache_entry(const float* inv_freq, int64_t max_pos, int64_t r, fl
 // some vector would hold more than two runs (axes narrower than a vector).
 
 constexpr int kMaxAxes = 8;
-#ifndef ET_MULTI_U
-#define ET_MULTI_U 4
-#endif
-constexpr int kMultiU = ET_MULTI_U;
+constexpr int kMultiU = 4;
 constexpr int kMultiMaxSpan = 1024;
 
 struct MultiArgs {
@@ -983,10 +954,6 @@ __device__ inline float lds_elem(const S* xs, int i) {
     return xs[i];
   }
 }
-
-#ifndef ET_MULTI_WIDE
-#define ET_MULTI_WIDE 1
-#endif
 
 // W consecutive entries of a staged row from column p (p a multiple of W).
 template <typename S, int W>
@@ -1109,9 +1076,7 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
     if constexpr (PS == 1) sv[u] = E::ld(rowp[u], cv[u]);
     else v[u] = ld16(rowp[u], static_cast<int64_t>(cv[u]) * PS);
   }
-#if ET_ROPE_SCHED_BARRIER
   __builtin_amdgcn_sched_barrier(0);
-#endif
 
   // Phase 2: angle table, vector descriptors, rows to LDS.
 #pragma unroll
@@ -1179,9 +1144,9 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
       // columns and the split are multiples of W (the usual case: half
       // widths even), else one entry at a time.
       const int al = kr | d.x | d.y;
-      if (PS >= 4 && ET_MULTI_WIDE && (al & 3) == 0) {
+      if (PS >= 4 && (al & 3) == 0) {
         rotate_runs<S, PS, (PS >= 4 ? 4 : 1)>(xr, x, y, d, kr, ang);
-      } else if (PS >= 2 && ET_MULTI_WIDE && (al & 1) == 0) {
+      } else if (PS >= 2 && (al & 1) == 0) {
         rotate_runs<S, PS, (PS >= 2 ? 2 : 1)>(xr, x, y, d, kr, ang);
       } else {
         rotate_runs<S, PS, 1>(xr, x, y, d, kr, ang);
@@ -1300,7 +1265,7 @@ et_status rope_multi_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* po
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (vec && store_policy(T * (hq + hk) * span * int64_t(sizeof(S)), ET_POL_ROPE) == kStoreDevice)
+  if (vec && store_policy(T * (hq + hk) * span * int64_t(sizeof(S))) == kStoreDevice)
     launch_multi<S, V, kStoreDevice>(q, k, pos, inv_freq, a, T, shmem, s);
   else if (vec)
     launch_multi<S, V, kStoreStream>(q, k, pos, inv_freq, a, T, shmem, s);

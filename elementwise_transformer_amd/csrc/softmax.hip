@@ -29,20 +29,23 @@
 //   * z = x * (1/t); exp(d) = hardware exp2(d * log2 e) for d = z - m <= 0;
 //     the output is exp(z - m_c) * (exp(m_c - M) / S), one product per
 //     element (the exponentials stay in registers between the passes).
+//   * A chunk whose entries are all -inf (a masked stretch of logits) has
+//     m_c = -inf; its exponentials are taken against 0 instead, so they are
+//     exp(-inf) = 0 and s_c = +0, and the chunk adds nothing to the row (the
+//     formula's exp(-inf - M) = 0 for a finite row max M).  A row of -inf
+//     still gives M = -inf and a NaN row.
 //   * y may be x (in place): every element is read before the thread that
 //     owns it writes it, and a row's statistics are complete before any of
-//     its outputs is written.
-#include <stdlib.h>
-
+//     its outputs is written.  With a workspace, in-place calls take the
+//     two-launch path, where a workgroup reads only its own chunk after the
+//     statistics are complete: the one-launch exchange's fallback re-reads
+//     the whole row, which other workgroups may already be overwriting.
 #include "et_common.hpp"
 
 namespace et {
 namespace {
 
-#ifndef ET_SM_CHUNK
-#define ET_SM_CHUNK 8192
-#endif
-constexpr int kChunkElems = ET_SM_CHUNK;  // elements per chunk (256 threads x VPT vectors)
+constexpr int kChunkElems = 8192;  // elements per chunk (256 threads x VPT vectors)
 constexpr int kChunkThreads = 256;
 constexpr int kRegMaxElems = 32768;   // register path up to this row length
 constexpr int kRegBlock = 128;        // threads per block for short rows
@@ -137,7 +140,7 @@ __device__ inline float expo(float d) {
 // Load the VPT slots of thread t covering vectors [v0, v0 + span) of a row
 // whose first element is p and whose length is n; z values of slots past n
 // are -inf (they add exp(-inf) = 0).  Loads are clamped, never guarded.
-template <typename S, int TPR, int VPT, bool VEC, bool KEEP = false>
+template <typename S, int TPR, int VPT, bool VEC>
 __device__ inline void load_z(const S* p, int n, int v0, int t, float tt, float inv_t,
                               float (&z)[VPT][Elem<S>::V]) {
   using E = Elem<S>;
@@ -149,7 +152,7 @@ __device__ inline void load_z(const S* p, int n, int v0, int t, float tt, float 
     for (int k = 0; k < VPT; ++k) {
       const int j = v0 + slot<TPR, VPT>(k, t);
       const int64_t off = static_cast<int64_t>(j < nvec ? j : nvec - 1) * V;
-      r[k] = KEEP ? ld16_keep(p, off) : ld16(p, off);
+      r[k] = ld16(p, off);
     }
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
@@ -230,6 +233,10 @@ __device__ inline float local_max(const float (&z)[VPT][Elem<S>::V]) {
   return m;
 }
 
+// The value a chunk's exponentials are taken against: its max, or 0 when
+// every entry is -inf (then each is exp(-inf) = 0 rather than exp(NaN)).
+__device__ inline float exp_base(float m) { return m == -__builtin_inff() ? 0.0f : m; }
+
 // z <- exp(z - m) in place; returns their sum in slot order.
 template <typename S, int VPT>
 __device__ inline float exp_in_place(float (&z)[VPT][Elem<S>::V], float m) {
@@ -279,21 +286,16 @@ struct Chunk {
   static constexpr int kVPT = kVec / kChunkThreads;
 };
 
-// (m_c, s_c) of chunk c of the row at p; every thread gets the result.
-#ifndef ET_SM_STATS_KEEP
-#define ET_SM_STATS_KEEP 0
-#endif
-
 // Chunk c of the row at p: its exponentials exp(z - m_c) in ev and
 // (m_c, s_c) returned to every thread.
 template <typename S, bool VEC>
 __device__ inline float2 chunk_exp(const S* p, int n, int c, float tt, float inv_t, float* lds,
                                    float (&ev)[Chunk<S>::kVPT][Elem<S>::V]) {
   constexpr int VPT = Chunk<S>::kVPT;
-  load_z<S, kChunkThreads, VPT, VEC, ET_SM_STATS_KEEP>(p, n, c * Chunk<S>::kVec, threadIdx.x, tt,
-                                                       inv_t, ev);
+  load_z<S, kChunkThreads, VPT, VEC>(p, n, c * Chunk<S>::kVec, threadIdx.x, tt, inv_t, ev);
   const float m = row_max<kChunkThreads>(local_max<S, VPT>(ev), lds, 0, threadIdx.x);
-  const float s = row_sum<kChunkThreads>(exp_in_place<S, VPT>(ev, m), lds + kLdsSum, 0, threadIdx.x);
+  const float s =
+      row_sum<kChunkThreads>(exp_in_place<S, VPT>(ev, exp_base(m)), lds + kLdsSum, 0, threadIdx.x);
   return float2{m, s};
 }
 
@@ -316,13 +318,14 @@ __device__ inline float2 chunk_stats(const S* p, int n, int c, float tt, float i
     for (int e = 0; e < V; ++e) m = fmaxf(m, z[e]);
   }
   m = row_max<kChunkThreads>(m, lds, 0, t);
+  const float mb = exp_base(m);
   float s = 0.0f;
 #pragma unroll 1
   for (int k = 0; k < VPT; ++k) {
     float z[V];
     load_one<S, VEC>(p, n, v0 + slot<kChunkThreads, VPT>(k, t), tt, inv_t, z);
 #pragma unroll
-    for (int e = 0; e < V; ++e) s += expo<S>(z[e] - m);
+    for (int e = 0; e < V; ++e) s += expo<S>(z[e] - mb);
   }
   s = row_sum<kChunkThreads>(s, lds + kLdsSum, 0, t);
   return float2{m, s};
@@ -393,10 +396,11 @@ __device__ inline float2 row_stats_self(const S* p, int n, int chunks, float tt,
   return float2{m, s};
 }
 
-// A published partial is one 64-bit word (m_c, s_c).  s_c >= 1 or NaN, so
-// its bits are never 0 (a NaN is stored as the canonical quiet NaN): a
-// zero-filled word means "not published yet", and the word itself is the
-// flag -- no fence is needed between data and flag.
+// A published partial is one 64-bit word (m_c, s_c).  s_c >= 1 or NaN, or
+// s_c = +0 with m_c = -inf (a chunk of -inf), so its bits are never 0 (a NaN
+// is stored as the canonical quiet NaN): a zero-filled word means "not
+// published yet", and the word itself is the flag -- no fence is needed
+// between data and flag.
 __device__ inline uint64_t partial_bits(float m, float s) {
   const float sc = s != s ? __uint_as_float(0x7FC00000u) : s;
   return __builtin_bit_cast(uint64_t, float2{m, sc});
@@ -599,26 +603,19 @@ inline int64_t counter_bytes(int64_t rows) { return ((rows * 8 + 15) / 16) * 16;
 // Polls of a row's partials (per thread) before a workgroup computes the
 // row's statistics itself.  Each poll is a device-coherent load plus a short
 // sleep (well under a microsecond), so the bound is a few milliseconds; in
-// a normal run every partial arrives within microseconds.  ET_SOFTMAX_SPIN_LIMIT overrides it,
-// up to 65536 (0 makes every workgroup take the self-computed path; used by
-// the tests).
-inline int spin_limit() {
-  const char* e = getenv("ET_SOFTMAX_SPIN_LIMIT");
-  if (e && *e) {
-    const long l = strtol(e, nullptr, 10);
-    return l < 0 ? 0 : (l > (1 << 16) ? (1 << 16) : static_cast<int>(l));
-  }
-  return 8192;
-}
+// a normal run every partial arrives within microseconds.  The entry points
+// use kSpinLimit; et_softmax_wait_limit takes the bound as an argument, up
+// to kSpinLimitMax (0 makes every workgroup take the self-computed path).
+constexpr int kSpinLimit = 8192;
+constexpr int kSpinLimitMax = 1 << 16;
 
 template <typename S, bool VEC>
 void launch_chunks(const S* x, S* y, int64_t rows, int n, float tt, float inv_t, void* ws,
-                   hipStream_t s) {
+                   int lim, hipStream_t s) {
   const int64_t chunks = chunks_of(n);
   const int64_t rows_per_launch = kMaxGrid / chunks;
   uint32_t* cnt = static_cast<uint32_t*>(ws);
   uint64_t* part = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + counter_bytes(rows));
-  const int lim = spin_limit();
   for (int64_t r0 = 0; r0 < rows; r0 += rows_per_launch) {
     const int64_t m = rows - r0 < rows_per_launch ? rows - r0 : rows_per_launch;
     const unsigned grid = static_cast<unsigned>(m * chunks);
@@ -660,7 +657,7 @@ void launch_row_blocks(const S* x, S* y, int64_t rows, int n, float tt, float in
 
 template <typename S>
 et_status softmax_entry(const S* x, S* y, int64_t rows, int64_t n, float temperature, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        size_t ws_bytes, void* stream, int spin = kSpinLimit) {
   if (rows < 0 || n < 0) return ET_ERR_BAD_SIZE;
   if (!(temperature > 0.0f) || !__builtin_isfinite(temperature)) return ET_ERR_BAD_ARG;
   if (rows == 0 || n == 0) return ET_OK;
@@ -689,13 +686,15 @@ et_status softmax_entry(const S* x, S* y, int64_t rows, int64_t n, float tempera
     if (!ranges_ok(ws, static_cast<int64_t>(ws_bytes), x, bytes, false) ||
         !ranges_ok(ws, static_cast<int64_t>(ws_bytes), y, bytes, false))
       return ET_ERR_OVERLAP;
-    if (chunks_of(n) > kMaxExchangeChunks) {
+    // In place, a workgroup must not read chunks other workgroups may
+    // already be writing, which the one-launch fallback would: two launches.
+    if (chunks_of(n) > kMaxExchangeChunks || static_cast<const void*>(x) == y) {
       if (vec) launch_two_pass<S, true>(x, y, rows, static_cast<int>(n), temperature, inv_t, ws, s);
       else launch_two_pass<S, false>(x, y, rows, static_cast<int>(n), temperature, inv_t, ws, s);
     } else if (vec) {
-      launch_chunks<S, true>(x, y, rows, static_cast<int>(n), temperature, inv_t, ws, s);
+      launch_chunks<S, true>(x, y, rows, static_cast<int>(n), temperature, inv_t, ws, spin, s);
     } else {
-      launch_chunks<S, false>(x, y, rows, static_cast<int>(n), temperature, inv_t, ws, s);
+      launch_chunks<S, false>(x, y, rows, static_cast<int>(n), temperature, inv_t, ws, spin, s);
     }
     return launch_status();
   }
@@ -736,6 +735,25 @@ et_status et_softmax_f16(const et_f16* x, et_f16* y, int64_t rows, int64_t n,
                           void* stream) {
   return et::softmax_entry<F16>(reinterpret_cast<const F16*>(x), reinterpret_cast<F16*>(y), rows,
                                  n, temperature, workspace, workspace_bytes, stream);
+}
+
+et_status et_softmax_wait_limit(int storage, const void* x, void* y, int64_t rows, int64_t n,
+                                float temperature, void* workspace, size_t workspace_bytes,
+                                int spin_limit, void* stream) {
+  if (spin_limit < 0 || spin_limit > et::kSpinLimitMax) return ET_ERR_BAD_ARG;
+  switch (storage) {
+    case ET_STORAGE_F32:
+      return et::softmax_entry<float>(static_cast<const float*>(x), static_cast<float*>(y), rows, n,
+                                      temperature, workspace, workspace_bytes, stream, spin_limit);
+    case ET_STORAGE_BF16:
+      return et::softmax_entry<Bf16>(static_cast<const Bf16*>(x), static_cast<Bf16*>(y), rows, n,
+                                     temperature, workspace, workspace_bytes, stream, spin_limit);
+    case ET_STORAGE_F16:
+      return et::softmax_entry<F16>(static_cast<const F16*>(x), static_cast<F16*>(y), rows, n,
+                                    temperature, workspace, workspace_bytes, stream, spin_limit);
+    default:
+      return ET_ERR_BAD_ARG;
+  }
 }
 
 }  // extern "C"

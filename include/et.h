@@ -70,6 +70,9 @@ typedef enum {
 
 enum { ET_ROPE_HALF = 0, ET_ROPE_INTERLEAVED = 1 };
 
+/* Storage type codes, for the entry points that take the type as an argument. */
+enum { ET_STORAGE_F32 = 0, ET_STORAGE_BF16 = 1, ET_STORAGE_F16 = 2 };
+
 /* ------------------------------------------------------------------------
  * RMSNorm  ([OPS] RmsNorm; [ELT] 2.1)
  *   y[r, i] = x[r, i] / sqrt(mean_i(x[r, :]^2) + eps) * w[i]
@@ -288,8 +291,10 @@ et_status et_embedding_f16(const et_f16* table, int64_t V,
  *   (-0 and +0 are equal; +inf is a number), or -1 when the row holds no
  *   number (all NaN, or n == 0).  x: [rows, n]; out: int32 [rows].
  *   n <= INT32_MAX.
- *   workspace: device scratch that lets long rows be split over several
- *   workgroups (still one launch).  Either workspace == NULL with
+ *   workspace: device scratch that lets the rows of a call of fewer than
+ *   1024 rows be split over several workgroups (still one launch);
+ *   et_argmax_workspace_bytes is 0 (none needed) for calls of 1024 rows or
+ *   more, which get one workgroup per row.  Either workspace == NULL with
  *   workspace_bytes == 0 (one workgroup per row, no scratch), or
  *   workspace != NULL with workspace_bytes >= et_argmax_workspace_bytes(rows,
  *   n) and 16-byte aligned, else ET_ERR_WORKSPACE (ET_ERR_NULL_POINTER for
@@ -363,6 +368,15 @@ et_status et_geglu_f16(const et_f16* gate, const et_f16* up, et_f16* y,
  *   the same with or without a workspace.
  */
 size_t et_softmax_workspace_bytes(int64_t rows, int64_t n);
+/*   Precision: statistics in f32 (z = x * (1/t), the exponentials by the
+ *   hardware exp2 of (z - m) log2 e).  That exp2 returns no subnormals, so a
+ *   probability below 2^-126 (about 1.2e-38) may be returned as 0 where the
+ *   exact value is a subnormal f32; no other result is affected.  Entries
+ *   of -inf get exactly 0 whenever the row max is finite, however many of
+ *   them there are and wherever they lie.
+ *   In place (y == x) with a workspace, rows longer than 32768 elements take
+ *   two launches (each element read twice), so that no workgroup reads a
+ *   part of the row another one is already writing. */
 et_status et_softmax_f32(const float* x, float* y, int64_t rows, int64_t n,
                          float temperature, void* workspace,
                          size_t workspace_bytes, void* stream);
@@ -372,6 +386,19 @@ et_status et_softmax_bf16(const et_bf16* x, et_bf16* y, int64_t rows,
 et_status et_softmax_f16(const et_f16* x, et_f16* y, int64_t rows,
                          int64_t n, float temperature, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* The softmax entry points with the chunk exchange's bounded wait given
+ * explicitly: storage is ET_STORAGE_F32, _BF16 or _F16 (x and y of that
+ * type), spin_limit the polls per thread, 0..65536 (the entry points above
+ * use 8192), else ET_ERR_BAD_ARG; every other argument as above.  A
+ * workgroup that runs out of polls computes its row's statistics itself,
+ * with the same bits, so any limit gives the same result; 0 forces that
+ * path in every workgroup.  For tests of the fallback, driven from the
+ * host: no kernel waits without bound either way. */
+et_status et_softmax_wait_limit(int storage, const void* x, void* y,
+                                int64_t rows, int64_t n, float temperature,
+                                void* workspace, size_t workspace_bytes,
+                                int spin_limit, void* stream);
 
 /* ------------------------------------------------------------------------
  * Library information. */

@@ -226,10 +226,10 @@ def test_embedding_and_argmax_validation(sfx):
     assert a(A, 4, 1 << 31, B, NULL, 0, S) == 2               # n > INT32_MAX
     assert a(A, 4, 8, NULL, NULL, 0, S) == 1
     assert a(A, 4, 8, B, NULL, 64, S) == 1                    # NULL workspace, nonzero size
-    need = et.argmax_workspace_bytes(256, 128256)
+    need = et.argmax_workspace_bytes(4, 128256)
     assert need > 0
-    assert a(A, 256, 128256, B, C, need - 1, S) == 5          # workspace too small
-    assert a(A, 256, 128256, B, P(3 * G + 8), need, S) == 5   # workspace not 16-byte aligned
+    assert a(A, 4, 128256, B, C, need - 1, S) == 5            # workspace too small
+    assert a(A, 4, 128256, B, P(3 * G + 8), need, S) == 5     # workspace not 16-byte aligned
     assert a(A, 4, 8, A, NULL, 0, S) == 4                     # out inside x
     assert a(NULL, 0, 8, NULL, NULL, 0, S) == 0
 
@@ -255,6 +255,24 @@ def test_softmax_validation(sfx):
     assert f(A, B, 256, 128256, 1.0, P(G + 64), need, S) == 4   # workspace inside x
     assert f(NULL, NULL, 0, 8, 1.0, NULL, 0, S) == 0
     assert f(A, B, 4, 0, 1.0, NULL, 0, S) == 0
+
+
+@gpu_visible
+def test_softmax_wait_limit_validation():
+    """The explicit-wait entry point: the storage code and the limit are
+    checked first, then every check of the typed entry points."""
+    import elementwise_transformer_amd as et
+    f = et.lib.et_softmax_wait_limit
+    for code in (0, 1, 2):
+        assert f(code, A, B, 4, 8, 1.0, NULL, 0, -1, S) == 3        # limit below 0
+        assert f(code, A, B, 4, 8, 1.0, NULL, 0, 65537, S) == 3     # limit above 65536
+        assert f(code, A, B, 4, 8, 0.0, NULL, 0, 0, S) == 3         # temperature
+        assert f(code, A, B, -1, 8, 1.0, NULL, 0, 0, S) == 2
+        assert f(code, NULL, B, 4, 8, 1.0, NULL, 0, 0, S) == 1
+        assert f(code, A, P(G + 4), 4, 8, 1.0, NULL, 0, 0, S) == 4
+        assert f(code, A, B, 4, 0, 1.0, NULL, 0, 65536, S) == 0
+    for code in (-1, 3, 7):
+        assert f(code, A, B, 4, 8, 1.0, NULL, 0, 0, S) == 3         # unknown storage
 
 
 @gpu_visible
@@ -296,9 +314,11 @@ def test_argmax_workspace_sizes():
     assert et.argmax_workspace_bytes(0, 100) == 0
     assert et.argmax_workspace_bytes(4, 0) == 0
     assert et.argmax_workspace_bytes(100000, 1000) == 0       # one chunk per row: none needed
-    n256 = et.argmax_workspace_bytes(256, 128256)
-    assert n256 == 256 * 16                     # per row: a 64-bit key and a counter
-    assert et.argmax_workspace_bytes(1, 128256) >= 8 * 2
+    assert et.argmax_workspace_bytes(1024, 128256) == 0       # 1024 rows: one workgroup each
+    assert et.argmax_workspace_bytes(1023, 128256) == 1023 * 16  # per row: a 64-bit key and a counter
+    assert et.argmax_workspace_bytes(256, 128256) == 256 * 16
+    assert et.argmax_workspace_bytes(1, 128256) == 16
+    assert et.argmax_workspace_bytes(6, 4096) == 0            # one granule per row: no split
 
 
 def test_fastdiv_host_logic():
@@ -342,31 +362,33 @@ int main() {
 
 @gpu_visible
 def test_stream_probe_validation():
-    """The plain-stream probe the benchmark measures against (libet_probe.so)
-    rejects bad sizes, stream shapes, vector counts, NULL and misaligned
-    buffers before any HIP call."""
-    lib = ctypes.CDLL(os.path.join(ROOT, "elementwise_transformer_amd", "libet_probe.so"))
+    """The plain-stream probe the benchmark measures against
+    (probe/libet_probe.so) rejects bad sizes, stream shapes, vector counts,
+    grid sizes, NULL and misaligned buffers before any HIP call."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "probe", "libet_probe.so"))
     f = lib.et_probe_stream
     vp = ctypes.c_void_p
     f.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                  ctypes.c_int, vp]
+                  ctypes.c_int, ctypes.c_int, vp]
     f.restype = ctypes.c_int
     A, B, Y, H = 0x100000, 0x200000, 0x300000, 0x400000   # fake, never dereferenced
     bad = [
-        (A, B, Y, H, 0, 1, 1, 4, 0),          # empty
-        (A, B, Y, H, 24, 1, 1, 4, 0),         # not whole 16-byte words
-        (A, B, Y, H, 1 << 31, 1, 1, 4, 0),    # past 32-bit buffer offsets
-        (A, B, Y, H, 64, 0, 0, 4, 0),         # nothing streamed
-        (A, B, Y, H, 64, 3, 1, 4, 0),         # three reads
-        (A, B, Y, H, 64, 0, 2, 4, 0),         # a shape not offered
-        (A, B, Y, H, 64, 2, 0, 4, 0),
-        (A, B, Y, H, 64, 1, 1, 5, 0),         # vectors per lane
-        (None, B, Y, H, 64, 1, 1, 4, 0),      # missing read buffer
-        (A, None, Y, H, 64, 2, 1, 4, 0),
-        (A, B, None, H, 64, 1, 0, 4, 0),      # y is needed even for a pure read
-        (A, B, Y, None, 64, 2, 2, 4, 1),
-        (A + 4, B, Y, H, 64, 1, 1, 4, 0),     # misaligned
-        (A, B, Y + 8, H, 64, 1, 1, 8, 1),
+        (A, B, Y, H, 0, 1, 1, 4, 0, 0),          # empty
+        (A, B, Y, H, 24, 1, 1, 4, 0, 0),         # not whole 16-byte words
+        (A, B, Y, H, 1 << 31, 1, 1, 4, 0, 0),    # past 32-bit buffer offsets
+        (A, B, Y, H, 64, 0, 0, 4, 0, 0),         # nothing streamed
+        (A, B, Y, H, 64, 3, 1, 4, 0, 0),         # three reads
+        (A, B, Y, H, 64, 0, 2, 4, 0, 0),         # a shape not offered
+        (A, B, Y, H, 64, 2, 0, 4, 0, 0),
+        (A, B, Y, H, 64, 1, 1, 5, 0, 0),         # vectors per lane
+        (A, B, Y, H, 64, 1, 1, 4, 0, -1),        # persistent grid size
+        (A, B, Y, H, 64, 1, 1, 4, 0, 65537),
+        (None, B, Y, H, 64, 1, 1, 4, 0, 0),      # missing read buffer
+        (A, None, Y, H, 64, 2, 1, 4, 0, 0),
+        (A, B, None, H, 64, 1, 0, 4, 0, 0),      # y is needed even for a pure read
+        (A, B, Y, None, 64, 2, 2, 4, 1, 0),
+        (A + 4, B, Y, H, 64, 1, 1, 4, 0, 0),     # misaligned
+        (A, B, Y + 8, H, 64, 1, 1, 8, 1, 2048),
     ]
     for args in bad:
         assert f(*args, None) == 1, args

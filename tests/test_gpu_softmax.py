@@ -71,8 +71,8 @@ def test_softmax_workspace_and_single_block_agree(et, dt, n):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("n", [40000, 128256])
-def test_softmax_bounded_wait_fallback_same_bits(et, dt, n, monkeypatch):
-    """Forced from the host: with a spin limit of 0 no workgroup waits for the
+def test_softmax_bounded_wait_fallback_same_bits(et, dt, n):
+    """Forced from the host: with a wait limit of 0 no workgroup waits for the
     row's other partials, every one computes the row statistics itself --
     same bits; the workspace is left zero-filled after each call."""
     xs = dev(_logits((7, n), dt, (n, 7)))
@@ -80,17 +80,103 @@ def test_softmax_bounded_wait_fallback_same_bits(et, dt, n, monkeypatch):
     a = host(et.softmax(xs, 1.1, workspace=ws))
     cnt = ws[:7 * 8].cpu().numpy()
     assert not cnt.any()
-    monkeypatch.setenv("ET_SOFTMAX_SPIN_LIMIT", "0")
-    b = host(et.softmax(xs, 1.1, workspace=ws))
+    b = host(et.softmax(xs, 1.1, workspace=ws, wait_limit=0))
     assert not ws[:7 * 8].cpu().numpy().any()
-    monkeypatch.setenv("ET_SOFTMAX_SPIN_LIMIT", "1")
-    c = host(et.softmax(xs, 1.1, workspace=ws))
-    monkeypatch.delenv("ET_SOFTMAX_SPIN_LIMIT")
+    c = host(et.softmax(xs, 1.1, workspace=ws, wait_limit=1))
     d = host(et.softmax(xs, 1.1, workspace=ws))
-    assert not ws[:7 * 8].cpu().numpy().any()
+    assert int(torch.count_nonzero(ws)) == 0
     assert_bits(b, a, f"{dt} n={n} fallback")
-    assert_bits(c, a, f"{dt} n={n} spin 1")
+    assert_bits(c, a, f"{dt} n={n} wait 1")
     assert_bits(d, a, f"{dt} n={n} reuse")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("n", [40000, 128256])
+@pytest.mark.parametrize("limit", [0, 1, None])
+def test_softmax_in_place_with_workspace(et, orc, dt, n, limit):
+    """y == x with a workspace, with the bounded wait forced to give up (0),
+    nearly so (1) or not at all: the same bits as out of place, against the
+    oracle, and the workspace left zero-filled.  (In place, no workgroup may
+    read a chunk another one is already writing.)"""
+    x = _logits((6, n), dt, (n, 17))
+    xs = dev(x)
+    ref = host(et.softmax(xs, 0.9))
+    ws = torch.zeros(et.softmax_workspace_bytes(6, n), dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        xi = xs.clone()
+        et.softmax(xi, 0.9, out=xi, workspace=ws, wait_limit=limit)
+        assert_bits(host(xi), ref, f"{dt} n={n} in place limit {limit} call {rep}")
+        assert int(torch.count_nonzero(ws)) == 0, "workspace not left zero-filled"
+    y, y64 = orc.softmax(x, 0.9)
+    check_softmax(ref, x, 0.9, y, y64, f"{dt} n={n}")
+
+
+def test_softmax_wait_limit_rejects_bad_values(et):
+    x = torch.zeros((1, 40000), device="cuda")
+    for bad in (-1, 65537):
+        with pytest.raises(et.ETError):
+            et.softmax(x, 1.0, wait_limit=bad)
+
+
+def _masked(n, dt, key, spans):
+    """N(0, 3) logits with the given [a, b) spans set to -inf."""
+    x = (_rng(*key).standard_normal((len(spans), n)) * 3).astype(np.float32)
+    for r, sp in enumerate(spans):
+        for a, b in sp:
+            x[r, a:b] = -np.inf
+    return wl.store(x, dt)
+
+
+def _mask_spans(n, rng):
+    """Rows of masked logits: a whole first chunk, the last chunk (partial
+    when n is not a multiple of 8192), every chunk but one, a top-k style
+    mask keeping 50 random entries, two whole chunks in the middle, and
+    masks that start and end inside chunks."""
+    C = 8192
+    chunks = -(-n // C)
+    keep = np.sort(rng.choice(n, 50, replace=False))
+    topk = []
+    prev = 0
+    for k in keep:
+        if k > prev:
+            topk.append((prev, int(k)))
+        prev = int(k) + 1
+    topk.append((prev, n))
+    mid = chunks // 2
+    return [
+        [(0, C)],
+        [((chunks - 1) * C, n)],
+        [(0, mid * C), ((mid + 1) * C, n)],
+        topk,
+        [(C, 3 * C)],
+        [(C // 2, C + C // 2), (n - C - 100, n - 7)],
+    ]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("n", [40000, 128256])
+def test_softmax_masked_chunks(et, orc, dt, n):
+    """Whole chunks of -inf (masked logits, a top-k mask, a short last
+    chunk): finite probabilities, 0 on the masked entries, against the
+    oracle; the one-launch exchange, the forced fallback, the two-launch
+    in-place path and one workgroup per row all give the same bits."""
+    spans = _mask_spans(n, _rng(n, 23))
+    xs = _masked(n, dt, (n, 24), spans)
+    y, y64 = orc.softmax(xs, 0.8)
+    assert np.all(np.isfinite(y64))
+    xd = dev(xs)
+    ws = torch.zeros(et.softmax_workspace_bytes(len(spans), n), dtype=torch.uint8, device="cuda")
+    a = host(et.softmax(xd, 0.8, workspace=ws))
+    check_softmax(a, xs, 0.8, y, y64, f"{dt} n={n} masked")
+    wa = widen(a)
+    assert np.all(np.isfinite(wa))
+    assert np.all(wa[np.isneginf(widen(xs))] == 0.0)
+    assert_bits(host(et.softmax(xd, 0.8, workspace=ws, wait_limit=0)), a, f"{dt} n={n} fallback")
+    assert_bits(host(et.softmax(xd, 0.8, split=False)), a, f"{dt} n={n} one workgroup per row")
+    xi = xd.clone()
+    et.softmax(xi, 0.8, out=xi, workspace=ws)
+    assert_bits(host(xi), a, f"{dt} n={n} in place")
+    assert int(torch.count_nonzero(ws)) == 0
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])

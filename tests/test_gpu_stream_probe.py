@@ -1,7 +1,8 @@
 """The plain-stream probe the benchmark measures the kernels against
-(libet_probe.so): each stream shape reads and writes what it says, in both
-store policies, so the ceiling it reports is the rate of real loads and
-stores of data.  Expected values are written out here from the probe's
+(probe/libet_probe.so, built apart from the library): each stream shape reads
+and writes what it says, in both store policies and both grid shapes (one
+workgroup per tile, or a persistent grid stepping through the buffer), so
+the ceiling it reports is the rate of real loads and stores of data.  Expected values are written out here from the probe's
 stated outputs (XOR and sum of the 16-byte words read, per 32-bit lane)."""
 import ctypes
 import os
@@ -19,11 +20,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def probe():
     assert torch.cuda.is_available(), "GPU tests need a ROCm device"
     import elementwise_transformer_amd  # noqa: F401  (same runtime as the library)
-    lib = ctypes.CDLL(os.path.join(ROOT, "elementwise_transformer_amd", "libet_probe.so"))
+    lib = ctypes.CDLL(os.path.join(ROOT, "probe", "libet_probe.so"))
     f = lib.et_probe_stream
     vp = ctypes.c_void_p
     f.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                  ctypes.c_int, vp]
+                  ctypes.c_int, ctypes.c_int, vp]
     f.restype = ctypes.c_int
     return f
 
@@ -31,7 +32,8 @@ def probe():
 @pytest.mark.parametrize("nbytes", [16, 16 * 1000 + 16 * 37, 32 << 20])
 @pytest.mark.parametrize("u", [4, 8])
 @pytest.mark.parametrize("dev_scope", [0, 1])
-def test_stream_probe_outputs(probe, nbytes, u, dev_scope):
+@pytest.mark.parametrize("persist", [0, 3, 512])
+def test_stream_probe_outputs(probe, nbytes, u, dev_scope, persist):
     g = np.random.default_rng([7070, nbytes, u])
     words = nbytes // 4
     a = g.integers(0, 2 ** 32, words, dtype=np.uint64).astype(np.uint32)
@@ -44,7 +46,7 @@ def test_stream_probe_outputs(probe, nbytes, u, dev_scope):
         y = torch.full((words,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
         h = torch.full((words,), 0x3C3C3C3C, dtype=torch.int32, device="cuda")
         assert probe(at.data_ptr(), bt.data_ptr(), y.data_ptr(), h.data_ptr(), nbytes, nr, nw, u,
-                     dev_scope, s) == 0
+                     dev_scope, persist, s) == 0
         torch.cuda.synchronize()
         return y.cpu().numpy().view(np.uint32), h.cpu().numpy().view(np.uint32)
 

@@ -173,6 +173,17 @@ def gen_embedding(w: Workload, n: Optional[int] = None):
     return store(table, w.dtype), ids
 
 
+def gen_embedding_ids(w: Workload, j: int) -> np.ndarray:
+    """Set j >= 1 of extra token ids for the embedding gather (same
+    distribution as gen_embedding's, U[0, V), its own stream
+    default_rng([1000 + workload, G_EMBED, j])): a benchmark that repeats
+    the gather rotates through such sets so it never re-reads rows the
+    previous call left in the caches."""
+    V, _, n, _ = w.embed
+    g = np.random.default_rng([1000 + w.number, G_EMBED, j])
+    return g.integers(0, V, size=n, dtype=np.int64).astype(np.int32)
+
+
 def gen_add(w: Workload):
     rows, d = w.add
     g = rng(w.number, G_ADD)
