@@ -74,6 +74,8 @@ lib.et_argmax_workspace_bytes.argtypes = [_i64, _i64]
 lib.et_argmax_workspace_bytes.restype = _sz
 lib.et_softmax_workspace_bytes.argtypes = [_i64, _i64]
 lib.et_softmax_workspace_bytes.restype = _sz
+lib.et_argmax_noalloc.argtypes = [_int, _vp, _i64, _i64, _vp, _vp]
+lib.et_argmax_noalloc.restype = ctypes.c_int
 lib.et_softmax_wait_limit.argtypes = [_int, _vp, _vp, _i64, _i64, _f32, _vp, _sz, _int, _vp]
 lib.et_softmax_wait_limit.restype = ctypes.c_int
 lib.et_rope_cache_f32.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp]

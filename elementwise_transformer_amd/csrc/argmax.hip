@@ -26,7 +26,19 @@
 //     one 1024-thread workgroup per row, 512-thread workgroups, 8 or 16
 //     vectors per lane, 2048 or 4096 workgroups, or a software-pipelined
 //     scan, and 22.2 us for a plain read of the same bytes on the same GPU.
+#include <mutex>
+
 #include "et_common.hpp"
+
+// Scratch of the entry point that allocates nothing (et_argmax_noalloc):
+// the split path's per-row 64-bit key and counter (16 bytes per row) for up
+// to kScratchRows rows.  The split path only runs for calls of fewer than
+// kFillBlocks (1024) rows, so 1024 rows (16 KiB) cover every call.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code
+// the name is only a stand-in: the device address comes from
+// hipGetSymbolAddress, once per device.
+constexpr int64_t kScratchRows = 1024;
+static __device__ __align__(256) unsigned long long scratch[2 * kScratchRows];
 
 namespace et {
 namespace {
@@ -263,9 +275,10 @@ void launch(const S* x, int64_t rows, int64_t n, int64_t chunk, int64_t chunks,
   }
 }
 
+// check_only: validate the arguments and return, enqueueing nothing.
 template <typename S>
 et_status argmax_entry(const S* x, int64_t rows, int64_t n, int32_t* out, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       size_t ws_bytes, void* stream, bool check_only = false) {
   if (rows < 0 || n < 0) return ET_ERR_BAD_SIZE;
   if (rows == 0) return ET_OK;
   if (n > INT32_MAX) return ET_ERR_BAD_SIZE;
@@ -275,6 +288,7 @@ et_status argmax_entry(const S* x, int64_t rows, int64_t n, int32_t* out, void* 
   if (!ws && ws_bytes != 0) return ET_ERR_NULL_POINTER;
   const int64_t obytes = rows * int64_t(sizeof(int32_t));
   if (!ranges_ok(out, obytes, x, xbytes, false)) return ET_ERR_OVERLAP;
+  if (check_only) return ET_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (n == 0) {
@@ -301,6 +315,51 @@ et_status argmax_entry(const S* x, int64_t rows, int64_t n, int32_t* out, void* 
   if (vec) launch<S, kThreads, true>(x, rows, n, chunk, chunks, slot, cnt, out, s);
   else launch<S, kThreads, false>(x, rows, n, chunk, chunks, slot, cnt, out, s);
   return launch_status();
+}
+
+// Zero n 64-bit words: the scratch's keys and counters before a split call
+// (a kernel on the caller's stream, so it is ordered before the call's own
+// kernel and may be captured into a graph).
+__global__ void zero_words(unsigned long long* p, int64_t n) {
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0ull;
+}
+
+// The device address of `scratch` on the current device, looked up once per
+// device with that device current (hipGetSymbolAddress), then kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+et_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ET_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ET_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ET_OK;
+}
+
+template <typename S>
+et_status argmax_noalloc(const S* x, int64_t rows, int64_t n, int32_t* out, void* stream) {
+  // The arguments are checked exactly as et_argmax_* checks them, before the
+  // scratch is touched; a call that needs no split passes no workspace.
+  const size_t need = (rows > 0 && n > 0 && n <= INT32_MAX) ? et_argmax_workspace_bytes(rows, n) : 0;
+  if (need == 0) return argmax_entry<S>(x, rows, n, out, nullptr, 0, stream);
+  if (need > sizeof(scratch)) return ET_ERR_WORKSPACE;  // (the split path needs rows < 1024)
+  if (const et_status st = argmax_entry<S>(x, rows, n, out, nullptr, 0, nullptr, true); st != ET_OK)
+    return st;
+  void* ws = nullptr;
+  if (const et_status st = scratch_ptr(&ws); st != ET_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  zero_words<<<1, 256, 0, s>>>(static_cast<unsigned long long*>(ws),
+                                static_cast<int64_t>(need / sizeof(unsigned long long)));
+  if (hipGetLastError() != hipSuccess) return ET_ERR_HIP;
+  return argmax_entry<S>(x, rows, n, out, ws, need, stream);
 }
 
 }  // namespace
@@ -334,6 +393,20 @@ et_status et_argmax_f16(const et_f16* x, int64_t rows, int64_t n, int32_t* out, 
                          size_t workspace_bytes, void* stream) {
   return et::argmax_entry<F16>(reinterpret_cast<const F16*>(x), rows, n, out, workspace,
                                 workspace_bytes, stream);
+}
+
+et_status et_argmax_noalloc(int storage, const void* x, int64_t rows, int64_t n, int32_t* out,
+                            void* stream) {
+  switch (storage) {
+    case ET_STORAGE_F32:
+      return et::argmax_noalloc<float>(static_cast<const float*>(x), rows, n, out, stream);
+    case ET_STORAGE_BF16:
+      return et::argmax_noalloc<Bf16>(static_cast<const Bf16*>(x), rows, n, out, stream);
+    case ET_STORAGE_F16:
+      return et::argmax_noalloc<F16>(static_cast<const F16*>(x), rows, n, out, stream);
+    default:
+      return ET_ERR_BAD_ARG;
+  }
 }
 
 const char* et_status_string(et_status s) {

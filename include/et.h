@@ -313,6 +313,22 @@ et_status et_argmax_f16(const et_f16* x, int64_t rows, int64_t n,
                         int32_t* out, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* Greedy argmax for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same results as et_argmax_* with a workspace, with no workspace
+ * argument and no allocation.  The split path's per-row key and counter
+ * live in a 16 KiB array inside the library, one per GPU, held until the
+ * process ends; it covers every call (the split path only runs for calls
+ * of fewer than 1024 rows, 16 bytes per row), and a need beyond it would
+ * be ET_ERR_WORKSPACE.  Each call that splits first clears the array with a
+ * kernel on `stream`, then runs et_argmax_*'s kernel on it.
+ *   storage: ET_STORAGE_F32, _BF16 or _F16 (x of that type), else
+ *   ET_ERR_BAD_ARG; every other argument and status as et_argmax_*.
+ *   Calls that overlap on one GPU (other streams, other host threads) share
+ *   the array and race: serialise them. */
+et_status et_argmax_noalloc(int storage, const void* x, int64_t rows,
+                            int64_t n, int32_t* out, void* stream);
+
 /* ------------------------------------------------------------------------
  * LayerNorm  ([OPS] 2 Normalization / LayerNorm; [DNN] 7)
  *   per row of d: mu = mean(x), var = mean((x - mu)^2) (the two-pass
