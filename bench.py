@@ -80,6 +80,8 @@ def parse():
                    help="summarise the rocprofv3 output under this directory and exit")
     p.add_argument("--title", default="", help="--summarize: heading of the summary")
     p.add_argument("--command", default="", help="--summarize: the command that made the profile")
+    p.add_argument("--labels", default="",
+                   help="--summarize: comma-separated label prefixes to report (default: all)")
     return p.parse_args()
 
 
@@ -903,7 +905,7 @@ def _dispatch_labels(log, n_kernels):
     return seq
 
 
-def summarize(d, log_path, title, command):
+def summarize(d, log_path, title, command, prefixes=()):
     """Markdown summary of a rocprofv3 run of this benchmark: a kernel trace
     (kernel_trace.csv) gives one row per (op, kernel, launch shape) with
     average / median / p10 / p90 durations and GB/s of algorithmic bytes; a
@@ -914,6 +916,7 @@ def summarize(d, log_path, title, command):
     bandwidth is marked invalid."""
     log = json.load(open(log_path))
     info = log.get("info", {})
+    keep = (lambda lab: any(lab.startswith(p) for p in prefixes)) if prefixes else (lambda lab: True)
     lines = [f"# {title or 'rocprofv3 summary'}", ""]
     if command:
         lines += ["Command:", "", "```", command, "```", ""]
@@ -945,6 +948,8 @@ def summarize(d, log_path, title, command):
                   "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
         for key, durs in groups.items():
             lab, kern, grid, blk, lds, vgpr = key
+            if not keep(lab):
+                continue
             t = np.asarray(durs)
             nb = info.get(lab, {}).get("bytes")
             if nb:
@@ -987,7 +992,7 @@ def summarize(d, log_path, title, command):
                           f"{'read' if key == 'bytes_read' else 'written'} bytes | sources sha256 |",
                       "|---|---|---|---|---|---|"]
             for (lab, cn), v in vals.items():
-                if cn != cname or lab == cal:
+                if cn != cname or lab == cal or not keep(lab):
                     continue
                 raw = float(np.mean(v)) * 1024
                 sc = raw * factor if factor else float("nan")
@@ -1030,7 +1035,8 @@ def main():
     if args.summarize:
         if not args.dispatch_log:
             raise SystemExit("--summarize needs --dispatch-log")
-        summarize(args.summarize, args.dispatch_log, args.title, args.command)
+        summarize(args.summarize, args.dispatch_log, args.title, args.command,
+                  tuple(x for x in args.labels.split(",") if x))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the ops shard by rows with "
