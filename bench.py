@@ -921,6 +921,7 @@ def summarize(d, log_path, title, command, prefixes=()):
     if command:
         lines += ["Command:", "", "```", command, "```", ""]
     trace = _find(d, "*kernel_trace.csv")
+    stats = _find(d, "*kernel_stats.csv")
     counters = _find(d, "*counter_collection.csv")
     if trace:
         rows = [r for r in _read_csv(trace) if _is_library_kernel(r["Kernel_Name"])]
@@ -965,6 +966,18 @@ def summarize(d, log_path, title, command, prefixes=()):
                          f"{np.median(t):.2f} | {np.percentile(t, 10):.2f} | {np.percentile(t, 90):.2f} | "
                          f"{mb} | {g_s} | {f_s} | {sha} |")
         lines.append("")
+        if stats:
+            # rocprofv3's own --stats rows (per kernel name, every launch of it
+            # in the run) for the kernels of the rows above.
+            names = {r["Kernel_Name"] for lab, r in zip(labels, rows) if keep(lab)}
+            lines += ["rocprofv3 --stats rows of these kernels (all their launches in the run):", "",
+                      "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+            for r in _read_csv(stats):
+                if r["Name"] in names:
+                    lines.append(f"| `{_short(r['Name'])[:90]}` | {r['Calls']} | "
+                                 f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                                 f"{float(r['MaxNs']) / 1e3:.2f} |")
+            lines.append("")
     if counters:
         rows = [r for r in _read_csv(counters) if _is_library_kernel(r["Kernel_Name"])]
         by_disp = {}
@@ -986,8 +999,9 @@ def summarize(d, log_path, title, command, prefixes=()):
             c = vals.get((cal, cname))
             truth = info.get(cal, {}).get(key)
             factor = truth / (np.mean(c) * 1024) if c and truth else None
-            lines += [f"Counter {cname}: calibration copy reads {np.mean(c) * 1024:.0f} B for "
-                      f"{truth} B, factor {factor:.4f}." if factor else f"Counter {cname}: no calibration.",
+            lines += [f"Counter {cname}: the calibration copy counts {np.mean(c) * 1024:.0f} B for the "
+                      f"{truth} B it {'reads' if key == 'bytes_read' else 'writes'}, factor {factor:.4f}."
+                      if factor else f"Counter {cname}: no calibration.",
                       "", f"| label | launches | counter bytes per launch | scaled bytes | algorithmic "
                           f"{'read' if key == 'bytes_read' else 'written'} bytes | sources sha256 |",
                       "|---|---|---|---|---|---|"]
