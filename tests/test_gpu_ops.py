@@ -270,6 +270,56 @@ def test_argmax(et, orc, dt, rows, n, split):
     assert_bits(got_m, ref, "misaligned")
 
 
+def _argmax_degenerate_rows(n):
+    """Rows whose answer hides in a stretch with nothing above -inf: the
+    scan's second pass (first number of a range) and the scalar tail."""
+    rows = []
+    r = np.full(n, np.nan, np.float32)
+    r[n // 2:] = -np.inf                          # NaN then -inf: the first -inf
+    rows.append(r)
+    r = np.full(n, -np.inf, np.float32)
+    r[: n // 3] = np.nan                          # -inf only after a NaN stretch
+    r[n - 1] = np.nan
+    rows.append(r)
+    r = np.full(n, np.nan, np.float32)
+    r[n - 1] = -np.inf                            # the only number is the last, -inf
+    rows.append(r)
+    r = np.full(n, -np.inf, np.float32)
+    r[n - 1] = -1e30                              # the only finite value is the last
+    rows.append(r)
+    r = np.full(n, np.nan, np.float32)
+    r[n - 2] = 5.0                                # a number in the tail, NaN around it
+    rows.append(r)
+    r = np.full(n, np.nan, np.float32)            # all NaN: -1
+    rows.append(r)
+    r = np.full(n, -np.inf, np.float32)
+    r[np.arange(7, n, 4099)] = np.nan             # -inf with scattered NaN: index 0
+    rows.append(r)
+    r = np.full(n, -np.inf, np.float32)
+    r[0] = np.nan
+    r[n // 2 + 1] = -0.0                          # -0 and +0 among -inf and NaN: the -0
+    r[min(n - 1, n // 2 + 3)] = 0.0
+    rows.append(r)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("n", [5, 2049, 40003, 70000, 128256])
+@pytest.mark.parametrize("copies", [1, 130])
+def test_argmax_ranges_without_numbers_above_minus_inf(et, orc, dt, n, copies):
+    """Rows of -inf and NaN only (and single numbers hidden among them), in
+    calls small enough to split (8 rows) and large enough for one workgroup
+    per row (1040 rows, the same rows repeated): with and without a
+    workspace, aligned and not, against the oracle."""
+    x = _store(np.tile(_argmax_degenerate_rows(n), (copies, 1)), dt)
+    ref = orc.argmax(x)
+    if dt == "f32" and copies == 1:
+        assert ref[:6].tolist() == [n // 2, n // 3, n - 1, n - 1, n - 2, -1]
+    for split in (True, False):
+        assert_bits(host(et.argmax(dev(x), split=split)), ref, f"{dt} n={n} x{copies} split={split}")
+    assert_bits(host(et.argmax(_misaligned(dev(x)))), ref, f"{dt} n={n} x{copies} misaligned")
+
+
 @pytest.mark.parametrize("dt", DTS)
 def test_argmax_empty_rows(et, dt):
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dt]
