@@ -21,11 +21,20 @@
 //     CU); each one atomically maxes a 64-bit key of its best into the row's
 //     slot and counts itself, and the last one of the row writes the index
 //     and re-zeroes the slot and the counter (one launch; the workspace is
-//     left as it was found).  Measured on [256, 128256] f32 over buffers
-//     rotated past the Infinity Cache: 25.0 us, against 25.3-27.3 us for
-//     one 1024-thread workgroup per row, 512-thread workgroups, 8 or 16
-//     vectors per lane, 2048 or 4096 workgroups, or a software-pipelined
-//     scan, and 22.2 us for a plain read of the same bytes on the same GPU.
+//     left as it was found).
+//   * Measured on [256, 128256] f32 over buffers rotated past the Infinity
+//     Cache, against a plain read of the same bytes in the same process
+//     (22.0 us on that GPU; this kernel 24.7 us): the scan's instruction
+//     stream costs little (software pipelining, 2 or 4 accumulators, 8
+//     vectors per lane, buffer loads: all within 1 % of one another), and
+//     so does the chunk size (1 to 8 granules of 1024 vectors per
+//     workgroup, or one 1024-thread workgroup per row); what the read does
+//     not pay is the end of each workgroup: its reduction (DPP exchanges,
+//     0.4 us faster than LDS-crossbar shuffles) and the merge's atomics
+//     (about 1.1 us).  Publishing each chunk's key with a device-scope
+//     store and having the last workgroup poll for them saves one round
+//     trip on paper but ran no faster with 4 chunks a row and 2.7 us slower
+//     with 16: such stores become visible later than atomics.
 #include <mutex>
 
 #include "et_common.hpp"
@@ -47,27 +56,46 @@ constexpr int kThreads = 256;        // threads per workgroup
 constexpr int kU = 4;                 // vectors in flight per lane per step
 constexpr int64_t kFillBlocks = 1024;  // workgroups a call aims at (four per CU)
 
+// A candidate: value and index.  kNone marks "no number seen" (with value
+// -inf); every real index is below it (n <= INT32_MAX).  Candidates never
+// hold NaN: the scans skip it.
+constexpr int32_t kNone = INT32_MAX;
+
 struct Best {
   float v;
-  int32_t i;  // -1: no number seen
+  int32_t i;
 };
 
+// The better of two candidates: the greater value, or of equal values the
+// lower index.  No candidate holds NaN, so this is a total order on distinct
+// indices, and a kNone candidate (-inf, INT32_MAX) loses to every real one.
 __device__ inline Best better(Best a, Best b) {
-  if (b.i < 0) return a;
-  if (a.i < 0) return b;
-  if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
-  return a;
+  const bool take_b = b.v > a.v || (b.v == a.v && b.i < a.i);
+  return take_b ? b : a;
 }
 
+template <int CTRL>
+__device__ inline Best dpp_better(Best b) {
+  const Best o{dpp::mov<CTRL>(b.v), __builtin_amdgcn_mov_dpp(b.i, CTRL, 0xF, 0xF, false)};
+  return better(b, o);
+}
+
+__device__ inline Best lane_of(Best b, int lane) {
+  return Best{__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, b.v), lane)),
+              __builtin_amdgcn_readlane(b.i, lane)};
+}
+
+// The best of a wave, the same in every lane: four DPP exchanges (partners
+// 1 and 2 apart inside a quad, then the mirrored lane of the 8- and 16-lane
+// half-row and row) leave every lane of each 16-lane row with that row's
+// best; the four rows' results are then read out of lanes 0, 16, 32, 48.
+// No step goes through the LDS crossbar.
 __device__ inline Best wave_best(Best b) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    Best o;
-    o.v = __shfl_xor(b.v, m, 64);
-    o.i = __shfl_xor(b.i, m, 64);
-    b = better(b, o);
-  }
-  return b;
+  b = dpp_better<dpp::kXor1>(b);
+  b = dpp_better<dpp::kXor2>(b);
+  b = dpp_better<dpp::kHalfMirror>(b);
+  b = dpp_better<dpp::kMirror>(b);
+  return better(better(lane_of(b, 0), lane_of(b, 16)), better(lane_of(b, 32), lane_of(b, 48)));
 }
 
 // The best of a T-thread workgroup, returned to every thread.
@@ -82,9 +110,9 @@ __device__ inline Best block_best(Best b) {
     si[w] = b.i;
   }
   __syncthreads();
-  Best r{0.0f, -1};
+  Best r{sv[0], si[0]};
 #pragma unroll
-  for (int k = 0; k < T / 64; ++k) r = better(r, Best{sv[k], si[k]});
+  for (int k = 1; k < T / 64; ++k) r = better(r, Best{sv[k], si[k]});
   return r;
 }
 
@@ -110,13 +138,13 @@ __device__ inline void run_update(Run& r, float v, int j, int e) {
 
 // The lowest index in [lo, hi) of row p holding a number (not NaN), as a
 // workgroup's Best (its value is then -inf, the largest value present), or
-// -1: the answer for a range where no value exceeds -inf.  Rare: only ranges
-// of -inf and NaN get here.
+// kNone: the answer for a range where no value exceeds -inf.  Rare: only
+// ranges of -inf and NaN get here.
 template <typename S, int T>
 __device__ __forceinline__ Best first_number(const S* p, int64_t lo, int64_t hi) {
   using E = Elem<S>;
   __syncthreads();  // every lane has read block_best's slots from the first pass
-  Best b{0.0f, -1};
+  Best b{-__builtin_inff(), kNone};
   for (int64_t i = lo + threadIdx.x; i < hi; i += T) {
     const float v = E::ld(p, i);
     if (v == v) {
@@ -137,8 +165,8 @@ __device__ __forceinline__ Best scan_range(const S* __restrict__ x, int64_t row,
   constexpr int kTileVec = T * kU;
   const S* p = x + row * n;
   Run r{-__builtin_inff(), -1, 0};
-  int32_t tail_i = -1;  // the scalar tail's candidate (vector path)
-  float tail_v = 0.0f;
+  int32_t tail_i = kNone;  // the scalar tail's candidate (vector path)
+  float tail_v = -__builtin_inff();
   if constexpr (VEC) {
     // Whole tiles without guards, then one clamped and guarded tile, then
     // the scalar tail (fewer than V elements).  Vector indices fit in int:
@@ -182,10 +210,10 @@ __device__ __forceinline__ Best scan_range(const S* __restrict__ x, int64_t row,
   } else {
     for (int64_t i = lo + threadIdx.x; i < hi; i += T) run_update(r, E::ld(p, i), static_cast<int>(i), 0);
   }
-  Best b{r.m, r.j < 0 ? -1 : (VEC ? r.j * V + r.e : r.j)};
+  Best b{r.m, r.j < 0 ? kNone : (VEC ? r.j * V + r.e : r.j)};
   b = better(b, Best{tail_v, tail_i});
   b = block_best<T>(b);
-  if (b.i < 0) b = first_number<S, T>(p, lo, hi);  // (uniform: every lane holds the block's best)
+  if (b.i == kNone) b = first_number<S, T>(p, lo, hi);  // (uniform: every lane holds the block's best)
   return b;
 }
 
@@ -194,7 +222,7 @@ template <typename S, int T, bool VEC>
 __global__ __launch_bounds__(T) void argmax_rows(const S* __restrict__ x, int64_t n,
                                                  int32_t* __restrict__ out) {
   const Best b = scan_range<S, T, VEC>(x, blockIdx.x, n, 0, n);
-  if (threadIdx.x == 0) out[blockIdx.x] = b.i;
+  if (threadIdx.x == 0) out[blockIdx.x] = b.i == kNone ? -1 : b.i;
 }
 
 // Rows split into chunks, merged through one 64-bit key per row: key =
@@ -203,7 +231,7 @@ __global__ __launch_bounds__(T) void argmax_rows(const S* __restrict__ x, int64_
 // into +0 first, so the two tie; 0 means "no number").  Workspace per row:
 // the key (8 bytes) and the counter (4 bytes, padded to 8).
 __device__ inline uint64_t best_key(Best b) {
-  if (b.i < 0) return 0;
+  if (b.i == kNone) return 0;
   uint32_t u = __float_as_uint(b.v);
   if ((u & 0x7FFFFFFFu) == 0) u = 0;  // -0 -> +0
   const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
