@@ -254,10 +254,25 @@ struct QkOut {
     return hh < a.hq ? static_cast<int>((t * a.hq + hh - qrow0) * a.D)
                      : static_cast<int>((t * a.hk + (hh - a.hq) - krow0) * a.D);
   }
-  __device__ void store(bool isq, int elem, const u32x4& v) const {
+  // Store v at element `elem` of the q or k rows (relative to this
+  // workgroup's resource base); p is the same element's address.  A buffer
+  // store needs its resource in scalar registers: a resource chosen per lane
+  // makes the compiler wrap every store in a loop over the distinct values.
+  // The rows of one store instruction are nearly always all query or all
+  // key heads, so when the wave's active lanes agree the resource is chosen
+  // for the whole wave (a uniform select); a wave that straddles the two
+  // stores through p with a plain non-temporal store instead, which the
+  // compiler cannot merge back into the buffer store.
+  __device__ void store(bool isq, int elem, S* p, const u32x4& v) const {
     const int off = elem * static_cast<int>(sizeof(S));
-    if (isq) st16_buf<POL>(rq, off, v);
-    else st16_buf<POL>(rk, off, v);
+    const unsigned long long lanes = __ballot(1), qlanes = __ballot(isq);
+    if (qlanes == lanes) {
+      st16_buf<POL>(rq, off, v);
+    } else if (qlanes == 0) {
+      st16_buf<POL>(rk, off, v);
+    } else {
+      st16(p, 0, v);
+    }
   }
 };
 
@@ -342,8 +357,8 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32
           rotate(xb[e], xb[e + 1], tab[eb[u] / 2 + e / 2]);
         }
       }
-      out.store(isq[u], rel[u] + ea[u], E::pack(xa));
-      out.store(isq[u], rel[u] + eb[u], E::pack(xb));
+      out.store(isq[u], rel[u] + ea[u], rowp[u] + ea[u], E::pack(xa));
+      out.store(isq[u], rel[u] + eb[u], rowp[u] + eb[u], E::pack(xb));
     }
   }
 }
@@ -497,8 +512,8 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
       }
     }
     if (head_row(u) < a.rows) {
-      out.store(isq[u], rel[u] + ea, E::pack(xa));
-      out.store(isq[u], rel[u] + eb, E::pack(xb));
+      out.store(isq[u], rel[u] + ea, rowp[u] + ea, E::pack(xa));
+      out.store(isq[u], rel[u] + eb, rowp[u] + eb, E::pack(xb));
     }
   }
 }
@@ -1166,7 +1181,7 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
     if constexpr (PS == 1) {
       E::st(rowp[u], cv[u], y[0]);
     } else {
-      out.store(isq[u], rel[u] + cv[u] * PS, E::pack(y));
+      out.store(isq[u], rel[u] + cv[u] * PS, rowp[u] + cv[u] * PS, E::pack(y));
     }
   }
 }
