@@ -151,3 +151,37 @@ def test_prefill_f16(et, orc, op):
     print(f"prefill f16 {op}", flush=True)
     FN[op](et, orc, dataclasses.replace(wl.WORKLOADS[2], dtype="f16"))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("layout,r", [(0, 128), (1, 64)])
+def test_rope_and_qknorm_past_128_mib_with_mixed_heads(et, orc, layout, r):
+    """RoPE and the fused RMSNorm+RoPE on bf16 q [70000, 5, 128] and k [70000,
+    3, 128]: 143 MB rotated, so the stores are non-temporal, and every store
+    instruction of a wave covers query and key heads of one token, so each one
+    takes the path for waves that straddle the two (the large-hidden shape,
+    64 + 8 heads, never does).  Sampled tokens against the oracle."""
+    T, Hq, Hk, D, eps, mu = 70000, 5, 3, 128, 1e-5, 1.0
+    g = np.random.default_rng([31, layout, r])
+    q = wl.store(g.standard_normal((T, Hq, D)).astype(np.float32), "bf16")
+    k = wl.store(g.standard_normal((T, Hk, D)).astype(np.float32), "bf16")
+    gq = wl.store(g.uniform(0.5, 1.5, D).astype(np.float32), "bf16")
+    gk = wl.store(g.uniform(0.5, 1.5, D).astype(np.float32), "bf16")
+    pos = g.integers(0, 1 << 17, T).astype(np.int32)
+    inv = wl.inv_freq(5e5, r)
+    assert T * (Hq + Hk) * D * 2 > 128 << 20
+    ts = _sample(T, 40, 900 + layout)
+    qt, kt = dev(q), dev(k)
+    et.rope_qk(qt, kt, dev(pos), dev(inv), d_rot=r, attn_scaling=mu, layout=layout)
+    for name, src, t in (("q", q, qt), ("k", k, kt)):
+        got = host(t)[ts]
+        ref, y64 = orc.rope(src[ts], pos[ts], r, inv, mu, layout)
+        assert_pair(got, y64, ref, r, layout, f"rope {name}")
+        assert_bits(got[..., r:], src[ts][..., r:], "pass-through")
+    qt, kt = dev(q), dev(k)
+    et.rmsnorm_rope_qk(qt, dev(gq), kt, dev(gk), eps, dev(pos), dev(inv), d_rot=r, attn_scaling=mu,
+                       layout=layout)
+    for name, src, gain, t in (("q", q, gq, qt), ("k", k, gk, kt)):
+        got = host(t)[ts]
+        ref, y64 = orc.rmsnorm_rope(src[ts], gain, eps, pos[ts], r, inv, mu, layout)
+        assert_pair(got, y64, ref, r, layout, f"qknorm {name}")
+        assert_close(got[..., r:], y64[..., r:], ref[..., r:], "qknorm tail")
