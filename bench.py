@@ -442,7 +442,7 @@ CEILING_CASES = [
     ("2R1W_32MiB_dev", 32 * MIB, 2, 1, 1, 0, False),
     ("2R2W_32MiB", 32 * MIB, 2, 2, 0, 0, False),
     ("inplace_40MiB_dev", 4096 * 40 * 128 * 2, 1, 1, 1, 0, True),
-    ("2R1W_112MiB_dev", 4096 * 14336 * 2, 2, 1, 1, 0, False),
+    ("2R1W_112MiB", 4096 * 14336 * 2, 2, 1, 0, 0, False),
     ("read_125MiB", 256 * 128256 * 4, 1, 0, 0, 0, False),
     ("inplace_128MiB_dev", 128 * MIB, 1, 1, 1, 0, True),
     ("1R1W_125MiB", 256 * 128256 * 4, 1, 1, 0, 0, False),
@@ -460,11 +460,11 @@ OP_CEILING = {
            "rmsnorm_rope": "inplace_144MiB", "silu_mul": "2R1W_448MiB"},
     "w2": {"rmsnorm": "1R1W_32MiB", "embedding": "1R1W_32MiB", "add": "2R1W_32MiB_dev",
            "add_rmsnorm": "2R2W_32MiB", "rope": "inplace_40MiB_dev",
-           "rmsnorm_rope": "inplace_40MiB_dev", "silu_mul": "2R1W_112MiB_dev"},
+           "rmsnorm_rope": "inplace_40MiB_dev", "silu_mul": "2R1W_112MiB"},
     "w3": {"argmax": "read_125MiB"},
     "w4": {"rmsnorm_rope": "inplace_128MiB_dev"},
-    "next": {"softmax": "1R1W_125MiB", "layernorm": "1R1W_32MiB", "geglu_erf": "2R1W_112MiB_dev",
-             "geglu_tanh": "2R1W_112MiB_dev", "rope_cached": "inplace_40MiB_dev",
+    "next": {"softmax": "1R1W_125MiB", "layernorm": "1R1W_32MiB", "geglu_erf": "2R1W_112MiB",
+             "geglu_tanh": "2R1W_112MiB", "rope_cached": "inplace_40MiB_dev",
              "rope_multi": "inplace_225MiB"},
 }
 

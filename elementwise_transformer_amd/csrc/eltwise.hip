@@ -251,7 +251,7 @@ et_status eltwise_entry(const S* a, const S* b, S* y, int64_t n, void* stream) {
     // a vector boundary, only the last one has a tail.
     const int64_t per_launch = kMaxGrid * kBlock * kU;  // vectors
     const int64_t nvec_all = n / V;
-    const int pol = store_policy(bytes);
+    const int pol = store_policy(bytes, kEltDeviceStoreMaxBytes);
     for (int64_t v0 = 0;; v0 += per_launch) {
       const int64_t nvec = nvec_all - v0 < per_launch ? nvec_all - v0 : per_launch;
       const bool last = v0 + nvec >= nvec_all;

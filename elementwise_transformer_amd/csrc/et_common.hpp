@@ -169,12 +169,15 @@ __device__ inline u32x4 ld16_keep(const S* p, int64_t elem) {
 // bits a plain pointer store cannot:
 //   kStoreStream (nt): non-temporal, the store streams to HBM.
 //   kStoreDevice (sc1): device-scope write-through; the line leaves this
-//     XCD's L2 at once.  Measured on MI355X: a SiLU-mul writing 117 MB ran
-//     51.4 us with these stores against 56.1 us with non-temporal ones (and
-//     the whole eight-op step 2.5 % faster), while one writing 470 MB ran
-//     2 % slower -- the gain holds while the output fits the 256 MB
-//     Infinity Cache, which then writes it back to HBM behind later work.
-// The host picks the policy from the output size (store_policy below).
+//     XCD's L2 at once, and the 256 MB Infinity Cache writes it back to HBM
+//     behind later work.  That helps while the output is small next to the
+//     cache.  Measured on MI355X over buffers rotated past the cache,
+//     back-to-back launches: in-place RoPE writing 42 MB and 67 MB, 17.9 and
+//     25.5 us against 18.3 and 25.9 with non-temporal stores; an add writing
+//     34 MB, 18.9 against 20.0 us; but a SiLU-mul writing 117 MB, 60.5
+//     against 58.8 us (the whole prefill step the same either way).
+// The host picks the policy from the output size (store_policy below), the
+// elementwise kernels with a lower limit than the rest.
 enum StorePolicy : int { kStoreStream = 2, kStoreDevice = 16 };
 
 // A resource for `bytes` bytes from `base` (a uniform pointer); stores at
@@ -282,11 +285,12 @@ inline et_status launch_status() {
 // Largest grid.x the launchers use per launch; longer work is split.
 constexpr int64_t kMaxGrid = int64_t{1} << 30;
 
-// Device-scope stores while a launch writes at most this much, else
+// Device-scope stores while a launch writes at most max_dev bytes, else
 // non-temporal ones (see StorePolicy).
 constexpr int64_t kDeviceStoreMaxBytes = int64_t{128} << 20;
-inline int store_policy(int64_t out_bytes) {
-  return out_bytes <= kDeviceStoreMaxBytes ? kStoreDevice : kStoreStream;
+constexpr int64_t kEltDeviceStoreMaxBytes = int64_t{64} << 20;  // add, SiLU-mul, GeGLU
+inline int store_policy(int64_t out_bytes, int64_t max_dev = kDeviceStoreMaxBytes) {
+  return out_bytes <= max_dev ? kStoreDevice : kStoreStream;
 }
 
 }  // namespace et
