@@ -175,15 +175,45 @@ class DispatchLog:
 LOG = DispatchLog()
 
 
+_HOLD = None
+
+
+def _hold(stream, launches):
+    """Keep `stream` busy while the host enqueues `launches` timed launches
+    (probe_hold_kernel, about 60 us of host time per launch, at most 100 ms),
+    so that kernels shorter than the host's enqueue time still run back to
+    back and their events time the GPU.  A no-op if the probe library cannot
+    be loaded."""
+    global _HOLD
+    if _HOLD is None:
+        import ctypes
+        try:
+            lib = ctypes.CDLL(os.path.join(ROOT, "probe", "libet_probe.so"))
+            f = lib.et_probe_hold
+            f.argtypes = [ctypes.c_int64, ctypes.c_void_p]
+            f.restype = ctypes.c_int
+            _HOLD = f
+        except (OSError, AttributeError):
+            _HOLD = False
+    if _HOLD:
+        import ctypes
+        us = min(100000, 60 * launches)
+        if _HOLD(us, ctypes.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("probe hold kernel failed to launch")
+
+
 def _time_launches(stream, fn, sets, launches, label, warm=5):
     """Per-launch HIP-event times (ms) of fn(i), i over rotating buffer sets.
     The events are created before the loop and Python's collector is paused
-    inside it, so no host pause lands between an event and its launch."""
+    inside it, so no host pause lands between an event and its launch; a
+    hold kernel ahead of the loop lets the host enqueue the whole batch
+    before the first timed launch runs."""
     import torch
     for i in range(warm):
         fn(i)
     evs = [TimingEvents(stream) for _ in range(launches)]
     torch.cuda.synchronize()
+    _hold(stream, launches)
     gc.disable()
     try:
         for j, ev in enumerate(evs):
@@ -541,6 +571,7 @@ def _time_launches_plain(stream, fn, launches, warm=5):
         fn(i)
     evs = [TimingEvents(stream) for _ in range(launches)]
     torch.cuda.synchronize()
+    _hold(stream, launches)
     gc.disable()
     try:
         for j, ev in enumerate(evs):

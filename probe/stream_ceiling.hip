@@ -19,6 +19,11 @@
 // that step through the buffer by the grid's span (grid-stride), so the
 // dispatch of workgroups is paid once per workgroup slot instead of once
 // per tile.
+//
+// Also here: a hold kernel for the benchmark's timing of small kernels.  It
+// keeps the stream busy for a given time, so the host can enqueue a whole
+// batch of timed launches behind it; they then run back to back, and their
+// events time the GPU, not the host's pace.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -110,7 +115,32 @@ void launch_u(int u, int persist_blocks, bool dev, const void* a, const void* b,
 }  // namespace
 }  // namespace etprobe
 
+// One wave that waits until `ticks` of the constant-rate wall clock have
+// passed since it started, then exits (the clock always advances, so every
+// launch ends; the host caps the time at 100 ms).  Outside the probe's
+// namespace, so profile summaries that match the library's and the probe's
+// kernels by namespace skip it.
+__global__ void probe_hold_kernel(long long ticks) {
+  const long long t0 = wall_clock64();
+  while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(32);
+}
+
 extern "C" {
+
+// Keeps `stream` busy for `microseconds` (1..100000) with one wave of
+// probe_hold_kernel, counting the 100 MHz reference clock that wall_clock64()
+// reads on this GPU family (the runtime's wall-clock-rate attribute gave a
+// hold 60 times too long here, so it is not used).  Returns 0 on a launch, 1
+// on a bad argument, 2 when the launch reports an error.
+int et_probe_hold(int64_t microseconds, void* stream) {
+  if (microseconds < 1 || microseconds > 100000) return 1;
+  constexpr long long kTicksPerUs = 100;
+  const long long ticks = static_cast<long long>(microseconds) * kTicksPerUs;
+  (void)hipGetLastError();
+  probe_hold_kernel<<<1, 64, 0, static_cast<hipStream_t>(stream)>>>(ticks);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
 
 // Streams `n_read` buffers of `bytes` bytes in and `n_write` out in one
 // launch on `stream`, (n_read, n_write) one of (0, 1), (1, 0), (1, 1),

@@ -392,3 +392,15 @@ def test_stream_probe_validation():
     ]
     for args in bad:
         assert f(*args, None) == 1, args
+
+
+@gpu_visible
+def test_probe_hold_validation():
+    """The benchmark's hold kernel (probe/libet_probe.so) rejects times
+    outside 1 us .. 100 ms before touching the device."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "probe", "libet_probe.so"))
+    f = lib.et_probe_hold
+    f.argtypes = [ctypes.c_int64, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    for bad in (0, -5, 100001, 1 << 40):
+        assert f(bad, None) == 1

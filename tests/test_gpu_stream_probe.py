@@ -64,3 +64,29 @@ def test_stream_probe_outputs(probe, nbytes, u, dev_scope, persist):
     lane = np.stack([i.astype(np.uint32), np.full_like(i, 0x5bd1e995, dtype=np.uint32),
                      (i >> 7).astype(np.uint32), np.full_like(i, 0x1b873593, dtype=np.uint32)], axis=1)
     assert np.array_equal(y, (lane ^ np.array([0x11, 0x22, 0x33, 0x44], np.uint32)).ravel())
+
+
+def test_probe_hold_keeps_the_stream_busy(probe):
+    """The hold kernel occupies the stream for about the time asked (at least
+    it, and well under the next power of ten) and then lets the work queued
+    behind it run."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "probe", "libet_probe.so"))
+    hold = lib.et_probe_hold
+    hold.argtypes = [ctypes.c_int64, ctypes.c_void_p]
+    hold.restype = ctypes.c_int
+    s = torch.cuda.current_stream()
+    x = torch.zeros(1024, device="cuda")
+    # one untimed round: the first launch of each kernel loads its code object
+    assert hold(1, ctypes.c_void_p(s.cuda_stream)) == 0
+    x += 1.0
+    torch.cuda.synchronize()
+    for us in (200, 3000):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        assert hold(us, ctypes.c_void_p(s.cuda_stream)) == 0
+        x += 1.0
+        b.record(s)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        assert us * 1e-3 * 0.98 <= ms < us * 1e-2, (us, ms)
+    assert float(x[0]) == 3.0
