@@ -69,8 +69,8 @@ __device__ inline float silu(float g) {
 //   a' = a sqrt(log2 e),  t8 = 1 / (8 + (4 / sqrt(log2 e)) a'),
 //   P'(t8) = (P(8 t8) + 2 ln 2) log2 e,
 // so coefficient i of P' is P's times 8^i log2 e (the power of 8 is exact)
-// and its constant term is (c0 + 2 ln 2) log2 e.  The factor 1/8 in t8 keeps
-// |x| t8 2^(K - floor K) below 2^-1.5 for every x.
+// and its constant term is (c0 + 2 ln 2) log2 e.  Since |x| t8 = |x| / (8 +
+// 2 sqrt(2) |x|) < 2^-1.5, |x| t8 2^(K - floor K) stays below 2^-0.5.
 constexpr double kLog2eD = 1.44269504088896340736;
 constexpr double kLn2D = 0.69314718055994530942;
 #define ET_ERFC_C(c, i) static_cast<float>((c) * (i) * kLog2eD)
@@ -109,18 +109,19 @@ __device__ inline float erfc_exp2_poly5(float t8) {
 // nonzero times an infinite one, and rounds once: one exp2 does.  Past that
 // (and for x = +-inf), the exact tail below; a wave runs it only when one of
 // its lanes needs it.
+constexpr float kGeluA = 0x1.b2da4ep-1f;   // sqrt(log2(e) / 2): a' = |x| kGeluA
+constexpr float kGeluT = 0x1.aa449ap+1f;   // 4 / sqrt(log2 e): 8 + 4a = 8 + kGeluT a'
+
 template <typename S>
-__device__ inline float gelu_erf_tail(float x, float u, float ap);
+__device__ inline float gelu_erf_tail(float x, float u);
 
 template <typename S>
 __device__ inline float gelu_erf_mul(float x, float u) {
-  constexpr float kA = 0x1.b2da4ep-1f;   // sqrt(log2(e) / 2): a' = |x| kA
-  constexpr float kT = 0x1.aa449ap+1f;   // 4 / sqrt(log2 e): 8 + 4a = 8 + kT a'
-  const float ap = __builtin_fabsf(x) * kA;
-  const float t8 = __builtin_amdgcn_rcpf(__builtin_fmaf(kT, ap, 8.0f));
+  const float ap = __builtin_fabsf(x) * kGeluA;
+  const float t8 = __builtin_amdgcn_rcpf(__builtin_fmaf(kGeluT, ap, 8.0f));
   const float p = sizeof(S) == 4 ? erfc_exp2_poly9(t8) : erfc_exp2_poly5(t8);
   const float k = __builtin_fmaf(-ap, ap, p);
-  if (k < -100.0f) return gelu_erf_tail<S>(x, u, ap);
+  if (k < -100.0f) return gelu_erf_tail<S>(x, u);
   const float q = t8 * __builtin_amdgcn_exp2f(k);              // Phi(-|x|)
   return x <= 0.0f ? x * q * u : x * (1.0f - q) * u;
 }
@@ -128,24 +129,29 @@ __device__ inline float gelu_erf_mul(float x, float u) {
 // The tail, K < -100.  The hardware exp2 returns no subnormals, so 2^K alone
 // would flush every Phi below 2^-126 -- results x Phi(x) u down to 2^-149
 // from x near -13 on in f32 and bf16 storage, and every product with a large
-// or infinite up beyond that.  So K (held above -320, where every product of
-// f32 values times 2^K is below the smallest subnormal) is split into its
-// floor n and a fraction: q = t8 2^(K - n), Phi(-|x|) = q 2^n, |x q| <
-// 2^-1.5, so x q u is finite for every finite u and ldexp(x q u, n) rounds a
-// subnormal result once and correctly.  a' is held at 2^100 in t8 (whose
-// reciprocal would flush from 2^127 on), so q is never 0 for a finite x: x
+// or infinite up beyond that.  So K (held above -320) is split into its floor
+// n and a fraction: q = t8 2^(K - n), Phi(-|x|) = q 2^n, |x q| < 2^-0.5, so
+// x q u is finite for every finite u (below 2^127.5) and ldexp(x q u, n)
+// rounds a subnormal result once and correctly; at K = -320 every such
+// product times 2^K is below half the smallest subnormal.  |x| is held at
+// 2^100 (a' below 2^100, whose reciprocal in t8 would flush from 2^127 on),
+// in the product on the negative side as well: past it the held K is -320,
+// and a larger |x| against the held t8 would break the bound on |x q| (x =
+// -3e38 gives |x q| near 2^26, and x q u overflows for |u| above 2^102
+// before ldexp could scale it to zero).  So q is never 0 for a finite x: x
 // Phi(x) is nonzero for every finite x, and its product with an infinite u
 // is an infinity.  Phi(-inf) is 0 and -inf * 0 has no value: NaN.
 template <typename S>
-__device__ inline float gelu_erf_tail(float x, float u, float ap) {
-  constexpr float kT = 0x1.aa449ap+1f;
-  const float t8 = __builtin_amdgcn_rcpf(__builtin_fmaf(kT, __builtin_fminf(ap, 0x1p100f), 8.0f));
+__device__ inline float gelu_erf_tail(float x, float u) {
+  const float xa = __builtin_fminf(__builtin_fabsf(x), 0x1p100f);
+  const float ap = xa * kGeluA;
+  const float t8 = __builtin_amdgcn_rcpf(__builtin_fmaf(kGeluT, ap, 8.0f));
   const float p = sizeof(S) == 4 ? erfc_exp2_poly9(t8) : erfc_exp2_poly5(t8);
   const float kc = __builtin_fmaxf(__builtin_fmaf(-ap, ap, p), -320.0f);
   const float n = __builtin_floorf(kc);
   const int ni = static_cast<int>(n);
   const float q = t8 * __builtin_amdgcn_exp2f(kc - n);         // Phi(-|x|) = q 2^n
-  const float r = x <= 0.0f ? __builtin_ldexpf(x * q * u, ni)
+  const float r = x <= 0.0f ? __builtin_ldexpf(-xa * q * u, ni)
                             : x * (1.0f - __builtin_ldexpf(q, ni)) * u;
   return x == -__builtin_inff() ? __builtin_nanf("") : r;
 }

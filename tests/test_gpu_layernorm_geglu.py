@@ -144,11 +144,14 @@ def test_geglu_matches_oracle(et, orc, dt, form, n):
 @pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("form", [0, 1])
 def test_geglu_large_up_and_deep_tail(et, orc, dt, form):
-    """Gates from -40 to 0 against ups near the f32 limit and far below it:
-    no intermediate may overflow where the product does not (x Phi(x) u for
-    x = -4.46, u = 3e38 is -5.6e33), and a GELU value below the f32 normal
-    range still gives its product with a large up in full precision."""
-    gates = np.concatenate([-np.linspace(0.0, 40.0, 81), [-1e-3, -0.5, -4.456161, -13.3, -15.9]])
+    """Gates from -40 to 0, and of magnitude up to the f32 limit, against ups
+    near that limit and far below it: no intermediate may overflow where the
+    product does not (x Phi(x) u for x = -4.46, u = 3e38 is -5.6e33; for x =
+    -3e38 it is far below the smallest subnormal, a signed zero), and a GELU
+    value below the f32 normal range still gives its product with a large up
+    in full precision."""
+    huge = [-1e20, -1e30, -2.0 ** 100, -2.0 ** 101, -1e37, -3e38, -3.4028235e38, 1e30, 3e38]
+    gates = np.concatenate([-np.linspace(0.0, 40.0, 81), [-1e-3, -0.5, -4.456161, -13.3, -15.9], huge])
     ups = np.array([3e38, -3e38, 1e30, -1e30, 1.0, 1e-30], np.float64)
     gg, uu = np.meshgrid(gates, ups)
     gs, us = wl.store(gg.ravel().astype(np.float32), dt), wl.store(uu.ravel().astype(np.float32), dt)
