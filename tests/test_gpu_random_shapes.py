@@ -309,6 +309,7 @@ def test_random_specials_rope(et, orc, dt, seed):
     pos[0] = 0                                          # the identity rotation (sin 0) included
     inv = wl.inv_freq(1e4, r)
     gq = wl.store(g.uniform(0.5, 1.5, D).astype(np.float32), dt)
+    gk = wl.store(g.uniform(0.5, 1.5, D).astype(np.float32), dt)
     what = f"{dt} T={T} Hq={Hq} Hk={Hk} D={D} r={r} layout={layout}"
     qt, kt = dev(q), (dev(k) if k is not None else None)
     et.rope_qk(qt, kt, dev(pos), dev(inv), d_rot=r, attn_scaling=mu, layout=layout)
@@ -319,11 +320,22 @@ def test_random_specials_rope(et, orc, dt, seed):
         got = host(t)
         _assert_pair_special(got, y64, ref, r, layout, f"rope {name} {what}")
         assert_bits(got[..., r:], src[..., r:], f"rope pass-through {name} {what}")
-    q2 = dev(q)
-    et.rmsnorm_rope_qk(q2, dev(gq), None, None, 1e-6, dev(pos), dev(inv), d_rot=r, attn_scaling=mu,
-                       layout=layout)
-    ref, y64 = orc.rmsnorm_rope(q, gq, 1e-6, pos, r, inv, mu, layout)
-    _assert_pair_special(host(q2), y64, ref, r, layout, f"rmsnorm_rope {what}")
+    # the rotation read from the library's cos/sin cache: the computed
+    # rotation's bits, NaN and infinities included
+    c, sn = et.rope_cache(dev(inv), int(pos.max()) + 1, r)
+    qc, kc = dev(q), (dev(k) if k is not None else None)
+    et.rope_qk_cached(qc, kc, dev(pos), c, sn, d_rot=r, attn_scaling=mu, layout=layout)
+    assert_bits(host(qc), host(qt), f"cached rope q {what}")
+    if k is not None:
+        assert_bits(host(kc), host(kt), f"cached rope k {what}")
+    q2, k2 = dev(q), (dev(k) if k is not None else None)
+    et.rmsnorm_rope_qk(q2, dev(gq), k2, dev(gk) if k is not None else None, 1e-6, dev(pos), dev(inv),
+                       d_rot=r, attn_scaling=mu, layout=layout)
+    for name, src, gain, t in (("q", q, gq, q2), ("k", k, gk, k2)):
+        if src is None:
+            continue
+        ref, y64 = orc.rmsnorm_rope(src, gain, 1e-6, pos, r, inv, mu, layout)
+        _assert_pair_special(host(t), y64, ref, r, layout, f"rmsnorm_rope {name} {what}")
     dims = (r // 2 - (r // 2) % 2, r - (r // 2 - (r // 2) % 2))     # two even widths summing to r
     pm = np.stack([pos, pos[::-1]], axis=1).astype(np.int32)
     inv2 = wl.multi_inv_freq(dims, [1e4, 1e3])
@@ -338,6 +350,45 @@ def test_random_specials_rope(et, orc, dt, seed):
                                  np.ascontiguousarray(ref[..., o:o + dw]), dw, layout, f"multi axis {a} {what}")
         o += dw
     assert_bits(got[..., r:], q[..., r:], f"multi pass-through {what}")
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("seed", range(8))
+def test_random_softmax_masks(et, orc, dt, seed):
+    """Softmax of rows up to 140,000 entries under random masks: a stretch of
+    -inf anywhere (whole 8192-entry chunks among them), top-k style rows
+    with one to eight finite entries, rows entirely -inf (NaN rows), a NaN or
+    a +inf planted (NaN rows); logits of scale 1 to 30 and temperatures from
+    0.05 to 20; through a workspace, without one, and in place."""
+    g = np.random.default_rng([5757, seed, DTS.index(dt)])
+    n = _length(g, 1, 140000)
+    rows = _rows(g, n, 1 << 20)
+    x = (g.standard_normal((rows, n)) * g.choice([1.0, 3.0, 30.0])).astype(np.float32)
+    for i in range(rows):
+        kind = g.uniform()
+        if kind < 0.4:
+            a = int(g.integers(0, n))
+            x[i, a:int(g.integers(a, n + 1))] = -np.inf
+        elif kind < 0.6:
+            keep = g.choice(n, size=min(n, int(g.integers(1, 9))), replace=False)
+            row = np.full(n, -np.inf, np.float32)
+            row[keep] = x[i, keep]
+            x[i] = row
+        elif kind < 0.65:
+            x[i] = -np.inf
+        elif kind < 0.7:
+            x[i, int(g.integers(0, n))] = np.nan
+        elif kind < 0.75:
+            x[i, int(g.integers(0, n))] = np.inf
+    xs = wl.store(x, dt)
+    t = float(np.float32(g.choice([0.05, 0.7, 1.0, 20.0])))
+    what = f"{dt} rows={rows} n={n} t={t}"
+    y, y64 = orc.softmax(xs, t)
+    check_softmax(host(et.softmax(dev(xs), t)), xs, t, y, y64, "softmax " + what)
+    check_softmax(host(et.softmax(dev(xs), t, split=False)), xs, t, y, y64, "softmax no workspace " + what)
+    xt = dev(xs)
+    et.softmax(xt, t, out=xt)
+    check_softmax(host(xt), xs, t, y, y64, "softmax in place " + what)
 
 
 @pytest.mark.parametrize("seed", range(3))
