@@ -1039,6 +1039,39 @@ __device__ inline void rotate_runs(const S* xr, const float (&x)[PS], float (&y)
   }
 }
 
+// The PS partners of a vector whose two runs start their partner columns,
+// and split, at multiples of 4, read 4 entries (8 or 16 bytes) at a time
+// and kept packed: 2-byte storage two entries per word, f32 one.
+template <typename S, int PS>
+struct Partners {
+  uint32_t w[PS * sizeof(S) / 4];
+};
+
+template <typename S, int PS>
+__device__ inline void read_partners4(const S* xr, int4 d, int kr, Partners<S, PS>& r) {
+#pragma unroll
+  for (int e0 = 0; e0 < PS; e0 += 4) {
+    const int p = (e0 < kr ? d.x : d.y) + e0;
+    if constexpr (sizeof(S) == 2) {
+      const uint2 w = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(xr) + p);
+      r.w[e0 / 2] = w.x;
+      r.w[e0 / 2 + 1] = w.y;
+    } else {
+      const uint4 w = *reinterpret_cast<const uint4*>(xr + p);
+      r.w[e0] = w.x; r.w[e0 + 1] = w.y; r.w[e0 + 2] = w.z; r.w[e0 + 3] = w.w;
+    }
+  }
+}
+
+template <typename S, int PS>
+__device__ inline float partner_of(const Partners<S, PS>& r, int e) {
+  if constexpr (sizeof(S) == 2) {
+    return (e & 1) ? Elem<S>::hi(r.w[e / 2]) : Elem<S>::lo(r.w[e / 2]);
+  } else {
+    return __uint_as_float(r.w[e]);
+  }
+}
+
 template <typename S, int PS, int U, int POL>
 __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
                                                            const int32_t* __restrict__ pos,
@@ -1135,10 +1168,48 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
   __syncthreads();
 
   // Phase 3: rotate and store.  A thread's slots usually share one column
-  // (the row length divides the slot stride) and advance through one token
-  // or a few, so the descriptor is read again only when the column changes
-  // and the angles are kept in registers until the token or column changes.
+  // (the row length divides the slot stride) and one token (a wave's rows
+  // lie in one token when the head count is a multiple of the rows a wave
+  // covers).  When that holds for every slot of every lane of the wave, and
+  // the partner runs sit at multiples of 4 entries, the wave takes one
+  // descriptor and one set of angles per lane and issues the partner reads
+  // of all its slots before the first rotation: one LDS round trip instead
+  // of one per slot, each of which held back that slot's store.  Otherwise
+  // the descriptor is read again only when the column changes and the
+  // angles are kept until the token or column changes.  Both paths give the
+  // same bits.
   const bool half = a.ra.layout == ET_ROPE_HALF;
+  if constexpr (PS > 1) {
+    bool uni = static_cast<int>(rope_slot<U>(0, threadIdx.x, U - 1)) < nslot;
+#pragma unroll
+    for (int u = 1; u < U; ++u) uni = uni && cv[u] == cv[0] && tl[u] == tl[0];
+    const int4 d0 = d4s[cv[0]];
+    const int d10 = d1s[cv[0]];
+    const int kr0 = d10 & 0xFF;
+    if (via_lds) uni = uni && ((kr0 | d0.x | d0.y) & 3) == 0;
+    if (__ballot(uni) == __ballot(1)) {
+      float2 an[PS];
+      entry_angles<PS>(cs + tl[0] * a.np, d0, d10, half, an);
+      Partners<S, PS> pr[U];
+      if (via_lds) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) read_partners4<S, PS>(xs + sl[u] * a.span, d0, kr0, pr[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float x[PS], y[PS];
+#pragma unroll
+        for (int e = 0; e < PS; ++e) x[e] = E::get(v[u], e);
+#pragma unroll
+        for (int e = 0; e < PS; ++e) {
+          const float xp = via_lds ? partner_of<S, PS>(pr[u], e) : x[e ^ 1];
+          y[e] = __builtin_fmaf(x[e], an[e].x, xp * an[e].y);
+        }
+        out.store(isq[u], rel[u] + cv[u] * PS, rowp[u] + cv[u] * PS, E::pack(y));
+      }
+      return;
+    }
+  }
   int4 d = make_int4(0, 0, 0, 0);
   int d1 = 0, kr = 0, cur_cv = -1, cur_tl = -1;
   float2 ang[PS];
