@@ -131,6 +131,23 @@ def test_rope_multi_rows_independent(et, dt):
         assert_bits(host(k1)[0], full_k[t], f"{dt} token {t} k")
 
 
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("layout", [0, 1])
+def test_rope_multi_wave_paths_agree(et, dt, layout):
+    """With 24 query and 24 key heads every wave's 16 head rows lie in one
+    token, so the kernel takes its batched path (one set of angles per lane,
+    all partner reads issued together); with the 24 query heads alone the
+    waves straddle tokens and take the per-slot path.  The query rows come
+    out with the same bits either way."""
+    case = (40, 24, 24, 128, (16, 56, 56), layout, 1.0, 64)
+    q, k, pos, inv = _inputs(case, dt, 90 + layout)
+    qa, ka = dev(q), dev(k)
+    et.rope_multi(qa, ka, dev(pos), case[4], dev(inv), layout=layout)
+    qb = dev(q)
+    et.rope_multi(qb, None, dev(pos), case[4], dev(inv), layout=layout)
+    assert_bits(host(qb), host(qa), f"{dt} layout {layout} q alone against q with k")
+
+
 def test_rope_multi_degenerate(et):
     """T == 0, no heads and all-zero widths are no-ops; bad arguments raise."""
     z = torch.empty((0, 2, 16), device="cuda")
