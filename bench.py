@@ -62,7 +62,7 @@ def parse():
     p.add_argument("--configs", default="2,3,4",
                    help="other workloads whose ops are timed one by one after the timed region "
                         "(comma-separated numbers; empty for none)")
-    p.add_argument("--op-launches", type=int, default=50,
+    p.add_argument("--op-launches", type=int, default=100,
                    help=f"launches per op in the per-op passes (at least {MIN_OP_LAUNCHES})")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
