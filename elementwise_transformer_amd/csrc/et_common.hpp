@@ -175,9 +175,12 @@ __device__ inline u32x4 ld16_keep(const S* p, int64_t elem) {
 //     back-to-back launches: in-place RoPE writing 42 MB and 67 MB, 17.9 and
 //     25.5 us against 18.3 and 25.9 with non-temporal stores; an add writing
 //     34 MB, 18.9 against 20.0 us; but a SiLU-mul writing 117 MB, 60.5
-//     against 58.8 us (the whole prefill step the same either way).
+//     against 58.8 us (the whole prefill step the same either way), and the
+//     fused RMSNorm+RoPE writing 42 MB, 19.76 against 19.30 us, with the
+//     write-back it left slowing the kernel after it.
 // The host picks the policy from the output size (store_policy below), the
-// elementwise kernels with a lower limit than the rest.
+// elementwise kernels with a lower limit than RoPE; the norms, the gather
+// and the fused RMSNorm+RoPE store non-temporally at every size.
 enum StorePolicy : int { kStoreStream = 2, kStoreDevice = 16 };
 
 // A resource for `bytes` bytes from `base` (a uniform pointer); stores at

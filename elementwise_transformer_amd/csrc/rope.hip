@@ -734,34 +734,24 @@ void launch_qknorm_vec(S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
   }
 }
 
+// The fused kernel stores non-temporally at every size: device-scope stores
+// made it slower on its own at the prefill size (in place 42 MB, 19.76 us
+// against 19.30 over buffers rotated past the Infinity Cache) and handed
+// their write-back to the next kernel (the plain RoPE launched after it,
+// 17.94 us against 17.61).
 template <typename S, int G>
 void launch_qknorm_vec_u(int u, S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
                          const float* inv_freq, QkNormArgs a, int64_t T, hipStream_t s) {
   const bool rot = a.rope.half > 0;
-  const bool dev = store_policy(T * (a.rope.hq + a.rope.hk) * a.rope.D * int64_t(sizeof(S))) ==
-                   kStoreDevice;
-  if (dev) {
-    if (u == 4) {
-      if (rot) launch_qknorm_vec<S, G, 4, true, kStoreDevice>(q, gq, k, gk, pos, inv_freq, a, T, s);
-      else launch_qknorm_vec<S, G, 4, false, kStoreDevice>(q, gq, k, gk, pos, inv_freq, a, T, s);
-    } else if (u == 2) {
-      if (rot) launch_qknorm_vec<S, G, 2, true, kStoreDevice>(q, gq, k, gk, pos, inv_freq, a, T, s);
-      else launch_qknorm_vec<S, G, 2, false, kStoreDevice>(q, gq, k, gk, pos, inv_freq, a, T, s);
-    } else {
-      if (rot) launch_qknorm_vec<S, G, 1, true, kStoreDevice>(q, gq, k, gk, pos, inv_freq, a, T, s);
-      else launch_qknorm_vec<S, G, 1, false, kStoreDevice>(q, gq, k, gk, pos, inv_freq, a, T, s);
-    }
+  if (u == 4) {
+    if (rot) launch_qknorm_vec<S, G, 4, true, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    else launch_qknorm_vec<S, G, 4, false, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
+  } else if (u == 2) {
+    if (rot) launch_qknorm_vec<S, G, 2, true, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    else launch_qknorm_vec<S, G, 2, false, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
   } else {
-    if (u == 4) {
-      if (rot) launch_qknorm_vec<S, G, 4, true, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
-      else launch_qknorm_vec<S, G, 4, false, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
-    } else if (u == 2) {
-      if (rot) launch_qknorm_vec<S, G, 2, true, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
-      else launch_qknorm_vec<S, G, 2, false, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
-    } else {
-      if (rot) launch_qknorm_vec<S, G, 1, true, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
-      else launch_qknorm_vec<S, G, 1, false, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
-    }
+    if (rot) launch_qknorm_vec<S, G, 1, true, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    else launch_qknorm_vec<S, G, 1, false, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
   }
 }
 
