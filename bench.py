@@ -446,16 +446,12 @@ def time_ops(ops, stream, launches, ceiling=None, cases=None):
 # Plain streams the kernels are measured against: (name, operand bytes,
 # reads, writes, device-scope stores, persistent-grid workgroups (0: one
 # per tile), in place).  Each op is compared with the stream of its own
-# shape and store policy (the policy its kernel picks at that output size:
-# device scope up to 128 MiB written per launch for RoPE and up to 64 MiB
-# for add, SiLU-mul and GeGLU; non-temporal otherwise, and at every size for
-# the norms, the gather and the fused RMSNorm+RoPE).
+# shape, with non-temporal stores as the kernels use.
 #   large hidden (T = 8192): fused add+RMSNorm reads and writes back x and
 #     the residual, 128 MiB each; RoPE q and k, 144 MiB, in place; SiLU-mul
 #     operands 448 MiB.
 #   prefill (T = 4096): [4096, 4096] bf16 operands of 32 MiB; q and k of the
-#     RoPE 40 MiB in place (device scope for RoPE, non-temporal for the fused
-#     RMSNorm+RoPE); SiLU-mul operands 112 MiB.
+#     RoPE 40 MiB in place; SiLU-mul operands 112 MiB.
 #   decode: the logits [256, 128256] f32 (125 MiB) argmax reads.
 #   partial RoPE: q [16384, 16, 128] f32 (128 MiB) the fused RMSNorm+RoPE
 #     rewrites in place.
@@ -471,9 +467,8 @@ CEILING_CASES = [
     ("inplace_144MiB", 8192 * 72 * 128 * 2, 1, 1, 0, 0, True),
     ("2R1W_448MiB", 8192 * 28672 * 2, 2, 1, 0, 0, False),
     ("1R1W_32MiB", 32 * MIB, 1, 1, 0, 0, False),
-    ("2R1W_32MiB_dev", 32 * MIB, 2, 1, 1, 0, False),
+    ("2R1W_32MiB", 32 * MIB, 2, 1, 0, 0, False),
     ("2R2W_32MiB", 32 * MIB, 2, 2, 0, 0, False),
-    ("inplace_40MiB_dev", 4096 * 40 * 128 * 2, 1, 1, 1, 0, True),
     ("inplace_40MiB", 4096 * 40 * 128 * 2, 1, 1, 0, 0, True),
     ("2R1W_112MiB", 4096 * 14336 * 2, 2, 1, 0, 0, False),
     ("read_125MiB", 256 * 128256 * 4, 1, 0, 0, 0, False),
@@ -491,13 +486,13 @@ MEMCPY_CASES = [("memcpy_32MiB", 32 * MIB), ("memcpy_64MiB", 64 * MIB)]
 OP_CEILING = {
     "w5": {"add_rmsnorm": "inplace_2R2W_128MiB", "rope": "inplace_144MiB",
            "rmsnorm_rope": "inplace_144MiB", "silu_mul": "2R1W_448MiB"},
-    "w2": {"rmsnorm": "1R1W_32MiB", "embedding": "1R1W_32MiB", "add": "2R1W_32MiB_dev",
-           "add_rmsnorm": "2R2W_32MiB", "rope": "inplace_40MiB_dev",
+    "w2": {"rmsnorm": "1R1W_32MiB", "embedding": "1R1W_32MiB", "add": "2R1W_32MiB",
+           "add_rmsnorm": "2R2W_32MiB", "rope": "inplace_40MiB",
            "rmsnorm_rope": "inplace_40MiB", "silu_mul": "2R1W_112MiB"},
     "w3": {"argmax": "read_125MiB"},
     "w4": {"rmsnorm_rope": "inplace_128MiB"},
     "next": {"softmax": "1R1W_125MiB", "layernorm": "1R1W_32MiB", "geglu_erf": "2R1W_112MiB",
-             "geglu_tanh": "2R1W_112MiB", "rope_cached": "inplace_40MiB_dev",
+             "geglu_tanh": "2R1W_112MiB", "rope_cached": "inplace_40MiB",
              "rope_multi": "inplace_225MiB"},
 }
 

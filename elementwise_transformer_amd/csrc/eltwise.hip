@@ -186,7 +186,7 @@ __device__ inline float apply(float a, float b) {
   }
 }
 
-template <typename S, int OP, int POL>
+template <typename S, int OP>
 __global__ __launch_bounds__(kBlock) void eltwise_vec(const S* a, const S* b, S* y, int64_t nvec,
                                                       int64_t n) {
   using E = Elem<S>;
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kBlock) void eltwise_vec(const S* a, const S* b, S*
       float o[V];
 #pragma unroll
       for (int e = 0; e < V; ++e) o[e] = apply<S, OP>(E::get(av[u], e), E::get(bv[u], e));
-      if (j < nvec) st16_buf<POL>(ry, static_cast<int>((j - vbase) * 16), E::pack(o));
+      if (j < nvec) st16_buf(ry, static_cast<int>((j - vbase) * 16), E::pack(o));
     }
   }
   // Tail: fewer than V elements after the last whole vector.
@@ -257,19 +257,14 @@ et_status eltwise_entry(const S* a, const S* b, S* y, int64_t n, void* stream) {
     // a vector boundary, only the last one has a tail.
     const int64_t per_launch = kMaxGrid * kBlock * kU;  // vectors
     const int64_t nvec_all = n / V;
-    const int pol = store_policy(bytes, kEltDeviceStoreMaxBytes);
     for (int64_t v0 = 0;; v0 += per_launch) {
       const int64_t nvec = nvec_all - v0 < per_launch ? nvec_all - v0 : per_launch;
       const bool last = v0 + nvec >= nvec_all;
       const int64_t elems = last ? n - v0 * V : nvec * V;
       const int64_t blocks = nvec > 0 ? (nvec + kBlock * kU - 1) / (kBlock * kU) : 1;
       const int64_t off = v0 * V;
-      if (pol == kStoreDevice)
-        eltwise_vec<S, OP, kStoreDevice><<<static_cast<unsigned>(blocks), kBlock, 0, s>>>(
-            a + off, b + off, y + off, nvec, elems);
-      else
-        eltwise_vec<S, OP, kStoreStream><<<static_cast<unsigned>(blocks), kBlock, 0, s>>>(
-            a + off, b + off, y + off, nvec, elems);
+      eltwise_vec<S, OP><<<static_cast<unsigned>(blocks), kBlock, 0, s>>>(a + off, b + off,
+                                                                        y + off, nvec, elems);
       if (last) break;
     }
   } else {

@@ -165,23 +165,19 @@ __device__ inline u32x4 ld16_keep(const S* p, int64_t elem) {
   return *reinterpret_cast<const u32x4*>(p + elem);
 }
 
-// Output stores through a buffer resource, which carries the cache-policy
-// bits a plain pointer store cannot:
-//   kStoreStream (nt): non-temporal, the store streams to HBM.
-//   kStoreDevice (sc1): device-scope write-through; the line leaves this
-//     XCD's L2 at once, and the 256 MB Infinity Cache writes it back to HBM
-//     behind later work.  That helps while the output is small next to the
-//     cache.  Measured on MI355X over buffers rotated past the cache,
-//     back-to-back launches: in-place RoPE writing 42 MB and 67 MB, 17.9 and
-//     25.5 us against 18.3 and 25.9 with non-temporal stores; an add writing
-//     34 MB, 18.9 against 20.0 us; but a SiLU-mul writing 117 MB, 60.5
-//     against 58.8 us (the whole prefill step the same either way), and the
-//     fused RMSNorm+RoPE writing 42 MB, 19.76 against 19.30 us, with the
-//     write-back it left slowing the kernel after it.
-// The host picks the policy from the output size (store_policy below), the
-// elementwise kernels with a lower limit than RoPE; the norms, the gather
-// and the fused RMSNorm+RoPE store non-temporally at every size.
-enum StorePolicy : int { kStoreStream = 2, kStoreDevice = 16 };
+// Output stores go through a buffer resource with the non-temporal bit set
+// (cache policy nt = 2), so the line streams to HBM.  Device-scope
+// write-through (sc1), which leaves the line in the 256 MB Infinity Cache to
+// be written back behind later work, was used for outputs up to 64-128 MB
+// and dropped: it made those kernels faster when timed alone over buffers
+// rotated past the cache (an add writing 34 MB, 18.9 against 20.0 us;
+// in-place RoPE writing 42 MB, 17.9 against 18.3 us) because each launch
+// left part of its write-back to the next, and the kernels after it paid
+// for that.  The whole prefill step (eight kernels, three interleaved
+// rounds of 200 steps) ran 0.1621-0.1625 ms with non-temporal stores
+// everywhere against 0.1637-0.1638 ms with device scope for add, SiLU-mul,
+// GeGLU and RoPE.
+constexpr int kStoreNT = 2;
 
 // A resource for `bytes` bytes from `base` (a uniform pointer); stores at
 // byte offsets beyond min(bytes, 2^31 - 1) are dropped by the hardware.
@@ -192,9 +188,8 @@ __device__ inline __amdgpu_buffer_rsrc_t out_rsrc(const void* base, int64_t byte
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-template <int POL>
 __device__ inline void st16_buf(__amdgpu_buffer_rsrc_t r, int byte_off, const u32x4& v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, byte_off, 0, POL);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, byte_off, 0, kStoreNT);
 }
 
 // -------------------------------------------------------- wave reductions
@@ -287,13 +282,5 @@ inline et_status launch_status() {
 
 // Largest grid.x the launchers use per launch; longer work is split.
 constexpr int64_t kMaxGrid = int64_t{1} << 30;
-
-// Device-scope stores while a launch writes at most max_dev bytes, else
-// non-temporal ones (see StorePolicy).
-constexpr int64_t kDeviceStoreMaxBytes = int64_t{128} << 20;
-constexpr int64_t kEltDeviceStoreMaxBytes = int64_t{64} << 20;  // add, SiLU-mul, GeGLU
-inline int store_policy(int64_t out_bytes, int64_t max_dev = kDeviceStoreMaxBytes) {
-  return out_bytes <= max_dev ? kStoreDevice : kStoreStream;
-}
 
 }  // namespace et

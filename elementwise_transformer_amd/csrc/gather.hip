@@ -16,7 +16,7 @@ namespace {
 constexpr int kBlock = 64;  // one wave per workgroup
 constexpr int kU = 8;       // vectors per lane
 
-template <typename S, bool VEC, int POL>
+template <typename S, bool VEC>
 __global__ __launch_bounds__(kBlock) void embedding_kernel(const S* __restrict__ table,
                                                            int64_t vocab,
                                                            const int32_t* __restrict__ ids,
@@ -46,14 +46,14 @@ __global__ __launch_bounds__(kBlock) void embedding_kernel(const S* __restrict__
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int j = first + u * kBlock;
-        if (j < nvec) st16_buf<POL>(ro, (threadIdx.x + u * kBlock) * 16, r[u]);
+        if (j < nvec) st16_buf(ro, (threadIdx.x + u * kBlock) * 16, r[u]);
       }
     } else {
       const u32x4 nan = u32x4{E::kQuietNaN, E::kQuietNaN, E::kQuietNaN, E::kQuietNaN};
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int j = first + u * kBlock;
-        if (j < nvec) st16_buf<POL>(ro, (threadIdx.x + u * kBlock) * 16, nan);
+        if (j < nvec) st16_buf(ro, (threadIdx.x + u * kBlock) * 16, nan);
       }
     }
   } else {
@@ -103,13 +103,11 @@ et_status embedding_entry(const S* table, int64_t vocab, const int32_t* ids, S* 
   for (int64_t t0 = 0; t0 < n; t0 += rows_per_launch) {
     const int64_t m = n - t0 < rows_per_launch ? n - t0 : rows_per_launch;
     const unsigned grid = static_cast<unsigned>(m * cpr);
-    // Non-temporal stores at every size: device-scope ones (see
-    // StorePolicy) made the measured eight-op step slower here.
     if (vec)
-      embedding_kernel<S, true, kStoreStream><<<grid, kBlock, 0, s>>>(
+      embedding_kernel<S, true><<<grid, kBlock, 0, s>>>(
           table, vocab, ids + t0, out + t0 * d, static_cast<int>(d), static_cast<int>(cpr));
     else
-      embedding_kernel<S, false, kStoreStream><<<grid, kBlock, 0, s>>>(
+      embedding_kernel<S, false><<<grid, kBlock, 0, s>>>(
           table, vocab, ids + t0, out + t0 * d, static_cast<int>(d), static_cast<int>(cpr));
   }
   return launch_status();

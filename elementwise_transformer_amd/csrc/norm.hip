@@ -35,7 +35,7 @@ __device__ inline float inv_rms(float ss, int d, float eps) {
 // __restrict__: y may be x and h may be res (in place).  Every load of a
 // thread is issued before its first store, and a thread touches only the
 // elements it owns.
-template <typename S, int TPR, int VPT, bool FUSED, bool VEC, int POL>
+template <typename S, int TPR, int VPT, bool FUSED, bool VEC>
 __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
     const S* x, const S* res, const S* __restrict__ w, S* y, S* h, int64_t rows, int d,
     float eps) {
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
         for (int e = 0; e < V; ++e) a[e] = E::get(xr[k], e) + E::get(rr[k], e);
         xr[k] = E::pack(a);  // h rounded to storage, normalised as stored
         if (live && j < nvec)
-          st16_buf<POL>(out_rsrc(h + row0 * d, span), (rel + j * V) * int(sizeof(S)), xr[k]);
+          st16_buf(out_rsrc(h + row0 * d, span), (rel + j * V) * int(sizeof(S)), xr[k]);
       }
     }
   } else {
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(NormShape<TPR>::kBlock) void rmsnorm_rows(
 #pragma unroll
       for (int e = 0; e < V; ++e) o[e] = E::get(xr[k], e) * inv * E::get(wr[k], e);
       if (j < nvec)
-        st16_buf<POL>(out_rsrc(y + row0 * d, span), (rel + j * V) * int(sizeof(S)), E::pack(o));
+        st16_buf(out_rsrc(y + row0 * d, span), (rel + j * V) * int(sizeof(S)), E::pack(o));
     }
   } else {
 #pragma unroll
@@ -237,16 +237,13 @@ __global__ __launch_bounds__(kLargeTPR) void rmsnorm_rows_large(
 template <typename S, int TPR, int VPT, bool FUSED, bool VEC>
 void launch_rows(const S* x, const S* res, const S* w, S* y, S* h, int64_t rows, int d, float eps,
                  hipStream_t s) {
-  // Non-temporal stores at every size: device-scope ones here (see
-  // StorePolicy) made the measured eight-op step 10 % slower, the cache's
-  // write-backs of the norm outputs competing with the next kernels' reads.
   using Sh = NormShape<TPR>;
   for (int64_t r0 = 0; r0 < rows; r0 += kMaxGrid * Sh::kRowsPerBlock) {
     const int64_t n = rows - r0 < kMaxGrid * Sh::kRowsPerBlock ? rows - r0
                                                                 : kMaxGrid * Sh::kRowsPerBlock;
     const int64_t off = r0 * d;
     const unsigned grid = static_cast<unsigned>((n + Sh::kRowsPerBlock - 1) / Sh::kRowsPerBlock);
-    rmsnorm_rows<S, TPR, VPT, FUSED, VEC, kStoreStream><<<grid, Sh::kBlock, 0, s>>>(
+    rmsnorm_rows<S, TPR, VPT, FUSED, VEC><<<grid, Sh::kBlock, 0, s>>>(
         x + off, FUSED ? res + off : nullptr, w, y + off, FUSED ? h + off : nullptr, n, d, eps);
   }
 }

@@ -35,12 +35,9 @@ namespace {
 constexpr int kBlock = 256;
 constexpr int kMaxTableBytes = 48 * 1024;
 // Slots per lane of the RoPE kernel (plain and cached angles): at most
-// kRopeUMax with non-temporal stores, kRopeUMaxDev with device-scope ones
-// (one slot per lane was 6 % faster there inside a prefill layer, and slower
-// with non-temporal stores at 144 MiB).  Head rows per lane group of the
-// fused RMSNorm + RoPE: at most kQkUMax.
+// kRopeUMax (one slot per lane was slower at 144 MiB).  Head rows per lane
+// group of the fused RMSNorm + RoPE: at most kQkUMax.
 constexpr int kRopeUMax = 2;
-constexpr int kRopeUMaxDev = 1;
 constexpr int kQkUMax = 2;
 
 struct RopeArgs {
@@ -235,7 +232,7 @@ __device__ inline uint32_t rope_slot(uint32_t base, int tid, int u) {
 // q rows (t * Hq + h) and the k rows (t * Hk + h - Hq) among them, so every
 // offset is below (head rows per workgroup) * D elements; the host keeps that
 // below 2^31 bytes.
-template <typename S, int POL>
+template <typename S>
 struct QkOut {
   __amdgpu_buffer_rsrc_t rq, rk;
   int64_t qrow0, krow0;
@@ -267,16 +264,16 @@ struct QkOut {
     const int off = elem * static_cast<int>(sizeof(S));
     const unsigned long long lanes = __ballot(1), qlanes = __ballot(isq);
     if (qlanes == lanes) {
-      st16_buf<POL>(rq, off, v);
+      st16_buf(rq, off, v);
     } else if (qlanes == 0) {
-      st16_buf<POL>(rk, off, v);
+      st16_buf(rk, off, v);
     } else {
       st16(p, 0, v);
     }
   }
 };
 
-template <typename S, int PS, int U, int POL>
+template <typename S, int PS, int U>
 __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32_t* __restrict__ pos,
                                                         const float* __restrict__ inv_freq,
                                                         RopeArgs a) {
@@ -288,7 +285,7 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32
   if (last >= a.total) last = a.total - 1;
   const int ntok = static_cast<int>(fdiv(last, a.fd_spt) - t0 + 1);
   const TabIn tin = table_inputs(t0, ntok, a, pos, inv_freq);
-  const QkOut<S, POL> out(q, k, t0, static_cast<int>(fdiv(base - t0 * a.spt, a.fd_sph)), a);
+  const QkOut<S> out(q, k, t0, static_cast<int>(fdiv(base - t0 * a.spt, a.fd_sph)), a);
 
   // Phase 1: issue every load of this thread.
   S* rowp[U];
@@ -379,7 +376,7 @@ struct QkNormArgs {
 // vector rotates (pairs inside it) if it lies below r.  Half layout: lanes
 // kk < rsl own the partners A = kk*V, B = kk*V + r/2; the other lanes own
 // tail vectors r + m*V and r + (nt + m)*V (m = kk - rsl, nt = G - rsl).
-template <typename S, int G, int U, bool ROT, int POL>
+template <typename S, int G, int U, bool ROT>
 __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __restrict__ gq, S* k,
                                                              const S* __restrict__ gk,
                                                              const int32_t* __restrict__ pos,
@@ -430,7 +427,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
     a_rot = b_rot = false;
   }
 
-  const QkOut<S, POL> out(q, k, t0, static_cast<int>(base - t0 * heads), ra);
+  const QkOut<S> out(q, k, t0, static_cast<int>(base - t0 * heads), ra);
   // The two gains (2G vectors each) go through LDS: thread t < 4G fetches
   // vector t % 2G of gq (t < 2G) or gk, before the row loads so that its
   // LDS write waits for nothing else.  (gk is gq when there are no key
@@ -614,7 +611,7 @@ RopeArgs make_args(int64_t T, int64_t hq, int64_t hk, int64_t D, int64_t r, floa
   return a;
 }
 
-template <typename S, int PS, int U, int POL>
+template <typename S, int PS, int U>
 void launch_rope(S* q, S* k, const int32_t* pos, const float* inv_freq, RopeArgs a, int64_t T,
                  hipStream_t s) {
   // Tokens per launch keep slot indices below 2^31.
@@ -626,12 +623,12 @@ void launch_rope(S* q, S* k, const int32_t* pos, const float* inv_freq, RopeArgs
     a.T = m;
     a.total = static_cast<uint32_t>(m * a.spt);
     const unsigned grid = (a.total + kBlock * U - 1) / (kBlock * U);
-    rope_qk_kernel<S, PS, U, POL><<<grid, kBlock, shmem, s>>>(
+    rope_qk_kernel<S, PS, U><<<grid, kBlock, shmem, s>>>(
         q + t0 * a.hq * a.D, a.hk ? k + t0 * a.hk * a.D : k, pos + t0, inv_freq, a);
   }
 }
 
-// Largest unroll (4, 2, 1) whose angle table fits the LDS budget.
+// Largest unroll (umax, umax / 2, ..., 1) whose angle table fits the LDS budget.
 inline int pick_u(int64_t spt, int64_t half, int64_t per_u, int umax) {
   for (int u = umax; u >= 1; u >>= 1) {
     const int64_t ntok = (per_u * u + spt - 1) / spt + 1;
@@ -673,8 +670,7 @@ et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int
   bool vec = (r % (2 * V)) == 0 && (D % V) == 0 && aligned16(q) && (hk == 0 || aligned16(k));
   RopeArgs a = make_args(T, hq, hk, D, r, mu, layout, vec ? V : 1);
   if (a.spt > (1u << 30)) return ET_ERR_BAD_SIZE;
-  const bool dev = store_policy(T * (hq + hk) * r * int64_t(sizeof(S))) == kStoreDevice;
-  int u = pick_u(a.spt, a.half, kBlock, vec && dev ? kRopeUMaxDev : kRopeUMax);
+  int u = pick_u(a.spt, a.half, kBlock, kRopeUMax);
   if (u == 0) return ET_ERR_BAD_SIZE;
   auto set_cache = [&](RopeArgs& ra) {
     if (!cache) return;
@@ -698,23 +694,17 @@ et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int
     }
   }
   (void)hipGetLastError();
-  if (vec && dev) {
-    if (u == 4) launch_rope<S, V, 4, kStoreDevice>(q, k, pos, inv_freq, a, T, s);
-    else if (u == 2) launch_rope<S, V, 2, kStoreDevice>(q, k, pos, inv_freq, a, T, s);
-    else launch_rope<S, V, 1, kStoreDevice>(q, k, pos, inv_freq, a, T, s);
-  } else if (vec) {
-    if (u == 4) launch_rope<S, V, 4, kStoreStream>(q, k, pos, inv_freq, a, T, s);
-    else if (u == 2) launch_rope<S, V, 2, kStoreStream>(q, k, pos, inv_freq, a, T, s);
-    else launch_rope<S, V, 1, kStoreStream>(q, k, pos, inv_freq, a, T, s);
+  if (vec) {
+    if (u == 2) launch_rope<S, V, 2>(q, k, pos, inv_freq, a, T, s);
+    else launch_rope<S, V, 1>(q, k, pos, inv_freq, a, T, s);
   } else {
-    if (u == 4) launch_rope<S, 1, 4, kStoreStream>(q, k, pos, inv_freq, a, T, s);
-    else if (u == 2) launch_rope<S, 1, 2, kStoreStream>(q, k, pos, inv_freq, a, T, s);
-    else launch_rope<S, 1, 1, kStoreStream>(q, k, pos, inv_freq, a, T, s);
+    if (u == 2) launch_rope<S, 1, 2>(q, k, pos, inv_freq, a, T, s);
+    else launch_rope<S, 1, 1>(q, k, pos, inv_freq, a, T, s);
   }
   return launch_status();
 }
 
-template <typename S, int G, int U, bool ROT, int POL>
+template <typename S, int G, int U, bool ROT>
 void launch_qknorm_vec(S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
                        const float* inv_freq, QkNormArgs a, int64_t T, hipStream_t s) {
   constexpr int kRowsPerPass = kBlock / G;
@@ -728,30 +718,22 @@ void launch_qknorm_vec(S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
     a.rows = static_cast<uint32_t>(m * heads);
     a.rope.T = m;
     const unsigned grid = static_cast<unsigned>((a.rows + rows_per_block - 1) / rows_per_block);
-    rmsnorm_rope_kernel<S, G, U, ROT, POL><<<grid, kBlock, shmem, s>>>(
+    rmsnorm_rope_kernel<S, G, U, ROT><<<grid, kBlock, shmem, s>>>(
         q + t0 * a.rope.hq * a.rope.D, gq, a.rope.hk ? k + t0 * a.rope.hk * a.rope.D : k, gk,
         pos + t0, inv_freq, a);
   }
 }
 
-// The fused kernel stores non-temporally at every size: device-scope stores
-// made it slower on its own at the prefill size (in place 42 MB, 19.76 us
-// against 19.30 over buffers rotated past the Infinity Cache) and handed
-// their write-back to the next kernel (the plain RoPE launched after it,
-// 17.94 us against 17.61).
 template <typename S, int G>
 void launch_qknorm_vec_u(int u, S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
                          const float* inv_freq, QkNormArgs a, int64_t T, hipStream_t s) {
   const bool rot = a.rope.half > 0;
-  if (u == 4) {
-    if (rot) launch_qknorm_vec<S, G, 4, true, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
-    else launch_qknorm_vec<S, G, 4, false, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
-  } else if (u == 2) {
-    if (rot) launch_qknorm_vec<S, G, 2, true, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
-    else launch_qknorm_vec<S, G, 2, false, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
+  if (u == 2) {
+    if (rot) launch_qknorm_vec<S, G, 2, true>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    else launch_qknorm_vec<S, G, 2, false>(q, gq, k, gk, pos, inv_freq, a, T, s);
   } else {
-    if (rot) launch_qknorm_vec<S, G, 1, true, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
-    else launch_qknorm_vec<S, G, 1, false, kStoreStream>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    if (rot) launch_qknorm_vec<S, G, 1, true>(q, gq, k, gk, pos, inv_freq, a, T, s);
+    else launch_qknorm_vec<S, G, 1, false>(q, gq, k, gk, pos, inv_freq, a, T, s);
   }
 }
 
@@ -1062,7 +1044,7 @@ __device__ inline float partner_of(const Partners<S, PS>& r, int e) {
   }
 }
 
-template <typename S, int PS, int U, int POL>
+template <typename S, int PS, int U>
 __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
                                                            const int32_t* __restrict__ pos,
                                                            const float* __restrict__ inv_freq,
@@ -1097,7 +1079,7 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
   }
 
   // Phase 1: every row load of this thread.
-  const QkOut<S, POL> out(q, k, t0, static_cast<int>(row0 - t0 * a.heads), a.ra);
+  const QkOut<S> out(q, k, t0, static_cast<int>(row0 - t0 * a.heads), a.ra);
   int sl[U], cv[U], tl[U], rel[U];
   bool isq[U];
   S* rowp[U];
@@ -1278,7 +1260,7 @@ inline bool runs_fit(const int64_t* dims, int64_t A, int layout, int ps) {
   return true;
 }
 
-template <typename S, int PS, int POL>
+template <typename S, int PS>
 void launch_multi(S* q, S* k, const int32_t* pos, const float* inv_freq, MultiArgs a, int64_t T,
                   size_t shmem, hipStream_t s) {
   const int64_t tok_per_launch = (int64_t{1} << 30) / a.heads;
@@ -1287,7 +1269,7 @@ void launch_multi(S* q, S* k, const int32_t* pos, const float* inv_freq, MultiAr
     a.ra.T = m;
     a.rows = static_cast<uint32_t>(m * a.heads);
     const unsigned grid = (a.rows + a.rpb - 1) / a.rpb;
-    rope_multi_kernel<S, PS, kMultiU, POL><<<grid, kBlock, shmem, s>>>(
+    rope_multi_kernel<S, PS, kMultiU><<<grid, kBlock, shmem, s>>>(
         q + t0 * a.ra.hq * a.ra.D, a.ra.hk ? k + t0 * a.ra.hk * a.ra.D : k, pos + t0 * a.A,
         inv_freq, a);
   }
@@ -1348,12 +1330,10 @@ et_status rope_multi_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* po
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (vec && store_policy(T * (hq + hk) * span * int64_t(sizeof(S))) == kStoreDevice)
-    launch_multi<S, V, kStoreDevice>(q, k, pos, inv_freq, a, T, shmem, s);
-  else if (vec)
-    launch_multi<S, V, kStoreStream>(q, k, pos, inv_freq, a, T, shmem, s);
+  if (vec)
+    launch_multi<S, V>(q, k, pos, inv_freq, a, T, shmem, s);
   else
-    launch_multi<S, 1, kStoreStream>(q, k, pos, inv_freq, a, T, shmem, s);
+    launch_multi<S, 1>(q, k, pos, inv_freq, a, T, shmem, s);
   return launch_status();
 }
 
