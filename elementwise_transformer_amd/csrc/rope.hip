@@ -34,10 +34,14 @@ namespace {
 
 constexpr int kBlock = 256;
 constexpr int kMaxTableBytes = 48 * 1024;
-// Slots per lane of the RoPE kernel (plain and cached angles): at most
-// kRopeUMax (one slot per lane was slower at 144 MiB).  Head rows per lane
-// group of the fused RMSNorm + RoPE: at most kQkUMax.
-constexpr int kRopeUMax = 2;
+// Slots per lane of the RoPE kernel (plain and cached angles): one.  With
+// non-temporal stores one slot per lane ran faster than two at every size
+// measured (in-place q and k writing 42, 67 and 151 MB: 17.59 against 18.45
+// us, 25.62 against 26.02, 50.35 against 51.27; four interleaved rounds over
+// buffers rotated past the Infinity Cache), and the prefill step 0.1612
+// against 0.1619 ms.  Head rows per lane group of the fused RMSNorm + RoPE:
+// at most kQkUMax.
+constexpr int kRopeU = 1;
 constexpr int kQkUMax = 2;
 
 struct RopeArgs {
@@ -670,7 +674,7 @@ et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int
   bool vec = (r % (2 * V)) == 0 && (D % V) == 0 && aligned16(q) && (hk == 0 || aligned16(k));
   RopeArgs a = make_args(T, hq, hk, D, r, mu, layout, vec ? V : 1);
   if (a.spt > (1u << 30)) return ET_ERR_BAD_SIZE;
-  int u = pick_u(a.spt, a.half, kBlock, kRopeUMax);
+  const int u = pick_u(a.spt, a.half, kBlock, kRopeU);
   if (u == 0) return ET_ERR_BAD_SIZE;
   auto set_cache = [&](RopeArgs& ra) {
     if (!cache) return;
@@ -689,18 +693,14 @@ et_status rope_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* pos, int
       a = make_args(T, hq, hk, D, r, mu, layout, 1);
       set_cache(a);
       if (a.spt > (1u << 30)) return ET_ERR_BAD_SIZE;
-      u = pick_u(a.spt, a.half, kBlock, kRopeUMax);
-      if (u == 0) return ET_ERR_BAD_SIZE;
+      if (pick_u(a.spt, a.half, kBlock, kRopeU) == 0) return ET_ERR_BAD_SIZE;
     }
   }
   (void)hipGetLastError();
-  if (vec) {
-    if (u == 2) launch_rope<S, V, 2>(q, k, pos, inv_freq, a, T, s);
-    else launch_rope<S, V, 1>(q, k, pos, inv_freq, a, T, s);
-  } else {
-    if (u == 2) launch_rope<S, 1, 2>(q, k, pos, inv_freq, a, T, s);
-    else launch_rope<S, 1, 1>(q, k, pos, inv_freq, a, T, s);
-  }
+  if (vec)
+    launch_rope<S, V, kRopeU>(q, k, pos, inv_freq, a, T, s);
+  else
+    launch_rope<S, 1, kRopeU>(q, k, pos, inv_freq, a, T, s);
   return launch_status();
 }
 
