@@ -9,8 +9,8 @@
 // would overstate the ceiling) and a pure read still has a data-dependent
 // store the compiler cannot drop.  The access pattern is the library's:
 // 16-byte buffer loads with the non-temporal cache policy and stores with
-// either the non-temporal or the device-scope one (the two policies the
-// library's kernels choose between), 256 threads per workgroup, each wave
+// the non-temporal one (the library's) or, as a yardstick, the device-scope
+// one, 256 threads per workgroup, each wave
 // owning 64 * U consecutive vectors (U = 4 or 8 per lane), every load index
 // clamped below the vector count and every store guarded by it.
 //
