@@ -40,9 +40,10 @@ constexpr int kMaxTableBytes = 48 * 1024;
 // us, 25.62 against 26.02, 50.35 against 51.27; four interleaved rounds over
 // buffers rotated past the Infinity Cache), and the prefill step 0.1612
 // against 0.1619 ms.  Head rows per lane group of the fused RMSNorm + RoPE:
-// at most kQkUMax.
+// one, likewise (42, 134 and 151 MB in place: 18.35 against 19.16 us, 44.82
+// against 45.31, 50.79 against 51.99).
 constexpr int kRopeU = 1;
-constexpr int kQkUMax = 2;
+constexpr int kQkU = 1;
 
 struct RopeArgs {
   int64_t T;
@@ -725,16 +726,12 @@ void launch_qknorm_vec(S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
 }
 
 template <typename S, int G>
-void launch_qknorm_vec_u(int u, S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
-                         const float* inv_freq, QkNormArgs a, int64_t T, hipStream_t s) {
-  const bool rot = a.rope.half > 0;
-  if (u == 2) {
-    if (rot) launch_qknorm_vec<S, G, 2, true>(q, gq, k, gk, pos, inv_freq, a, T, s);
-    else launch_qknorm_vec<S, G, 2, false>(q, gq, k, gk, pos, inv_freq, a, T, s);
-  } else {
-    if (rot) launch_qknorm_vec<S, G, 1, true>(q, gq, k, gk, pos, inv_freq, a, T, s);
-    else launch_qknorm_vec<S, G, 1, false>(q, gq, k, gk, pos, inv_freq, a, T, s);
-  }
+void launch_qknorm_vec_rot(S* q, const S* gq, S* k, const S* gk, const int32_t* pos,
+                           const float* inv_freq, QkNormArgs a, int64_t T, hipStream_t s) {
+  if (a.rope.half > 0)
+    launch_qknorm_vec<S, G, kQkU, true>(q, gq, k, gk, pos, inv_freq, a, T, s);
+  else
+    launch_qknorm_vec<S, G, kQkU, false>(q, gq, k, gk, pos, inv_freq, a, T, s);
 }
 
 template <typename S>
@@ -768,17 +765,16 @@ et_status qknorm_entry(S* q, const S* gq, int64_t hq, S* k, const S* gk, int64_t
   if (vec) {
     a.rope = make_args(T, hq, hk, D, r, mu, layout, V);
     a.rsl = static_cast<int>(r / (2 * V));
-    const int u = pick_u(heads, a.rope.half, kBlock / g, kQkUMax);
-    if (u == 0) return ET_ERR_BAD_SIZE;
+    if (pick_u(heads, a.rope.half, kBlock / g, kQkU) == 0) return ET_ERR_BAD_SIZE;
     const S* gkk = hk > 0 ? gk : gq;
     switch (g) {
-      case 1: launch_qknorm_vec_u<S, 1>(u, q, gq, k, gkk, pos, inv_freq, a, T, s); break;
-      case 2: launch_qknorm_vec_u<S, 2>(u, q, gq, k, gkk, pos, inv_freq, a, T, s); break;
-      case 4: launch_qknorm_vec_u<S, 4>(u, q, gq, k, gkk, pos, inv_freq, a, T, s); break;
-      case 8: launch_qknorm_vec_u<S, 8>(u, q, gq, k, gkk, pos, inv_freq, a, T, s); break;
-      case 16: launch_qknorm_vec_u<S, 16>(u, q, gq, k, gkk, pos, inv_freq, a, T, s); break;
-      case 32: launch_qknorm_vec_u<S, 32>(u, q, gq, k, gkk, pos, inv_freq, a, T, s); break;
-      default: launch_qknorm_vec_u<S, 64>(u, q, gq, k, gkk, pos, inv_freq, a, T, s); break;
+      case 1: launch_qknorm_vec_rot<S, 1>(q, gq, k, gkk, pos, inv_freq, a, T, s); break;
+      case 2: launch_qknorm_vec_rot<S, 2>(q, gq, k, gkk, pos, inv_freq, a, T, s); break;
+      case 4: launch_qknorm_vec_rot<S, 4>(q, gq, k, gkk, pos, inv_freq, a, T, s); break;
+      case 8: launch_qknorm_vec_rot<S, 8>(q, gq, k, gkk, pos, inv_freq, a, T, s); break;
+      case 16: launch_qknorm_vec_rot<S, 16>(q, gq, k, gkk, pos, inv_freq, a, T, s); break;
+      case 32: launch_qknorm_vec_rot<S, 32>(q, gq, k, gkk, pos, inv_freq, a, T, s); break;
+      default: launch_qknorm_vec_rot<S, 64>(q, gq, k, gkk, pos, inv_freq, a, T, s); break;
     }
   } else {
     a.rope = make_args(T, hq, hk, D, r, mu, layout, 1);
