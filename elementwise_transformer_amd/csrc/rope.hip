@@ -871,6 +871,7 @@ struct MultiArgs {
   int nv;                   // vectors (or scalars) per head row: span / PS
   int ntok_max;             // tokens one workgroup can touch
   int heads;                // hq + hk
+  int perm;                 // half pairing with partners read across lanes (perm_fits)
   FastDiv fd_heads, fd_nv, fd_np;
   uint32_t d4_off, d1_off, xs_off;  // LDS byte offsets of the descriptors and the rows
 };
@@ -1040,7 +1041,7 @@ __device__ inline float partner_of(const Partners<S, PS>& r, int e) {
   }
 }
 
-template <typename S, int PS, int U>
+template <typename S, int PS, int U, bool PERM>
 __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
                                                            const int32_t* __restrict__ pos,
                                                            const float* __restrict__ inv_freq,
@@ -1123,7 +1124,7 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
   // Partners come from LDS for the half pairing, and on the scalar path for
   // both; interleaved partners of a vector sit in the vector itself.
   const bool via_lds = PS == 1 || a.ra.layout == ET_ROPE_HALF;
-  if (via_lds) {
+  if (via_lds && !PERM) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int s = static_cast<int>(rope_slot<U>(0, threadIdx.x, u));
@@ -1147,7 +1148,66 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
   // angles are kept until the token or column changes.  Both paths give the
   // same bits.
   const bool half = a.ra.layout == ET_ROPE_HALF;
-  if constexpr (PS > 1) {
+  if constexpr (PERM) {
+    {
+      // Partners across lanes, no LDS copy of the rows.  A head row's nv
+      // vectors sit in nv consecutive lanes (nv divides 64), and in every
+      // vector each 32-bit word holds entries of one run whose partner
+      // offset is a whole number of words (the host checks this layout).  The
+      // partners of word j of a vector are then one word of another lane of
+      // the row: word (j + off / EPD) mod 4 of the vector off / EPD words
+      // away.  Each lane first rotates its own words by the amount its
+      // readers need, (-off_own / EPD) mod 4 (the same for both of its runs,
+      // also checked), so a reader fetches word j of the rotated set from
+      // the source lane: four cross-lane reads per vector.  Every lane takes
+      // part in the reads; clamped slots only feed rows that are not stored.
+      constexpr int EPD = 4 / static_cast<int>(sizeof(S));   // entries per word
+      const int4 dd = d4s[cv[0]];
+      const int dd1 = d1s[cv[0]];
+      const int krp = dd1 & 0xFF;
+      const int c0 = cv[0] * PS;
+      const int offA = dd.x - c0, offB = dd.y - c0;
+      const int rot = ((-offA) / EPD) & 3;
+      const int rowlane = static_cast<int>(threadIdx.x % 64) - cv[0];
+      int addr[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int off = EPD * j < krp ? offA : offB;
+        addr[j] = (rowlane + (c0 + EPD * j + off) / PS) * 4;
+      }
+      float2 an[PS];
+      int cur = -1;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        u32x4 r = (rot & 1) ? v[u].yzwx : v[u];
+        r = (rot & 2) ? r.zwxy : r;
+        u32x4 pw;
+        pw.x = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr[0], static_cast<int>(r.x)));
+        pw.y = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr[1], static_cast<int>(r.y)));
+        pw.z = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr[2], static_cast<int>(r.z)));
+        pw.w = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr[3], static_cast<int>(r.w)));
+        const int s = static_cast<int>(rope_slot<U>(0, threadIdx.x, u));
+        if (s < nslot) {
+          if (tl[u] != cur) {
+            entry_angles<PS>(cs + tl[u] * a.np, dd, dd1, half, an);
+            cur = tl[u];
+          }
+          float y[PS];
+#pragma unroll
+          for (int e = 0; e < PS; ++e) {
+            const uint32_t w = pw[e / EPD];
+            float xp;
+            if constexpr (EPD == 2) xp = (e & 1) ? E::hi(w) : E::lo(w);
+            else xp = __uint_as_float(w);
+            y[e] = __builtin_fmaf(E::get(v[u], e), an[e].x, xp * an[e].y);
+          }
+          out.store(isq[u], rel[u] + cv[u] * PS, rowp[u] + cv[u] * PS, E::pack(y));
+        }
+      }
+      return;
+    }
+  }
+  if constexpr (PS > 1 && !PERM) {
     bool uni = static_cast<int>(rope_slot<U>(0, threadIdx.x, U - 1)) < nslot;
 #pragma unroll
     for (int u = 1; u < U; ++u) uni = uni && cv[u] == cv[0] && tl[u] == tl[0];
@@ -1256,7 +1316,41 @@ inline bool runs_fit(const int64_t* dims, int64_t A, int layout, int ps) {
   return true;
 }
 
-template <typename S, int PS>
+// Whether the half pairing can take its partners across lanes: a head row's
+// vectors fill whole groups of lanes (nv divides 64), every 32-bit word of a
+// vector holds entries of one run whose partner offset is a whole number of
+// words, and the rotation (-offset / words) mod 4 is the same for every run
+// of a vector (it is what the lanes reading that vector need).
+inline bool perm_fits(const int64_t* dims, int64_t A, int layout, int ps, int es) {
+  if (layout != ET_ROPE_HALF || ps <= 1) return false;
+  int64_t span = 0;
+  for (int64_t ax = 0; ax < A; ++ax) span += dims[ax];
+  const int64_t nv = span / ps;
+  if (nv <= 0 || 64 % nv != 0) return false;
+  const int epd = 4 / es;
+  std::vector<int64_t> off(static_cast<size_t>(span));
+  int64_t o = 0;
+  for (int64_t ax = 0; ax < A; ++ax) {
+    const int64_t hd = dims[ax] / 2;
+    for (int64_t l = 0; l < dims[ax]; ++l) off[static_cast<size_t>(o + l)] = l < hd ? hd : -hd;
+    o += dims[ax];
+  }
+  for (int64_t c0 = 0; c0 < span; c0 += ps) {
+    int rot = -1;
+    for (int64_t c = c0; c < c0 + ps; c += epd) {
+      const int64_t d = off[static_cast<size_t>(c)];
+      for (int e = 1; e < epd; ++e)
+        if (off[static_cast<size_t>(c + e)] != d) return false;
+      if (d % epd != 0) return false;
+      const int r = static_cast<int>((-d / epd) & 3);
+      if (rot >= 0 && r != rot) return false;
+      rot = r;
+    }
+  }
+  return true;
+}
+
+template <typename S, int PS, bool PERM>
 void launch_multi(S* q, S* k, const int32_t* pos, const float* inv_freq, MultiArgs a, int64_t T,
                   size_t shmem, hipStream_t s) {
   const int64_t tok_per_launch = (int64_t{1} << 30) / a.heads;
@@ -1265,7 +1359,7 @@ void launch_multi(S* q, S* k, const int32_t* pos, const float* inv_freq, MultiAr
     a.ra.T = m;
     a.rows = static_cast<uint32_t>(m * a.heads);
     const unsigned grid = (a.rows + a.rpb - 1) / a.rpb;
-    rope_multi_kernel<S, PS, kMultiU><<<grid, kBlock, shmem, s>>>(
+    rope_multi_kernel<S, PS, kMultiU, PERM><<<grid, kBlock, shmem, s>>>(
         q + t0 * a.ra.hq * a.ra.D, a.ra.hk ? k + t0 * a.ra.hk * a.ra.D : k, pos + t0 * a.A,
         inv_freq, a);
   }
@@ -1311,6 +1405,7 @@ et_status rope_multi_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* po
     if (ax < A) o += static_cast<int>(dims[ax]);
   }
   a.heads = static_cast<int>(hq + hk);
+  a.perm = vec && perm_fits(dims, A, layout, ps, static_cast<int>(sizeof(S))) ? 1 : 0;
   a.nv = a.span / ps;
   a.rpb = (kBlock * kMultiU) / a.nv;
   size_t shmem = 0;
@@ -1326,10 +1421,12 @@ et_status rope_multi_entry(S* q, int64_t hq, S* k, int64_t hk, const int32_t* po
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (vec)
-    launch_multi<S, V>(q, k, pos, inv_freq, a, T, shmem, s);
+  if (vec && a.perm)
+    launch_multi<S, V, true>(q, k, pos, inv_freq, a, T, shmem, s);
+  else if (vec)
+    launch_multi<S, V, false>(q, k, pos, inv_freq, a, T, shmem, s);
   else
-    launch_multi<S, 1>(q, k, pos, inv_freq, a, T, shmem, s);
+    launch_multi<S, 1, false>(q, k, pos, inv_freq, a, T, shmem, s);
   return launch_status();
 }
 
