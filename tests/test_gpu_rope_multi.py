@@ -62,6 +62,8 @@ CASES = [
     (1, 64, 8, 128, (16, 56, 56), 0, 1.0, 100),        # one token, many heads
     (33, 1, 0, 1024, (512, 256, 256), 0, 1.0, 5000),   # widest span, one head per token
     (5, 2, 3, 256, (2, 2, 2, 2, 2, 2, 2, 242), 1, 1.0, 7),  # eight axes
+    (6, 3, 2, 512, (128, 192, 192), 0, 1.0, 500),      # a 2-byte head row of 64 vectors: one wave
+    (9, 4, 1, 256, (64, 96, 96), 0, 1.0, 500),         # 32 vectors (2-byte), 64 (f32) per head row
 ]
 
 
