@@ -1149,63 +1149,61 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
   // same bits.
   const bool half = a.ra.layout == ET_ROPE_HALF;
   if constexpr (PERM) {
-    {
-      // Partners across lanes, no LDS copy of the rows.  A head row's nv
-      // vectors sit in nv consecutive lanes (nv divides 64), and in every
-      // vector each 32-bit word holds entries of one run whose partner
-      // offset is a whole number of words (the host checks this layout).  The
-      // partners of word j of a vector are then one word of another lane of
-      // the row: word (j + off / EPD) mod 4 of the vector off / EPD words
-      // away.  Each lane first rotates its own words by the amount its
-      // readers need, (-off_own / EPD) mod 4 (the same for both of its runs,
-      // also checked), so a reader fetches word j of the rotated set from
-      // the source lane: four cross-lane reads per vector.  Every lane takes
-      // part in the reads; clamped slots only feed rows that are not stored.
-      constexpr int EPD = 4 / static_cast<int>(sizeof(S));   // entries per word
-      const int4 dd = d4s[cv[0]];
-      const int dd1 = d1s[cv[0]];
-      const int krp = dd1 & 0xFF;
-      const int c0 = cv[0] * PS;
-      const int offA = dd.x - c0, offB = dd.y - c0;
-      const int rot = ((-offA) / EPD) & 3;
-      const int rowlane = static_cast<int>(threadIdx.x % 64) - cv[0];
-      int addr[4];
+    // Partners across lanes, no LDS copy of the rows.  A head row's nv
+    // vectors sit in nv consecutive lanes (nv divides 64), and in every
+    // vector each 32-bit word holds entries of one run whose partner
+    // offset is a whole number of words (the host checks this layout).  The
+    // partners of word j of a vector are then one word of another lane of
+    // the row: word (j + off / EPD) mod 4 of the vector off / EPD words
+    // away.  Each lane first rotates its own words by the amount its
+    // readers need, (-off_own / EPD) mod 4 (the same for both of its runs,
+    // also checked), so a reader fetches word j of the rotated set from
+    // the source lane: four cross-lane reads per vector.  Every lane takes
+    // part in the reads; clamped slots only feed rows that are not stored.
+    constexpr int EPD = 4 / static_cast<int>(sizeof(S));   // entries per word
+    const int4 dd = d4s[cv[0]];
+    const int dd1 = d1s[cv[0]];
+    const int krp = dd1 & 0xFF;
+    const int c0 = cv[0] * PS;
+    const int offA = dd.x - c0, offB = dd.y - c0;
+    const int rot = ((-offA) / EPD) & 3;
+    const int rowlane = static_cast<int>(threadIdx.x % 64) - cv[0];
+    int addr[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int off = EPD * j < krp ? offA : offB;
-        addr[j] = (rowlane + (c0 + EPD * j + off) / PS) * 4;
-      }
-      float2 an[PS];
-      int cur = -1;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        u32x4 r = (rot & 1) ? v[u].yzwx : v[u];
-        r = (rot & 2) ? r.zwxy : r;
-        u32x4 pw;
-        pw.x = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr[0], static_cast<int>(r.x)));
-        pw.y = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr[1], static_cast<int>(r.y)));
-        pw.z = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr[2], static_cast<int>(r.z)));
-        pw.w = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr[3], static_cast<int>(r.w)));
-        const int s = static_cast<int>(rope_slot<U>(0, threadIdx.x, u));
-        if (s < nslot) {
-          if (tl[u] != cur) {
-            entry_angles<PS>(cs + tl[u] * a.np, dd, dd1, half, an);
-            cur = tl[u];
-          }
-          float y[PS];
-#pragma unroll
-          for (int e = 0; e < PS; ++e) {
-            const uint32_t w = pw[e / EPD];
-            float xp;
-            if constexpr (EPD == 2) xp = (e & 1) ? E::hi(w) : E::lo(w);
-            else xp = __uint_as_float(w);
-            y[e] = __builtin_fmaf(E::get(v[u], e), an[e].x, xp * an[e].y);
-          }
-          out.store(isq[u], rel[u] + cv[u] * PS, rowp[u] + cv[u] * PS, E::pack(y));
-        }
-      }
-      return;
+    for (int j = 0; j < 4; ++j) {
+      const int off = EPD * j < krp ? offA : offB;
+      addr[j] = (rowlane + (c0 + EPD * j + off) / PS) * 4;
     }
+    float2 an[PS];
+    int cur = -1;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      u32x4 r = (rot & 1) ? v[u].yzwx : v[u];
+      r = (rot & 2) ? r.zwxy : r;
+      u32x4 pw;
+      pw.x = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr[0], static_cast<int>(r.x)));
+      pw.y = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr[1], static_cast<int>(r.y)));
+      pw.z = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr[2], static_cast<int>(r.z)));
+      pw.w = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr[3], static_cast<int>(r.w)));
+      const int s = static_cast<int>(rope_slot<U>(0, threadIdx.x, u));
+      if (s < nslot) {
+        if (tl[u] != cur) {
+          entry_angles<PS>(cs + tl[u] * a.np, dd, dd1, half, an);
+          cur = tl[u];
+        }
+        float y[PS];
+#pragma unroll
+        for (int e = 0; e < PS; ++e) {
+          const uint32_t w = pw[e / EPD];
+          float xp;
+          if constexpr (EPD == 2) xp = (e & 1) ? E::hi(w) : E::lo(w);
+          else xp = __uint_as_float(w);
+          y[e] = __builtin_fmaf(E::get(v[u], e), an[e].x, xp * an[e].y);
+        }
+        out.store(isq[u], rel[u] + cv[u] * PS, rowp[u] + cv[u] * PS, E::pack(y));
+      }
+    }
+    return;
   }
   if constexpr (PS > 1 && !PERM) {
     bool uni = static_cast<int>(rope_slot<U>(0, threadIdx.x, U - 1)) < nslot;
