@@ -854,6 +854,9 @@ et_status rope_cache_entry(const float* inv_freq, int64_t max_pos, int64_t r, fl
 // reads all of its rows before the barrier and writes after it, each
 // element by the thread that loaded it.  The host takes the scalar path when
 // some vector would hold more than two runs (axes narrower than a vector).
+// When the row's vectors fill whole lane groups and every 32-bit word's
+// partners are one word of another lane (perm_fits), a separate instance
+// takes the partners across lanes instead of from an LDS copy of the rows.
 
 constexpr int kMaxAxes = 8;
 constexpr int kMultiU = 4;
