@@ -370,10 +370,29 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32
 struct QkNormArgs {
   RopeArgs rope;      // fd_spt unused here
   float eps;
+  float inv_d;        // 1/D when D is a power of two (exact), else 0
   uint32_t rows;      // head rows in the call (T * (Hq + Hk))
   FastDiv fd_heads;   // divide by Hq + Hk
   int rsl;            // rotated slots per head row (r / (2V))
 };
+
+// 1/sqrt(ss/D + eps) of a head row's sum of squares.  The mean square is a
+// multiplication by 1/D when D is a power of two (the same correctly rounded
+// value as the division).  In the normal range the inverse root is the
+// hardware estimate (within 1 ulp) refined by one Newton step,
+// y (1.5 - 0.5 m y^2) with fused multiply-adds, which leaves it within about
+// 1 ulp like the correctly rounded root and division it replaces, at a
+// fraction of their instructions.  Zero, subnormal, huge, infinite and NaN
+// arguments take the IEEE root and division, so those keep their exact
+// results (1/0 = inf, 1/inf = 0, NaN).
+__device__ inline float inv_rms(float ss, const QkNormArgs& a) {
+  const float m = (a.inv_d > 0.0f ? ss * a.inv_d : ss / static_cast<float>(a.rope.D)) + a.eps;
+  if (__builtin_expect(m >= 0x1p-126f && m <= 0x1p+126f, 1)) {
+    const float y = __builtin_amdgcn_rsqf(m);
+    return __builtin_fmaf(y, __builtin_fmaf(-0.5f * m * y, y, 0.5f), y);
+  }
+  return 1.0f / sqrtf(m);
+}
 
 // Vector path: G lanes per head row, each owns two 16-byte vectors A and B.
 // Interleaved layout: A = vector kk, B = vector kk + G (element D/2 + kk*V),
@@ -433,11 +452,11 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
   }
 
   const QkOut<S> out(q, k, t0, static_cast<int>(base - t0 * heads), ra);
-  // The two gains (2G vectors each) go through LDS: thread t < 4G fetches
-  // vector t % 2G of gq (t < 2G) or gk, before the row loads so that its
-  // LDS write waits for nothing else.  (gk is gq when there are no key
-  // heads: the host passes it so.)
-  __shared__ u32x4 gsh[4 * G];
+  // The two gains (2G vectors each) go through LDS, widened to f32 once per
+  // workgroup: thread t < 4G fetches vector t % 2G of gq (t < 2G) or gk,
+  // before the row loads so that its LDS write waits for nothing else.  (gk
+  // is gq when there are no key heads: the host passes it so.)
+  __shared__ float gsh[4 * G * V];
   const int gi = threadIdx.x < 4 * G ? static_cast<int>(threadIdx.x) : 4 * G - 1;
   const u32x4 gv = ld16_keep(gi < 2 * G ? gq : gk, (gi % (2 * G)) * V);
   S* rowp[U];
@@ -460,9 +479,11 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
   }
   __builtin_amdgcn_sched_barrier(0);  // table inputs are used only below
 
-  if (threadIdx.x < 4 * G) gsh[threadIdx.x] = gv;
+  if (threadIdx.x < 4 * G) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) gsh[threadIdx.x * V + e] = E::get(gv, e);
+  }
   if constexpr (ROT) table_fill(cs, tin, t0, ntok, ra, pos, inv_freq);
-  __syncthreads();
 
   // Sums of squares of all U rows first, so their butterflies interleave.
   float inv[U];
@@ -484,17 +505,20 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
 #pragma unroll
   for (int u = 0; u < U; ++u) inv[u] = group_sum<G>(inv[u]);
 #pragma unroll
-  for (int u = 0; u < U; ++u) inv[u] = 1.0f / sqrtf(inv[u] / static_cast<float>(ra.D) + a.eps);
+  for (int u = 0; u < U; ++u) inv[u] = inv_rms(inv[u], a);
+  // The barrier after the norm statistics: a wave whose rows arrived early
+  // finishes them while the workgroup's table and gains are completed.
+  __syncthreads();
 
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     float xa[V], xb[V];
-    const u32x4 ga = gsh[(isq[u] ? 0 : 2 * G) + ea / V];
-    const u32x4 gb = gsh[(isq[u] ? 0 : 2 * G) + eb / V];
+    const float* ga = gsh + ((isq[u] ? 0 : 2 * G) + ea / V) * V;
+    const float* gb = gsh + ((isq[u] ? 0 : 2 * G) + eb / V) * V;
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      xa[e] = E::get(va[u], e) * inv[u] * E::get(ga, e);
-      xb[e] = E::get(vb[u], e) * inv[u] * E::get(gb, e);
+      xa[e] = E::get(va[u], e) * inv[u] * ga[e];
+      xb[e] = E::get(vb[u], e) * inv[u] * gb[e];
     }
     const float2* tab = cs + tl[u] * ra.half;  // this token's (mu cos, mu sin)
     if (!ROT) {
@@ -554,7 +578,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_wave_kernel(
     ss = __builtin_fmaf(x, x, ss);
   }
   ss = group_sum<64>(ss);
-  const float inv = 1.0f / sqrtf(ss / static_cast<float>(ra.D) + a.eps);
+  const float inv = inv_rms(ss, a);
   const int32_t p = ra.half > 0 ? pos[t] : 0;  // pos may be NULL when nothing rotates
   for (int i = lane; i < ra.half; i += 64) {
     int ia, ib;
@@ -755,6 +779,7 @@ et_status qknorm_entry(S* q, const S* gq, int64_t hq, S* k, const S* gk, int64_t
   hipStream_t s = static_cast<hipStream_t>(stream);
   QkNormArgs a{};
   a.eps = eps;
+  a.inv_d = (D & (D - 1)) == 0 ? 1.0f / static_cast<float>(D) : 0.0f;
   const int64_t heads = hq + hk;
   a.fd_heads = make_fastdiv(static_cast<uint32_t>(heads));
   const int64_t g = D / (2 * V);
