@@ -468,3 +468,46 @@ def test_rmsnorm_rope_past_the_f32_range(et, orc, dt, layout):
     assert_pair(got[:, fin], y64[:, fin], ref[:, fin], r, layout, f"{dt} layout={layout}")
     assert_close(got[..., r:], y64[..., r:], ref[..., r:], f"{dt} tail")
     assert np.all(widen(got[:, :2]) == 0)
+
+
+def _root_range_rows(D, g):
+    """Head rows whose mean square (eps = 0) falls on each side of the range
+    in which the fused kernel takes the hardware inverse root: a single
+    nonzero entry 2^-62 and 2^-60 (mean square subnormal), 1.5 * 2^-60 and
+    2^-59 (just above the smallest normal), 2^60, a plain row, and a zero row
+    (mean square 0: 0 * inf = NaN, the literal formula)."""
+    rows = np.zeros((7, D), np.float32)
+    for i, a in enumerate([2.0 ** -62, 2.0 ** -60, 1.5 * 2.0 ** -60, 2.0 ** -59, 2.0 ** 60]):
+        rows[i, 0] = a
+    rows[5] = g.standard_normal(D)
+    return rows
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("D,r", [(128, 128), (128, 64), (130, 128)])
+@pytest.mark.parametrize("layout", [0, 1])
+def test_rmsnorm_rope_inverse_root_ranges(et, orc, dt, D, r, layout):
+    """Fused RMSNorm+RoPE with mean squares at the edges of the hardware
+    inverse root's range (subnormal, just normal, zero) and, through a huge
+    eps, above 2^126; D = 130 takes the one-wave-per-row kernel and the
+    division by D.  Equal to the oracle within the pair tolerance, NaN where
+    the formula gives NaN."""
+    g = _rng(43, D, r, layout, DTS.index(dt))
+    pos = np.array([0, 3], np.int32)
+    inv = wl.inv_freq(1e4, r)
+    gq = _store(g.uniform(0.5, 1.5, D).astype(np.float32), dt)
+    for eps, rows in ((0.0, _root_range_rows(D, g)),
+                      (1e38, g.standard_normal((3, D)).astype(np.float32) * 1e18),
+                      (8e37, g.standard_normal((3, D)).astype(np.float32))):
+        q = _store(np.broadcast_to(rows, (2,) + rows.shape).copy(), dt)
+        qt = dev(q)
+        et.rmsnorm_rope_qk(qt, dev(gq), None, None, eps, dev(pos), dev(inv), d_rot=r, layout=layout)
+        ref, y64 = orc.rmsnorm_rope(q, gq, eps, pos, r, inv, 1.0, layout)
+        got = host(qt)
+        what = f"{dt} D={D} r={r} layout={layout} eps={eps}"
+        nan = np.isnan(y64)
+        assert np.array_equal(np.isnan(widen(got)), nan), f"{what}: NaN positions"
+        fin = [h for h in range(rows.shape[0]) if not nan[:, h].any()]
+        assert len(fin) == rows.shape[0] - (1 if eps == 0.0 else 0)
+        assert_pair(got[:, fin], y64[:, fin], ref[:, fin], r, layout, what)
+        assert_close(got[:, fin, r:], y64[:, fin, r:], ref[:, fin, r:], f"{what} tail")
