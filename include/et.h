@@ -221,6 +221,9 @@ et_status et_rope_multi_f16(et_f16* q, int64_t Hq, et_f16* k, int64_t Hk,
  *   with the gain gq [D] (query heads) or gk [D] (key heads) and eps, then
  *   rotated as et_rope_qk_* on its first d_rot entries; the f32
  *   intermediate is not rounded; entries d_rot..D-1 are normalised only.
+ *   The inverse root 1/sqrt(ss/D + eps) is the hardware estimate refined by
+ *   one Newton step (within about 1 ulp) for mean squares in
+ *   [2^-126, 2^126], the correctly rounded root and division outside it.
  *   q: [T, Hq, D]; k: [T, Hk, D] (NULL with Hk == 0; gk may then be NULL).
  */
 et_status et_rmsnorm_rope_qk_f32(float* q, const float* gq, int64_t Hq,
