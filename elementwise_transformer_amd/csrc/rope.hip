@@ -1110,21 +1110,41 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
   S* rowp[U];
   u32x4 v[U];
   float sv[U];
+  // Cross-lane instance: nv divides 64, so it is a power of two, a lane keeps
+  // one column for all its slots, and slot u lies u * 64 / nv rows below
+  // slot 0.  Rows past the workgroup's are clamped to its last row (loaded,
+  // never stored; their lanes only feed each other's partner reads).
+  const int lg_nv = PERM ? __builtin_ctz(static_cast<unsigned>(a.nv)) : 0;
+  const int s0 = static_cast<int>(rope_slot<U>(0, threadIdx.x, 0));
+  const int last_row = static_cast<int>(row_end - row0) - 1;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    int s = static_cast<int>(rope_slot<U>(0, threadIdx.x, u));
-    if (s >= nslot) s = nslot - 1;  // clamped: loaded, never stored
-    const int r = static_cast<int>(fdiv(static_cast<uint32_t>(s), a.fd_nv));
+    int r;
+    if constexpr (PERM) {
+      r = (s0 >> lg_nv) + u * (64 >> lg_nv);
+      if (r > last_row) r = last_row;
+      cv[u] = s0 & (a.nv - 1);
+    } else {
+      int s = static_cast<int>(rope_slot<U>(0, threadIdx.x, u));
+      if (s >= nslot) s = nslot - 1;  // clamped: loaded, never stored
+      r = static_cast<int>(fdiv(static_cast<uint32_t>(s), a.fd_nv));
+      cv[u] = s - r * a.nv;
+    }
     sl[u] = r;
-    cv[u] = s - r * a.nv;
     const uint32_t g = row0 + r;
     const uint32_t t = fdiv(g, a.fd_heads);
     const int hh = static_cast<int>(g - t * a.heads);
     tl[u] = static_cast<int>(t - t0);
     isq[u] = hh < a.ra.hq;
-    rowp[u] = isq[u] ? q + (static_cast<int64_t>(t) * a.ra.hq + hh) * a.ra.D
-                     : k + (static_cast<int64_t>(t) * a.ra.hk + (hh - a.ra.hq)) * a.ra.D;
-    rel[u] = out.rel(t, hh, a.ra);
+    // Row index within q or k: a launch holds fewer than 2^30 head rows, so
+    // it is a 32-bit value, the address one 32 x 32 + 64-bit multiply-add,
+    // and the store offset (below 2^31 bytes) a 32-bit product.
+    const uint32_t ri = isq[u] ? t * static_cast<uint32_t>(a.ra.hq) + static_cast<uint32_t>(hh)
+                               : t * static_cast<uint32_t>(a.ra.hk) + static_cast<uint32_t>(hh - a.ra.hq);
+    rowp[u] = reinterpret_cast<S*>(reinterpret_cast<char*>(isq[u] ? q : k) +
+                                   static_cast<uint64_t>(ri) * static_cast<uint32_t>(a.ra.D * sizeof(S)));
+    rel[u] = static_cast<int>((ri - static_cast<uint32_t>(isq[u] ? out.qrow0 : out.krow0)) *
+                              static_cast<uint32_t>(a.ra.D));
     if constexpr (PS == 1) sv[u] = E::ld(rowp[u], cv[u]);
     else v[u] = ld16(rowp[u], static_cast<int64_t>(cv[u]) * PS);
   }
@@ -1194,13 +1214,16 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
     const int krp = dd1 & 0xFF;
     const int c0 = cv[0] * PS;
     const int offA = dd.x - c0, offB = dd.y - c0;
-    const int rot = ((-offA) / EPD) & 3;
+    // offA is a whole number of words (the host checks it), and a partner
+    // column is never negative: both quotients are plain shifts.
+    constexpr int kLgEpd = EPD == 2 ? 1 : 0;
+    const int rot = ((-offA) >> kLgEpd) & 3;
     const int rowlane = static_cast<int>(threadIdx.x % 64) - cv[0];
     int addr[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int off = EPD * j < krp ? offA : offB;
-      addr[j] = (rowlane + (c0 + EPD * j + off) / PS) * 4;
+      addr[j] = (rowlane + static_cast<int>(static_cast<unsigned>(c0 + EPD * j + off) / PS)) * 4;
     }
     float2 an[PS];
     int cur = -1;
