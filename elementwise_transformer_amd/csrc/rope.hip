@@ -251,10 +251,19 @@ struct QkOut {
     rq = out_rsrc(q + qrow0 * a.D, (a.T * a.hq - qrow0) * a.D * es);
     rk = out_rsrc(a.hk > 0 ? k + krow0 * a.D : q, a.hk > 0 ? (a.T * a.hk - krow0) * a.D * es : 0);
   }
-  // Element offset of head h of token t from its resource's base.
-  __device__ int rel(int64_t t, int hh, const RopeArgs& a) const {
-    return hh < a.hq ? static_cast<int>((t * a.hq + hh - qrow0) * a.D)
-                     : static_cast<int>((t * a.hk + (hh - a.hq) - krow0) * a.D);
+  // Address of head row (t, hh) of the launch (a query row for hh < hq, else
+  // a key row), and in *rel its element offset from this workgroup's
+  // resource base.  A launch holds fewer than 2^31 head rows, so the row
+  // index is a 32-bit value and the address one 32 x 32 + 64-bit
+  // multiply-add; the offset is below 2^31 bytes, a 32-bit product.
+  __device__ S* row(S* q, S* k, uint32_t t, int hh, const RopeArgs& a, int* rel_out) const {
+    const bool isq = hh < a.hq;
+    const uint32_t ri = isq ? t * static_cast<uint32_t>(a.hq) + static_cast<uint32_t>(hh)
+                            : t * static_cast<uint32_t>(a.hk) + static_cast<uint32_t>(hh - a.hq);
+    *rel_out = static_cast<int>((ri - static_cast<uint32_t>(isq ? qrow0 : krow0)) *
+                                static_cast<uint32_t>(a.D));
+    return reinterpret_cast<S*>(reinterpret_cast<char*>(isq ? q : k) +
+                                static_cast<uint64_t>(ri) * static_cast<uint32_t>(a.D * sizeof(S)));
   }
   // Store v at element `elem` of the q or k rows (relative to this
   // workgroup's resource base); p is the same element's address.  A buffer
@@ -308,9 +317,7 @@ __global__ __launch_bounds__(kBlock) void rope_qk_kernel(S* q, S* k, const int32
     kk[u] = static_cast<int>(rem - hh * a.sph);
     tl[u] = static_cast<int>(t - t0);
     isq[u] = static_cast<int>(hh) < a.hq;
-    rowp[u] = isq[u] ? q + (static_cast<int64_t>(t) * a.hq + hh) * a.D
-                     : k + (static_cast<int64_t>(t) * a.hk + (hh - a.hq)) * a.D;
-    rel[u] = out.rel(t, static_cast<int>(hh), a);
+    rowp[u] = out.row(q, k, t, static_cast<int>(hh), a, &rel[u]);
     slot_offsets<PS>(kk[u], a, &ea[u], &eb[u]);
     if constexpr (PS == 1) {
       sa[u] = E::ld(rowp[u], ea[u]);
@@ -471,9 +478,7 @@ __global__ __launch_bounds__(kBlock) void rmsnorm_rope_kernel(S* q, const S* __r
     const int hh = static_cast<int>(hr - t * heads);
     tl[u] = static_cast<int>(t - t0);
     isq[u] = hh < ra.hq;
-    rowp[u] = isq[u] ? q + (static_cast<int64_t>(t) * ra.hq + hh) * ra.D
-                     : k + (static_cast<int64_t>(t) * ra.hk + (hh - ra.hq)) * ra.D;
-    rel[u] = out.rel(t, hh, ra);
+    rowp[u] = out.row(q, k, t, hh, ra, &rel[u]);
     va[u] = ld16(rowp[u], ea);
     vb[u] = ld16(rowp[u], eb);
   }
@@ -1136,15 +1141,7 @@ __global__ __launch_bounds__(kBlock) void rope_multi_kernel(S* q, S* k,
     const int hh = static_cast<int>(g - t * a.heads);
     tl[u] = static_cast<int>(t - t0);
     isq[u] = hh < a.ra.hq;
-    // Row index within q or k: a launch holds fewer than 2^30 head rows, so
-    // it is a 32-bit value, the address one 32 x 32 + 64-bit multiply-add,
-    // and the store offset (below 2^31 bytes) a 32-bit product.
-    const uint32_t ri = isq[u] ? t * static_cast<uint32_t>(a.ra.hq) + static_cast<uint32_t>(hh)
-                               : t * static_cast<uint32_t>(a.ra.hk) + static_cast<uint32_t>(hh - a.ra.hq);
-    rowp[u] = reinterpret_cast<S*>(reinterpret_cast<char*>(isq[u] ? q : k) +
-                                   static_cast<uint64_t>(ri) * static_cast<uint32_t>(a.ra.D * sizeof(S)));
-    rel[u] = static_cast<int>((ri - static_cast<uint32_t>(isq[u] ? out.qrow0 : out.krow0)) *
-                              static_cast<uint32_t>(a.ra.D));
+    rowp[u] = out.row(q, k, t, hh, a.ra, &rel[u]);
     if constexpr (PS == 1) sv[u] = E::ld(rowp[u], cv[u]);
     else v[u] = ld16(rowp[u], static_cast<int64_t>(cv[u]) * PS);
   }
