@@ -170,3 +170,16 @@ def test_counters_scaled_and_traffic_lookup(tmp_path, monkeypatch):
     # once the kernel's source changes, the committed counters no longer apply
     (src / "eltwise.hip").write_text("kernel v2\n")
     assert bench.traffic_record("w5/silu_mul") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py --gpus N > 1 exits with a message (one GPU only) before
+    touching a device."""
+    import json
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
