@@ -241,6 +241,13 @@ def _stats(t_ms, nbytes, rows=None):
            "p10_us": round(float(np.percentile(t, 10)) * 1e3, 2),
            "p90_us": round(float(np.percentile(t, 90)) * 1e3, 2),
            "samples": int(t.size), "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_GBPS, 4)}
+    if t.size >= 40:
+        # Launches back to back can slow as the GPU's clock drops under
+        # sustained load: the first 20 launches' mean and the slowest mean of
+        # 20 consecutive launches show it.
+        blocks = [float(np.mean(t[j:j + 20])) for j in range(0, t.size - 19, 20)]
+        rec["first20_us"] = round(blocks[0] * 1e3, 2)
+        rec["slowest20_us"] = round(max(blocks) * 1e3, 2)
     if rows:
         rec["rows_per_s"] = float(f"{rows / (avg * 1e-3):.4g}")
     return rec
