@@ -156,6 +156,31 @@ __device__ inline float gelu_erf_tail(float x, float u) {
   return x == -__builtin_inff() ? __builtin_nanf("") : r;
 }
 
+// The exact form over one vector of W elements: the one-exp2 evaluation of
+// every element first, then the tail, for the elements that need it, in one
+// branch per vector instead of one per element (the same results element by
+// element: the tail replaces exactly the elements gelu_erf_mul sends to it).
+template <typename S, int W>
+__device__ inline void gelu_erf_mul_vec(const float (&x)[W], const float (&u)[W], float (&o)[W]) {
+  float k[W];
+  bool tail = false;
+#pragma unroll
+  for (int e = 0; e < W; ++e) {
+    const float ap = __builtin_fabsf(x[e]) * kGeluA;
+    const float t8 = __builtin_amdgcn_rcpf(__builtin_fmaf(kGeluT, ap, 8.0f));
+    const float p = sizeof(S) == 4 ? erfc_exp2_poly9(t8) : erfc_exp2_poly5(t8);
+    k[e] = __builtin_fmaf(-ap, ap, p);
+    tail = tail || k[e] < -100.0f;
+    const float q = t8 * __builtin_amdgcn_exp2f(k[e]);           // Phi(-|x|)
+    o[e] = x[e] <= 0.0f ? x[e] * q * u[e] : x[e] * (1.0f - q) * u[e];
+  }
+  if (tail) {
+#pragma unroll
+    for (int e = 0; e < W; ++e)
+      if (k[e] < -100.0f) o[e] = gelu_erf_tail<S>(x[e], u[e]);
+  }
+}
+
 // GELU, tanh form: (1 + tanh u) / 2 = 1 / (1 + e^(-2u)) with
 // u = sqrt(2/pi) (x + 0.044715 x^3), so it is x / (1 + e^(-2u)) -- the SiLU
 // shape, computed the same way (library expf and IEEE division in f32; the
@@ -208,8 +233,18 @@ __global__ __launch_bounds__(kBlock) void eltwise_vec(const S* a, const S* b, S*
     for (int u = 0; u < kU; ++u) {
       const int64_t j = slot_index(blk, threadIdx.x, u);
       float o[V];
+      if constexpr (OP == kGeluErfMul) {
+        float xa[V], xb[V];
 #pragma unroll
-      for (int e = 0; e < V; ++e) o[e] = apply<S, OP>(E::get(av[u], e), E::get(bv[u], e));
+        for (int e = 0; e < V; ++e) {
+          xa[e] = E::get(av[u], e);
+          xb[e] = E::get(bv[u], e);
+        }
+        gelu_erf_mul_vec<S, V>(xa, xb, o);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) o[e] = apply<S, OP>(E::get(av[u], e), E::get(bv[u], e));
+      }
       if (j < nvec) st16_buf(ry, static_cast<int>((j - vbase) * 16), E::pack(o));
     }
   }
